@@ -1,0 +1,204 @@
+/*
+ * Scalar CPU oracle for the clipped, mixed-precision AdamW step on one
+ * GPU's parameter shard.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library never
+ * links, includes or calls it, and it shares no source with that library.
+ *
+ * What it computes, and where that comes from:
+ *   - "TorchTitan: a one-stop PyTorch-native solution for production LLM
+ *     pre-training" (zenmind digest), section 3.3 (mixed-precision bullet)
+ *     and section 4, steps 5 and 7: parameters are gathered and used in
+ *     BF16, gradients are reduce-scattered in FP32, and the sharded optimizer
+ *     state is updated in FP32.  Hence the update arithmetic below is fp32.
+ *   - Lecture 9 exercises page, answer deriving the 16N state accounting and
+ *     its three-basis table: bf16 params (2N) and grads (2N), fp32 m and v
+ *     (8N), fp32 master weights (4N); the pure-fp32 basis has fp32 grads and
+ *     no separate master.  Hence: grads arrive as bf16 or fp32, m, v and the
+ *     master are fp32, and the bf16 parameter is a rounded copy of the master.
+ *   - The same page's ZeRO-2 + AdamW scenario answer names AdamW with bf16
+ *     params and grads, an fp32 master and no loss scaling.
+ *
+ * The pages give no AdamW formula, no eps placement, no clipping rule and no
+ * summation precision.  The readings taken here (all listed in the design
+ * notes):
+ *   - AdamW with decoupled, multiplicative weight decay applied to the
+ *     pre-update master, and Adam's bias corrections; eps is added to the
+ *     bias-corrected sqrt(v).
+ *   - Global-norm clipping: c = min(1, max_norm / (||g|| + 1e-6)), with the
+ *     norm over every gradient of the call; c scales the gradient in fp32
+ *     inside the update.
+ *   - The norm is accumulated in fp64 (each product g*g is exact in fp64),
+ *     sequentially in list order.
+ *   - Derived scalars are formed in fp64 from the hyperparameters and rounded
+ *     once to fp32; beta^t by binary exponentiation.
+ *   - Each fp32 operation rounds once (build with -ffp-contract=off, no
+ *     fast-math), in the order written below.
+ *   - bf16 copy: round to nearest, ties to even; NaN stays a NaN of the same
+ *     sign with the quiet bit set.
+ *
+ * Parity status: every function here is pinned by CPU tests against library
+ * routines, closed forms, exact rational arithmetic or brute force.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- bf16 --- */
+
+/* bf16 is the upper half of an IEEE binary32 word; widening is exact. */
+float oracle_bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Narrow binary32 to bf16 by round-to-nearest, ties to even. */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u) {
+        /* NaN: keep sign and the top payload bits, force the quiet bit. */
+        return (uint16_t)((u >> 16) | 0x0040u);
+    }
+    uint32_t kept = u >> 16;
+    uint32_t dropped = u & 0xffffu;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) {
+        kept += 1u; /* may carry into the exponent, up to infinity */
+    }
+    return (uint16_t)kept;
+}
+
+void oracle_f32_to_bf16_array(const float* x, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16(x[i]);
+}
+
+/* ------------------------------------------------------------ grad norm --- */
+
+/* Continue the running fp64 sum of squares `acc` over one fp32 gradient. */
+double oracle_sumsq_f32(const float* g, int64_t n, double acc)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double x = (double)g[i];
+        acc = acc + x * x;
+    }
+    return acc;
+}
+
+/* Same for a bf16 gradient. */
+double oracle_sumsq_bf16(const uint16_t* g, int64_t n, double acc)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double x = (double)oracle_bf16_to_f32(g[i]);
+        acc = acc + x * x;
+    }
+    return acc;
+}
+
+/* ----------------------------------------------------------------- clip --- */
+
+/* c = min(1, max_norm / (sqrt(S) + 1e-6)) in fp64, rounded once to fp32.
+ * The comparison is written so that a NaN norm gives a NaN coefficient and
+ * an infinite norm gives 0. */
+float oracle_clip_coef(double sumsq, double max_norm)
+{
+    double norm = sqrt(sumsq);
+    double c = max_norm / (norm + 1e-6);
+    if (c > 1.0) c = 1.0;
+    return (float)c;
+}
+
+/* ------------------------------------------------------- step scalars --- */
+
+typedef struct {
+    float beta1;      /* b1                                  */
+    float beta2;      /* b2                                  */
+    float one_m_b1;   /* 1 - b1                              */
+    float one_m_b2;   /* 1 - b2                              */
+    float decay;      /* 1 - lr * wd                         */
+    float step_size;  /* lr / (1 - b1^t)                     */
+    float bc2_sqrt;   /* sqrt(1 - b2^t)                      */
+    float eps;        /* eps                                 */
+} oracle_scalars;
+
+/* beta^t by binary exponentiation, low bit first. */
+double oracle_pow_int(double beta, int64_t t)
+{
+    double r = 1.0;
+    double b = beta;
+    while (t > 0) {
+        if (t & 1) r = r * b;
+        b = b * b;
+        t >>= 1;
+    }
+    return r;
+}
+
+void oracle_step_scalars(int64_t t, double lr, double beta1, double beta2,
+                         double eps, double wd, oracle_scalars* s)
+{
+    double p1 = oracle_pow_int(beta1, t);
+    double p2 = oracle_pow_int(beta2, t);
+    s->beta1 = (float)beta1;
+    s->beta2 = (float)beta2;
+    s->one_m_b1 = (float)(1.0 - beta1);
+    s->one_m_b2 = (float)(1.0 - beta2);
+    s->decay = (float)(1.0 - lr * wd);
+    s->step_size = (float)(lr / (1.0 - p1));
+    s->bc2_sqrt = (float)sqrt(1.0 - p2);
+    s->eps = (float)eps;
+}
+
+/* ---------------------------------------------------------------- update --- */
+
+/* One element of the step.  `g_raw` is the unclipped gradient widened to
+ * fp32; every line is one correctly rounded fp32 operation. */
+static void oracle_update_one(float* w, float* m, float* v, float g_raw,
+                              float c, const oracle_scalars* s)
+{
+    float g = g_raw * c;
+
+    float m_old = s->beta1 * *m;
+    float m_in = s->one_m_b1 * g;
+    float m_new = m_old + m_in;
+
+    float v_old = s->beta2 * *v;
+    float g2 = g * g;
+    float v_in = s->one_m_b2 * g2;
+    float v_new = v_old + v_in;
+
+    float root = sqrtf(v_new);
+    float root_hat = root / s->bc2_sqrt;
+    float den = root_hat + s->eps;
+
+    float w_decayed = *w * s->decay;
+    float ratio = m_new / den;
+    float delta = s->step_size * ratio;
+    float w_new = w_decayed - delta;
+
+    *m = m_new;
+    *v = v_new;
+    *w = w_new;
+}
+
+/* The step over one tensor.  grad_is_bf16 selects the gradient's type
+ * (uint16_t bf16 words or float).  param_bf16 may be NULL (no copy). */
+void oracle_adamw_step(float* master, float* exp_avg, float* exp_avg_sq,
+                       const void* grad, int grad_is_bf16, uint16_t* param_bf16,
+                       int64_t n, float clip, int64_t t, double lr,
+                       double beta1, double beta2, double eps, double wd)
+{
+    oracle_scalars s;
+    oracle_step_scalars(t, lr, beta1, beta2, eps, wd, &s);
+    for (int64_t i = 0; i < n; ++i) {
+        float g = grad_is_bf16 ? oracle_bf16_to_f32(((const uint16_t*)grad)[i])
+                               : ((const float*)grad)[i];
+        oracle_update_one(&master[i], &exp_avg[i], &exp_avg_sq[i], g, clip, &s);
+        if (param_bf16) param_bf16[i] = oracle_f32_to_bf16(master[i]);
+    }
+}

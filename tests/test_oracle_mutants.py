@@ -1,0 +1,65 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+Each mutant is oracle.c with one textual change (a dropped term, a wrong
+coefficient, sign or index, a skipped rounding rule), built with the same
+flags into a temporary library.  This shows the pins in oracle_pins.py are
+strong enough that a plausible slip anywhere in the oracle is caught.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+from oracle_pins import ALL_PINS
+
+MUTANTS = {
+    "m_uses_beta2": ("float m_old = s->beta1 * *m;", "float m_old = s->beta2 * *m;"),
+    "v_uses_g_not_g2": ("float v_in = s->one_m_b2 * g2;", "float v_in = s->one_m_b2 * g;"),
+    "no_bias_correction_2": ("float root_hat = root / s->bc2_sqrt;", "float root_hat = root;"),
+    "no_eps": ("float den = root_hat + s->eps;", "float den = root_hat;"),
+    "no_weight_decay": ("float w_decayed = *w * s->decay;", "float w_decayed = *w;"),
+    "update_sign": ("float w_new = w_decayed - delta;", "float w_new = w_decayed + delta;"),
+    "clip_ignored": ("float g = g_raw * c;", "float g = g_raw;"),
+    "norm_sums_values": ("acc = acc + x * x;\n    }\n    return acc;\n}\n\n/* Same for a bf16",
+                         "acc = acc + x;\n    }\n    return acc;\n}\n\n/* Same for a bf16"),
+    "clip_no_clamp": ("if (c > 1.0) c = 1.0;", ""),
+    "clip_no_epsilon": ("double c = max_norm / (norm + 1e-6);", "double c = max_norm / norm;"),
+    "step_size_no_correction": ("s->step_size = (float)(lr / (1.0 - p1));",
+                                "s->step_size = (float)lr;"),
+    "decay_ignores_lr": ("s->decay = (float)(1.0 - lr * wd);", "s->decay = (float)(1.0 - wd);"),
+    "power_off_by_one": ("while (t > 0) {", "t += 1;\n    while (t > 0) {"),
+    "bf16_truncates": ("kept += 1u;", "kept += 0u;"),
+    "bf16_ties_away": ("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)"),
+    "bf16_grad_decode": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
+    "copy_of_old_master": (
+        "oracle_update_one(&master[i], &exp_avg[i], &exp_avg_sq[i], g, clip, &s);\n"
+        "        if (param_bf16) param_bf16[i] = oracle_f32_to_bf16(master[i]);",
+        "if (param_bf16) param_bf16[i] = oracle_f32_to_bf16(master[i]);\n"
+        "        oracle_update_one(&master[i], &exp_avg[i], &exp_avg_sq[i], g, clip, &s);"),
+    "moment_order_swapped": ("*m = m_new;\n    *v = v_new;", "*m = v_new;\n    *v = m_new;"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle_build.SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, source, tmp_path):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation anchor for {name} not unique in oracle.c"
+    src = tmp_path / "oracle_mutant.c"
+    src.write_text(source.replace(old, new))
+    lib = oracle_build.build(str(src), str(tmp_path / "liboracle_mutant.so"))
+    o = oracle.Oracle(lib)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(o)
+        except (AssertionError, ValueError, OverflowError, ZeroDivisionError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
+    os.remove(lib)
