@@ -1,0 +1,239 @@
+"""Throughput of the fused, clipped, mixed-precision AdamW step on one GPU.
+
+A step is one pass of the whole path over one shard: grad_norm_sq (sum of
+g^2), clip_coef, adamw_multi_tensor_step (update + optional bf16 copy + step
+counter), all on one stream, inputs resident in HBM.  Prints ONE JSON line:
+params updated per second (value), the step's algorithmic GB/s, and for the
+dominant kernel (the update) its roofline against MI355X's 8 TB/s HBM peak,
+timed live with events on the launch stream; plus the CPU oracle timed on a
+bounded sample on the host (single thread).
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--rotate R]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBPS = 8000.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "mixed_precision_sharded_amd", "csrc", "kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", type=int, default=2,
+                   help="workload 1..5 (default 2: Llama-3.1-8B FSDP2 shard at 128-way)")
+    p.add_argument("--rotate", type=int, default=1,
+                   help="cycle over this many independent buffer sets (cache-cold small shards)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="host time budget of the oracle baseline (0 = skip)")
+    p.add_argument("--no-kernel-events", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_digest():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def stored_traffic(workload_name):
+    """HBM bytes per update launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = table.get(workload_name)
+    if not rec or rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's shard only; multi-GPU runs are not part of this "
+              "build (the path needs one scalar all-reduce per step across ranks, see the "
+              "design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mixed_precision_sharded_amd import binding, synth
+    from mixed_precision_sharded_amd.configs import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.lib()  # fails loudly if the HIP library is missing
+
+    w = WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {w.cfg} {w.name}: {w.numel:,} params in {w.n_tensors} tensors, "
+        f"{'bf16' if w.grad_bf16 else 'fp32'} grads, copy={w.copy_bf16}, rotate={args.rotate}")
+
+    sets = []
+    for r in range(args.rotate):
+        cols = synth.workload_inputs(w, dev, cfg_key=w.cfg * 1000 + r if r else None)
+        tl = binding.TensorList(cols["master"], cols["exp_avg"], cols["exp_avg_sq"], cols["grad"],
+                                cols["param_bf16"])
+        sets.append((cols, tl))
+    sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+    coef = torch.zeros(1, dtype=torch.float32, device=dev)
+    step = torch.tensor([w.step - 1], dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    def one_step(tl, ev=None):
+        if ev is not None:
+            ev[0].record()
+        binding.grad_norm_sq(tl, sumsq)
+        if ev is not None:
+            ev[1].record()
+        binding.clip_coef(sumsq, w.max_norm, coef)
+        if ev is not None:
+            ev[2].record()
+        binding.adamw_multi_tensor_step(tl, coef, step, w.lr, w.beta1, w.beta2, w.eps,
+                                        w.weight_decay)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        one_step(sets[i % len(sets)][1])
+    torch.cuda.synchronize()
+
+    # Timed region: K whole steps back to back.
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        one_step(sets[i % len(sets)][1])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+
+    # Per-kernel durations: the same K steps again with events between the
+    # launches, on the stream the kernels run on.
+    kern_us = None
+    if not args.no_kernel_events:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            one_step(sets[i % len(sets)][1], evs[i])
+        torch.cuda.synchronize()
+        norm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+        clip_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+        upd_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+        kern_us = {"grad_norm_sq": norm_ms * 1e3, "clip_coef": clip_ms * 1e3,
+                   "adamw_multi_tensor_step": upd_ms * 1e3}
+
+    n = w.numel
+    step_bytes = w.algorithmic_bytes_per_param() * n
+    params_per_s = n / (ms_per_step * 1e-3)
+    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"{ms_per_step * 1e3:.1f} us/step, {params_per_s:.3e} params/s, {step_gbps:.0f} GB/s "
+        f"algorithmic ({step_gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s); host wall {wall:.3f} s")
+
+    roofline = None
+    if kern_us is not None:
+        upd_bytes = w.update_bytes_per_param() * n
+        achieved = upd_bytes / (kern_us["adamw_multi_tensor_step"] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "kernel": "adamw_step_kernel",
+                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": stored_traffic(w.name),
+                    "algorithmic_bytes_per_launch": upd_bytes,
+                    "avg_launch_us": round(kern_us["adamw_multi_tensor_step"], 2)}
+        log(f"kernels (us): " + ", ".join(f"{k} {v:.1f}" for k, v in kern_us.items()))
+
+    cpu = cpu_baseline(w, sets[0][0], args.cpu_seconds) if args.cpu_seconds > 0 else None
+
+    out = {
+        "metric": "params updated/sec and achieved HBM GB/s (fraction of peak) per AdamW step",
+        "value": params_per_s,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "params": n, "tensors": w.n_tensors,
+                   "grad_dtype": "bf16" if w.grad_bf16 else "f32", "bf16_copy": w.copy_bf16,
+                   "step": w.step, "algorithmic_bytes_per_param": w.algorithmic_bytes_per_param(),
+                   "buffer_sets": args.rotate, "parallelism": "one GPU's shard"},
+        "step_gbps": round(step_gbps, 1),
+        "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "kernel_us": kern_us,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, cols, budget_s):
+    """The oracle, untuned and single-threaded, on the host: the whole step
+    (norm, clip, update) over the first workload tensors that fit the time
+    budget, repeated until it is spent.  Scaled to params/s."""
+    import numpy as np
+
+    import oracle
+    from mixed_precision_sharded_amd.synth import to_numpy
+
+    o = oracle.default()
+    host = {k: [None if t is None else to_numpy(t).copy() for t in v] for k, v in cols.items()}
+    t_done = w.step
+    steps = 0
+    elems = 0
+    t0 = time.perf_counter()
+    while True:
+        S = o.grad_norm_sq(host["grad"])
+        c = o.clip_coef(S, w.max_norm)
+        for i in range(w.n_tensors):
+            o.adamw_step(host["master"][i], host["exp_avg"][i], host["exp_avg_sq"][i],
+                         host["grad"][i], host["param_bf16"][i], c, t_done, w.lr, w.beta1,
+                         w.beta2, w.eps, w.weight_decay)
+        t_done += 1
+        steps += 1
+        elems += w.numel
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    log(f"cpu oracle: {steps} steps of {w.numel:,} params in {dt:.2f} s")
+    return {"value": elems / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole {w.name} shard ({w.numel:,} params): norm + clip + update, "
+                      f"{steps} consecutive steps, 1 thread, {dt:.1f} s",
+            "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+if __name__ == "__main__":
+    main()

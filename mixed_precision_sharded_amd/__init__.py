@@ -1,0 +1,10 @@
+"""Fused, clipped, mixed-precision AdamW step for one GPU's shard (gfx950).
+
+The compute path is the HIP library libmps_adamw.so (C ABI in
+include/mps_adamw.h); `binding` marshals torch tensors into it.  `configs`
+and `synth` describe and generate the seeded synthetic workloads.  Importing
+the package does not load the library: the first call does, and raises if it
+is not built.
+"""
+from .binding import (MPS_DTYPE_BF16, MPS_DTYPE_F32, MpsError, TensorList,  # noqa: F401
+                      adamw_multi_tensor_step, clip_coef, grad_norm_sq, last_error)

@@ -1,0 +1,197 @@
+"""ctypes binding of libmps_adamw.so (C ABI in include/mps_adamw.h).
+
+Argument marshalling only: every step of the optimizer runs in the HIP
+kernels.  PyTorch supplies device memory and the stream.  If the library is
+not built, every call raises; there is no fallback.
+"""
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmps_adamw.so")
+
+MPS_OK = 0
+MPS_DTYPE_F32 = 0
+MPS_DTYPE_BF16 = 1
+WORKSPACE_ALIGN = 256
+
+
+class MpsTensor(ctypes.Structure):
+    """Mirror of `mps_tensor`."""
+    _fields_ = [
+        ("master", ctypes.c_void_p),
+        ("exp_avg", ctypes.c_void_p),
+        ("exp_avg_sq", ctypes.c_void_p),
+        ("grad", ctypes.c_void_p),
+        ("param_bf16", ctypes.c_void_p),
+        ("numel", ctypes.c_int64),
+    ]
+
+
+class MpsError(RuntimeError):
+    def __init__(self, code: int, where: str, message: str):
+        super().__init__(f"{where} failed with code {code}: {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m mixed_precision_sharded_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        L.adamw_workspace_bytes.restype = ctypes.c_size_t
+        L.adamw_workspace_bytes.argtypes = [ctypes.POINTER(MpsTensor), ctypes.c_int]
+        L.adamw_workspace_release.restype = ctypes.c_int
+        L.adamw_workspace_release.argtypes = [P]
+        L.grad_norm_sq.restype = ctypes.c_int
+        L.grad_norm_sq.argtypes = [ctypes.POINTER(MpsTensor), ctypes.c_int, ctypes.c_int,
+                                   P, P, ctypes.c_size_t, P]
+        L.clip_coef.restype = ctypes.c_int
+        L.clip_coef.argtypes = [P, ctypes.c_double, P, P]
+        L.adamw_multi_tensor_step.restype = ctypes.c_int
+        L.adamw_multi_tensor_step.argtypes = [
+            ctypes.POINTER(MpsTensor), ctypes.c_int, ctypes.c_int, P, P,
+            ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+            ctypes.c_double, P, ctypes.c_size_t, P]
+        L.adamw_last_error.restype = ctypes.c_char_p
+        L.adamw_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().adamw_last_error().decode()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != MPS_OK:
+        raise MpsError(rc, where, last_error())
+
+
+def _stream_handle(stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+class TensorList:
+    """A host array of `mps_tensor` records built from torch tensors, plus a
+    device workspace sized for it.  Holds references to every tensor, so the
+    buffers outlive the calls that use them.
+
+    masters, exp_avgs, exp_avg_sqs: fp32 CUDA tensors; grads: fp32 or bf16
+    (one dtype for the whole list); params_bf16: bf16 tensors or None entries.
+    Each tensor must be contiguous; its storage offset may be anything.
+    """
+
+    def __init__(self, masters: Sequence[torch.Tensor], exp_avgs: Sequence[torch.Tensor],
+                 exp_avg_sqs: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
+                 params_bf16: Optional[Sequence[Optional[torch.Tensor]]] = None):
+        n = len(masters)
+        if not (len(exp_avgs) == len(exp_avg_sqs) == len(grads) == n) or n == 0:
+            raise ValueError("masters, exp_avgs, exp_avg_sqs and grads: same non-zero length")
+        if params_bf16 is None:
+            params_bf16 = [None] * n
+        if len(params_bf16) != n:
+            raise ValueError("params_bf16 must have one entry per tensor")
+        gdt = grads[0].dtype
+        if gdt not in (torch.float32, torch.bfloat16):
+            raise TypeError("grads must be float32 or bfloat16")
+        self.grad_dtype = MPS_DTYPE_BF16 if gdt == torch.bfloat16 else MPS_DTYPE_F32
+        self.device = masters[0].device
+        self.array = (MpsTensor * n)()
+        for i in range(n):
+            w, m, v, g, p = masters[i], exp_avgs[i], exp_avg_sqs[i], grads[i], params_bf16[i]
+            k = w.numel()
+            for name, t, dt in (("master", w, torch.float32), ("exp_avg", m, torch.float32),
+                                ("exp_avg_sq", v, torch.float32), ("grad", g, gdt)):
+                _require(t, dt, k, self.device, f"{name}[{i}]")
+            if p is not None:
+                _require(p, torch.bfloat16, k, self.device, f"param_bf16[{i}]")
+            self.array[i] = MpsTensor(_ptr(w), _ptr(m), _ptr(v), _ptr(g), _ptr(p), k)
+        self.n = n
+        self._refs = (list(masters), list(exp_avgs), list(exp_avg_sqs), list(grads),
+                      list(params_bf16))
+        self.workspace_bytes = lib().adamw_workspace_bytes(self.array, n)
+        if self.workspace_bytes == 0:
+            raise MpsError(-22, "adamw_workspace_bytes", last_error())
+        # Over-allocate so the base can be rounded up to 256 bytes.
+        self._ws_storage = torch.empty(self.workspace_bytes + WORKSPACE_ALIGN,
+                                       dtype=torch.uint8, device=self.device)
+        base = self._ws_storage.data_ptr()
+        self.workspace_ptr = (base + WORKSPACE_ALIGN - 1) // WORKSPACE_ALIGN * WORKSPACE_ALIGN
+
+    def release(self) -> None:
+        """Tell the library the workspace is going away (see the header)."""
+        if getattr(self, "_ws_storage", None) is not None:
+            lib().adamw_workspace_release(self.workspace_ptr)
+            self._ws_storage = None
+
+    def __del__(self):
+        try:
+            self.release()
+        except Exception:
+            pass
+
+
+def _require(t: torch.Tensor, dtype, numel: int, device, name: str) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name}: must be on {device}")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def grad_norm_sq(tl: TensorList, out: torch.Tensor,
+                 stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """out[0] (float64, on the device) = sum of g^2 over the list."""
+    if out.dtype != torch.float64 or out.device != tl.device or out.numel() < 1:
+        raise ValueError("out: float64 tensor on the list's device")
+    _check(lib().grad_norm_sq(tl.array, tl.n, tl.grad_dtype, out.data_ptr(), tl.workspace_ptr,
+                              tl.workspace_bytes, _stream_handle(stream)), "grad_norm_sq")
+    return out
+
+
+def clip_coef(sumsq: torch.Tensor, max_norm: float, out: torch.Tensor,
+              stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """out[0] (float32) = min(1, max_norm / (sqrt(sumsq[0]) + 1e-6))."""
+    if sumsq.dtype != torch.float64 or sumsq.device.type != "cuda":
+        raise ValueError("sumsq: float64 CUDA tensor")
+    if out.dtype != torch.float32 or out.device != sumsq.device:
+        raise ValueError("out: float32 tensor on sumsq's device")
+    _check(lib().clip_coef(sumsq.data_ptr(), float(max_norm), out.data_ptr(),
+                           _stream_handle(stream)), "clip_coef")
+    return out
+
+
+def adamw_multi_tensor_step(tl: TensorList, coef: Optional[torch.Tensor], step: torch.Tensor,
+                            lr: float, beta1: float, beta2: float, eps: float,
+                            weight_decay: float,
+                            stream: Optional[torch.cuda.Stream] = None) -> None:
+    """One AdamW step over the list; `step` (int32, device) counts completed
+    steps and is incremented on the device."""
+    if coef is not None and (coef.dtype != torch.float32 or coef.device != tl.device):
+        raise ValueError("coef: float32 tensor on the list's device, or None")
+    if step.dtype != torch.int32 or step.device != tl.device:
+        raise ValueError("step: int32 tensor on the list's device")
+    _check(lib().adamw_multi_tensor_step(
+        tl.array, tl.n, tl.grad_dtype, _ptr(coef), step.data_ptr(), float(lr), float(beta1),
+        float(beta2), float(eps), float(weight_decay), tl.workspace_ptr, tl.workspace_bytes,
+        _stream_handle(stream)), "adamw_multi_tensor_step")

@@ -1,0 +1,343 @@
+// C ABI of the clipped mixed-precision AdamW step: argument validation, the
+// multi-tensor chunk table, its upload into the caller's workspace, and the
+// kernel launches.  Declared in include/mps_adamw.h.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/mps_adamw.h"
+#include "kernels.h"
+#include "layout.h"
+
+namespace {
+
+using mps::TensorEntry;
+using mps::WorkspaceHeader;
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok()
+{
+    g_last_error.clear();
+    return MPS_OK;
+}
+
+// ------------------------------------------------------------ the plan ---
+
+// Host image of everything the kernels read from the workspace, plus where
+// each part sits.
+struct Plan {
+    std::vector<unsigned char> image;  // header + tensor entries + chunk map
+    size_t tensors_off = 0;
+    size_t chunks_off = 0;
+    size_t partials_off = 0;
+    size_t total_bytes = 0;
+    int n_chunks = 0;
+    int64_t chunk_elems = 0;
+    uint64_t tag = 0;
+};
+
+int64_t pick_chunk_elems(int64_t total)
+{
+    int64_t c = total / mps::kChunkTarget;
+    c = (c / mps::kChunkQuantum) * mps::kChunkQuantum;
+    if (c < mps::kChunkMin) c = mps::kChunkMin;
+    if (c > mps::kChunkMax) c = mps::kChunkMax;
+    return c;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Smallest h in [0, 4) such that every present stream is 16-byte aligned
+// (fp32) or 8-byte aligned (bf16) at element h; -1 if there is none.
+int common_head(const mps::TensorEntry& e, bool grad_bf16)
+{
+    for (int h = 0; h < 4; ++h) {
+        bool good = true;
+        auto need = [&](const void* p, int elem_bytes) {
+            if (!p) return;
+            const uintptr_t a = reinterpret_cast<uintptr_t>(p) + static_cast<uintptr_t>(h) * elem_bytes;
+            if (a % (4 * elem_bytes) != 0) good = false;
+        };
+        need(e.master, 4);
+        need(e.exp_avg, 4);
+        need(e.exp_avg_sq, 4);
+        need(e.grad, grad_bf16 ? 2 : 4);
+        need(e.param_bf16, 2);
+        if (good) return h;
+    }
+    return -1;
+}
+
+uint64_t fnv1a(const unsigned char* p, size_t n, uint64_t h = 1469598103934665603ull)
+{
+    for (size_t i = 0; i < n; ++i) {
+        h ^= p[i];
+        h *= 1099511628211ull;
+    }
+    return h;
+}
+
+// Validate the list and lay out the workspace.  `need_state` asks for the
+// master / moment pointers (the step); the norm reads gradients only.
+int build_plan(const mps_tensor* tensors, int n, int grad_dtype, bool need_state, Plan& plan)
+{
+    if (!tensors) return fail(MPS_ERR_INVALID_ARGUMENT, "tensors is NULL");
+    if (n <= 0) return fail(MPS_ERR_INVALID_ARGUMENT, "n_tensors must be >= 1 (got %d)", n);
+    if (grad_dtype != MPS_DTYPE_F32 && grad_dtype != MPS_DTYPE_BF16) {
+        return fail(MPS_ERR_INVALID_ARGUMENT, "unknown gradient dtype %d", grad_dtype);
+    }
+    const bool bf16 = grad_dtype == MPS_DTYPE_BF16;
+    const int gbytes = bf16 ? 2 : 4;
+
+    int64_t total = 0;
+    for (int i = 0; i < n; ++i) {
+        const mps_tensor& t = tensors[i];
+        if (t.numel < 0) return fail(MPS_ERR_INVALID_ARGUMENT, "tensor %d: numel < 0", i);
+        if (t.numel == 0) continue;
+        if (!t.grad) return fail(MPS_ERR_INVALID_ARGUMENT, "tensor %d: grad is NULL", i);
+        if (reinterpret_cast<uintptr_t>(t.grad) % gbytes) {
+            return fail(MPS_ERR_INVALID_ARGUMENT, "tensor %d: grad not %d-byte aligned", i, gbytes);
+        }
+        if (need_state) {
+            if (!t.master || !t.exp_avg || !t.exp_avg_sq) {
+                return fail(MPS_ERR_INVALID_ARGUMENT, "tensor %d: master/exp_avg/exp_avg_sq NULL", i);
+            }
+            if ((reinterpret_cast<uintptr_t>(t.master) | reinterpret_cast<uintptr_t>(t.exp_avg) |
+                 reinterpret_cast<uintptr_t>(t.exp_avg_sq)) % 4) {
+                return fail(MPS_ERR_INVALID_ARGUMENT, "tensor %d: fp32 state not 4-byte aligned", i);
+            }
+            if (reinterpret_cast<uintptr_t>(t.param_bf16) % 2) {
+                return fail(MPS_ERR_INVALID_ARGUMENT, "tensor %d: param_bf16 not 2-byte aligned", i);
+            }
+        }
+        if (total > INT64_MAX - t.numel) return fail(MPS_ERR_INVALID_ARGUMENT, "total numel overflows");
+        total += t.numel;
+    }
+
+    plan.chunk_elems = pick_chunk_elems(total);
+    int64_t n_chunks = 0;
+    std::vector<TensorEntry> entries(n);
+    for (int i = 0; i < n; ++i) {
+        const mps_tensor& t = tensors[i];
+        TensorEntry& e = entries[i];
+        std::memset(&e, 0, sizeof e);
+        e.numel = t.numel;
+        e.first_chunk = static_cast<int32_t>(n_chunks);
+        if (t.numel == 0) continue;  // no chunks; pointers stay NULL
+        e.master = t.master;
+        e.exp_avg = t.exp_avg;
+        e.exp_avg_sq = t.exp_avg_sq;
+        e.grad = t.grad;
+        e.param_bf16 = t.param_bf16;  // the same list gives the same tables for both calls
+        e.head = common_head(e, bf16);
+        n_chunks += (t.numel + plan.chunk_elems - 1) / plan.chunk_elems;
+        if (n_chunks > INT32_MAX) return fail(MPS_ERR_INVALID_ARGUMENT, "too many chunks");
+    }
+    plan.n_chunks = static_cast<int>(n_chunks);
+
+    plan.tensors_off = sizeof(WorkspaceHeader);
+    plan.chunks_off = plan.tensors_off + sizeof(TensorEntry) * static_cast<size_t>(n);
+    plan.partials_off = round_up(plan.chunks_off + sizeof(uint32_t) * n_chunks, 256);
+    plan.total_bytes = plan.partials_off + sizeof(double) * mps::kNormMaxBlocks;
+
+    plan.image.assign(plan.partials_off, 0);
+    unsigned char* base = plan.image.data();
+    std::memcpy(base + plan.tensors_off, entries.data(), sizeof(TensorEntry) * n);
+    uint32_t* map = reinterpret_cast<uint32_t*>(base + plan.chunks_off);
+    for (int i = 0; i < n; ++i) {
+        const int64_t k = (entries[i].numel + plan.chunk_elems - 1) / plan.chunk_elems;
+        for (int64_t j = 0; j < k; ++j) map[entries[i].first_chunk + j] = static_cast<uint32_t>(i);
+    }
+
+    // The tag identifies the tables; it never equals zero, so freshly
+    // zeroed memory is never mistaken for an upload.
+    uint64_t tag = fnv1a(base + plan.tensors_off, plan.partials_off - plan.tensors_off);
+    tag = fnv1a(reinterpret_cast<const unsigned char*>(&plan.chunk_elems), sizeof plan.chunk_elems, tag);
+    plan.tag = tag ? tag : 1;
+
+    WorkspaceHeader* hdr = reinterpret_cast<WorkspaceHeader*>(base);
+    hdr->norm_ticket = 0;
+    hdr->step_ticket = 0;
+    hdr->tag = plan.tag;
+    hdr->n_tensors = n;
+    hdr->n_chunks = plan.n_chunks;
+    hdr->chunk_elems = plan.chunk_elems;
+    return MPS_OK;
+}
+
+// -------------------------------------------------- workspace upload cache ---
+
+struct Uploaded {
+    uint64_t tag = 0;
+    std::vector<unsigned char> image;  // source of the last upload, kept alive
+    hipEvent_t done = nullptr;         // recorded after that upload
+};
+
+std::mutex g_cache_mutex;
+std::unordered_map<void*, Uploaded> g_cache;
+
+int check_workspace(void* ws, size_t bytes, const Plan& plan)
+{
+    if (!ws) return fail(MPS_ERR_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MPS_ERR_WORKSPACE, "workspace not 256-byte aligned");
+    if (bytes < plan.total_bytes) {
+        return fail(MPS_ERR_WORKSPACE, "workspace too small: %zu bytes, need %zu", bytes, plan.total_bytes);
+    }
+    return MPS_OK;
+}
+
+// Make the workspace hold `plan`'s tables (stream-ordered), uploading them
+// only when the workspace last received different ones.
+int ensure_uploaded(void* ws, Plan& plan, hipStream_t stream)
+{
+    std::lock_guard<std::mutex> lock(g_cache_mutex);
+    Uploaded& u = g_cache[ws];
+    if (u.tag == plan.tag && u.done) return MPS_OK;
+    if (u.done) {
+        // The previous upload may still be reading the old image.
+        hipError_t e = hipEventSynchronize(u.done);
+        if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "hipEventSynchronize: %s", hipGetErrorString(e));
+    } else {
+        hipError_t e = hipEventCreateWithFlags(&u.done, hipEventDisableTiming);
+        if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "hipEventCreate: %s", hipGetErrorString(e));
+    }
+    u.tag = 0;
+    u.image.swap(plan.image);
+    hipError_t e = hipMemcpyAsync(ws, u.image.data(), u.image.size(), hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "table upload: %s", hipGetErrorString(e));
+    e = hipEventRecord(u.done, stream);
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "hipEventRecord: %s", hipGetErrorString(e));
+    u.tag = plan.tag;
+    return MPS_OK;
+}
+
+mps::WorkspaceView view_of(void* ws, const Plan& plan)
+{
+    unsigned char* base = static_cast<unsigned char*>(ws);
+    mps::WorkspaceView v;
+    v.header = reinterpret_cast<WorkspaceHeader*>(base);
+    v.tensors = reinterpret_cast<const TensorEntry*>(base + plan.tensors_off);
+    v.chunk_map = reinterpret_cast<const uint32_t*>(base + plan.chunks_off);
+    v.partials = reinterpret_cast<double*>(base + plan.partials_off);
+    v.n_chunks = plan.n_chunks;
+    v.chunk_elems = plan.chunk_elems;
+    v.tag = plan.tag;
+    return v;
+}
+
+int grid_for(int n_chunks, int cap)
+{
+    if (n_chunks < 1) return 1;
+    return n_chunks < cap ? n_chunks : cap;
+}
+
+bool finite_in(double x, double lo, double hi_exclusive)
+{
+    return std::isfinite(x) && x >= lo && x < hi_exclusive;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t adamw_workspace_bytes(const mps_tensor* tensors, int n_tensors)
+{
+    Plan plan;
+    // The table size does not depend on the gradient dtype; validate with the
+    // weaker (bf16, 2-byte) alignment so that either dtype is accepted here.
+    if (build_plan(tensors, n_tensors, MPS_DTYPE_BF16, false, plan) != MPS_OK) return 0;
+    ok();
+    return plan.total_bytes;
+}
+
+int adamw_workspace_release(void* d_workspace)
+{
+    std::lock_guard<std::mutex> lock(g_cache_mutex);
+    auto it = g_cache.find(d_workspace);
+    if (it != g_cache.end()) {
+        if (it->second.done) {
+            (void)hipEventSynchronize(it->second.done);
+            (void)hipEventDestroy(it->second.done);
+        }
+        g_cache.erase(it);
+    }
+    return ok();
+}
+
+int grad_norm_sq(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype, double* d_sumsq,
+                 void* d_workspace, size_t workspace_bytes, void* stream)
+{
+    if (!d_sumsq) return fail(MPS_ERR_INVALID_ARGUMENT, "d_sumsq is NULL");
+    Plan plan;
+    int rc = build_plan(tensors, n_tensors, grad_dtype, false, plan);
+    if (rc) return rc;
+    if ((rc = check_workspace(d_workspace, workspace_bytes, plan))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
+    const int grid = grid_for(plan.n_chunks, mps::kNormMaxBlocks);
+    hipError_t e = mps::launch_grad_norm(view_of(d_workspace, plan), grad_dtype == MPS_DTYPE_BF16,
+                                         grid, d_sumsq, st);
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "grad_norm launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int clip_coef(const double* d_sumsq, double max_norm, float* d_coef, void* stream)
+{
+    if (!d_sumsq || !d_coef) return fail(MPS_ERR_INVALID_ARGUMENT, "d_sumsq / d_coef is NULL");
+    if (!(std::isfinite(max_norm) && max_norm > 0.0)) {
+        return fail(MPS_ERR_INVALID_ARGUMENT, "max_norm must be finite and > 0");
+    }
+    hipError_t e = mps::launch_clip_coef(d_sumsq, max_norm, d_coef, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "clip_coef launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int adamw_multi_tensor_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
+                            const float* d_coef, int32_t* d_step, double lr, double beta1,
+                            double beta2, double eps, double weight_decay, void* d_workspace,
+                            size_t workspace_bytes, void* stream)
+{
+    if (!d_step) return fail(MPS_ERR_INVALID_ARGUMENT, "d_step is NULL");
+    if (!(std::isfinite(lr) && lr >= 0.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "lr must be finite and >= 0");
+    if (!finite_in(beta1, 0.0, 1.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "beta1 must be in [0, 1)");
+    if (!finite_in(beta2, 0.0, 1.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "beta2 must be in [0, 1)");
+    if (!(std::isfinite(eps) && eps >= 0.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+    if (!(std::isfinite(weight_decay) && weight_decay >= 0.0)) {
+        return fail(MPS_ERR_INVALID_ARGUMENT, "weight_decay must be finite and >= 0");
+    }
+    Plan plan;
+    int rc = build_plan(tensors, n_tensors, grad_dtype, true, plan);
+    if (rc) return rc;
+    if ((rc = check_workspace(d_workspace, workspace_bytes, plan))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
+    mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
+    const int grid = grid_for(plan.n_chunks, mps::kStepMaxBlocks);
+    hipError_t e = mps::launch_adamw_step(view_of(d_workspace, plan), grad_dtype == MPS_DTYPE_BF16,
+                                          grid, d_coef, d_step, hp, st);
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "adamw_step launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+const char* adamw_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

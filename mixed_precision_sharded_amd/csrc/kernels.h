@@ -1,0 +1,31 @@
+// Launchers for the gfx950 kernels (defined in kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include "layout.h"
+
+namespace mps {
+
+// Pointers into one workspace, derived by the host library from its base.
+struct WorkspaceView {
+    WorkspaceHeader* header;
+    const TensorEntry* tensors;
+    const uint32_t* chunk_map;
+    double* partials;
+    int n_chunks;
+    int64_t chunk_elems;
+    uint64_t tag;
+};
+
+hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid,
+                            double* d_sumsq, hipStream_t stream);
+
+hipError_t launch_clip_coef(const double* d_sumsq, double max_norm, float* d_coef,
+                            hipStream_t stream);
+
+hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, int grid,
+                             const float* d_coef, int32_t* d_step,
+                             const HyperParams& hp, hipStream_t stream);
+
+}  // namespace mps

@@ -1,0 +1,452 @@
+// gfx950 kernels of the clipped mixed-precision AdamW step.
+//
+// The path is HBM-bound elementwise streaming plus one reduction (about
+// 0.6 flop per byte), so there is no matrix-core work here: every kernel is
+// built around 128-bit coalesced loads and stores on 64-wide wavefronts.
+//
+//   grad_norm_kernel  sum of g^2 over the tensor list: exact squares summed in
+//                     fp64 per thread, a DPP/cross-lane wavefront reduction, an
+//                     LDS combine per block, and a deterministic second stage
+//                     run by the last block to finish (atomic ticket).
+//   clip_coef_kernel  c = min(1, max_norm / (sqrt(S) + 1e-6)), fp64, one lane.
+//   adamw_step_kernel the fused update: clip scaling, both moments, decoupled
+//                     weight decay, bias corrections derived on the device from
+//                     the step counter, the optional bf16 copy, and the
+//                     counter write-back by the last block.
+//
+// Build with -ffp-contract=off: every fp32 operation below must round once,
+// in source order; division and sqrt are the correctly rounded defaults.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace mps {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// ----------------------------------------------------------------- bf16 ---
+
+__device__ __forceinline__ float bf16_lo(uint32_t word) { return __uint_as_float(word << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t word) { return __uint_as_float(word & 0xffff0000u); }
+
+// Round to nearest even: add half an ulp of the kept part, plus one when the
+// kept part is odd, then truncate.  NaN keeps its sign and gets the quiet bit.
+__device__ __forceinline__ uint32_t bf16_bits(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ------------------------------------------------------ reductions (fp64) ---
+
+template <int kCtrl>
+__device__ __forceinline__ double dpp_move(double x)
+{
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), kCtrl, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), kCtrl, 0xf, 0xf, false);
+    return __hiloint2double(hi, lo);
+}
+
+// Sum over the 64 lanes of a wavefront; every lane ends with the total.
+// Within each row of 16 lanes the exchange uses DPP (quad permutes, then the
+// half-row and row mirrors); the two cross-row steps use lane shuffles.
+// All lanes must be active.
+__device__ __forceinline__ double wave_sum(double x)
+{
+    constexpr int kQuadSwap1 = 0xb1;   // quad_perm [1,0,3,2]
+    constexpr int kQuadSwap2 = 0x4e;   // quad_perm [2,3,0,1]
+    constexpr int kHalfMirror = 0x141; // row_half_mirror
+    constexpr int kRowMirror = 0x140;  // row_mirror
+    x = x + dpp_move<kQuadSwap1>(x);
+    x = x + dpp_move<kQuadSwap2>(x);
+    x = x + dpp_move<kHalfMirror>(x);
+    x = x + dpp_move<kRowMirror>(x);
+    x = x + __shfl_xor(x, 16, kWave);
+    x = x + __shfl_xor(x, 32, kWave);
+    return x;
+}
+
+// Sum over the block in a fixed order; the result is valid in thread 0.
+// `lds` holds one double per wavefront.  Ends with a barrier so that `lds`
+// may be reused right away.
+__device__ __forceinline__ double block_sum(double x, double* lds)
+{
+    x = wave_sum(x);
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    if (lane == 0) lds[wave] = x;
+    __syncthreads();
+    double r = 0.0;
+    if (threadIdx.x == 0) {
+        for (int w = 0; w < kWavesPerBlock; ++w) r = r + lds[w];
+    }
+    __syncthreads();
+    return r;
+}
+
+// ------------------------------------------------------------ grad norm ---
+
+template <bool kBf16>
+struct GradTraits;
+
+template <>
+struct GradTraits<false> {
+    using Vec = f32x4;  // four fp32 gradients per 16 bytes
+    static constexpr int kPerVec = 4;
+    __device__ static float scalar(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
+    __device__ static double accumulate(double acc, const Vec& v)
+    {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const double d = static_cast<double>(v[k]);
+            acc = __builtin_fma(d, d, acc);  // d*d is exact in fp64
+        }
+        return acc;
+    }
+};
+
+template <>
+struct GradTraits<true> {
+    using Vec = u32x4;  // eight bf16 gradients per 16 bytes
+    static constexpr int kPerVec = 8;
+    __device__ static float scalar(const void* p, int64_t i)
+    {
+        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+    }
+    __device__ static double accumulate(double acc, const Vec& v)
+    {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const double lo = static_cast<double>(bf16_lo(v[k]));
+            const double hi = static_cast<double>(bf16_hi(v[k]));
+            acc = __builtin_fma(lo, lo, acc);
+            acc = __builtin_fma(hi, hi, acc);
+        }
+        return acc;
+    }
+};
+
+template <bool kBf16, int kUnroll>
+__global__ __launch_bounds__(kBlock) void grad_norm_kernel(
+    WorkspaceHeader* header, const TensorEntry* tensors, const uint32_t* chunk_map,
+    double* partials, int n_chunks, int64_t chunk_elems, uint64_t tag, double* d_sumsq)
+{
+    using T = GradTraits<kBf16>;
+    using Vec = typename T::Vec;
+    constexpr int kPerVec = T::kPerVec;
+    constexpr int64_t kElemBytes = kBf16 ? 2 : 4;
+
+    if (header->tag != tag) {  // tables overwritten: touch nothing, report NaN
+        if (blockIdx.x == 0 && threadIdx.x == 0) *d_sumsq = __builtin_nan("");
+        return;
+    }
+
+    const int tid = threadIdx.x;
+    double acc[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
+
+    for (int c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+        const TensorEntry* te = &tensors[chunk_map[c]];
+        const void* grad = te->grad;
+        const int64_t begin = static_cast<int64_t>(c - te->first_chunk) * chunk_elems;
+        const int64_t end = min(begin + chunk_elems, te->numel);
+
+        // Peel elements until the gradient address is 16-byte aligned.
+        const uintptr_t addr = reinterpret_cast<uintptr_t>(grad) + begin * kElemBytes;
+        int64_t head = static_cast<int64_t>((16 - (addr & 15)) & 15) / kElemBytes;
+        head = min(head, end - begin);
+        if (tid < head) {
+            const double d = static_cast<double>(T::scalar(grad, begin + tid));
+            acc[0] = __builtin_fma(d, d, acc[0]);
+        }
+        const int64_t vbegin = begin + head;
+        const int64_t nvec = (end - vbegin) / kPerVec;
+        const Vec* gv = reinterpret_cast<const Vec*>(
+            static_cast<const char*>(grad) + vbegin * kElemBytes);
+
+        for (int64_t base = 0; base < nvec; base += static_cast<int64_t>(kBlock) * kUnroll) {
+            Vec x[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t i = base + u * kBlock + tid;
+                x[u] = (i < nvec) ? gv[i] : Vec(0);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) acc[u] = T::accumulate(acc[u], x[u]);
+        }
+
+        const int64_t tail = vbegin + nvec * kPerVec;
+        if (tid < end - tail) {
+            const double d = static_cast<double>(T::scalar(grad, tail + tid));
+            acc[0] = __builtin_fma(d, d, acc[0]);
+        }
+    }
+
+    double mine = acc[0];
+#pragma unroll
+    for (int u = 1; u < kUnroll; ++u) mine = mine + acc[u];
+
+    __shared__ double lds[kWavesPerBlock];
+    __shared__ bool is_last;
+    const double block_total = block_sum(mine, lds);
+    if (tid == 0) {
+        __hip_atomic_store(&partials[blockIdx.x], block_total, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __threadfence();
+        const unsigned prev = atomicInc(&header->norm_ticket, gridDim.x - 1);
+        is_last = (prev == gridDim.x - 1);  // the ticket wraps back to 0 here
+    }
+    __syncthreads();
+    if (!is_last) return;
+
+    // Second stage: the last block sums the partials in block-index order.
+    __threadfence();
+    double q = 0.0;
+    for (int i = tid; i < static_cast<int>(gridDim.x); i += kBlock) {
+        q = q + __hip_atomic_load(&partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const double total = block_sum(q, lds);
+    if (tid == 0) *d_sumsq = total;
+}
+
+// ----------------------------------------------------------------- clip ---
+
+__global__ __launch_bounds__(kWave) void clip_coef_kernel(const double* d_sumsq, double max_norm,
+                                                          float* d_coef)
+{
+    if (threadIdx.x != 0) return;
+    const double norm = __builtin_sqrt(*d_sumsq);
+    double c = max_norm / (norm + 1e-6);
+    c = (c > 1.0) ? 1.0 : c;  // NaN stays NaN
+    *d_coef = static_cast<float>(c);
+}
+
+// ---------------------------------------------------------------- update ---
+
+struct StepScalars {
+    float beta1, beta2, one_m_b1, one_m_b2, decay, step_size, bc2_sqrt, eps, clip;
+};
+
+// beta^t, squaring the base and multiplying in the set bits from the lowest.
+__device__ __forceinline__ double power_by_squaring(double beta, int64_t t)
+{
+    double result = 1.0;
+    double base = beta;
+    for (; t > 0; t >>= 1) {
+        if (t & 1) result = result * base;
+        base = base * base;
+    }
+    return result;
+}
+
+__device__ __forceinline__ StepScalars step_scalars(int64_t t, const HyperParams& hp, float clip)
+{
+    StepScalars s;
+    const double p1 = power_by_squaring(hp.beta1, t);
+    const double p2 = power_by_squaring(hp.beta2, t);
+    s.beta1 = static_cast<float>(hp.beta1);
+    s.beta2 = static_cast<float>(hp.beta2);
+    s.one_m_b1 = static_cast<float>(1.0 - hp.beta1);
+    s.one_m_b2 = static_cast<float>(1.0 - hp.beta2);
+    s.decay = static_cast<float>(1.0 - hp.lr * hp.weight_decay);
+    s.step_size = static_cast<float>(hp.lr / (1.0 - p1));
+    s.bc2_sqrt = static_cast<float>(__builtin_sqrt(1.0 - p2));
+    s.eps = static_cast<float>(hp.eps);
+    s.clip = clip;
+    return s;
+}
+
+// One element; each statement is a single correctly rounded fp32 operation.
+__device__ __forceinline__ void adamw_element(float& w, float& m, float& v, float grad,
+                                              const StepScalars& s)
+{
+    const float g = grad * s.clip;
+    const float m_keep = s.beta1 * m;
+    const float m_add = s.one_m_b1 * g;
+    m = m_keep + m_add;
+    const float v_keep = s.beta2 * v;
+    const float g_sq = g * g;
+    const float v_add = s.one_m_b2 * g_sq;
+    v = v_keep + v_add;
+    const float root = __builtin_sqrtf(v);
+    const float root_hat = root / s.bc2_sqrt;
+    const float den = root_hat + s.eps;
+    const float w_decayed = w * s.decay;
+    const float ratio = m / den;
+    const float delta = s.step_size * ratio;
+    w = w_decayed - delta;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ void adamw_scalar_at(const TensorEntry* te, int64_t i, const StepScalars& s)
+{
+    const float grad = kBf16 ? GradTraits<true>::scalar(te->grad, i)
+                             : GradTraits<false>::scalar(te->grad, i);
+    float w = te->master[i], m = te->exp_avg[i], v = te->exp_avg_sq[i];
+    adamw_element(w, m, v, grad, s);
+    te->master[i] = w;
+    te->exp_avg[i] = m;
+    te->exp_avg_sq[i] = v;
+    if (te->param_bf16) te->param_bf16[i] = static_cast<uint16_t>(bf16_bits(w));
+}
+
+// Four consecutive gradients: 16 bytes of fp32 or 8 bytes of bf16.
+template <bool kBf16>
+struct QuadGrad;
+
+template <>
+struct QuadGrad<false> {
+    using Vec = f32x4;
+    __device__ static float get(const Vec& v, int k) { return v[k]; }
+};
+
+template <>
+struct QuadGrad<true> {
+    using Vec = u32x2;
+    __device__ static float get(const Vec& v, int k)
+    {
+        return (k & 1) ? bf16_hi(v[k >> 1]) : bf16_lo(v[k >> 1]);
+    }
+};
+
+template <bool kBf16, int kUnroll>
+__global__ __launch_bounds__(kBlock) void adamw_step_kernel(
+    WorkspaceHeader* header, const TensorEntry* tensors, const uint32_t* chunk_map,
+    int n_chunks, int64_t chunk_elems, uint64_t tag, const float* d_coef, int32_t* d_step,
+    HyperParams hp)
+{
+    using GVec = typename QuadGrad<kBf16>::Vec;
+
+    if (header->tag != tag) return;  // tables overwritten: touch nothing
+
+    const int tid = threadIdx.x;
+    const int64_t t = static_cast<int64_t>(*d_step) + 1;
+    const StepScalars s = step_scalars(t, hp, d_coef ? *d_coef : 1.0f);
+
+    for (int c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+        const TensorEntry* te = &tensors[chunk_map[c]];
+        const int64_t begin = static_cast<int64_t>(c - te->first_chunk) * chunk_elems;
+        const int64_t end = min(begin + chunk_elems, te->numel);
+
+        if (te->head < 0) {  // streams share no alignment: element-wise
+            for (int64_t i = begin + tid; i < end; i += kBlock) adamw_scalar_at<kBf16>(te, i, s);
+            continue;
+        }
+
+        const int64_t qbegin = min(begin + te->head, end);
+        if (tid < qbegin - begin) adamw_scalar_at<kBf16>(te, begin + tid, s);
+        const int64_t nquad = (end - qbegin) / 4;
+
+        f32x4* W = reinterpret_cast<f32x4*>(te->master + qbegin);
+        f32x4* M = reinterpret_cast<f32x4*>(te->exp_avg + qbegin);
+        f32x4* V = reinterpret_cast<f32x4*>(te->exp_avg_sq + qbegin);
+        const GVec* G = reinterpret_cast<const GVec*>(
+            static_cast<const char*>(te->grad) + qbegin * (kBf16 ? 2 : 4));
+        u32x2* P = te->param_bf16 ? reinterpret_cast<u32x2*>(te->param_bf16 + qbegin) : nullptr;
+
+        for (int64_t base = 0; base < nquad; base += static_cast<int64_t>(kBlock) * kUnroll) {
+            f32x4 w[kUnroll], m[kUnroll], v[kUnroll];
+            GVec g[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t i = base + u * kBlock + tid;
+                if (i < nquad) {
+                    w[u] = W[i];
+                    m[u] = M[i];
+                    v[u] = V[i];
+                    g[u] = G[i];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t i = base + u * kBlock + tid;
+                if (i < nquad) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        float wk = w[u][k], mk = m[u][k], vk = v[u][k];
+                        adamw_element(wk, mk, vk, QuadGrad<kBf16>::get(g[u], k), s);
+                        w[u][k] = wk;
+                        m[u][k] = mk;
+                        v[u][k] = vk;
+                    }
+                    W[i] = w[u];
+                    M[i] = m[u];
+                    V[i] = v[u];
+                    if (P) {
+                        u32x2 packed;
+                        packed[0] = bf16_bits(w[u][0]) | (bf16_bits(w[u][1]) << 16);
+                        packed[1] = bf16_bits(w[u][2]) | (bf16_bits(w[u][3]) << 16);
+                        P[i] = packed;
+                    }
+                }
+            }
+        }
+
+        const int64_t tail = qbegin + nquad * 4;
+        if (tid < end - tail) adamw_scalar_at<kBf16>(te, tail + tid, s);
+    }
+
+    // The last block to finish stores the new step count.  Every block read
+    // the old count before taking its ticket.
+    __syncthreads();
+    if (tid == 0) {
+        __threadfence();
+        const unsigned prev = atomicInc(&header->step_ticket, gridDim.x - 1);
+        if (prev == gridDim.x - 1) *d_step = static_cast<int32_t>(t);
+    }
+}
+
+}  // namespace
+
+// --------------------------------------------------------------- launchers ---
+
+constexpr int kNormUnroll = 4;
+constexpr int kStepUnroll = 2;
+
+hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid, double* d_sumsq,
+                            hipStream_t stream)
+{
+    if (grad_bf16) {
+        grad_norm_kernel<true, kNormUnroll><<<grid, kBlock, 0, stream>>>(
+            ws.header, ws.tensors, ws.chunk_map, ws.partials, ws.n_chunks, ws.chunk_elems, ws.tag,
+            d_sumsq);
+    } else {
+        grad_norm_kernel<false, kNormUnroll><<<grid, kBlock, 0, stream>>>(
+            ws.header, ws.tensors, ws.chunk_map, ws.partials, ws.n_chunks, ws.chunk_elems, ws.tag,
+            d_sumsq);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_clip_coef(const double* d_sumsq, double max_norm, float* d_coef,
+                            hipStream_t stream)
+{
+    clip_coef_kernel<<<1, kWave, 0, stream>>>(d_sumsq, max_norm, d_coef);
+    return hipGetLastError();
+}
+
+hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, int grid,
+                             const float* d_coef, int32_t* d_step, const HyperParams& hp,
+                             hipStream_t stream)
+{
+    if (grad_bf16) {
+        adamw_step_kernel<true, kStepUnroll><<<grid, kBlock, 0, stream>>>(
+            ws.header, ws.tensors, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag, d_coef,
+            d_step, hp);
+    } else {
+        adamw_step_kernel<false, kStepUnroll><<<grid, kBlock, 0, stream>>>(
+            ws.header, ws.tensors, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag, d_coef,
+            d_step, hp);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mps

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fno-semantic-interposition", "-ffp-contract=off",
           "-fno-fast-math", "-fno-math-errno", "-Wall", "-Wextra"]
 
 

@@ -1,0 +1,145 @@
+"""The C ABI: the library loads, exports every function the header declares,
+and rejects bad arguments with error codes before touching the GPU.
+
+Runs without a GPU: only host-side validation paths are called (no kernel is
+launched and no HIP call is made on these paths).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from mixed_precision_sharded_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mps_adamw.h")
+
+EINVAL, EWORKSPACE = -22, -28
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\([^;{]*\)\s*;", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from mixed_precision_sharded_amd import build
+        build.build()
+    return binding.lib()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "adamw_workspace_bytes", "adamw_workspace_release", "grad_norm_sq", "clip_coef",
+        "adamw_multi_tensor_step", "adamw_last_error"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def fake_list(n=2, numel=1000, base=0x7f0000000000, misalign=0):
+    arr = (binding.MpsTensor * n)()
+    for i in range(n):
+        off = base + i * (1 << 24) + misalign
+        arr[i] = binding.MpsTensor(off, off + 4096 * 1024, off + 8192 * 1024, off + 12288 * 1024,
+                                   None, numel)
+    return arr
+
+
+def test_workspace_bytes(lib):
+    arr = fake_list(3, 5000)
+    size = lib.adamw_workspace_bytes(arr, 3)
+    assert size > 0 and size < 1 << 20
+    # chunk tables grow with the parameter count, the fixed part does not
+    big = lib.adamw_workspace_bytes(fake_list(3, 50_000_000), 3)
+    assert big > size
+    assert big < 50_000_000 * 3 // 1000  # far below one byte per parameter
+
+
+def test_workspace_bytes_rejects_bad_lists(lib):
+    assert lib.adamw_workspace_bytes(None, 1) == 0
+    assert "NULL" in binding.last_error()
+    assert lib.adamw_workspace_bytes(fake_list(1), 0) == 0
+    bad = fake_list(1)
+    bad[0].numel = -1
+    assert lib.adamw_workspace_bytes(bad, 1) == 0
+    assert "numel" in binding.last_error()
+
+
+def test_argument_errors(lib):
+    arr = fake_list(1, 4096)
+    ws = ctypes.c_void_p(0x7e0000000000)
+    good = dict(coef=None, step=ctypes.c_void_p(0x7d0000000000), lr=3e-4, b1=0.9, b2=0.95,
+                eps=1e-8, wd=0.1)
+
+    def step(**kw):
+        a = {**good, **kw}
+        return lib.adamw_multi_tensor_step(arr, 1, 0, a["coef"], a["step"], a["lr"], a["b1"],
+                                           a["b2"], a["eps"], a["wd"], ws, 1 << 30, None)
+
+    assert step(step=None) == EINVAL
+    assert step(b1=1.0) == EINVAL
+    assert step(b2=-0.1) == EINVAL
+    assert step(lr=float("nan")) == EINVAL
+    assert step(lr=-1.0) == EINVAL
+    assert step(eps=float("inf")) == EINVAL
+    assert step(wd=-0.1) == EINVAL
+    assert "weight_decay" in binding.last_error()
+    # wrong dtype code, empty list, NULL state with numel > 0
+    assert lib.adamw_multi_tensor_step(arr, 1, 7, None, good["step"], 3e-4, 0.9, 0.95, 1e-8,
+                                       0.1, ws, 1 << 30, None) == EINVAL
+    assert lib.adamw_multi_tensor_step(arr, 0, 0, None, good["step"], 3e-4, 0.9, 0.95, 1e-8,
+                                       0.1, ws, 1 << 30, None) == EINVAL
+    nostate = fake_list(1)
+    nostate[0].master = None
+    assert lib.adamw_multi_tensor_step(nostate, 1, 0, None, good["step"], 3e-4, 0.9, 0.95,
+                                       1e-8, 0.1, ws, 1 << 30, None) == EINVAL
+    # fp32 state not 4-byte aligned; bf16 gradient not 2-byte aligned
+    odd = fake_list(1, misalign=2)
+    assert lib.adamw_multi_tensor_step(odd, 1, 0, None, good["step"], 3e-4, 0.9, 0.95, 1e-8,
+                                       0.1, ws, 1 << 30, None) == EINVAL
+    odd1 = fake_list(1, misalign=1)
+    assert lib.grad_norm_sq(odd1, 1, 1, ctypes.c_void_p(0x7d0000000000), ws, 1 << 30,
+                            None) == EINVAL
+
+
+def test_workspace_errors(lib):
+    arr = fake_list(1, 4096)
+    step = ctypes.c_void_p(0x7d0000000000)
+    need = lib.adamw_workspace_bytes(arr, 1)
+    args = (arr, 1, 0, None, step, 3e-4, 0.9, 0.95, 1e-8, 0.1)
+    assert lib.adamw_multi_tensor_step(*args, None, need, None) == EWORKSPACE
+    assert lib.adamw_multi_tensor_step(*args, ctypes.c_void_p(0x7e0000000040), need,
+                                       None) == EWORKSPACE
+    assert "aligned" in binding.last_error()
+    assert lib.adamw_multi_tensor_step(*args, ctypes.c_void_p(0x7e0000000000), need - 1,
+                                       None) == EWORKSPACE
+    assert "too small" in binding.last_error()
+    assert lib.grad_norm_sq(arr, 1, 0, ctypes.c_void_p(0x7d0000000000), None, need,
+                            None) == EWORKSPACE
+    assert lib.grad_norm_sq(arr, 1, 0, None, ctypes.c_void_p(0x7e0000000000), need,
+                            None) == EINVAL
+
+
+def test_clip_argument_errors(lib):
+    p = ctypes.c_void_p(0x7d0000000000)
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert lib.clip_coef(p, bad, p, None) == EINVAL
+    assert lib.clip_coef(None, 1.0, p, None) == EINVAL
+    assert lib.clip_coef(p, 1.0, None, None) == EINVAL
+
+
+def test_release_unknown_workspace_is_harmless(lib):
+    assert lib.adamw_workspace_release(ctypes.c_void_p(0x1234500)) == 0
