@@ -1,8 +1,9 @@
 """Throughput of the fused, clipped, mixed-precision AdamW step on one GPU.
 
 A step is one pass of the whole path over one shard: grad_norm_sq (sum of
-g^2), clip_coef, adamw_multi_tensor_step (update + optional bf16 copy + step
-counter), all on one stream, inputs resident in HBM.  Prints ONE JSON line:
+g^2 and, in the same launch, the clip coefficient), then
+adamw_multi_tensor_step (update + optional bf16 copy + step counter), on one
+stream, inputs resident in HBM.  Prints ONE JSON line:
 params updated per second (value), the step's algorithmic GB/s, and for the
 dominant kernel (the update) its roofline against MI355X's 8 TB/s HBM peak,
 timed live with events on the launch stream; plus the CPU oracle timed on a
@@ -39,6 +40,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="host time budget of the oracle baseline (0 = skip)")
     p.add_argument("--no-kernel-events", action="store_true")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="after the measurement, run 5 plain device copies of this many MiB "
+                        "(known bytes, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -99,16 +103,13 @@ def main():
     def one_step(tl, ev=None):
         if ev is not None:
             ev[0].record()
-        binding.grad_norm_sq(tl, sumsq)
+        binding.grad_norm_sq(tl, sumsq, w.max_norm, coef)  # norm + clip coefficient
         if ev is not None:
             ev[1].record()
-        binding.clip_coef(sumsq, w.max_norm, coef)
-        if ev is not None:
-            ev[2].record()
         binding.adamw_multi_tensor_step(tl, coef, step, w.lr, w.beta1, w.beta2, w.eps,
                                         w.weight_decay)
         if ev is not None:
-            ev[3].record()
+            ev[2].record()
 
     for i in range(args.warmup):
         one_step(sets[i % len(sets)][1])
@@ -131,16 +132,14 @@ def main():
     # launches, on the stream the kernels run on.
     kern_us = None
     if not args.no_kernel_events:
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         for i in range(args.steps):
             one_step(sets[i % len(sets)][1], evs[i])
         torch.cuda.synchronize()
         norm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-        clip_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-        upd_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-        kern_us = {"grad_norm_sq": norm_ms * 1e3, "clip_coef": clip_ms * 1e3,
-                   "adamw_multi_tensor_step": upd_ms * 1e3}
+        upd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+        kern_us = {"grad_norm_sq+clip": norm_ms * 1e3, "adamw_multi_tensor_step": upd_ms * 1e3}
 
     n = w.numel
     step_bytes = w.algorithmic_bytes_per_param() * n
@@ -160,6 +159,16 @@ def main():
                     "algorithmic_bytes_per_launch": upd_bytes,
                     "avg_launch_us": round(kern_us["adamw_multi_tensor_step"], 2)}
         log(f"kernels (us): " + ", ".join(f"{k} {v:.1f}" for k, v in kern_us.items()))
+
+    if args.copy_calibration_mib > 0:
+        n_f32 = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n_f32, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 5 copies of {args.copy_calibration_mib} MiB")
+        del src, dst
 
     cpu = cpu_baseline(w, sets[0][0], args.cpu_seconds) if args.cpu_seconds > 0 else None
 

@@ -14,10 +14,14 @@
  * (2N, mixed basis) or fp32 (4N, pure-fp32 basis), and a bf16 parameter copy
  * (2N) that is only ever written from the fp32 master.
  *
- * A step is three calls on one stream, none of which waits on the host:
+ * A step is two or three calls on one stream, none of which waits on the host:
  *
- *     grad_norm_sq(list, ..., d_sumsq, ws, ...)        S = sum of g^2
- *     clip_coef(d_sumsq, max_norm, d_coef, ...)         c = min(1, max_norm/(sqrt(S)+1e-6))
+ *     grad_norm_sq(list, ..., d_sumsq, max_norm, d_coef, ws, ...)
+ *                      S = sum of g^2, and (optionally, same launch)
+ *                      c = min(1, max_norm / (sqrt(S) + 1e-6))
+ *     clip_coef(d_sumsq, max_norm, d_coef, ...)
+ *                      c from an S the caller combined itself (e.g. the sum
+ *                      of every rank's S in a sharded group)
  *     adamw_multi_tensor_step(list, ..., d_coef, d_step, ..., ws, ...)
  *
  * Conventions shared by every entry point:
@@ -94,7 +98,8 @@ int adamw_workspace_release(void* d_workspace);
 
 /*
  * grad_norm_sq — global squared L2 norm of the gradients of every tensor in
- * the list:  *d_sumsq = sum_i sum_j g_ij^2   (fp64, written on the device).
+ * the list:  *d_sumsq = sum_i sum_j g_ij^2   (fp64, written on the device),
+ * and optionally the clip coefficient of that norm, from the same launch.
  *
  * The pages log the gradient norm as a first-class training metric
  * (Lecture 9 exercises page, failure-handling answer: the grad norm is
@@ -106,14 +111,18 @@ int adamw_workspace_release(void* d_workspace);
  *                        the workspace tables are shared.
  *   grad_dtype         : MPS_DTYPE_F32 or MPS_DTYPE_BF16.
  *   d_sumsq            : device double, written.
+ *   max_norm, d_coef   : if d_coef is non-NULL, *d_coef receives exactly what
+ *                        clip_coef(d_sumsq, max_norm, d_coef) would write
+ *                        (max_norm must then be finite and > 0); if NULL,
+ *                        max_norm is ignored.
  *   d_workspace, workspace_bytes : see adamw_workspace_bytes.
  *
  * Each g^2 is formed exactly and summed in fp64 in a fixed order that depends
  * only on the list: repeated calls give bitwise identical results.
  */
 int grad_norm_sq(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
-                 double* d_sumsq, void* d_workspace, size_t workspace_bytes,
-                 void* stream);
+                 double* d_sumsq, double max_norm, float* d_coef, void* d_workspace,
+                 size_t workspace_bytes, void* stream);
 
 /*
  * clip_coef — global-norm clipping coefficient

@@ -56,7 +56,7 @@ def lib() -> ctypes.CDLL:
         L.adamw_workspace_release.argtypes = [P]
         L.grad_norm_sq.restype = ctypes.c_int
         L.grad_norm_sq.argtypes = [ctypes.POINTER(MpsTensor), ctypes.c_int, ctypes.c_int,
-                                   P, P, ctypes.c_size_t, P]
+                                   P, ctypes.c_double, P, P, ctypes.c_size_t, P]
         L.clip_coef.restype = ctypes.c_int
         L.clip_coef.argtypes = [P, ctypes.c_double, P, P]
         L.adamw_multi_tensor_step.restype = ctypes.c_int
@@ -159,13 +159,22 @@ def _require(t: torch.Tensor, dtype, numel: int, device, name: str) -> None:
         raise ValueError(f"{name}: must be contiguous")
 
 
-def grad_norm_sq(tl: TensorList, out: torch.Tensor,
+def grad_norm_sq(tl: TensorList, out: torch.Tensor, max_norm: Optional[float] = None,
+                 coef_out: Optional[torch.Tensor] = None,
                  stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """out[0] (float64, on the device) = sum of g^2 over the list."""
+    """out[0] (float64, on the device) = sum of g^2 over the list; with
+    coef_out (float32) also the clip coefficient for max_norm, same launch."""
     if out.dtype != torch.float64 or out.device != tl.device or out.numel() < 1:
         raise ValueError("out: float64 tensor on the list's device")
-    _check(lib().grad_norm_sq(tl.array, tl.n, tl.grad_dtype, out.data_ptr(), tl.workspace_ptr,
-                              tl.workspace_bytes, _stream_handle(stream)), "grad_norm_sq")
+    if coef_out is not None:
+        if coef_out.dtype != torch.float32 or coef_out.device != tl.device:
+            raise ValueError("coef_out: float32 tensor on the list's device")
+        if max_norm is None:
+            raise ValueError("coef_out needs max_norm")
+    _check(lib().grad_norm_sq(tl.array, tl.n, tl.grad_dtype, out.data_ptr(),
+                              float(max_norm) if max_norm is not None else 0.0, _ptr(coef_out),
+                              tl.workspace_ptr, tl.workspace_bytes, _stream_handle(stream)),
+           "grad_norm_sq")
     return out
 
 

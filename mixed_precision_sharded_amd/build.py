@@ -42,6 +42,19 @@ def build(out: str = LIB, extra=()) -> str:
     return out
 
 
+CEILING_SRC = os.path.join(CSRC, "stream_ceiling.hip")
+CEILING_BIN = os.path.join(HERE, "stream_ceiling")
+
+
+def build_ceiling(out: str = CEILING_BIN) -> str:
+    """Compile the streaming-ceiling probe (an executable, not part of the library)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    flags = [f for f in FLAGS if f not in ("-shared", "-fPIC")]
+    subprocess.run([HIPCC, *flags, "-o", tmp, CEILING_SRC], check=True)
+    os.replace(tmp, out)
+    return out
+
+
 def isa(out_dir: str) -> list:
     """Write the gfx950 assembly of kernels.hip under out_dir (for reading)."""
     os.makedirs(out_dir, exist_ok=True)
@@ -57,3 +70,4 @@ if __name__ == "__main__":
         print(isa(sys.argv[2] if len(sys.argv) > 2 else os.path.join(HERE, "..", "_work", "isa")))
     else:
         print(build())
+        print(build_ceiling())

@@ -244,10 +244,13 @@ mps::WorkspaceView view_of(void* ws, const Plan& plan)
     return v;
 }
 
+// At most `cap` blocks, every block taking the same number of chunks (the
+// last one possibly fewer): ceil(n / ceil(n / cap)).
 int grid_for(int n_chunks, int cap)
 {
     if (n_chunks < 1) return 1;
-    return n_chunks < cap ? n_chunks : cap;
+    const int per_block = (n_chunks + cap - 1) / cap;
+    return (n_chunks + per_block - 1) / per_block;
 }
 
 bool finite_in(double x, double lo, double hi_exclusive)
@@ -284,9 +287,13 @@ int adamw_workspace_release(void* d_workspace)
 }
 
 int grad_norm_sq(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype, double* d_sumsq,
-                 void* d_workspace, size_t workspace_bytes, void* stream)
+                 double max_norm, float* d_coef, void* d_workspace, size_t workspace_bytes,
+                 void* stream)
 {
     if (!d_sumsq) return fail(MPS_ERR_INVALID_ARGUMENT, "d_sumsq is NULL");
+    if (d_coef && !(std::isfinite(max_norm) && max_norm > 0.0)) {
+        return fail(MPS_ERR_INVALID_ARGUMENT, "max_norm must be finite and > 0");
+    }
     Plan plan;
     int rc = build_plan(tensors, n_tensors, grad_dtype, false, plan);
     if (rc) return rc;
@@ -295,7 +302,7 @@ int grad_norm_sq(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
     if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
     const int grid = grid_for(plan.n_chunks, mps::kNormMaxBlocks);
     hipError_t e = mps::launch_grad_norm(view_of(d_workspace, plan), grad_dtype == MPS_DTYPE_BF16,
-                                         grid, d_sumsq, st);
+                                         grid, d_sumsq, max_norm, d_coef, st);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "grad_norm launch: %s", hipGetErrorString(e));
     return ok();
 }

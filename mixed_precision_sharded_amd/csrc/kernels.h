@@ -19,7 +19,8 @@ struct WorkspaceView {
 };
 
 hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid,
-                            double* d_sumsq, hipStream_t stream);
+                            double* d_sumsq, double max_norm, float* d_coef,
+                            hipStream_t stream);
 
 hipError_t launch_clip_coef(const double* d_sumsq, double max_norm, float* d_coef,
                             hipStream_t stream);

@@ -2,7 +2,8 @@
 //
 // The path is HBM-bound elementwise streaming plus one reduction (about
 // 0.6 flop per byte), so there is no matrix-core work here: every kernel is
-// built around 128-bit coalesced loads and stores on 64-wide wavefronts.
+// built around 128-bit coalesced buffer loads and stores on 64-wide
+// wavefronts.
 //
 //   grad_norm_kernel  sum of g^2 over the tensor list: exact squares summed in
 //                     fp64 per thread, a DPP/cross-lane wavefront reduction, an
@@ -14,11 +15,44 @@
 //                     the step counter, the optional bf16 copy, and the
 //                     counter write-back by the last block.
 //
+// Memory access: each chunk's aligned body is addressed through buffer
+// resources (base and size in scalar registers, 32-bit per-lane offsets).
+// Lanes past the end of the body read zeros and their stores are dropped by
+// the hardware range check, so the loops carry no per-load branches.  The
+// streams are touched once, so loads and stores use the nontemporal policy.
+//
 // Build with -ffp-contract=off: every fp32 operation below must round once,
 // in source order; division and sqrt are the correctly rounded defaults.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
+
+#ifndef MPS_STEP_UNROLL
+#define MPS_STEP_UNROLL 2   // groups of four elements per thread per iteration
+#endif
+#ifndef MPS_NORM_UNROLL
+#define MPS_NORM_UNROLL 8   // 16-byte vectors per thread per iteration
+#endif
+// Buffer cache policies (the aux operand of buffer loads and stores):
+// 0 = default, 2 = nontemporal.
+#ifndef MPS_LOAD_POLICY
+#define MPS_LOAD_POLICY 2   // update: master, m, v, gradient
+#endif
+#ifndef MPS_STORE_POLICY
+#define MPS_STORE_POLICY 2  // update: master, m, v, bf16 copy
+#endif
+#ifndef MPS_STEP_CONTIGUOUS
+#define MPS_STEP_CONTIGUOUS 0  // 1: each update block takes one contiguous run of chunks
+#endif
+#ifndef MPS_NORM_CONTIGUOUS
+#define MPS_NORM_CONTIGUOUS 0  // 1: each norm block takes one contiguous run of chunks
+#endif
+#ifndef MPS_STEP_REVERSE
+#define MPS_STEP_REVERSE 0  // 1: the update walks the chunks from the last one
+#endif
+#ifndef MPS_NORM_POLICY
+#define MPS_NORM_POLICY 0   // norm: gradient (read again by the update)
+#endif
 
 namespace mps {
 namespace {
@@ -29,6 +63,44 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kLoadPolicy = MPS_LOAD_POLICY;
+constexpr int kStorePolicy = MPS_STORE_POLICY;
+constexpr int kNormPolicy = MPS_NORM_POLICY;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+
+// ------------------------------------------------------ buffer resources ---
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                             kRsrcWord3);
+}
+
+__device__ __forceinline__ f32x4 load_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadPolicy));
+}
+
+template <int kAux>
+__device__ __forceinline__ u32x4 load_u32x4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAux);
+}
+
+__device__ __forceinline__ u32x2 load_u32x2(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadPolicy);
+}
+
+__device__ __forceinline__ void store_f32x4(f32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kStorePolicy);
+}
+
+__device__ __forceinline__ void store_u32x2(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kStorePolicy);
+}
 
 // ----------------------------------------------------------------- bf16 ---
 
@@ -91,60 +163,80 @@ __device__ __forceinline__ double block_sum(double x, double* lds)
     return r;
 }
 
+__device__ __forceinline__ double add_square(double acc, float x)
+{
+    const double d = static_cast<double>(x);
+    return __builtin_fma(d, d, acc);  // d*d is exact in fp64: one rounding
+}
+
+// Chunks of block b: either b, b + G, b + 2G, ... (kContiguous = false) or
+// the run [b * n / G, (b + 1) * n / G).  Returns the k-th chunk, or -1.
+template <bool kContiguous>
+struct ChunkWalk {
+    int first, step, stop;
+    __device__ ChunkWalk(int n_chunks)
+    {
+        const int b = blockIdx.x, g = gridDim.x;
+        if (kContiguous) {
+            first = static_cast<int>(static_cast<int64_t>(b) * n_chunks / g);
+            stop = static_cast<int>(static_cast<int64_t>(b + 1) * n_chunks / g);
+            step = 1;
+        } else {
+            first = b;
+            stop = n_chunks;
+            step = g;
+        }
+    }
+};
+
+// c = min(1, max_norm / (sqrt(S) + 1e-6)) in fp64, rounded once to fp32;
+// a NaN S gives NaN (the comparison is false), an infinite S gives 0.
+__device__ __forceinline__ float clip_from_sumsq(double sumsq, double max_norm)
+{
+    const double norm = __builtin_sqrt(sumsq);
+    double c = max_norm / (norm + 1e-6);
+    c = (c > 1.0) ? 1.0 : c;
+    return static_cast<float>(c);
+}
+
 // ------------------------------------------------------------ grad norm ---
 
 template <bool kBf16>
-struct GradTraits;
+__device__ __forceinline__ float grad_at(const void* p, int64_t i)
+{
+    if (kBf16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+    return static_cast<const float*>(p)[i];
+}
 
-template <>
-struct GradTraits<false> {
-    using Vec = f32x4;  // four fp32 gradients per 16 bytes
-    static constexpr int kPerVec = 4;
-    __device__ static float scalar(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
-    __device__ static double accumulate(double acc, const Vec& v)
-    {
+template <bool kBf16>
+__device__ __forceinline__ double add_vector(double acc, u32x4 v)
+{
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const double d = static_cast<double>(v[k]);
-            acc = __builtin_fma(d, d, acc);  // d*d is exact in fp64
+    for (int k = 0; k < 4; ++k) {
+        if (kBf16) {
+            acc = add_square(acc, bf16_lo(v[k]));
+            acc = add_square(acc, bf16_hi(v[k]));
+        } else {
+            acc = add_square(acc, __uint_as_float(v[k]));
         }
-        return acc;
     }
-};
-
-template <>
-struct GradTraits<true> {
-    using Vec = u32x4;  // eight bf16 gradients per 16 bytes
-    static constexpr int kPerVec = 8;
-    __device__ static float scalar(const void* p, int64_t i)
-    {
-        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
-    }
-    __device__ static double accumulate(double acc, const Vec& v)
-    {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const double lo = static_cast<double>(bf16_lo(v[k]));
-            const double hi = static_cast<double>(bf16_hi(v[k]));
-            acc = __builtin_fma(lo, lo, acc);
-            acc = __builtin_fma(hi, hi, acc);
-        }
-        return acc;
-    }
-};
+    return acc;
+}
 
 template <bool kBf16, int kUnroll>
 __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
     WorkspaceHeader* header, const TensorEntry* tensors, const uint32_t* chunk_map,
-    double* partials, int n_chunks, int64_t chunk_elems, uint64_t tag, double* d_sumsq)
+    double* partials, int n_chunks, int64_t chunk_elems, uint64_t tag, double* d_sumsq,
+    double max_norm, float* d_coef)
 {
-    using T = GradTraits<kBf16>;
-    using Vec = typename T::Vec;
-    constexpr int kPerVec = T::kPerVec;
     constexpr int64_t kElemBytes = kBf16 ? 2 : 4;
+    constexpr int64_t kPerVec = 16 / kElemBytes;
 
     if (header->tag != tag) {  // tables overwritten: touch nothing, report NaN
-        if (blockIdx.x == 0 && threadIdx.x == 0) *d_sumsq = __builtin_nan("");
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            *d_sumsq = __builtin_nan("");
+            if (d_coef) *d_coef = __builtin_nanf("");
+        }
         return;
     }
 
@@ -153,7 +245,8 @@ __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
 
-    for (int c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+    const ChunkWalk<MPS_NORM_CONTIGUOUS != 0> walk(n_chunks);
+    for (int c = walk.first; c < walk.stop; c += walk.step) {
         const TensorEntry* te = &tensors[chunk_map[c]];
         const void* grad = te->grad;
         const int64_t begin = static_cast<int64_t>(c - te->first_chunk) * chunk_elems;
@@ -163,31 +256,22 @@ __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
         const uintptr_t addr = reinterpret_cast<uintptr_t>(grad) + begin * kElemBytes;
         int64_t head = static_cast<int64_t>((16 - (addr & 15)) & 15) / kElemBytes;
         head = min(head, end - begin);
-        if (tid < head) {
-            const double d = static_cast<double>(T::scalar(grad, begin + tid));
-            acc[0] = __builtin_fma(d, d, acc[0]);
-        }
+        if (tid < head) acc[0] = add_square(acc[0], grad_at<kBf16>(grad, begin + tid));
         const int64_t vbegin = begin + head;
-        const int64_t nvec = (end - vbegin) / kPerVec;
-        const Vec* gv = reinterpret_cast<const Vec*>(
-            static_cast<const char*>(grad) + vbegin * kElemBytes);
+        const int nvec = static_cast<int>((end - vbegin) / kPerVec);
+        const __amdgpu_buffer_rsrc_t g =
+            rsrc(static_cast<const char*>(grad) + vbegin * kElemBytes, nvec * 16u);
 
-        for (int64_t base = 0; base < nvec; base += static_cast<int64_t>(kBlock) * kUnroll) {
-            Vec x[kUnroll];
+        for (int base = 0; base < nvec; base += kBlock * kUnroll) {
+            u32x4 x[kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int64_t i = base + u * kBlock + tid;
-                x[u] = (i < nvec) ? gv[i] : Vec(0);
-            }
+            for (int u = 0; u < kUnroll; ++u) x[u] = load_u32x4<kNormPolicy>(g, (base + u * kBlock + tid) * 16u);
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) acc[u] = T::accumulate(acc[u], x[u]);
+            for (int u = 0; u < kUnroll; ++u) acc[u] = add_vector<kBf16>(acc[u], x[u]);
         }
 
-        const int64_t tail = vbegin + nvec * kPerVec;
-        if (tid < end - tail) {
-            const double d = static_cast<double>(T::scalar(grad, tail + tid));
-            acc[0] = __builtin_fma(d, d, acc[0]);
-        }
+        const int64_t tail = vbegin + static_cast<int64_t>(nvec) * kPerVec;
+        if (tid < end - tail) acc[0] = add_square(acc[0], grad_at<kBf16>(grad, tail + tid));
     }
 
     double mine = acc[0];
@@ -214,7 +298,10 @@ __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
         q = q + __hip_atomic_load(&partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     const double total = block_sum(q, lds);
-    if (tid == 0) *d_sumsq = total;
+    if (tid == 0) {
+        *d_sumsq = total;
+        if (d_coef) *d_coef = clip_from_sumsq(total, max_norm);
+    }
 }
 
 // ----------------------------------------------------------------- clip ---
@@ -223,10 +310,7 @@ __global__ __launch_bounds__(kWave) void clip_coef_kernel(const double* d_sumsq,
                                                           float* d_coef)
 {
     if (threadIdx.x != 0) return;
-    const double norm = __builtin_sqrt(*d_sumsq);
-    double c = max_norm / (norm + 1e-6);
-    c = (c > 1.0) ? 1.0 : c;  // NaN stays NaN
-    *d_coef = static_cast<float>(c);
+    *d_coef = clip_from_sumsq(*d_sumsq, max_norm);
 }
 
 // ---------------------------------------------------------------- update ---
@@ -288,8 +372,7 @@ __device__ __forceinline__ void adamw_element(float& w, float& m, float& v, floa
 template <bool kBf16>
 __device__ __forceinline__ void adamw_scalar_at(const TensorEntry* te, int64_t i, const StepScalars& s)
 {
-    const float grad = kBf16 ? GradTraits<true>::scalar(te->grad, i)
-                             : GradTraits<false>::scalar(te->grad, i);
+    const float grad = grad_at<kBf16>(te->grad, i);
     float w = te->master[i], m = te->exp_avg[i], v = te->exp_avg_sq[i];
     adamw_element(w, m, v, grad, s);
     te->master[i] = w;
@@ -298,24 +381,60 @@ __device__ __forceinline__ void adamw_scalar_at(const TensorEntry* te, int64_t i
     if (te->param_bf16) te->param_bf16[i] = static_cast<uint16_t>(bf16_bits(w));
 }
 
-// Four consecutive gradients: 16 bytes of fp32 or 8 bytes of bf16.
-template <bool kBf16>
-struct QuadGrad;
+// The aligned body of one chunk: `nquad` groups of four elements starting at
+// element `q0` of the tensor, every stream 16-byte (fp32) or 8-byte (bf16)
+// aligned there.
+template <bool kBf16, int kUnroll>
+__device__ __forceinline__ void adamw_body(const TensorEntry* te, int64_t q0, int nquad,
+                                           const StepScalars& s)
+{
+    const int tid = threadIdx.x;
+    const __amdgpu_buffer_rsrc_t W = rsrc(te->master + q0, nquad * 16u);
+    const __amdgpu_buffer_rsrc_t M = rsrc(te->exp_avg + q0, nquad * 16u);
+    const __amdgpu_buffer_rsrc_t V = rsrc(te->exp_avg_sq + q0, nquad * 16u);
+    const __amdgpu_buffer_rsrc_t G = rsrc(static_cast<const char*>(te->grad) + q0 * (kBf16 ? 2 : 4),
+                                          nquad * (kBf16 ? 8u : 16u));
+    const bool copy = te->param_bf16 != nullptr;
+    const __amdgpu_buffer_rsrc_t P = rsrc(copy ? te->param_bf16 + q0 : nullptr, copy ? nquad * 8u : 0u);
 
-template <>
-struct QuadGrad<false> {
-    using Vec = f32x4;
-    __device__ static float get(const Vec& v, int k) { return v[k]; }
-};
-
-template <>
-struct QuadGrad<true> {
-    using Vec = u32x2;
-    __device__ static float get(const Vec& v, int k)
-    {
-        return (k & 1) ? bf16_hi(v[k >> 1]) : bf16_lo(v[k >> 1]);
+    for (int base = 0; base < nquad; base += kBlock * kUnroll) {
+        f32x4 w[kUnroll], m[kUnroll], v[kUnroll], g[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t q = base + u * kBlock + tid;
+            w[u] = load_f32x4(W, q * 16u);
+            m[u] = load_f32x4(M, q * 16u);
+            v[u] = load_f32x4(V, q * 16u);
+            if (kBf16) {
+                const u32x2 h = load_u32x2(G, q * 8u);
+                g[u] = f32x4{bf16_lo(h[0]), bf16_hi(h[0]), bf16_lo(h[1]), bf16_hi(h[1])};
+            } else {
+                g[u] = load_f32x4(G, q * 16u);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t q = base + u * kBlock + tid;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float wk = w[u][k], mk = m[u][k], vk = v[u][k];
+                adamw_element(wk, mk, vk, g[u][k], s);
+                w[u][k] = wk;
+                m[u][k] = mk;
+                v[u][k] = vk;
+            }
+            store_f32x4(w[u], W, q * 16u);
+            store_f32x4(m[u], M, q * 16u);
+            store_f32x4(v[u], V, q * 16u);
+            if (copy) {
+                u32x2 packed;
+                packed[0] = bf16_bits(w[u][0]) | (bf16_bits(w[u][1]) << 16);
+                packed[1] = bf16_bits(w[u][2]) | (bf16_bits(w[u][3]) << 16);
+                store_u32x2(packed, P, q * 8u);
+            }
+        }
     }
-};
+}
 
 template <bool kBf16, int kUnroll>
 __global__ __launch_bounds__(kBlock) void adamw_step_kernel(
@@ -323,15 +442,15 @@ __global__ __launch_bounds__(kBlock) void adamw_step_kernel(
     int n_chunks, int64_t chunk_elems, uint64_t tag, const float* d_coef, int32_t* d_step,
     HyperParams hp)
 {
-    using GVec = typename QuadGrad<kBf16>::Vec;
-
     if (header->tag != tag) return;  // tables overwritten: touch nothing
 
     const int tid = threadIdx.x;
     const int64_t t = static_cast<int64_t>(*d_step) + 1;
     const StepScalars s = step_scalars(t, hp, d_coef ? *d_coef : 1.0f);
 
-    for (int c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+    const ChunkWalk<MPS_STEP_CONTIGUOUS != 0> walk(n_chunks);
+    for (int k = walk.first; k < walk.stop; k += walk.step) {
+        const int c = MPS_STEP_REVERSE ? n_chunks - 1 - k : k;
         const TensorEntry* te = &tensors[chunk_map[c]];
         const int64_t begin = static_cast<int64_t>(c - te->first_chunk) * chunk_elems;
         const int64_t end = min(begin + chunk_elems, te->numel);
@@ -340,57 +459,11 @@ __global__ __launch_bounds__(kBlock) void adamw_step_kernel(
             for (int64_t i = begin + tid; i < end; i += kBlock) adamw_scalar_at<kBf16>(te, i, s);
             continue;
         }
-
         const int64_t qbegin = min(begin + te->head, end);
         if (tid < qbegin - begin) adamw_scalar_at<kBf16>(te, begin + tid, s);
-        const int64_t nquad = (end - qbegin) / 4;
-
-        f32x4* W = reinterpret_cast<f32x4*>(te->master + qbegin);
-        f32x4* M = reinterpret_cast<f32x4*>(te->exp_avg + qbegin);
-        f32x4* V = reinterpret_cast<f32x4*>(te->exp_avg_sq + qbegin);
-        const GVec* G = reinterpret_cast<const GVec*>(
-            static_cast<const char*>(te->grad) + qbegin * (kBf16 ? 2 : 4));
-        u32x2* P = te->param_bf16 ? reinterpret_cast<u32x2*>(te->param_bf16 + qbegin) : nullptr;
-
-        for (int64_t base = 0; base < nquad; base += static_cast<int64_t>(kBlock) * kUnroll) {
-            f32x4 w[kUnroll], m[kUnroll], v[kUnroll];
-            GVec g[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int64_t i = base + u * kBlock + tid;
-                if (i < nquad) {
-                    w[u] = W[i];
-                    m[u] = M[i];
-                    v[u] = V[i];
-                    g[u] = G[i];
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int64_t i = base + u * kBlock + tid;
-                if (i < nquad) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        float wk = w[u][k], mk = m[u][k], vk = v[u][k];
-                        adamw_element(wk, mk, vk, QuadGrad<kBf16>::get(g[u], k), s);
-                        w[u][k] = wk;
-                        m[u][k] = mk;
-                        v[u][k] = vk;
-                    }
-                    W[i] = w[u];
-                    M[i] = m[u];
-                    V[i] = v[u];
-                    if (P) {
-                        u32x2 packed;
-                        packed[0] = bf16_bits(w[u][0]) | (bf16_bits(w[u][1]) << 16);
-                        packed[1] = bf16_bits(w[u][2]) | (bf16_bits(w[u][3]) << 16);
-                        P[i] = packed;
-                    }
-                }
-            }
-        }
-
-        const int64_t tail = qbegin + nquad * 4;
+        const int nquad = static_cast<int>((end - qbegin) / 4);
+        adamw_body<kBf16, kUnroll>(te, qbegin, nquad, s);
+        const int64_t tail = qbegin + static_cast<int64_t>(nquad) * 4;
         if (tid < end - tail) adamw_scalar_at<kBf16>(te, tail + tid, s);
     }
 
@@ -408,20 +481,17 @@ __global__ __launch_bounds__(kBlock) void adamw_step_kernel(
 
 // --------------------------------------------------------------- launchers ---
 
-constexpr int kNormUnroll = 4;
-constexpr int kStepUnroll = 2;
-
 hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid, double* d_sumsq,
-                            hipStream_t stream)
+                            double max_norm, float* d_coef, hipStream_t stream)
 {
     if (grad_bf16) {
-        grad_norm_kernel<true, kNormUnroll><<<grid, kBlock, 0, stream>>>(
+        grad_norm_kernel<true, MPS_NORM_UNROLL><<<grid, kBlock, 0, stream>>>(
             ws.header, ws.tensors, ws.chunk_map, ws.partials, ws.n_chunks, ws.chunk_elems, ws.tag,
-            d_sumsq);
+            d_sumsq, max_norm, d_coef);
     } else {
-        grad_norm_kernel<false, kNormUnroll><<<grid, kBlock, 0, stream>>>(
+        grad_norm_kernel<false, MPS_NORM_UNROLL><<<grid, kBlock, 0, stream>>>(
             ws.header, ws.tensors, ws.chunk_map, ws.partials, ws.n_chunks, ws.chunk_elems, ws.tag,
-            d_sumsq);
+            d_sumsq, max_norm, d_coef);
     }
     return hipGetLastError();
 }
@@ -438,11 +508,11 @@ hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, int grid,
                              hipStream_t stream)
 {
     if (grad_bf16) {
-        adamw_step_kernel<true, kStepUnroll><<<grid, kBlock, 0, stream>>>(
+        adamw_step_kernel<true, MPS_STEP_UNROLL><<<grid, kBlock, 0, stream>>>(
             ws.header, ws.tensors, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag, d_coef,
             d_step, hp);
     } else {
-        adamw_step_kernel<false, kStepUnroll><<<grid, kBlock, 0, stream>>>(
+        adamw_step_kernel<false, MPS_STEP_UNROLL><<<grid, kBlock, 0, stream>>>(
             ws.header, ws.tensors, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag, d_coef,
             d_step, hp);
     }

@@ -13,13 +13,34 @@
 
 namespace mps {
 
-constexpr int kBlock = 256;               // threads per block, both kernels
-constexpr int kNormMaxBlocks = 2048;      // norm grid cap (size of the partials)
-constexpr int kStepMaxBlocks = 2048;      // update grid cap
-constexpr int64_t kChunkQuantum = 2048;   // chunk sizes are multiples of this
-constexpr int64_t kChunkMin = 2048;
-constexpr int64_t kChunkMax = 65536;
-constexpr int64_t kChunkTarget = 8192;    // aim for about this many chunks
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X).
+// Both kernels walk the chunks with a persistent grid (block b takes chunks
+// b, b + G, ...): few, long-lived waves streaming neighbouring addresses
+// beat one block per chunk on MI355X's HBM3E (measured: 2 update blocks and
+// 1 norm block per CU).
+#ifndef MPS_NORM_MAX_BLOCKS
+#define MPS_NORM_MAX_BLOCKS 256    // norm grid cap (= number of fp64 partials)
+#endif
+#ifndef MPS_STEP_MAX_BLOCKS
+#define MPS_STEP_MAX_BLOCKS 512    // update grid cap
+#endif
+#ifndef MPS_CHUNK_MIN
+#define MPS_CHUNK_MIN 2048
+#endif
+#ifndef MPS_CHUNK_MAX
+#define MPS_CHUNK_MAX 16384
+#endif
+#ifndef MPS_CHUNK_TARGET
+#define MPS_CHUNK_TARGET 3072       // aim for about this many chunks
+#endif
+
+constexpr int kBlock = 256;                        // threads per block, both kernels
+constexpr int kNormMaxBlocks = MPS_NORM_MAX_BLOCKS;
+constexpr int kStepMaxBlocks = MPS_STEP_MAX_BLOCKS;
+constexpr int64_t kChunkQuantum = 2048;            // chunk sizes are multiples of this
+constexpr int64_t kChunkMin = MPS_CHUNK_MIN;
+constexpr int64_t kChunkMax = MPS_CHUNK_MAX;
+constexpr int64_t kChunkTarget = MPS_CHUNK_TARGET;
 
 struct alignas(64) WorkspaceHeader {
     uint32_t norm_ticket;   // blocks of the norm kernel that have finished

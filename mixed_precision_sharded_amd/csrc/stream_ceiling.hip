@@ -1,0 +1,104 @@
+// Practical HBM ceilings for the roofline of the AdamW step: plain streaming
+// kernels with the same access patterns and trivial arithmetic — read only,
+// copy, and 4 reads / 3 writes (master, m, v, gradient in; master, m, v out).
+// Usage: stream_ceiling [floats per buffer]   (default 62,736,416: one
+// 8B-parameter model's FSDP shard at 128-way).  Prints GB/s per variant.
+// Every kernel is a grid-stride loop with i < n guards; buffers hold n f32x4.
+#include <hip/hip_runtime.h>
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+#include <string>
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+#define CHECK(x) do { hipError_t e = (x); if (e != hipSuccess) { printf("HIP error %s at %d\n", hipGetErrorString(e), __LINE__); exit(1);} } while (0)
+
+template <int U, bool NT>
+__global__ __launch_bounds__(256) void read_kernel(const f4* __restrict__ a, long n, float* out) {
+  float acc = 0.f;
+  long stride = (long)gridDim.x * 256 * U;
+  for (long base = (long)blockIdx.x * 256 * U + threadIdx.x; base < n; base += stride) {
+    f4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) { long i = base + u * 256; x[u] = i < n ? (NT ? __builtin_nontemporal_load(&a[i]) : a[i]) : f4(0); }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc += x[u][0] + x[u][1] + x[u][2] + x[u][3];
+  }
+  if (acc == 123.456f) out[0] = acc;
+}
+
+template <int U, bool NT>
+__global__ __launch_bounds__(256) void copy_kernel(const f4* __restrict__ a, f4* __restrict__ b, long n) {
+  long stride = (long)gridDim.x * 256 * U;
+  for (long base = (long)blockIdx.x * 256 * U + threadIdx.x; base < n; base += stride) {
+    f4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) { long i = base + u * 256; if (i < n) x[u] = NT ? __builtin_nontemporal_load(&a[i]) : a[i]; }
+#pragma unroll
+    for (int u = 0; u < U; ++u) { long i = base + u * 256; if (i < n) { if (NT) __builtin_nontemporal_store(x[u], &b[i]); else b[i] = x[u]; } }
+  }
+}
+
+// 4 reads (w, m, v, g), 3 writes (w, m, v).
+template <int U, bool NT>
+__global__ __launch_bounds__(256) void adam_like(f4* __restrict__ w, f4* __restrict__ m, f4* __restrict__ v, const f4* __restrict__ g, long n) {
+  long stride = (long)gridDim.x * 256 * U;
+  for (long base = (long)blockIdx.x * 256 * U + threadIdx.x; base < n; base += stride) {
+    f4 W[U], M[U], V[U], G[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) { long i = base + u * 256; if (i < n) {
+      W[u] = NT ? __builtin_nontemporal_load(&w[i]) : w[i];
+      M[u] = NT ? __builtin_nontemporal_load(&m[i]) : m[i];
+      V[u] = NT ? __builtin_nontemporal_load(&v[i]) : v[i];
+      G[u] = NT ? __builtin_nontemporal_load(&g[i]) : g[i]; } }
+#pragma unroll
+    for (int u = 0; u < U; ++u) { long i = base + u * 256; if (i < n) {
+      f4 mm = M[u] * 0.9f + G[u] * 0.1f; f4 vv = V[u] * 0.95f + G[u] * G[u] * 0.05f; f4 ww = W[u] - mm * 0.001f;
+      if (NT) { __builtin_nontemporal_store(ww, &w[i]); __builtin_nontemporal_store(mm, &m[i]); __builtin_nontemporal_store(vv, &v[i]); }
+      else { w[i] = ww; m[i] = mm; v[i] = vv; } } }
+  }
+}
+
+template <typename F>
+float time_ms(F launch, int reps) {
+  hipEvent_t a, b; CHECK(hipEventCreate(&a)); CHECK(hipEventCreate(&b));
+  for (int i = 0; i < 3; ++i) launch();
+  CHECK(hipDeviceSynchronize());
+  CHECK(hipEventRecord(a));
+  for (int i = 0; i < reps; ++i) launch();
+  CHECK(hipEventRecord(b)); CHECK(hipEventSynchronize(b));
+  float ms; CHECK(hipEventElapsedTime(&ms, a, b));
+  CHECK(hipEventDestroy(a)); CHECK(hipEventDestroy(b));
+  return ms / reps;
+}
+
+int main(int argc, char** argv) {
+  long n = 62736416 / 4;  // f32x4 per buffer (the 8B / 128 shard)
+  if (argc > 1) n = atol(argv[1]) / 4;
+  f4 *w, *m, *v, *g, *b; float* out;
+  CHECK(hipMalloc(&w, n * 16)); CHECK(hipMalloc(&m, n * 16)); CHECK(hipMalloc(&v, n * 16));
+  CHECK(hipMalloc(&g, n * 16)); CHECK(hipMalloc(&b, n * 16)); CHECK(hipMalloc(&out, 16));
+  CHECK(hipMemset(w, 0, n * 16)); CHECK(hipMemset(m, 0, n * 16)); CHECK(hipMemset(v, 0, n * 16));
+  CHECK(hipMemset(g, 0, n * 16)); CHECK(hipMemset(b, 0, n * 16));
+  hipDeviceProp_t prop; CHECK(hipGetDeviceProperties(&prop, 0));
+  printf("device %s CUs %d clock %d kHz L2 %d MB, n=%ld floats per buffer\n", prop.gcnArchName, prop.multiProcessorCount, prop.clockRate, prop.l2CacheSize >> 20, n * 4);
+  int cus = prop.multiProcessorCount;
+  const int reps = 20;
+  for (int bpc : {2, 4, 8, 16, 32}) {
+    int grid = cus * bpc;
+#define RUN(NAME, U, NT, BYTES, ...) { float ms = time_ms([&]{ NAME<U, NT><<<grid, 256>>>(__VA_ARGS__); }, reps); \
+      printf("%-10s U=%d NT=%d blocks/CU=%2d  %8.1f us  %7.0f GB/s\n", #NAME, U, (int)NT, bpc, ms * 1e3, (double)(BYTES) / (ms * 1e-3) / 1e9); fflush(stdout); }
+    RUN(read_kernel, 4, false, n * 16.0, g, n, out);
+    RUN(read_kernel, 8, false, n * 16.0, g, n, out);
+    RUN(read_kernel, 4, true, n * 16.0, g, n, out);
+    RUN(copy_kernel, 2, false, n * 32.0, g, b, n);
+    RUN(copy_kernel, 4, false, n * 32.0, g, b, n);
+    RUN(copy_kernel, 4, true, n * 32.0, g, b, n);
+    RUN(adam_like, 1, false, n * 112.0, w, m, v, g, n);
+    RUN(adam_like, 2, false, n * 112.0, w, m, v, g, n);
+    RUN(adam_like, 2, true, n * 112.0, w, m, v, g, n);
+    RUN(adam_like, 4, false, n * 112.0, w, m, v, g, n);
+  }
+  return 0;
+}

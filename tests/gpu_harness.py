@@ -35,6 +35,11 @@ class Step:
         binding.grad_norm_sq(self.tl, self.sumsq)
         return self
 
+    def norm_clip(self, max_norm):
+        """Norm and clip coefficient from one launch."""
+        binding.grad_norm_sq(self.tl, self.sumsq, max_norm, self.coef)
+        return self
+
     def clip(self, max_norm):
         binding.clip_coef(self.sumsq, max_norm, self.coef)
         return self
@@ -45,8 +50,8 @@ class Step:
         return self
 
     def full(self, w):
-        """norm -> clip -> update with a workload's hyperparameters."""
-        return self.norm().clip(w.max_norm).update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
+        """norm + clip (one launch) -> update with a workload's hyperparameters."""
+        return self.norm_clip(w.max_norm).update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
 
     def results(self):
         torch.cuda.synchronize()

@@ -111,8 +111,12 @@ def test_argument_errors(lib):
     assert lib.adamw_multi_tensor_step(odd, 1, 0, None, good["step"], 3e-4, 0.9, 0.95, 1e-8,
                                        0.1, ws, 1 << 30, None) == EINVAL
     odd1 = fake_list(1, misalign=1)
-    assert lib.grad_norm_sq(odd1, 1, 1, ctypes.c_void_p(0x7d0000000000), ws, 1 << 30,
-                            None) == EINVAL
+    assert lib.grad_norm_sq(odd1, 1, 1, ctypes.c_void_p(0x7d0000000000), 0.0, None, ws,
+                            1 << 30, None) == EINVAL
+    # a clip output needs a finite positive max_norm
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert lib.grad_norm_sq(arr, 1, 0, ctypes.c_void_p(0x7d0000000000), bad,
+                                ctypes.c_void_p(0x7d0000000100), ws, 1 << 30, None) == EINVAL
 
 
 def test_workspace_errors(lib):
@@ -127,9 +131,9 @@ def test_workspace_errors(lib):
     assert lib.adamw_multi_tensor_step(*args, ctypes.c_void_p(0x7e0000000000), need - 1,
                                        None) == EWORKSPACE
     assert "too small" in binding.last_error()
-    assert lib.grad_norm_sq(arr, 1, 0, ctypes.c_void_p(0x7d0000000000), None, need,
+    assert lib.grad_norm_sq(arr, 1, 0, ctypes.c_void_p(0x7d0000000000), 1.0, None, None, need,
                             None) == EWORKSPACE
-    assert lib.grad_norm_sq(arr, 1, 0, None, ctypes.c_void_p(0x7e0000000000), need,
+    assert lib.grad_norm_sq(arr, 1, 0, None, 1.0, None, ctypes.c_void_p(0x7e0000000000), need,
                             None) == EINVAL
 
 

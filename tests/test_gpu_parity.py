@@ -49,10 +49,12 @@ def make_cols(sizes, grad_bf16, copy, seed, warm=True, grad_std=1e-3, device=DEV
     return cols
 
 
-def run_and_check(cols, t, max_norm=1.0, what="", hp=HP, use_coef=True):
-    """One GPU step vs the oracle; returns (S_gpu, c_gpu, stats)."""
+def run_and_check(cols, t, max_norm=1.0, what="", hp=HP, use_coef=True, fused=True):
+    """One GPU step vs the oracle; returns (S_gpu, c_gpu, stats).  `fused`:
+    the clip coefficient comes from the norm's launch (else from clip_coef)."""
     host = host_copy(cols)
-    st = Step(cols, completed_steps=t - 1).norm().clip(max_norm)
+    st = Step(cols, completed_steps=t - 1)
+    st = st.norm_clip(max_norm) if fused else st.norm().clip(max_norm)
     st.update(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["wd"], use_coef=use_coef)
     S, c, step = st.results()
     assert step == t, f"{what}: step counter {step}, expected {t}"
@@ -78,12 +80,13 @@ def run_and_check(cols, t, max_norm=1.0, what="", hp=HP, use_coef=True):
 RAGGED = [0, 1, 3, 4, 5, 7, 8, 9, 63, 64, 65, 2047, 2048, 2049, 4097, 100003]
 
 
-@pytest.mark.parametrize("grad_bf16,copy", [(False, False), (True, True), (False, True),
-                                            (True, False)])
-def test_ragged_list(grad_bf16, copy):
-    say(f"ragged list grad_bf16={grad_bf16} copy={copy}")
+@pytest.mark.parametrize("grad_bf16,copy,fused", [(False, False, True), (True, True, True),
+                                                  (False, True, False), (True, False, False)])
+def test_ragged_list(grad_bf16, copy, fused):
+    say(f"ragged list grad_bf16={grad_bf16} copy={copy} fused clip={fused}")
     cols = make_cols(RAGGED, grad_bf16, copy, seed=1)
-    _, _, stats = run_and_check(cols, t=3, what=f"ragged bf16={grad_bf16} copy={copy}")
+    _, _, stats = run_and_check(cols, t=3, what=f"ragged bf16={grad_bf16} copy={copy}",
+                                fused=fused)
     assert stats["w"][0] == stats["m"][0] == stats["v"][0] == 0, "expected bitwise agreement"
 
 
@@ -180,6 +183,17 @@ def test_clip_bitwise_given_the_same_sum():
         want = np.array([o.clip_coef(s, max_norm) for s in vals], np.float32)
         same = (got.view(np.uint32) == want.view(np.uint32)) | (np.isnan(got) & np.isnan(want))
         assert same.all(), (max_norm, np.array(vals)[~same], got[~same], want[~same])
+
+
+def test_fused_clip_equals_standalone_clip():
+    """The coefficient written by the norm's launch equals clip_coef's."""
+    for seed, std, max_norm in ((20, 1e-3, 1.0), (21, 1.0, 0.5), (22, 1e-6, 1.0), (23, 1e2, 3.0)):
+        cols = make_cols([100003, 17, 4096], seed % 2 == 0, False, seed=seed, grad_std=std)
+        st = Step(cols).norm_clip(max_norm)
+        S1, c1, _ = st.results()
+        st.clip(max_norm)
+        S2, c2, _ = st.results()
+        assert S1 == S2 and c1 == c2 == oracle.default().clip_coef(S1, max_norm), (seed, c1, c2)
 
 
 # ---------------------------------------------------- determinism, resume ---
