@@ -1,0 +1,90 @@
+"""GPU parity at the full sizes of the two largest workloads, in the launch
+configuration bench.py times (same library calls on the same list).
+
+The sum of squares is checked against the oracle over every gradient; the
+update is checked element by element on sampled positions (random ones, the
+first and last elements of every tensor, and chunk edges), which the oracle
+computes one by one from the inputs gathered before the step.  Whole-tensor
+properties (finite state, step counter) are checked at every position.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_harness import NORM_REL_TOL, Step, check_bf16, check_f32, sample_indices, say
+from mixed_precision_sharded_amd import synth
+from mixed_precision_sharded_amd.configs import WORKLOADS, warm
+from mixed_precision_sharded_amd.synth import to_numpy
+
+pytestmark = pytest.mark.gpu
+
+FIELDS = ("master", "exp_avg", "exp_avg_sq")
+
+
+@pytest.fixture(autouse=True)
+def _gpu_only():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def sampled_parity(w, per_tensor, seed):
+    say(f"workload {w.name}: {w.numel:,} params in {w.n_tensors} tensors; generating")
+    cols = synth.workload_inputs(w, "cuda")
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(seed)
+    idx = [sample_indices(n, per_tensor, gen) for _, n in w.tensors]
+    idx_dev = [torch.tensor(ix, dtype=torch.int64, device="cuda") for ix in idx]
+    before = {k: [to_numpy(t[ix]) for t, ix in zip(cols[k], idx_dev)] for k in FIELDS + ("grad",)}
+
+    say("oracle sum of squares over every gradient")
+    o = oracle.default()
+    S_ref = o.grad_norm_sq(to_numpy(g) for g in cols["grad"])  # one tensor on the host at a time
+
+    say("GPU step")
+    st = Step(cols, completed_steps=w.step - 1).full(w)
+    S, c, step = st.results()
+    assert step == w.step
+    assert abs(S - S_ref) <= NORM_REL_TOL * S_ref, (S, S_ref)
+    assert c == o.clip_coef(S, w.max_norm)
+    say(f"S={S:.9e} oracle {S_ref:.9e} rel {abs(S - S_ref) / S_ref:.2e} c={c}")
+
+    nbit = 0
+    n_checked = 0
+    for i in range(w.n_tensors):
+        wv, mv, vv = (before[k][i].copy() for k in FIELDS)
+        gv = before["grad"][i]
+        pv = np.zeros(wv.size, np.uint16) if w.copy_bf16 else None
+        o.adamw_step(wv, mv, vv, gv, pv, c, w.step, w.lr, w.beta1, w.beta2, w.eps,
+                     w.weight_decay)
+        for k, want in zip(FIELDS, (wv, mv, vv)):
+            got = to_numpy(cols[k][i][idx_dev[i]])
+            nb, _ = check_f32(got, want, f"{w.name} tensor {i} {k}")
+            nbit += nb
+        if w.copy_bf16:
+            check_bf16(to_numpy(cols["param_bf16"][i][idx_dev[i]]), pv,
+                       f"{w.name} tensor {i} param_bf16")
+        n_checked += wv.size
+        assert bool(torch.isfinite(cols["master"][i]).all()), i
+    say(f"{n_checked:,} sampled elements checked; {nbit} not bitwise equal")
+    del st, cols
+
+
+def test_llama405b_share_sampled():
+    sampled_parity(WORKLOADS[5], per_tensor=2000, seed=50)
+
+
+def test_llama405b_share_warm_moments_sampled():
+    sampled_parity(warm(WORKLOADS[5]), per_tensor=2000, seed=51)
+
+
+def test_llama8b_full_list_sampled():
+    """8,030,261,248 parameters (128.5 GB of state) on one GPU."""
+    free, total = torch.cuda.mem_get_info()
+    need = WORKLOADS[3].numel * WORKLOADS[3].state_bytes_per_param() + (8 << 30)
+    if free < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB free, {free / 2**30:.0f} GiB available")
+    sampled_parity(WORKLOADS[3], per_tensor=20000, seed=52)
