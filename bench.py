@@ -198,38 +198,51 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(w, cols, budget_s):
-    """The oracle, untuned and single-threaded, on the host: the whole step
-    (norm, clip, update) over the first workload tensors that fit the time
-    budget, repeated until it is spent.  Scaled to params/s."""
-    import numpy as np
+CPU_SAMPLE_MAX_ELEMS = 64 << 20
 
+
+def cpu_baseline(w, cols, budget_s):
+    """The oracle, untuned and single-threaded, on the host: whole steps
+    (norm, clip, update) over a bounded sample of the workload — its first
+    tensors, at most CPU_SAMPLE_MAX_ELEMS elements (the whole shard when it is
+    smaller) — repeated until the time budget is spent.  Scaled to params/s."""
     import oracle
     from mixed_precision_sharded_amd.synth import to_numpy
 
     o = oracle.default()
-    host = {k: [None if t is None else to_numpy(t).copy() for t in v] for k, v in cols.items()}
+    host = {k: [] for k in cols}
+    taken = 0
+    for i in range(w.n_tensors):
+        n = min(w.tensors[i][1], CPU_SAMPLE_MAX_ELEMS - taken)
+        if n <= 0:
+            break
+        for k in cols:
+            t = cols[k][i]
+            host[k].append(None if t is None else to_numpy(t[:n]).copy())
+        taken += n
+    n_tensors = len(host["master"])
     t_done = w.step
     steps = 0
-    elems = 0
     t0 = time.perf_counter()
     while True:
         S = o.grad_norm_sq(host["grad"])
         c = o.clip_coef(S, w.max_norm)
-        for i in range(w.n_tensors):
+        for i in range(n_tensors):
             o.adamw_step(host["master"][i], host["exp_avg"][i], host["exp_avg_sq"][i],
                          host["grad"][i], host["param_bf16"][i], c, t_done, w.lr, w.beta1,
                          w.beta2, w.eps, w.weight_decay)
         t_done += 1
         steps += 1
-        elems += w.numel
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    log(f"cpu oracle: {steps} steps of {w.numel:,} params in {dt:.2f} s")
-    return {"value": elems / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole {w.name} shard ({w.numel:,} params): norm + clip + update, "
-                      f"{steps} consecutive steps, 1 thread, {dt:.1f} s",
+    whole = taken == w.numel
+    what = (f"whole {w.name} shard" if whole else
+            f"first {n_tensors} of {w.n_tensors} tensors of {w.name}")
+    log(f"cpu oracle: {steps} steps of {taken:,} params in {dt:.2f} s")
+    return {"value": taken * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{what} ({taken:,} params): norm + clip + update, {steps} consecutive "
+                      f"steps, 1 thread, {dt:.1f} s",
             "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
 
 

@@ -28,7 +28,7 @@
 #include "kernels.h"
 
 #ifndef MPS_STEP_UNROLL
-#define MPS_STEP_UNROLL 2   // groups of four elements per thread per iteration
+#define MPS_STEP_UNROLL 1   // groups of four elements per thread per tile
 #endif
 #ifndef MPS_NORM_UNROLL
 #define MPS_NORM_UNROLL 8   // 16-byte vectors per thread per iteration
@@ -40,15 +40,6 @@
 #endif
 #ifndef MPS_STORE_POLICY
 #define MPS_STORE_POLICY 2  // update: master, m, v, bf16 copy
-#endif
-#ifndef MPS_STEP_CONTIGUOUS
-#define MPS_STEP_CONTIGUOUS 0  // 1: each update block takes one contiguous run of chunks
-#endif
-#ifndef MPS_NORM_CONTIGUOUS
-#define MPS_NORM_CONTIGUOUS 0  // 1: each norm block takes one contiguous run of chunks
-#endif
-#ifndef MPS_STEP_REVERSE
-#define MPS_STEP_REVERSE 0  // 1: the update walks the chunks from the last one
 #endif
 #ifndef MPS_NORM_POLICY
 #define MPS_NORM_POLICY 0   // norm: gradient (read again by the update)
@@ -169,26 +160,6 @@ __device__ __forceinline__ double add_square(double acc, float x)
     return __builtin_fma(d, d, acc);  // d*d is exact in fp64: one rounding
 }
 
-// Chunks of block b: either b, b + G, b + 2G, ... (kContiguous = false) or
-// the run [b * n / G, (b + 1) * n / G).  Returns the k-th chunk, or -1.
-template <bool kContiguous>
-struct ChunkWalk {
-    int first, step, stop;
-    __device__ ChunkWalk(int n_chunks)
-    {
-        const int b = blockIdx.x, g = gridDim.x;
-        if (kContiguous) {
-            first = static_cast<int>(static_cast<int64_t>(b) * n_chunks / g);
-            stop = static_cast<int>(static_cast<int64_t>(b + 1) * n_chunks / g);
-            step = 1;
-        } else {
-            first = b;
-            stop = n_chunks;
-            step = g;
-        }
-    }
-};
-
 // c = min(1, max_norm / (sqrt(S) + 1e-6)) in fp64, rounded once to fp32;
 // a NaN S gives NaN (the comparison is false), an infinite S gives 0.
 __device__ __forceinline__ float clip_from_sumsq(double sumsq, double max_norm)
@@ -245,32 +216,67 @@ __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
 
-    const ChunkWalk<MPS_NORM_CONTIGUOUS != 0> walk(n_chunks);
-    for (int c = walk.first; c < walk.stop; c += walk.step) {
-        const TensorEntry* te = &tensors[chunk_map[c]];
-        const void* grad = te->grad;
-        const int64_t begin = static_cast<int64_t>(c - te->first_chunk) * chunk_elems;
-        const int64_t end = min(begin + chunk_elems, te->numel);
+    // Block b takes the contiguous run of chunks [b*n/G, (b+1)*n/G).  Within
+    // the run, consecutive chunks of one tensor are one contiguous stretch of
+    // memory, streamed as a single body so the load pipeline only restarts
+    // at tensor boundaries.
+    const int run_first = static_cast<int>(static_cast<int64_t>(blockIdx.x) * n_chunks / gridDim.x);
+    const int run_stop = static_cast<int>(static_cast<int64_t>(blockIdx.x + 1) * n_chunks / gridDim.x);
+    for (int c = run_first; c < run_stop;) {
+        const TensorEntry te = tensors[chunk_map[c]];
+        const int tensor_chunks = static_cast<int>((te.numel + chunk_elems - 1) / chunk_elems);
+        const int c_lo = c;  // this body: chunks [c_lo, c_hi) of one tensor
+        const int c_hi = min(run_stop, te.first_chunk + tensor_chunks);
+        c = c_hi;
+        const void* grad = te.grad;
+        const int64_t begin = static_cast<int64_t>(c_lo - te.first_chunk) * chunk_elems;
+        const int64_t end = min(static_cast<int64_t>(c_hi - te.first_chunk) * chunk_elems, te.numel);
 
         // Peel elements until the gradient address is 16-byte aligned.
         const uintptr_t addr = reinterpret_cast<uintptr_t>(grad) + begin * kElemBytes;
         int64_t head = static_cast<int64_t>((16 - (addr & 15)) & 15) / kElemBytes;
         head = min(head, end - begin);
         if (tid < head) acc[0] = add_square(acc[0], grad_at<kBf16>(grad, begin + tid));
-        const int64_t vbegin = begin + head;
-        const int nvec = static_cast<int>((end - vbegin) / kPerVec);
-        const __amdgpu_buffer_rsrc_t g =
-            rsrc(static_cast<const char*>(grad) + vbegin * kElemBytes, nvec * 16u);
+        int64_t vbegin = begin + head;
+        const int64_t nvec_all = (end - vbegin) / kPerVec;
+        const int64_t tail = vbegin + nvec_all * kPerVec;
 
-        for (int base = 0; base < nvec; base += kBlock * kUnroll) {
-            u32x4 x[kUnroll];
+        // The body in pieces of at most 2^26 vectors (1 GiB), so that byte
+        // offsets fit the 32-bit buffer addressing.
+        for (int64_t done = 0; done < nvec_all;) {
+            const int nvec = static_cast<int>(min(nvec_all - done, static_cast<int64_t>(1) << 26));
+            const __amdgpu_buffer_rsrc_t g =
+                rsrc(static_cast<const char*>(grad) + (vbegin + done * kPerVec) * kElemBytes,
+                     static_cast<uint32_t>(nvec) * 16u);
+            done += nvec;
+
+            // Two register sets in turn: the loads of one are in flight while
+            // the other is accumulated.  Offsets past the body read zeros
+            // without touching memory, so the loop needs no bounds branches.
+            constexpr int kStride = kBlock * kUnroll;
+            u32x4 x[kUnroll], y[kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) x[u] = load_u32x4<kNormPolicy>(g, (base + u * kBlock + tid) * 16u);
+            for (int u = 0; u < kUnroll; ++u) x[u] = load_u32x4<kNormPolicy>(g, (u * kBlock + tid) * 16u);
+            for (int base = 0; base < nvec; base += 2 * kStride) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) acc[u] = add_vector<kBf16>(acc[u], x[u]);
+                for (int u = 0; u < kUnroll; ++u) {
+                    y[u] = load_u32x4<kNormPolicy>(g, (base + kStride + u * kBlock + tid) * 16u);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) acc[u] = add_vector<kBf16>(acc[u], x[u]);
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    x[u] = load_u32x4<kNormPolicy>(g, (base + 2 * kStride + u * kBlock + tid) * 16u);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (base + kStride < nvec) {  // uniform: skip the math of an empty tile
+#pragma unroll
+                    for (int u = 0; u < kUnroll; ++u) acc[u] = add_vector<kBf16>(acc[u], y[u]);
+                }
+            }
         }
 
-        const int64_t tail = vbegin + static_cast<int64_t>(nvec) * kPerVec;
         if (tid < end - tail) acc[0] = add_square(acc[0], grad_at<kBf16>(grad, tail + tid));
     }
 
@@ -397,42 +403,63 @@ __device__ __forceinline__ void adamw_body(const TensorEntry* te, int64_t q0, in
     const bool copy = te->param_bf16 != nullptr;
     const __amdgpu_buffer_rsrc_t P = rsrc(copy ? te->param_bf16 + q0 : nullptr, copy ? nquad * 8u : 0u);
 
-    for (int base = 0; base < nquad; base += kBlock * kUnroll) {
+    // One tile = kUnroll groups of four per thread.  Two tiles are held in
+    // registers in turn: the loads of the next tile are in flight while the
+    // current one is computed and stored.  Lanes past the body read zeros and
+    // their stores are dropped, so the tail needs no branches.
+    struct Tile {
         f32x4 w[kUnroll], m[kUnroll], v[kUnroll], g[kUnroll];
+    };
+    auto load_tile = [&](Tile& t, int base) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint32_t q = base + u * kBlock + tid;
-            w[u] = load_f32x4(W, q * 16u);
-            m[u] = load_f32x4(M, q * 16u);
-            v[u] = load_f32x4(V, q * 16u);
+            t.w[u] = load_f32x4(W, q * 16u);
+            t.m[u] = load_f32x4(M, q * 16u);
+            t.v[u] = load_f32x4(V, q * 16u);
             if (kBf16) {
                 const u32x2 h = load_u32x2(G, q * 8u);
-                g[u] = f32x4{bf16_lo(h[0]), bf16_hi(h[0]), bf16_lo(h[1]), bf16_hi(h[1])};
+                t.g[u] = f32x4{bf16_lo(h[0]), bf16_hi(h[0]), bf16_lo(h[1]), bf16_hi(h[1])};
             } else {
-                g[u] = load_f32x4(G, q * 16u);
+                t.g[u] = load_f32x4(G, q * 16u);
             }
         }
+    };
+    auto update_tile = [&](Tile& t, int base) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint32_t q = base + u * kBlock + tid;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                float wk = w[u][k], mk = m[u][k], vk = v[u][k];
-                adamw_element(wk, mk, vk, g[u][k], s);
-                w[u][k] = wk;
-                m[u][k] = mk;
-                v[u][k] = vk;
+                float wk = t.w[u][k], mk = t.m[u][k], vk = t.v[u][k];
+                adamw_element(wk, mk, vk, t.g[u][k], s);
+                t.w[u][k] = wk;
+                t.m[u][k] = mk;
+                t.v[u][k] = vk;
             }
-            store_f32x4(w[u], W, q * 16u);
-            store_f32x4(m[u], M, q * 16u);
-            store_f32x4(v[u], V, q * 16u);
+            store_f32x4(t.w[u], W, q * 16u);
+            store_f32x4(t.m[u], M, q * 16u);
+            store_f32x4(t.v[u], V, q * 16u);
             if (copy) {
                 u32x2 packed;
-                packed[0] = bf16_bits(w[u][0]) | (bf16_bits(w[u][1]) << 16);
-                packed[1] = bf16_bits(w[u][2]) | (bf16_bits(w[u][3]) << 16);
+                packed[0] = bf16_bits(t.w[u][0]) | (bf16_bits(t.w[u][1]) << 16);
+                packed[1] = bf16_bits(t.w[u][2]) | (bf16_bits(t.w[u][3]) << 16);
                 store_u32x2(packed, P, q * 8u);
             }
         }
+    };
+
+    constexpr int kStride = kBlock * kUnroll;
+    Tile a, b;
+    load_tile(a, 0);
+    for (int base = 0; base < nquad; base += 2 * kStride) {
+        load_tile(b, base + kStride);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+        update_tile(a, base);
+        if (base + kStride >= nquad) break;  // uniform: the other tile is empty
+        load_tile(a, base + 2 * kStride);
+        __builtin_amdgcn_sched_barrier(0);
+        update_tile(b, base + kStride);
     }
 }
 
@@ -448,10 +475,16 @@ __global__ __launch_bounds__(kBlock) void adamw_step_kernel(
     const int64_t t = static_cast<int64_t>(*d_step) + 1;
     const StepScalars s = step_scalars(t, hp, d_coef ? *d_coef : 1.0f);
 
-    const ChunkWalk<MPS_STEP_CONTIGUOUS != 0> walk(n_chunks);
-    for (int k = walk.first; k < walk.stop; k += walk.step) {
-        const int c = MPS_STEP_REVERSE ? n_chunks - 1 - k : k;
-        const TensorEntry* te = &tensors[chunk_map[c]];
+    // Block b takes chunks b, b + G, b + 2G, ...: at any moment the blocks
+    // stream neighbouring chunks.  The next chunk's table entry is fetched
+    // before the current chunk streams, so the two dependent scalar lookups
+    // overlap the data loads.
+    TensorEntry next{};
+    if (static_cast<int>(blockIdx.x) < n_chunks) next = tensors[chunk_map[blockIdx.x]];
+    for (int c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+        const TensorEntry entry = next;
+        if (c + static_cast<int>(gridDim.x) < n_chunks) next = tensors[chunk_map[c + gridDim.x]];
+        const TensorEntry* te = &entry;
         const int64_t begin = static_cast<int64_t>(c - te->first_chunk) * chunk_elems;
         const int64_t end = min(begin + chunk_elems, te->numel);
 
