@@ -16,13 +16,13 @@
  *
  * A step is two or three calls on one stream, none of which waits on the host:
  *
- *     grad_norm_sq(list, ..., d_sumsq, max_norm, d_coef, ws, ...)
+ *     grad_norm_sq(list, ..., d_sumsq, max_norm, grad_scale, d_coef, ws, ...)
  *                      S = sum of g^2, and (optionally, same launch)
- *                      c = min(1, max_norm / (sqrt(S) + 1e-6))
- *     clip_coef(d_sumsq, max_norm, d_coef, ...)
+ *                      c = s * min(1, max_norm / (s * sqrt(S) + 1e-6))
+ *     clip_coef(d_sumsq, max_norm, grad_scale, d_coef, ...)
  *                      c from an S the caller combined itself (e.g. the sum
  *                      of every rank's S in a sharded group)
- *     adamw_multi_tensor_step(list, ..., d_coef, d_step, ..., ws, ...)
+ *     adamw_multi_tensor_step(list, ..., d_coef, d_skip, d_step, ..., ws, ...)
  *
  * Conventions shared by every entry point:
  *   - Every buffer pointer is a DEVICE pointer owned by the caller.  The
@@ -111,31 +111,44 @@ int adamw_workspace_release(void* d_workspace);
  *                        the workspace tables are shared.
  *   grad_dtype         : MPS_DTYPE_F32 or MPS_DTYPE_BF16.
  *   d_sumsq            : device double, written.
- *   max_norm, d_coef   : if d_coef is non-NULL, *d_coef receives exactly what
- *                        clip_coef(d_sumsq, max_norm, d_coef) would write
- *                        (max_norm must then be finite and > 0); if NULL,
- *                        max_norm is ignored.
+ *   max_norm, grad_scale, d_coef :
+ *                        if d_coef is non-NULL, *d_coef receives exactly what
+ *                        clip_coef(d_sumsq, max_norm, grad_scale, d_coef)
+ *                        would write (max_norm and grad_scale must then be
+ *                        finite and > 0); if NULL, both are ignored.
  *   d_workspace, workspace_bytes : see adamw_workspace_bytes.
  *
  * Each g^2 is formed exactly and summed in fp64 in a fixed order that depends
  * only on the list: repeated calls give bitwise identical results.
  */
 int grad_norm_sq(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
-                 double* d_sumsq, double max_norm, float* d_coef, void* d_workspace,
-                 size_t workspace_bytes, void* stream);
+                 double* d_sumsq, double max_norm, double grad_scale, float* d_coef,
+                 void* d_workspace, size_t workspace_bytes, void* stream);
 
 /*
- * clip_coef — global-norm clipping coefficient
- *     *d_coef = (float) min(1, max_norm / (sqrt(*d_sumsq) + 1e-6))
+ * clip_coef — global-norm clipping coefficient, with an optional gradient
+ * scale folded in:
+ *     *d_coef = (float) ( s * min(1, max_norm / (s * sqrt(*d_sumsq) + 1e-6)) )
  * evaluated in fp64 on the device and rounded once to fp32.  A NaN norm gives
  * a NaN coefficient; an infinite norm gives 0.
  *
- *   d_sumsq  : device double (e.g. grad_norm_sq's output, or its sum over
- *              the ranks of a shard group).
- *   max_norm : finite, > 0.
- *   d_coef   : device float, written.
+ * s = grad_scale is the factor between the stored gradient and the one the
+ * step should see: 1/K when K micro-batch gradients were summed (the Lecture
+ * 9 exercises page's gradient-accumulation answer: the accumulated gradient
+ * must be divided by K to equal the large-batch one), 1/world for an average
+ * over ranks (its DDP answer: the synchronized gradient is the average), or
+ * 1/loss_scale to undo loss scaling (its answer on FP16 loss scaling).  The
+ * update's single product grad * c then applies scale and clip together.
+ * s = 1 gives the plain clip coefficient.
+ *
+ *   d_sumsq    : device double (e.g. grad_norm_sq's output, or its sum over
+ *                the ranks of a shard group).
+ *   max_norm   : finite, > 0.
+ *   grad_scale : finite, > 0 (1.0 for none).
+ *   d_coef     : device float, written.
  */
-int clip_coef(const double* d_sumsq, double max_norm, float* d_coef, void* stream);
+int clip_coef(const double* d_sumsq, double max_norm, double grad_scale, float* d_coef,
+              void* stream);
 
 /*
  * adamw_multi_tensor_step — one AdamW step over every tensor in the list.
@@ -157,19 +170,25 @@ int clip_coef(const double* d_sumsq, double max_norm, float* d_coef, void* strea
  *   tensors, n_tensors : the list (n_tensors >= 1).
  *   grad_dtype         : MPS_DTYPE_F32 or MPS_DTYPE_BF16.
  *   d_coef             : device float, or NULL for no clipping.
+ *   d_skip_if_nonfinite: device double, or NULL.  If non-NULL and its value
+ *                        is not finite (pass d_sumsq: NaN or inf gradients),
+ *                        the whole step is skipped: no element is written and
+ *                        *d_step is left as it is — what a loss-scaled step
+ *                        does when its gradients overflowed.
  *   d_step             : device int32, the number of completed steps; read
  *                        and incremented (also when the gradients are not
- *                        finite).  Must stay below INT32_MAX.
+ *                        finite, unless the step is skipped as above).  Must
+ *                        stay below INT32_MAX.
  *   lr >= 0, 0 <= beta1 < 1, 0 <= beta2 < 1, eps >= 0, weight_decay >= 0,
  *   all finite.
  *   d_workspace, workspace_bytes : see adamw_workspace_bytes.
  */
 int adamw_multi_tensor_step(const mps_tensor* tensors, int n_tensors,
                             mps_dtype grad_dtype, const float* d_coef,
-                            int32_t* d_step, double lr, double beta1,
-                            double beta2, double eps, double weight_decay,
-                            void* d_workspace, size_t workspace_bytes,
-                            void* stream);
+                            const double* d_skip_if_nonfinite, int32_t* d_step,
+                            double lr, double beta1, double beta2, double eps,
+                            double weight_decay, void* d_workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* The calling thread's last error message ("" if none). */
 const char* adamw_last_error(void);

@@ -56,12 +56,12 @@ def lib() -> ctypes.CDLL:
         L.adamw_workspace_release.argtypes = [P]
         L.grad_norm_sq.restype = ctypes.c_int
         L.grad_norm_sq.argtypes = [ctypes.POINTER(MpsTensor), ctypes.c_int, ctypes.c_int,
-                                   P, ctypes.c_double, P, P, ctypes.c_size_t, P]
+                                   P, ctypes.c_double, ctypes.c_double, P, P, ctypes.c_size_t, P]
         L.clip_coef.restype = ctypes.c_int
-        L.clip_coef.argtypes = [P, ctypes.c_double, P, P]
+        L.clip_coef.argtypes = [P, ctypes.c_double, ctypes.c_double, P, P]
         L.adamw_multi_tensor_step.restype = ctypes.c_int
         L.adamw_multi_tensor_step.argtypes = [
-            ctypes.POINTER(MpsTensor), ctypes.c_int, ctypes.c_int, P, P,
+            ctypes.POINTER(MpsTensor), ctypes.c_int, ctypes.c_int, P, P, P,
             ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double,
             ctypes.c_double, P, ctypes.c_size_t, P]
         L.adamw_last_error.restype = ctypes.c_char_p
@@ -160,10 +160,11 @@ def _require(t: torch.Tensor, dtype, numel: int, device, name: str) -> None:
 
 
 def grad_norm_sq(tl: TensorList, out: torch.Tensor, max_norm: Optional[float] = None,
-                 coef_out: Optional[torch.Tensor] = None,
+                 coef_out: Optional[torch.Tensor] = None, grad_scale: float = 1.0,
                  stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """out[0] (float64, on the device) = sum of g^2 over the list; with
-    coef_out (float32) also the clip coefficient for max_norm, same launch."""
+    coef_out (float32) also the clip coefficient for max_norm and grad_scale,
+    from the same launch."""
     if out.dtype != torch.float64 or out.device != tl.device or out.numel() < 1:
         raise ValueError("out: float64 tensor on the list's device")
     if coef_out is not None:
@@ -172,35 +173,40 @@ def grad_norm_sq(tl: TensorList, out: torch.Tensor, max_norm: Optional[float] = 
         if max_norm is None:
             raise ValueError("coef_out needs max_norm")
     _check(lib().grad_norm_sq(tl.array, tl.n, tl.grad_dtype, out.data_ptr(),
-                              float(max_norm) if max_norm is not None else 0.0, _ptr(coef_out),
-                              tl.workspace_ptr, tl.workspace_bytes, _stream_handle(stream)),
-           "grad_norm_sq")
+                              float(max_norm) if max_norm is not None else 0.0, float(grad_scale),
+                              _ptr(coef_out), tl.workspace_ptr, tl.workspace_bytes,
+                              _stream_handle(stream)), "grad_norm_sq")
     return out
 
 
-def clip_coef(sumsq: torch.Tensor, max_norm: float, out: torch.Tensor,
+def clip_coef(sumsq: torch.Tensor, max_norm: float, out: torch.Tensor, grad_scale: float = 1.0,
               stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """out[0] (float32) = min(1, max_norm / (sqrt(sumsq[0]) + 1e-6))."""
+    """out[0] (float32) = s * min(1, max_norm / (s * sqrt(sumsq[0]) + 1e-6)), s = grad_scale."""
     if sumsq.dtype != torch.float64 or sumsq.device.type != "cuda":
         raise ValueError("sumsq: float64 CUDA tensor")
     if out.dtype != torch.float32 or out.device != sumsq.device:
         raise ValueError("out: float32 tensor on sumsq's device")
-    _check(lib().clip_coef(sumsq.data_ptr(), float(max_norm), out.data_ptr(),
+    _check(lib().clip_coef(sumsq.data_ptr(), float(max_norm), float(grad_scale), out.data_ptr(),
                            _stream_handle(stream)), "clip_coef")
     return out
 
 
 def adamw_multi_tensor_step(tl: TensorList, coef: Optional[torch.Tensor], step: torch.Tensor,
                             lr: float, beta1: float, beta2: float, eps: float,
-                            weight_decay: float,
+                            weight_decay: float, skip_if_nonfinite: Optional[torch.Tensor] = None,
                             stream: Optional[torch.cuda.Stream] = None) -> None:
     """One AdamW step over the list; `step` (int32, device) counts completed
-    steps and is incremented on the device."""
+    steps and is incremented on the device.  With skip_if_nonfinite (a
+    float64 device scalar, e.g. the sum of squares), a non-finite value skips
+    the whole step."""
     if coef is not None and (coef.dtype != torch.float32 or coef.device != tl.device):
         raise ValueError("coef: float32 tensor on the list's device, or None")
     if step.dtype != torch.int32 or step.device != tl.device:
         raise ValueError("step: int32 tensor on the list's device")
+    if skip_if_nonfinite is not None and (skip_if_nonfinite.dtype != torch.float64 or
+                                          skip_if_nonfinite.device != tl.device):
+        raise ValueError("skip_if_nonfinite: float64 tensor on the list's device, or None")
     _check(lib().adamw_multi_tensor_step(
-        tl.array, tl.n, tl.grad_dtype, _ptr(coef), step.data_ptr(), float(lr), float(beta1),
-        float(beta2), float(eps), float(weight_decay), tl.workspace_ptr, tl.workspace_bytes,
-        _stream_handle(stream)), "adamw_multi_tensor_step")
+        tl.array, tl.n, tl.grad_dtype, _ptr(coef), _ptr(skip_if_nonfinite), step.data_ptr(),
+        float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), tl.workspace_ptr,
+        tl.workspace_bytes, _stream_handle(stream)), "adamw_multi_tensor_step")

@@ -287,12 +287,15 @@ int adamw_workspace_release(void* d_workspace)
 }
 
 int grad_norm_sq(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype, double* d_sumsq,
-                 double max_norm, float* d_coef, void* d_workspace, size_t workspace_bytes,
-                 void* stream)
+                 double max_norm, double grad_scale, float* d_coef, void* d_workspace,
+                 size_t workspace_bytes, void* stream)
 {
     if (!d_sumsq) return fail(MPS_ERR_INVALID_ARGUMENT, "d_sumsq is NULL");
     if (d_coef && !(std::isfinite(max_norm) && max_norm > 0.0)) {
         return fail(MPS_ERR_INVALID_ARGUMENT, "max_norm must be finite and > 0");
+    }
+    if (d_coef && !(std::isfinite(grad_scale) && grad_scale > 0.0)) {
+        return fail(MPS_ERR_INVALID_ARGUMENT, "grad_scale must be finite and > 0");
     }
     Plan plan;
     int rc = build_plan(tensors, n_tensors, grad_dtype, false, plan);
@@ -302,26 +305,32 @@ int grad_norm_sq(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
     if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
     const int grid = grid_for(plan.n_chunks, mps::kNormMaxBlocks);
     hipError_t e = mps::launch_grad_norm(view_of(d_workspace, plan), grad_dtype == MPS_DTYPE_BF16,
-                                         grid, d_sumsq, max_norm, d_coef, st);
+                                         grid, d_sumsq, max_norm, grad_scale, d_coef, st);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "grad_norm launch: %s", hipGetErrorString(e));
     return ok();
 }
 
-int clip_coef(const double* d_sumsq, double max_norm, float* d_coef, void* stream)
+int clip_coef(const double* d_sumsq, double max_norm, double grad_scale, float* d_coef,
+              void* stream)
 {
     if (!d_sumsq || !d_coef) return fail(MPS_ERR_INVALID_ARGUMENT, "d_sumsq / d_coef is NULL");
     if (!(std::isfinite(max_norm) && max_norm > 0.0)) {
         return fail(MPS_ERR_INVALID_ARGUMENT, "max_norm must be finite and > 0");
     }
-    hipError_t e = mps::launch_clip_coef(d_sumsq, max_norm, d_coef, static_cast<hipStream_t>(stream));
+    if (!(std::isfinite(grad_scale) && grad_scale > 0.0)) {
+        return fail(MPS_ERR_INVALID_ARGUMENT, "grad_scale must be finite and > 0");
+    }
+    hipError_t e = mps::launch_clip_coef(d_sumsq, max_norm, grad_scale, d_coef,
+                                         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "clip_coef launch: %s", hipGetErrorString(e));
     return ok();
 }
 
 int adamw_multi_tensor_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
-                            const float* d_coef, int32_t* d_step, double lr, double beta1,
-                            double beta2, double eps, double weight_decay, void* d_workspace,
-                            size_t workspace_bytes, void* stream)
+                            const float* d_coef, const double* d_skip_if_nonfinite,
+                            int32_t* d_step, double lr, double beta1, double beta2, double eps,
+                            double weight_decay, void* d_workspace, size_t workspace_bytes,
+                            void* stream)
 {
     if (!d_step) return fail(MPS_ERR_INVALID_ARGUMENT, "d_step is NULL");
     if (!(std::isfinite(lr) && lr >= 0.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "lr must be finite and >= 0");
@@ -340,7 +349,7 @@ int adamw_multi_tensor_step(const mps_tensor* tensors, int n_tensors, mps_dtype 
     mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
     const int grid = grid_for(plan.n_chunks, mps::kStepMaxBlocks);
     hipError_t e = mps::launch_adamw_step(view_of(d_workspace, plan), grad_dtype == MPS_DTYPE_BF16,
-                                          grid, d_coef, d_step, hp, st);
+                                          grid, d_coef, d_skip_if_nonfinite, d_step, hp, st);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "adamw_step launch: %s", hipGetErrorString(e));
     return ok();
 }

@@ -19,14 +19,14 @@ struct WorkspaceView {
 };
 
 hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid,
-                            double* d_sumsq, double max_norm, float* d_coef,
-                            hipStream_t stream);
+                            double* d_sumsq, double max_norm, double grad_scale,
+                            float* d_coef, hipStream_t stream);
 
-hipError_t launch_clip_coef(const double* d_sumsq, double max_norm, float* d_coef,
-                            hipStream_t stream);
+hipError_t launch_clip_coef(const double* d_sumsq, double max_norm, double grad_scale,
+                            float* d_coef, hipStream_t stream);
 
 hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, int grid,
-                             const float* d_coef, int32_t* d_step,
-                             const HyperParams& hp, hipStream_t stream);
+                             const float* d_coef, const double* d_skip_if_nonfinite,
+                             int32_t* d_step, const HyperParams& hp, hipStream_t stream);
 
 }  // namespace mps

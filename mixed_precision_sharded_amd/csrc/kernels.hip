@@ -160,14 +160,18 @@ __device__ __forceinline__ double add_square(double acc, float x)
     return __builtin_fma(d, d, acc);  // d*d is exact in fp64: one rounding
 }
 
-// c = min(1, max_norm / (sqrt(S) + 1e-6)) in fp64, rounded once to fp32;
-// a NaN S gives NaN (the comparison is false), an infinite S gives 0.
-__device__ __forceinline__ float clip_from_sumsq(double sumsq, double max_norm)
+// The multiplier the update applies to the stored gradient g, whose value
+// for the step is s*g (s: 1/K accumulation, 1/world averaging, 1/loss scale):
+//     s * min(1, max_norm / (s * sqrt(S) + 1e-6))
+// in fp64, rounded once to fp32.  With s = 1 it is the plain clip
+// coefficient.  A NaN S gives NaN (the comparison is false), an infinite S
+// gives 0.
+__device__ __forceinline__ float clip_from_sumsq(double sumsq, double max_norm, double grad_scale)
 {
-    const double norm = __builtin_sqrt(sumsq);
-    double c = max_norm / (norm + 1e-6);
-    c = (c > 1.0) ? 1.0 : c;
-    return static_cast<float>(c);
+    const double norm = grad_scale * __builtin_sqrt(sumsq);
+    double clip = max_norm / (norm + 1e-6);
+    clip = (clip > 1.0) ? 1.0 : clip;
+    return static_cast<float>(grad_scale * clip);
 }
 
 // ------------------------------------------------------------ grad norm ---
@@ -198,7 +202,7 @@ template <bool kBf16, int kUnroll>
 __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
     WorkspaceHeader* header, const TensorEntry* tensors, const uint32_t* chunk_map,
     double* partials, int n_chunks, int64_t chunk_elems, uint64_t tag, double* d_sumsq,
-    double max_norm, float* d_coef)
+    double max_norm, double grad_scale, float* d_coef)
 {
     constexpr int64_t kElemBytes = kBf16 ? 2 : 4;
     constexpr int64_t kPerVec = 16 / kElemBytes;
@@ -313,17 +317,17 @@ __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
     const double total = block_sum(q, lds);
     if (tid == 0) {
         *d_sumsq = total;
-        if (d_coef) *d_coef = clip_from_sumsq(total, max_norm);
+        if (d_coef) *d_coef = clip_from_sumsq(total, max_norm, grad_scale);
     }
 }
 
 // ----------------------------------------------------------------- clip ---
 
 __global__ __launch_bounds__(kWave) void clip_coef_kernel(const double* d_sumsq, double max_norm,
-                                                          float* d_coef)
+                                                          double grad_scale, float* d_coef)
 {
     if (threadIdx.x != 0) return;
-    *d_coef = clip_from_sumsq(*d_sumsq, max_norm);
+    *d_coef = clip_from_sumsq(*d_sumsq, max_norm, grad_scale);
 }
 
 // ---------------------------------------------------------------- update ---
@@ -473,10 +477,13 @@ __device__ __forceinline__ void adamw_body(const TensorEntry* te, int64_t q0, in
 template <bool kBf16, int kUnroll>
 __global__ __launch_bounds__(kBlock) void adamw_step_kernel(
     WorkspaceHeader* header, const TensorEntry* tensors, const uint32_t* chunk_map,
-    int n_chunks, int64_t chunk_elems, uint64_t tag, const float* d_coef, int32_t* d_step,
-    HyperParams hp)
+    int n_chunks, int64_t chunk_elems, uint64_t tag, const float* d_coef,
+    const double* d_skip_if_nonfinite, int32_t* d_step, HyperParams hp)
 {
     if (header->tag != tag) return;  // tables overwritten: touch nothing
+    // A skipped step writes nothing and leaves the counter (no block takes a
+    // ticket).  The value is uniform, so every block makes the same choice.
+    if (d_skip_if_nonfinite && !__builtin_isfinite(*d_skip_if_nonfinite)) return;
 
     const int tid = threadIdx.x;
     const int64_t t = static_cast<int64_t>(*d_step) + 1;
@@ -529,39 +536,39 @@ __global__ __launch_bounds__(kBlock) void adamw_step_kernel(
 // --------------------------------------------------------------- launchers ---
 
 hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid, double* d_sumsq,
-                            double max_norm, float* d_coef, hipStream_t stream)
+                            double max_norm, double grad_scale, float* d_coef, hipStream_t stream)
 {
     if (grad_bf16) {
         grad_norm_kernel<true, MPS_NORM_UNROLL><<<grid, kBlock, 0, stream>>>(
             ws.header, ws.tensors, ws.chunk_map, ws.partials, ws.n_chunks, ws.chunk_elems, ws.tag,
-            d_sumsq, max_norm, d_coef);
+            d_sumsq, max_norm, grad_scale, d_coef);
     } else {
         grad_norm_kernel<false, MPS_NORM_UNROLL><<<grid, kBlock, 0, stream>>>(
             ws.header, ws.tensors, ws.chunk_map, ws.partials, ws.n_chunks, ws.chunk_elems, ws.tag,
-            d_sumsq, max_norm, d_coef);
+            d_sumsq, max_norm, grad_scale, d_coef);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_clip_coef(const double* d_sumsq, double max_norm, float* d_coef,
-                            hipStream_t stream)
+hipError_t launch_clip_coef(const double* d_sumsq, double max_norm, double grad_scale,
+                            float* d_coef, hipStream_t stream)
 {
-    clip_coef_kernel<<<1, kWave, 0, stream>>>(d_sumsq, max_norm, d_coef);
+    clip_coef_kernel<<<1, kWave, 0, stream>>>(d_sumsq, max_norm, grad_scale, d_coef);
     return hipGetLastError();
 }
 
 hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, int grid,
-                             const float* d_coef, int32_t* d_step, const HyperParams& hp,
-                             hipStream_t stream)
+                             const float* d_coef, const double* d_skip_if_nonfinite,
+                             int32_t* d_step, const HyperParams& hp, hipStream_t stream)
 {
     if (grad_bf16) {
         adamw_step_kernel<true, MPS_STEP_UNROLL><<<grid, kBlock, 0, stream>>>(
             ws.header, ws.tensors, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag, d_coef,
-            d_step, hp);
+            d_skip_if_nonfinite, d_step, hp);
     } else {
         adamw_step_kernel<false, MPS_STEP_UNROLL><<<grid, kBlock, 0, stream>>>(
             ws.header, ws.tensors, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag, d_coef,
-            d_step, hp);
+            d_skip_if_nonfinite, d_step, hp);
     }
     return hipGetLastError();
 }

@@ -47,6 +47,8 @@ class Oracle:
         lib.oracle_sumsq_bf16.argtypes = [_c_u16p, ctypes.c_int64, ctypes.c_double]
         lib.oracle_clip_coef.restype = ctypes.c_float
         lib.oracle_clip_coef.argtypes = [ctypes.c_double, ctypes.c_double]
+        lib.oracle_clip_coef_scaled.restype = ctypes.c_float
+        lib.oracle_clip_coef_scaled.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double]
         lib.oracle_pow_int.restype = ctypes.c_double
         lib.oracle_pow_int.argtypes = [ctypes.c_double, ctypes.c_int64]
         lib.oracle_step_scalars.restype = None
@@ -88,8 +90,17 @@ class Oracle:
                 raise TypeError("gradient must be float32 or bf16 words (uint16)")
         return acc
 
-    def clip_coef(self, sumsq: float, max_norm: float) -> np.float32:
-        return np.float32(self.lib.oracle_clip_coef(sumsq, max_norm))
+    def clip_coef(self, sumsq: float, max_norm: float, grad_scale: float = None) -> np.float32:
+        """The clip coefficient; with grad_scale s, the multiplier for the
+        stored gradient whose effective value is s * g."""
+        if grad_scale is None:
+            return np.float32(self.lib.oracle_clip_coef(sumsq, max_norm))
+        return np.float32(self.lib.oracle_clip_coef_scaled(sumsq, max_norm, grad_scale))
+
+    @staticmethod
+    def skips(sumsq: float) -> bool:
+        """A loss-scaled step is skipped when the gradients were not finite."""
+        return not np.isfinite(sumsq)
 
     # -- scalars and update ---------------------------------------------------
     def pow_int(self, beta: float, t: int) -> float:

@@ -37,6 +37,10 @@
  *     fast-math), in the order written below.
  *   - bf16 copy: round to nearest, ties to even; NaN stays a NaN of the same
  *     sign with the quiet bit set.
+ *   - A gradient scale s (1/K accumulation, 1/world averaging, 1/loss scale)
+ *     is folded into the coefficient: the step sees s*g, clipped by the norm
+ *     of s*g.  A step with non-finite gradients may be skipped whole (the
+ *     caller's choice), as a loss-scaled step is.
  *
  * Parity status: every function here is pinned by CPU tests against library
  * routines, closed forms, exact rational arithmetic or brute force.
@@ -111,6 +115,20 @@ float oracle_clip_coef(double sumsq, double max_norm)
     double c = max_norm / (norm + 1e-6);
     if (c > 1.0) c = 1.0;
     return (float)c;
+}
+
+/* Gradient scaling folded into the coefficient.  The gradient the step should
+ * see is s * g (s = 1/K after K accumulated micro-batches, 1/world for an
+ * average over ranks, 1/loss_scale to undo loss scaling).  Its norm is
+ * s * sqrt(S); the clip factor of that norm times s is the single multiplier
+ * the update applies to the stored g:
+ *     c = s * min(1, max_norm / (s * sqrt(S) + 1e-6))   (fp64, rounded once). */
+float oracle_clip_coef_scaled(double sumsq, double max_norm, double grad_scale)
+{
+    double norm = grad_scale * sqrt(sumsq);
+    double clip = max_norm / (norm + 1e-6);
+    if (clip > 1.0) clip = 1.0;
+    return (float)(grad_scale * clip);
 }
 
 /* ------------------------------------------------------- step scalars --- */

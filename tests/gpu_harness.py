@@ -35,18 +35,19 @@ class Step:
         binding.grad_norm_sq(self.tl, self.sumsq)
         return self
 
-    def norm_clip(self, max_norm):
+    def norm_clip(self, max_norm, grad_scale=1.0):
         """Norm and clip coefficient from one launch."""
-        binding.grad_norm_sq(self.tl, self.sumsq, max_norm, self.coef)
+        binding.grad_norm_sq(self.tl, self.sumsq, max_norm, self.coef, grad_scale=grad_scale)
         return self
 
-    def clip(self, max_norm):
-        binding.clip_coef(self.sumsq, max_norm, self.coef)
+    def clip(self, max_norm, grad_scale=1.0):
+        binding.clip_coef(self.sumsq, max_norm, self.coef, grad_scale=grad_scale)
         return self
 
-    def update(self, lr, beta1, beta2, eps, wd, use_coef=True):
+    def update(self, lr, beta1, beta2, eps, wd, use_coef=True, skip_if_nonfinite=False):
         binding.adamw_multi_tensor_step(self.tl, self.coef if use_coef else None, self.step, lr,
-                                        beta1, beta2, eps, wd)
+                                        beta1, beta2, eps, wd,
+                                        skip_if_nonfinite=self.sumsq if skip_if_nonfinite else None)
         return self
 
     def full(self, w):

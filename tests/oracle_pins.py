@@ -214,6 +214,69 @@ def pin_clip_matches_torch(o):
         assert abs(float(c) - coef) <= ulp32(coef) + 1e-15, (scale, mn, c, coef)
 
 
+def pin_scaled_clip_reduces_to_unscaled(o):
+    rng = np.random.default_rng(30)
+    for S in [0.0, 1e-12, 0.25, 1.0, 1.049, 4.0, 1e6, float("inf"), float("nan")] + \
+            list(rng.lognormal(0, 8, 100)):
+        for mn in (1.0, 0.5, 3.0):
+            a, b = o.clip_coef(S, mn), o.clip_coef(S, mn, 1.0)
+            assert a.view(np.uint32) == b.view(np.uint32) or (np.isnan(a) and np.isnan(b)), (S, mn)
+
+
+def pin_scaled_clip_matches_torch(o):
+    """The multiplier for stored g equals s times torch's clip coefficient of s*g."""
+    rng = np.random.default_rng(31)
+    for scale, s, mn in ((1e-3, 0.125, 1.0), (1.0, 1 / 3, 1.0), (1e-2, 1 / 65536, 0.05),
+                         (1e2, 0.25, 1.0), (1e-4, 1.0 / 7, 0.3)):
+        parts = [(rng.standard_normal(n) * scale).astype(np.float32) for n in (3000, 41)]
+        S = o.grad_norm_sq(parts)
+        c = o.clip_coef(S, mn, s)
+        ps = [torch.nn.Parameter(torch.zeros(p.size, dtype=torch.float64)) for p in parts]
+        for p, g in zip(ps, parts):
+            p.grad = torch.from_numpy(g.astype(np.float64)) * s
+        before = [p.grad.clone() for p in ps]
+        torch.nn.utils.clip_grad_norm_(ps, mn)
+        k = int(np.argmax(np.abs(parts[0])))
+        want = s * float(ps[0].grad[k] / before[0][k])
+        assert abs(float(c) - want) <= ulp32(want) + 1e-300, (scale, s, mn, c, want)
+
+
+def pin_power_of_two_scale_is_exact(o):
+    """With s = 2^-k and S scaled by 4^k, the coefficient is 2^-k times the
+    unscaled one, bitwise."""
+    rng = np.random.default_rng(32)
+    for S in list(rng.lognormal(0, 4, 200)) + [0.0, 1.0, 4.0]:
+        for k in (1, 3, 10, 16):
+            got = o.clip_coef(S * 4.0 ** k, 1.0, 2.0 ** -k)
+            want = np.float32(o.clip_coef(S, 1.0) * np.float32(2.0 ** -k))
+            assert got.view(np.uint32) == want.view(np.uint32), (S, k, got, want)
+
+
+def pin_accumulation_scale_equals_averaged_gradient(o):
+    """Lecture 9 exercises page, gradient-accumulation answer: summing K
+    micro-batch gradients and dividing by K gives the large-batch gradient.
+    Stepping on the summed gradient with s = 1/K matches stepping on the
+    averaged one with s = 1 (K a power of two, so the average is exact)."""
+    rng = np.random.default_rng(33)
+    for K in (2, 4, 8):
+        micro = [(rng.standard_normal(5000) * 1e-2).astype(np.float32) for _ in range(K)]
+        summed = np.sum(np.stack(micro).astype(np.float64), axis=0).astype(np.float32)
+        avg = (summed / np.float32(K)).astype(np.float32)
+        c_sum = o.clip_coef(o.grad_norm_sq([summed]), 1.0, 1.0 / K)
+        c_avg = o.clip_coef(o.grad_norm_sq([avg]), 1.0)
+        assert c_sum.view(np.uint32) == np.float32(c_avg / np.float32(K)).view(np.uint32), K
+        w, m, v, _ = rand_state(5000, 34 + K, warm=True)
+        a = run_step(o, w, m, v, summed, c_sum, 3)
+        b = run_step(o, w, m, v, avg, c_avg, 3)
+        for x, y in zip(a, b):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), K
+
+
+def pin_skip_rule(o):
+    assert o.skips(float("nan")) and o.skips(float("inf")) and o.skips(float("-inf"))
+    assert not o.skips(0.0) and not o.skips(1e300)
+
+
 # ------------------------------------------------------------ scalars ---
 
 def pin_power_matches_exact(o):

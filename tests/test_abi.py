@@ -86,8 +86,8 @@ def test_argument_errors(lib):
 
     def step(**kw):
         a = {**good, **kw}
-        return lib.adamw_multi_tensor_step(arr, 1, 0, a["coef"], a["step"], a["lr"], a["b1"],
-                                           a["b2"], a["eps"], a["wd"], ws, 1 << 30, None)
+        return lib.adamw_multi_tensor_step(arr, 1, 0, a["coef"], None, a["step"], a["lr"],
+                                           a["b1"], a["b2"], a["eps"], a["wd"], ws, 1 << 30, None)
 
     assert step(step=None) == EINVAL
     assert step(b1=1.0) == EINVAL
@@ -98,32 +98,34 @@ def test_argument_errors(lib):
     assert step(wd=-0.1) == EINVAL
     assert "weight_decay" in binding.last_error()
     # wrong dtype code, empty list, NULL state with numel > 0
-    assert lib.adamw_multi_tensor_step(arr, 1, 7, None, good["step"], 3e-4, 0.9, 0.95, 1e-8,
-                                       0.1, ws, 1 << 30, None) == EINVAL
-    assert lib.adamw_multi_tensor_step(arr, 0, 0, None, good["step"], 3e-4, 0.9, 0.95, 1e-8,
-                                       0.1, ws, 1 << 30, None) == EINVAL
+    assert lib.adamw_multi_tensor_step(arr, 1, 7, None, None, good["step"], 3e-4, 0.9, 0.95,
+                                       1e-8, 0.1, ws, 1 << 30, None) == EINVAL
+    assert lib.adamw_multi_tensor_step(arr, 0, 0, None, None, good["step"], 3e-4, 0.9, 0.95,
+                                       1e-8, 0.1, ws, 1 << 30, None) == EINVAL
     nostate = fake_list(1)
     nostate[0].master = None
-    assert lib.adamw_multi_tensor_step(nostate, 1, 0, None, good["step"], 3e-4, 0.9, 0.95,
-                                       1e-8, 0.1, ws, 1 << 30, None) == EINVAL
+    assert lib.adamw_multi_tensor_step(nostate, 1, 0, None, None, good["step"], 3e-4, 0.9,
+                                       0.95, 1e-8, 0.1, ws, 1 << 30, None) == EINVAL
     # fp32 state not 4-byte aligned; bf16 gradient not 2-byte aligned
     odd = fake_list(1, misalign=2)
-    assert lib.adamw_multi_tensor_step(odd, 1, 0, None, good["step"], 3e-4, 0.9, 0.95, 1e-8,
-                                       0.1, ws, 1 << 30, None) == EINVAL
+    assert lib.adamw_multi_tensor_step(odd, 1, 0, None, None, good["step"], 3e-4, 0.9, 0.95,
+                                       1e-8, 0.1, ws, 1 << 30, None) == EINVAL
     odd1 = fake_list(1, misalign=1)
-    assert lib.grad_norm_sq(odd1, 1, 1, ctypes.c_void_p(0x7d0000000000), 0.0, None, ws,
+    assert lib.grad_norm_sq(odd1, 1, 1, ctypes.c_void_p(0x7d0000000000), 0.0, 1.0, None, ws,
                             1 << 30, None) == EINVAL
-    # a clip output needs a finite positive max_norm
+    # a clip output needs a finite positive max_norm and grad_scale
+    out, coef = ctypes.c_void_p(0x7d0000000000), ctypes.c_void_p(0x7d0000000100)
     for bad in (0.0, -1.0, float("nan"), float("inf")):
-        assert lib.grad_norm_sq(arr, 1, 0, ctypes.c_void_p(0x7d0000000000), bad,
-                                ctypes.c_void_p(0x7d0000000100), ws, 1 << 30, None) == EINVAL
+        assert lib.grad_norm_sq(arr, 1, 0, out, bad, 1.0, coef, ws, 1 << 30, None) == EINVAL
+        assert lib.grad_norm_sq(arr, 1, 0, out, 1.0, bad, coef, ws, 1 << 30, None) == EINVAL
+    assert "grad_scale" in binding.last_error()
 
 
 def test_workspace_errors(lib):
     arr = fake_list(1, 4096)
     step = ctypes.c_void_p(0x7d0000000000)
     need = lib.adamw_workspace_bytes(arr, 1)
-    args = (arr, 1, 0, None, step, 3e-4, 0.9, 0.95, 1e-8, 0.1)
+    args = (arr, 1, 0, None, None, step, 3e-4, 0.9, 0.95, 1e-8, 0.1)
     assert lib.adamw_multi_tensor_step(*args, None, need, None) == EWORKSPACE
     assert lib.adamw_multi_tensor_step(*args, ctypes.c_void_p(0x7e0000000040), need,
                                        None) == EWORKSPACE
@@ -131,18 +133,19 @@ def test_workspace_errors(lib):
     assert lib.adamw_multi_tensor_step(*args, ctypes.c_void_p(0x7e0000000000), need - 1,
                                        None) == EWORKSPACE
     assert "too small" in binding.last_error()
-    assert lib.grad_norm_sq(arr, 1, 0, ctypes.c_void_p(0x7d0000000000), 1.0, None, None, need,
-                            None) == EWORKSPACE
-    assert lib.grad_norm_sq(arr, 1, 0, None, 1.0, None, ctypes.c_void_p(0x7e0000000000), need,
-                            None) == EINVAL
+    assert lib.grad_norm_sq(arr, 1, 0, ctypes.c_void_p(0x7d0000000000), 1.0, 1.0, None, None,
+                            need, None) == EWORKSPACE
+    assert lib.grad_norm_sq(arr, 1, 0, None, 1.0, 1.0, None, ctypes.c_void_p(0x7e0000000000),
+                            need, None) == EINVAL
 
 
 def test_clip_argument_errors(lib):
     p = ctypes.c_void_p(0x7d0000000000)
     for bad in (0.0, -1.0, float("nan"), float("inf")):
-        assert lib.clip_coef(p, bad, p, None) == EINVAL
-    assert lib.clip_coef(None, 1.0, p, None) == EINVAL
-    assert lib.clip_coef(p, 1.0, None, None) == EINVAL
+        assert lib.clip_coef(p, bad, 1.0, p, None) == EINVAL
+        assert lib.clip_coef(p, 1.0, bad, p, None) == EINVAL
+    assert lib.clip_coef(None, 1.0, 1.0, p, None) == EINVAL
+    assert lib.clip_coef(p, 1.0, 1.0, None, None) == EINVAL
 
 
 def test_release_unknown_workspace_is_harmless(lib):

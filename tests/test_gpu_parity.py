@@ -196,6 +196,53 @@ def test_fused_clip_equals_standalone_clip():
         assert S1 == S2 and c1 == c2 == oracle.default().clip_coef(S1, max_norm), (seed, c1, c2)
 
 
+@pytest.mark.parametrize("grad_scale", [1.0, 0.25, 1.0 / 3, 2.0 ** -16, 1.0 / 7])
+def test_scaled_clip_and_step(grad_scale):
+    """Gradient scale folded into the coefficient (fused and standalone),
+    then the step, against the oracle."""
+    say(f"grad_scale {grad_scale}")
+    o = oracle.default()
+    cols = make_cols([100003, 4097, 5], True, True, seed=40, grad_std=5e-2 / grad_scale)
+    host = host_copy(cols)
+    st = Step(cols, completed_steps=6).norm_clip(1.0, grad_scale)
+    S, c_fused, _ = st.results()
+    st.clip(1.0, grad_scale)
+    _, c_alone, _ = st.results()
+    assert c_fused == c_alone == o.clip_coef(S, 1.0, grad_scale), (c_fused, c_alone)
+    st.update(**_hp())
+    _, _, step = st.results()
+    assert step == 7
+    oracle_step(host, c_fused, 7, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+    stats = compare_state(cols, host, f"scale {grad_scale}")
+    assert stats["w"][0] == stats["m"][0] == stats["v"][0] == 0
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_skip_if_nonfinite_leaves_everything(bad):
+    """A non-finite sum of squares skips the whole step: state, copy and the
+    counter stay bitwise as they were."""
+    cols = make_cols([70001, 33], True, True, seed=41)
+    cols["grad"][0][123] = bad
+    before = {k: [t.clone() for t in v] for k, v in cols.items()}
+    st = Step(cols, completed_steps=9).norm_clip(1.0).update(**_hp(), skip_if_nonfinite=True)
+    S, _, step = st.results()
+    assert not np.isfinite(S) and step == 9
+    for k in ("master", "exp_avg", "exp_avg_sq", "param_bf16"):
+        for x, y in zip(cols[k], before[k]):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16)), k
+
+
+def test_skip_pointer_with_finite_gradients_steps_normally():
+    a = make_cols([50000, 7], False, True, seed=42)
+    b = make_cols([50000, 7], False, True, seed=42)
+    sa = Step(a, completed_steps=3).norm_clip(1.0).update(**_hp(), skip_if_nonfinite=True)
+    sb = Step(b, completed_steps=3).norm_clip(1.0).update(**_hp())
+    assert sa.results()[2] == sb.results()[2] == 4
+    for k in ("master", "exp_avg", "exp_avg_sq"):
+        for x, y in zip(a[k], b[k]):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32)), k
+
+
 # ---------------------------------------------------- determinism, resume ---
 
 def test_repeatable_bitwise():

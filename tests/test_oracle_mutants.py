@@ -38,6 +38,9 @@ MUTANTS = {
         "if (param_bf16) param_bf16[i] = oracle_f32_to_bf16(master[i]);\n"
         "        oracle_update_one(&master[i], &exp_avg[i], &exp_avg_sq[i], g, clip, &s);"),
     "moment_order_swapped": ("*m = m_new;\n    *v = v_new;", "*m = v_new;\n    *v = m_new;"),
+    "scale_not_applied": ("return (float)(grad_scale * clip);", "return (float)clip;"),
+    "scale_squared_in_norm": ("double norm = grad_scale * sqrt(sumsq);",
+                              "double norm = grad_scale * grad_scale * sqrt(sumsq);"),
 }
 
 
