@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="host time budget of the oracle baseline (0 = skip)")
     p.add_argument("--no-kernel-events", action="store_true")
+    p.add_argument("--fused", action="store_true",
+                   help="time the single-launch step (adamw_fused_step) instead of the "
+                        "two launches (grad_norm_sq with the clip output, then the update)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="after the measurement, run 5 plain device copies of this many MiB "
                         "(known bytes, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -103,6 +106,13 @@ def main():
     def one_step(tl, ev=None):
         if ev is not None:
             ev[0].record()
+        if args.fused:
+            binding.adamw_fused_step(tl, step, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay,
+                                     w.max_norm, sumsq_out=sumsq, coef_out=coef)
+            if ev is not None:
+                ev[1].record()
+                ev[2].record()
+            return
         binding.grad_norm_sq(tl, sumsq, w.max_norm, coef)  # norm + clip coefficient
         if ev is not None:
             ev[1].record()
@@ -139,7 +149,10 @@ def main():
         torch.cuda.synchronize()
         norm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
         upd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-        kern_us = {"grad_norm_sq+clip": norm_ms * 1e3, "adamw_multi_tensor_step": upd_ms * 1e3}
+        if args.fused:
+            kern_us = {"adamw_fused_step": norm_ms * 1e3}
+        else:
+            kern_us = {"grad_norm_sq+clip": norm_ms * 1e3, "adamw_multi_tensor_step": upd_ms * 1e3}
 
     n = w.numel
     step_bytes = w.algorithmic_bytes_per_param() * n
@@ -150,14 +163,18 @@ def main():
 
     roofline = None
     if kern_us is not None:
-        upd_bytes = w.update_bytes_per_param() * n
-        achieved = upd_bytes / (kern_us["adamw_multi_tensor_step"] * 1e-6) / 1e9
-        roofline = {"bound": "hbm", "kernel": "adamw_step_kernel",
+        if args.fused:  # one kernel does the whole step
+            name, launch_bytes, us = "adamw_fused_kernel", step_bytes, kern_us["adamw_fused_step"]
+        else:
+            name, launch_bytes = "adamw_step_kernel", w.update_bytes_per_param() * n
+            us = kern_us["adamw_multi_tensor_step"]
+        achieved = launch_bytes / (us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "kernel": name,
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": stored_traffic(w.name),
-                    "algorithmic_bytes_per_launch": upd_bytes,
-                    "avg_launch_us": round(kern_us["adamw_multi_tensor_step"], 2)}
+                    "traffic": None if args.fused else stored_traffic(w.name),
+                    "algorithmic_bytes_per_launch": launch_bytes,
+                    "avg_launch_us": round(us, 2)}
         log(f"kernels (us): " + ", ".join(f"{k} {v:.1f}" for k, v in kern_us.items()))
 
     if args.copy_calibration_mib > 0:
@@ -188,7 +205,8 @@ def main():
         "config": {"workload": w.name, "params": n, "tensors": w.n_tensors,
                    "grad_dtype": "bf16" if w.grad_bf16 else "f32", "bf16_copy": w.copy_bf16,
                    "step": w.step, "algorithmic_bytes_per_param": w.algorithmic_bytes_per_param(),
-                   "buffer_sets": args.rotate, "parallelism": "one GPU's shard"},
+                   "buffer_sets": args.rotate, "launches": "fused" if args.fused else "two",
+                   "parallelism": "one GPU's shard"},
         "step_gbps": round(step_gbps, 1),
         "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "kernel_us": kern_us,

@@ -190,6 +190,40 @@ int adamw_multi_tensor_step(const mps_tensor* tensors, int n_tensors,
                             double weight_decay, void* d_workspace,
                             size_t workspace_bytes, void* stream);
 
+/*
+ * adamw_fused_step — the whole step in ONE launch: the sum of squares, the
+ * clip coefficient (with grad_scale folded in, exactly as clip_coef), the
+ * optional skip on non-finite gradients, and the update of every tensor,
+ * with the same per-element arithmetic as adamw_multi_tensor_step.  For
+ * small shards, where two launches and the hand-off between them cost more
+ * than the bytes (the survey's single-launch row; the update follows the
+ * same pages as adamw_multi_tensor_step).
+ *
+ * One cooperative launch of blocks that are all resident: each block sums
+ * its share of g^2, the blocks meet at a device-wide barrier kept in the
+ * workspace header, the last block to arrive sums the partials in block
+ * order (a fixed order: results are repeatable), publishes S and the new
+ * step count, and every block then updates its chunks with the same
+ * coefficient.  S may differ from grad_norm_sq's in the last bits (another
+ * block count, so another summation order); both are within the fp64
+ * rounding of the exact sum.
+ *
+ *   tensors, n_tensors, grad_dtype : as adamw_multi_tensor_step.
+ *   max_norm, grad_scale : finite, > 0 (grad_scale 1.0 for none).
+ *   skip_if_nonfinite : non-zero: if S is NaN or inf, no element is written
+ *                       and *d_step is left as it is.
+ *   d_sumsq, d_coef  : device double / float receiving S and the coefficient,
+ *                      or NULL.
+ *   d_step, lr, beta1, beta2, eps, weight_decay : as adamw_multi_tensor_step.
+ *   d_workspace, workspace_bytes : see adamw_workspace_bytes; the same
+ *                      workspace may serve all entry points.
+ */
+int adamw_fused_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
+                     double max_norm, double grad_scale, int skip_if_nonfinite,
+                     double* d_sumsq, float* d_coef, int32_t* d_step, double lr,
+                     double beta1, double beta2, double eps, double weight_decay,
+                     void* d_workspace, size_t workspace_bytes, void* stream);
+
 /* The calling thread's last error message ("" if none). */
 const char* adamw_last_error(void);
 

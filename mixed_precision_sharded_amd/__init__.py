@@ -7,4 +7,5 @@ the package does not load the library: the first call does, and raises if it
 is not built.
 """
 from .binding import (MPS_DTYPE_BF16, MPS_DTYPE_F32, MpsError, TensorList,  # noqa: F401
-                      adamw_multi_tensor_step, clip_coef, grad_norm_sq, last_error)
+                      adamw_fused_step, adamw_multi_tensor_step, clip_coef, grad_norm_sq,
+                      last_error)

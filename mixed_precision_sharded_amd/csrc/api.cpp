@@ -157,7 +157,7 @@ int build_plan(const mps_tensor* tensors, int n, int grad_dtype, bool need_state
     plan.tensors_off = sizeof(WorkspaceHeader);
     plan.chunks_off = plan.tensors_off + sizeof(TensorEntry) * static_cast<size_t>(n);
     plan.partials_off = round_up(plan.chunks_off + sizeof(uint32_t) * n_chunks, 256);
-    plan.total_bytes = plan.partials_off + sizeof(double) * mps::kNormMaxBlocks;
+    plan.total_bytes = plan.partials_off + sizeof(double) * mps::kPartials;
 
     plan.image.assign(plan.partials_off, 0);
     unsigned char* base = plan.image.data();
@@ -351,6 +351,47 @@ int adamw_multi_tensor_step(const mps_tensor* tensors, int n_tensors, mps_dtype 
     hipError_t e = mps::launch_adamw_step(view_of(d_workspace, plan), grad_dtype == MPS_DTYPE_BF16,
                                           grid, d_coef, d_skip_if_nonfinite, d_step, hp, st);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "adamw_step launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int adamw_fused_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
+                     double max_norm, double grad_scale, int skip_if_nonfinite, double* d_sumsq,
+                     float* d_coef, int32_t* d_step, double lr, double beta1, double beta2,
+                     double eps, double weight_decay, void* d_workspace, size_t workspace_bytes,
+                     void* stream)
+{
+    if (!d_step) return fail(MPS_ERR_INVALID_ARGUMENT, "d_step is NULL");
+    if (!(std::isfinite(max_norm) && max_norm > 0.0)) {
+        return fail(MPS_ERR_INVALID_ARGUMENT, "max_norm must be finite and > 0");
+    }
+    if (!(std::isfinite(grad_scale) && grad_scale > 0.0)) {
+        return fail(MPS_ERR_INVALID_ARGUMENT, "grad_scale must be finite and > 0");
+    }
+    if (!(std::isfinite(lr) && lr >= 0.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "lr must be finite and >= 0");
+    if (!finite_in(beta1, 0.0, 1.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "beta1 must be in [0, 1)");
+    if (!finite_in(beta2, 0.0, 1.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "beta2 must be in [0, 1)");
+    if (!(std::isfinite(eps) && eps >= 0.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+    if (!(std::isfinite(weight_decay) && weight_decay >= 0.0)) {
+        return fail(MPS_ERR_INVALID_ARGUMENT, "weight_decay must be finite and >= 0");
+    }
+    Plan plan;
+    int rc = build_plan(tensors, n_tensors, grad_dtype, true, plan);
+    if (rc) return rc;
+    if ((rc = check_workspace(d_workspace, workspace_bytes, plan))) return rc;
+    const bool bf16 = grad_dtype == MPS_DTYPE_BF16;
+    int resident = 0;
+    hipError_t e = mps::fused_grid_limit(bf16, &resident);
+    if (e != hipSuccess || resident < 1) {
+        return fail(MPS_ERR_DEVICE, "fused step occupancy query: %s", hipGetErrorString(e));
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
+    const int cap = resident < mps::kFusedMaxBlocks ? resident : mps::kFusedMaxBlocks;
+    const int grid = grid_for(plan.n_chunks, cap);
+    mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
+    e = mps::launch_fused_step(view_of(d_workspace, plan), bf16, grid, max_norm, grad_scale,
+                               skip_if_nonfinite ? 1 : 0, d_sumsq, d_coef, d_step, hp, st);
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "fused step launch: %s", hipGetErrorString(e));
     return ok();
 }
 

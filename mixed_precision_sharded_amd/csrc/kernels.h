@@ -29,4 +29,14 @@ hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, int grid,
                              const float* d_coef, const double* d_skip_if_nonfinite,
                              int32_t* d_step, const HyperParams& hp, hipStream_t stream);
 
+// Largest grid of the single-launch step whose blocks can all be resident.
+hipError_t fused_grid_limit(bool grad_bf16, int* max_blocks);
+
+// The single-launch step (cooperative launch; `grid` must not exceed
+// fused_grid_limit nor kFusedMaxBlocks).
+hipError_t launch_fused_step(const WorkspaceView& ws, bool grad_bf16, int grid, double max_norm,
+                             double grad_scale, int skip_if_nonfinite, double* d_sumsq,
+                             float* d_coef, int32_t* d_step, const HyperParams& hp,
+                             hipStream_t stream);
+
 }  // namespace mps

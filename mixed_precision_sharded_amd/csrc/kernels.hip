@@ -198,34 +198,21 @@ __device__ __forceinline__ double add_vector(double acc, u32x4 v)
     return acc;
 }
 
+// This thread's share of the sum of g^2 over the chunks [run_first,
+// run_stop), in a fixed order.  Consecutive chunks of one tensor are one
+// contiguous stretch of memory, streamed as a single body so the load
+// pipeline only restarts at tensor boundaries.
 template <bool kBf16, int kUnroll>
-__global__ __launch_bounds__(kBlock) void grad_norm_kernel(
-    WorkspaceHeader* header, const TensorEntry* tensors, const uint32_t* chunk_map,
-    double* partials, int n_chunks, int64_t chunk_elems, uint64_t tag, double* d_sumsq,
-    double max_norm, double grad_scale, float* d_coef)
+__device__ __forceinline__ double norm_of_run(const TensorEntry* tensors, const uint32_t* chunk_map,
+                                              int64_t chunk_elems, int run_first, int run_stop)
 {
     constexpr int64_t kElemBytes = kBf16 ? 2 : 4;
     constexpr int64_t kPerVec = 16 / kElemBytes;
-
-    if (header->tag != tag) {  // tables overwritten: touch nothing, report NaN
-        if (blockIdx.x == 0 && threadIdx.x == 0) {
-            *d_sumsq = __builtin_nan("");
-            if (d_coef) *d_coef = __builtin_nanf("");
-        }
-        return;
-    }
-
     const int tid = threadIdx.x;
     double acc[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
 
-    // Block b takes the contiguous run of chunks [b*n/G, (b+1)*n/G).  Within
-    // the run, consecutive chunks of one tensor are one contiguous stretch of
-    // memory, streamed as a single body so the load pipeline only restarts
-    // at tensor boundaries.
-    const int run_first = static_cast<int>(static_cast<int64_t>(blockIdx.x) * n_chunks / gridDim.x);
-    const int run_stop = static_cast<int>(static_cast<int64_t>(blockIdx.x + 1) * n_chunks / gridDim.x);
     for (int c = run_first; c < run_stop;) {
         const TensorEntry te = tensors[chunk_map[c]];
         const int tensor_chunks = static_cast<int>((te.numel + chunk_elems - 1) / chunk_elems);
@@ -287,6 +274,33 @@ __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
     double mine = acc[0];
 #pragma unroll
     for (int u = 1; u < kUnroll; ++u) mine = mine + acc[u];
+    return mine;
+}
+
+// The run of chunks of block b among G: [b*n/G, (b+1)*n/G).
+__device__ __forceinline__ int run_begin(int b, int n_chunks)
+{
+    return static_cast<int>(static_cast<int64_t>(b) * n_chunks / gridDim.x);
+}
+
+template <bool kBf16, int kUnroll>
+__global__ __launch_bounds__(kBlock) void grad_norm_kernel(
+    WorkspaceHeader* header, const TensorEntry* tensors, const uint32_t* chunk_map,
+    double* partials, int n_chunks, int64_t chunk_elems, uint64_t tag, double* d_sumsq,
+    double max_norm, double grad_scale, float* d_coef)
+{
+    if (header->tag != tag) {  // tables overwritten: touch nothing, report NaN
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            *d_sumsq = __builtin_nan("");
+            if (d_coef) *d_coef = __builtin_nanf("");
+        }
+        return;
+    }
+
+    const int tid = threadIdx.x;
+    const double mine = norm_of_run<kBf16, kUnroll>(tensors, chunk_map, chunk_elems,
+                                                    run_begin(blockIdx.x, n_chunks),
+                                                    run_begin(blockIdx.x + 1, n_chunks));
 
     __shared__ double lds[kWavesPerBlock];
     __shared__ bool is_last;
@@ -474,25 +488,16 @@ __device__ __forceinline__ void adamw_body(const TensorEntry* te, int64_t q0, in
     }
 }
 
+// Update the chunks b, b + G, b + 2G, ... of this block (G = gridDim.x): at
+// any moment the blocks stream neighbouring chunks.  The next chunk's table
+// entry is fetched before the current chunk streams, so the two dependent
+// scalar lookups overlap the data loads.
 template <bool kBf16, int kUnroll>
-__global__ __launch_bounds__(kBlock) void adamw_step_kernel(
-    WorkspaceHeader* header, const TensorEntry* tensors, const uint32_t* chunk_map,
-    int n_chunks, int64_t chunk_elems, uint64_t tag, const float* d_coef,
-    const double* d_skip_if_nonfinite, int32_t* d_step, HyperParams hp)
+__device__ __forceinline__ void update_chunks(const TensorEntry* tensors, const uint32_t* chunk_map,
+                                              int n_chunks, int64_t chunk_elems,
+                                              const StepScalars& s)
 {
-    if (header->tag != tag) return;  // tables overwritten: touch nothing
-    // A skipped step writes nothing and leaves the counter (no block takes a
-    // ticket).  The value is uniform, so every block makes the same choice.
-    if (d_skip_if_nonfinite && !__builtin_isfinite(*d_skip_if_nonfinite)) return;
-
     const int tid = threadIdx.x;
-    const int64_t t = static_cast<int64_t>(*d_step) + 1;
-    const StepScalars s = step_scalars(t, hp, d_coef ? *d_coef : 1.0f);
-
-    // Block b takes chunks b, b + G, b + 2G, ...: at any moment the blocks
-    // stream neighbouring chunks.  The next chunk's table entry is fetched
-    // before the current chunk streams, so the two dependent scalar lookups
-    // overlap the data loads.
     TensorEntry next{};
     if (static_cast<int>(blockIdx.x) < n_chunks) next = tensors[chunk_map[blockIdx.x]];
     for (int c = blockIdx.x; c < n_chunks; c += gridDim.x) {
@@ -513,7 +518,23 @@ __global__ __launch_bounds__(kBlock) void adamw_step_kernel(
         const int64_t tail = qbegin + static_cast<int64_t>(nquad) * 4;
         if (tid < end - tail) adamw_scalar_at<kBf16>(te, tail + tid, s);
     }
+}
 
+template <bool kBf16, int kUnroll>
+__global__ __launch_bounds__(kBlock) void adamw_step_kernel(
+    WorkspaceHeader* header, const TensorEntry* tensors, const uint32_t* chunk_map,
+    int n_chunks, int64_t chunk_elems, uint64_t tag, const float* d_coef,
+    const double* d_skip_if_nonfinite, int32_t* d_step, HyperParams hp)
+{
+    if (header->tag != tag) return;  // tables overwritten: touch nothing
+    // A skipped step writes nothing and leaves the counter (no block takes a
+    // ticket).  The value is uniform, so every block makes the same choice.
+    if (d_skip_if_nonfinite && !__builtin_isfinite(*d_skip_if_nonfinite)) return;
+
+    const int tid = threadIdx.x;
+    const int64_t t = static_cast<int64_t>(*d_step) + 1;
+    const StepScalars s = step_scalars(t, hp, d_coef ? *d_coef : 1.0f);
+    update_chunks<kBf16, kUnroll>(tensors, chunk_map, n_chunks, chunk_elems, s);
     // The last block to take a ticket stores the new step count.  The only
     // order this needs is that every block's read of the old count comes
     // before that store: a block with work consumed the count in its
@@ -529,6 +550,98 @@ __global__ __launch_bounds__(kBlock) void adamw_step_kernel(
         const unsigned prev = atomicInc(&header->step_ticket, gridDim.x - 1);
         if (prev == gridDim.x - 1) *d_step = static_cast<int32_t>(t);
     }
+}
+
+// ------------------------------------------------------ single launch ---
+
+constexpr uint32_t kSpinLimit = 1u << 23;  // x s_sleep(2): about 1 s, never reached
+
+// The whole step in one launch: norm, grid barrier, clip, update.  Launched
+// cooperatively, so every block is resident and the barrier completes; the
+// bounded wait only guards against a broken launch (it then flags the error
+// and the waiting block stops without writing state).
+template <bool kBf16, int kNormUnroll, int kStepUnroll>
+__global__ __launch_bounds__(kBlock) void adamw_fused_kernel(
+    WorkspaceHeader* header, const TensorEntry* tensors, const uint32_t* chunk_map,
+    double* partials, int n_chunks, int64_t chunk_elems, uint64_t tag, double max_norm,
+    double grad_scale, int skip_if_nonfinite, double* d_sumsq, float* d_coef, int32_t* d_step,
+    HyperParams hp)
+{
+    if (header->tag != tag) {  // tables overwritten: touch nothing, report NaN
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            if (d_sumsq) *d_sumsq = __builtin_nan("");
+            if (d_coef) *d_coef = __builtin_nanf("");
+        }
+        return;
+    }
+    const int tid = threadIdx.x;
+    const int grid = gridDim.x;
+    // Every block reads the step count before it arrives at the barrier; the
+    // last block to arrive is therefore free to store the new count.
+    const int64_t t = static_cast<int64_t>(*d_step) + 1;
+
+    // Phase 1: this block's partial of S.
+    const double mine = norm_of_run<kBf16, kNormUnroll>(tensors, chunk_map, chunk_elems,
+                                                        run_begin(blockIdx.x, n_chunks),
+                                                        run_begin(blockIdx.x + 1, n_chunks));
+    __shared__ double lds[kWavesPerBlock];
+    __shared__ uint64_t launch;
+    __shared__ bool last, failed;
+    const double block_total = block_sum(mine, lds);
+    if (tid == 0) {
+        __hip_atomic_store(&partials[blockIdx.x], block_total, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);  // the partial is visible device-wide
+        const uint64_t arrival = __hip_atomic_fetch_add(&header->fused_arrived, uint64_t{1},
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        launch = arrival / grid;
+        last = arrival % grid == static_cast<uint64_t>(grid - 1);
+        failed = false;
+    }
+    __syncthreads();
+
+    // Barrier.  The last block to arrive sums the partials in block order,
+    // publishes S and the new step count, then releases the others.
+    if (last) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        double q = 0.0;
+        for (int i = tid; i < grid; i += kBlock) {
+            q = q + __hip_atomic_load(&partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const double total = block_sum(q, lds);
+        if (tid == 0) {
+            const bool skip = skip_if_nonfinite && !__builtin_isfinite(total);
+            __hip_atomic_store(&header->fused_sumsq, total, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            if (d_sumsq) *d_sumsq = total;
+            if (d_coef) *d_coef = clip_from_sumsq(total, max_norm, grad_scale);
+            if (!skip) *d_step = static_cast<int32_t>(t);
+            __builtin_amdgcn_s_waitcnt(0);  // S is visible before the release
+            __hip_atomic_store(&header->fused_released, launch + 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else if (tid == 0) {
+        uint32_t spins = 0;
+        while (__hip_atomic_load(&header->fused_released, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT) < launch + 1) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins == kSpinLimit) {
+                __hip_atomic_store(&header->fused_error, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                failed = true;
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    if (failed) return;
+
+    // Phase 2: every block sees the same S, hence the same coefficient.
+    const double total = __hip_atomic_load(&header->fused_sumsq, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    if (skip_if_nonfinite && !__builtin_isfinite(total)) return;
+    const StepScalars s = step_scalars(t, hp, clip_from_sumsq(total, max_norm, grad_scale));
+    update_chunks<kBf16, kStepUnroll>(tensors, chunk_map, n_chunks, chunk_elems, s);
 }
 
 }  // namespace
@@ -571,6 +684,56 @@ hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, int grid,
             d_skip_if_nonfinite, d_step, hp);
     }
     return hipGetLastError();
+}
+
+namespace {
+
+template <bool kBf16>
+auto fused_kernel()
+{
+    return adamw_fused_kernel<kBf16, MPS_NORM_UNROLL, MPS_STEP_UNROLL>;
+}
+
+}  // namespace
+
+hipError_t fused_grid_limit(bool grad_bf16, int* max_blocks)
+{
+    int device = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e == hipSuccess) {
+        e = grad_bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                            &per_cu, reinterpret_cast<const void*>(fused_kernel<true>()), kBlock, 0)
+                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                            &per_cu, reinterpret_cast<const void*>(fused_kernel<false>()), kBlock, 0);
+    }
+    *max_blocks = (e == hipSuccess) ? cus * per_cu : 0;
+    return e;
+}
+
+hipError_t launch_fused_step(const WorkspaceView& ws, bool grad_bf16, int grid, double max_norm,
+                             double grad_scale, int skip_if_nonfinite, double* d_sumsq,
+                             float* d_coef, int32_t* d_step, const HyperParams& hp,
+                             hipStream_t stream)
+{
+    WorkspaceHeader* header = ws.header;
+    const TensorEntry* tensors = ws.tensors;
+    const uint32_t* chunk_map = ws.chunk_map;
+    double* partials = ws.partials;
+    int n_chunks = ws.n_chunks;
+    int64_t chunk_elems = ws.chunk_elems;
+    uint64_t tag = ws.tag;
+    HyperParams params = hp;
+    void* args[] = {&header,     &tensors,   &chunk_map,         &partials, &n_chunks,
+                    &chunk_elems, &tag,      &max_norm,          &grad_scale, &skip_if_nonfinite,
+                    &d_sumsq,    &d_coef,    &d_step,            &params};
+    const void* fn = grad_bf16 ? reinterpret_cast<const void*>(fused_kernel<true>())
+                               : reinterpret_cast<const void*>(fused_kernel<false>());
+    // Cooperative: the runtime refuses the launch unless every block can be
+    // resident, which the barrier needs.  (Measured on MI355X: this launch
+    // costs about 20 us more than a plain one, so the single-launch step is
+    // slower than the two-launch step even on a 2^20-parameter shard.)
+    return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kBlock), args, 0, stream);
 }
 
 }  // namespace mps

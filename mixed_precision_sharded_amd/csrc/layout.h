@@ -4,7 +4,7 @@
 //   [0, 64)                      WorkspaceHeader
 //   [64, 64 + 64*T)              TensorEntry[T]
 //   [.., + 4*K rounded to 8)     uint32 chunk -> tensor index, K chunks
-//   [.., + 8*kNormMaxBlocks)     fp64 per-block partial sums of the norm
+//   [.., + 8*kPartials)          fp64 per-block partial sums of the norm
 // Everything before the partials is written by one host-to-device copy when
 // the list changes; the partials need no initial value.
 #pragma once
@@ -34,9 +34,15 @@ namespace mps {
 #define MPS_CHUNK_TARGET 3072       // aim for about this many chunks
 #endif
 
-constexpr int kBlock = 256;                        // threads per block, both kernels
+#ifndef MPS_FUSED_MAX_BLOCKS
+#define MPS_FUSED_MAX_BLOCKS 512   // single-launch step grid cap (all co-resident)
+#endif
+
+constexpr int kBlock = 256;                        // threads per block, all kernels
 constexpr int kNormMaxBlocks = MPS_NORM_MAX_BLOCKS;
 constexpr int kStepMaxBlocks = MPS_STEP_MAX_BLOCKS;
+constexpr int kFusedMaxBlocks = MPS_FUSED_MAX_BLOCKS;
+constexpr int kPartials = kNormMaxBlocks > kFusedMaxBlocks ? kNormMaxBlocks : kFusedMaxBlocks;
 constexpr int64_t kChunkQuantum = 2048;            // chunk sizes are multiples of this
 constexpr int64_t kChunkMin = MPS_CHUNK_MIN;
 constexpr int64_t kChunkMax = MPS_CHUNK_MAX;
@@ -49,7 +55,14 @@ struct alignas(64) WorkspaceHeader {
     int32_t n_tensors;
     int32_t n_chunks;
     int64_t chunk_elems;
-    uint8_t reserved[32];
+    // Grid barrier of the single-launch step.  Both counters only grow (from
+    // zero at upload): launch k of a grid of G blocks takes arrivals
+    // [kG, (k+1)G) and is released when `released` reaches k + 1.
+    uint64_t fused_arrived;
+    uint64_t fused_released;
+    double fused_sumsq;     // S, published by the last block to arrive
+    uint32_t fused_error;   // set if a barrier wait ever ran out (never expected)
+    uint32_t reserved;
 };
 static_assert(sizeof(WorkspaceHeader) == 64, "header is one 64-byte record");
 

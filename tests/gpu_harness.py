@@ -50,6 +50,20 @@ class Step:
                                         skip_if_nonfinite=self.sumsq if skip_if_nonfinite else None)
         return self
 
+    def fused(self, max_norm, lr, beta1, beta2, eps, wd, grad_scale=1.0, skip_if_nonfinite=False):
+        """Norm, clip and update in one launch (adamw_fused_step)."""
+        binding.adamw_fused_step(self.tl, self.step, lr, beta1, beta2, eps, wd, max_norm,
+                                 grad_scale=grad_scale, skip_if_nonfinite=skip_if_nonfinite,
+                                 sumsq_out=self.sumsq, coef_out=self.coef)
+        return self
+
+    def header_words(self):
+        """The workspace header as 64-bit words (for the barrier counters)."""
+        torch.cuda.synchronize()
+        ws = self.tl._ws_storage
+        off = self.tl.workspace_ptr - ws.data_ptr()
+        return ws[off:off + 64].cpu().view(torch.int64).tolist()
+
     def full(self, w):
         """norm + clip (one launch) -> update with a workload's hyperparameters."""
         return self.norm_clip(w.max_norm).update(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)

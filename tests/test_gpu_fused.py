@@ -1,0 +1,122 @@
+"""GPU parity of the single-launch step (adamw_fused_step) against the oracle:
+norm, clip and update from one cooperative launch, on the same cases as the
+three-call path, plus repeated launches on one workspace (the grid barrier's
+counters only grow) and the barrier's error flag."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_harness import NORM_REL_TOL, Step, compare_state, host_copy, oracle_norm, oracle_step, say
+from mixed_precision_sharded_amd import synth
+from mixed_precision_sharded_amd.configs import WORKLOADS
+from test_gpu_parity import HP, RAGGED, make_cols
+
+pytestmark = pytest.mark.gpu
+
+# header layout: 64-bit words 4 and 5 are the barrier's arrival and release
+# counters, word 7 holds the error flag
+ARRIVED, RELEASED, ERROR = 4, 5, 7
+
+
+@pytest.fixture(autouse=True)
+def _gpu_only():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def fused_and_check(cols, t, hp=HP, max_norm=1.0, grad_scale=1.0, what=""):
+    host = host_copy(cols)
+    st = Step(cols, completed_steps=t - 1)
+    st.fused(max_norm, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["wd"],
+             grad_scale=grad_scale)
+    S, c, step = st.results()
+    assert step == t, what
+    S_ref = oracle_norm(host["grad"])
+    assert abs(S - S_ref) <= NORM_REL_TOL * abs(S_ref), (what, S, S_ref)
+    assert c == oracle.default().clip_coef(S, max_norm, grad_scale), what
+    oracle_step(host, c, t, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["wd"])
+    stats = compare_state(cols, host, what)
+    say(f"[fused {what}] S rel {abs(S - S_ref) / max(S_ref, 1e-300):.1e} c={c} "
+        f"non-bitwise w/m/v/p = {stats['w'][0]}/{stats['m'][0]}/{stats['v'][0]}/{stats['p'][0]}")
+    words = st.header_words()
+    assert words[ERROR] == 0, "barrier wait ran out"
+    assert words[ARRIVED] % max(1, words[RELEASED]) == 0
+    return stats
+
+
+@pytest.mark.parametrize("grad_bf16,copy", [(False, False), (True, True)])
+def test_fused_ragged(grad_bf16, copy):
+    cols = make_cols(RAGGED, grad_bf16, copy, seed=60)
+    stats = fused_and_check(cols, t=3, what=f"ragged bf16={grad_bf16}")
+    assert stats["w"][0] == stats["m"][0] == stats["v"][0] == 0
+
+
+def test_fused_many_tensors_and_scale():
+    rng = np.random.default_rng(61)
+    cols = make_cols(rng.integers(0, 5000, 400).tolist(), True, True, seed=61, grad_std=1e-1)
+    fused_and_check(cols, t=12, grad_scale=0.125, what="400 tensors, scale 1/8")
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_fused_workloads(cfg):
+    w = WORKLOADS[cfg]
+    say(f"fused, workload {w.name}")
+    cols = synth.workload_inputs(w, "cuda")
+    fused_and_check(cols, t=w.step, max_norm=w.max_norm, what=w.name,
+                    hp=dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, wd=w.weight_decay))
+
+
+def test_fused_consecutive_launches_match_the_oracle():
+    """Five steps in a row on one workspace: every launch goes through the
+    barrier (the counters keep growing) and matches the oracle stepping."""
+    cols = make_cols([300001, 77], False, True, seed=62)
+    host = host_copy(cols)
+    st = Step(cols, completed_steps=0)
+    o = oracle.default()
+    for t in range(1, 6):
+        st.fused(1.0, **{k: HP[k] for k in ("lr", "beta1", "beta2", "eps")}, wd=HP["wd"])
+        S, c, step = st.results()
+        assert step == t
+        assert c == o.clip_coef(S, 1.0)
+        oracle_step(host, c, t, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+    stats = compare_state(cols, host, "5 fused steps")
+    assert stats["w"][0] == 0
+    words = st.header_words()
+    assert words[RELEASED] == 5 and words[ARRIVED] == 5 * (words[ARRIVED] // 5) and words[ERROR] == 0
+
+
+def test_fused_skip_if_nonfinite():
+    cols = make_cols([40000, 9], True, True, seed=63)
+    cols["grad"][1][4] = float("nan")
+    before = {k: [t.clone() for t in v] for k, v in cols.items()}
+    st = Step(cols, completed_steps=4)
+    st.fused(1.0, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"], skip_if_nonfinite=True)
+    S, _, step = st.results()
+    assert np.isnan(S) and step == 4
+    for k in ("master", "exp_avg", "exp_avg_sq", "param_bf16"):
+        for x, y in zip(cols[k], before[k]):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16)), k
+    assert st.header_words()[ERROR] == 0
+
+
+def test_fused_and_two_launch_paths_agree_given_the_same_coefficient():
+    """Same inputs through both paths: the coefficients may differ in the last
+    bit (different summation orders of S); where they are equal the states are
+    bitwise equal."""
+    a = make_cols([250000, 3], False, False, seed=64)
+    b = make_cols([250000, 3], False, False, seed=64)
+    sa = Step(a, completed_steps=1).fused(1.0, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"],
+                                          HP["wd"])
+    sb = Step(b, completed_steps=1).norm_clip(1.0).update(HP["lr"], HP["beta1"], HP["beta2"],
+                                                          HP["eps"], HP["wd"])
+    Sa, ca, _ = sa.results()
+    Sb, cb, _ = sb.results()
+    assert abs(Sa - Sb) <= 1e-12 * Sb
+    if ca == cb:
+        for k in ("master", "exp_avg", "exp_avg_sq"):
+            for x, y in zip(a[k], b[k]):
+                assert torch.equal(x.view(torch.int32), y.view(torch.int32)), k
