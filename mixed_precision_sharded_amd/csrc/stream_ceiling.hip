@@ -60,6 +60,55 @@ __global__ __launch_bounds__(256) void adam_like(f4* __restrict__ w, f4* __restr
   }
 }
 
+typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+// The bf16-gradient update's streams, four elements per lane: fp32 w, m, v
+// (16 B loads and stores), bf16 g in (8 B), bf16 copy out (8 B).
+template <bool NT>
+__global__ __launch_bounds__(256) void adam_bf16_quads(f4* __restrict__ w, f4* __restrict__ m, f4* __restrict__ v,
+                                                       const u2* __restrict__ g, u2* __restrict__ p, long n) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    f4 W = NT ? __builtin_nontemporal_load(&w[i]) : w[i];
+    f4 M = NT ? __builtin_nontemporal_load(&m[i]) : m[i];
+    f4 V = NT ? __builtin_nontemporal_load(&v[i]) : v[i];
+    u2 G = NT ? __builtin_nontemporal_load(&g[i]) : g[i];
+    f4 gf = f4{__uint_as_float(G[0] << 16), __uint_as_float(G[0] & 0xffff0000u), __uint_as_float(G[1] << 16), __uint_as_float(G[1] & 0xffff0000u)};
+    f4 mm = M * 0.9f + gf * 0.1f; f4 vv = V * 0.95f + gf * gf * 0.05f; f4 ww = W - mm * 0.001f;
+    u2 P = u2{(__float_as_uint(ww[0]) >> 16) | (__float_as_uint(ww[1]) & 0xffff0000u), (__float_as_uint(ww[2]) >> 16) | (__float_as_uint(ww[3]) & 0xffff0000u)};
+    if (NT) { __builtin_nontemporal_store(ww, &w[i]); __builtin_nontemporal_store(mm, &m[i]); __builtin_nontemporal_store(vv, &v[i]); __builtin_nontemporal_store(P, &p[i]); }
+    else { w[i] = ww; m[i] = mm; v[i] = vv; p[i] = P; }
+  }
+}
+
+// Same streams, eight elements per lane: bf16 g and copy as 16 B accesses,
+// fp32 w, m, v as two 16 B accesses each (lanes 32 B apart).
+template <bool NT>
+__global__ __launch_bounds__(256) void adam_bf16_octets(f4* __restrict__ w, f4* __restrict__ m, f4* __restrict__ v,
+                                                        const u4* __restrict__ g, u4* __restrict__ p, long n8) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)gridDim.x * 256) {
+    f4 W0 = NT ? __builtin_nontemporal_load(&w[2 * i]) : w[2 * i], W1 = NT ? __builtin_nontemporal_load(&w[2 * i + 1]) : w[2 * i + 1];
+    f4 M0 = NT ? __builtin_nontemporal_load(&m[2 * i]) : m[2 * i], M1 = NT ? __builtin_nontemporal_load(&m[2 * i + 1]) : m[2 * i + 1];
+    f4 V0 = NT ? __builtin_nontemporal_load(&v[2 * i]) : v[2 * i], V1 = NT ? __builtin_nontemporal_load(&v[2 * i + 1]) : v[2 * i + 1];
+    u4 G = NT ? __builtin_nontemporal_load(&g[i]) : g[i];
+    f4 g0 = f4{__uint_as_float(G[0] << 16), __uint_as_float(G[0] & 0xffff0000u), __uint_as_float(G[1] << 16), __uint_as_float(G[1] & 0xffff0000u)};
+    f4 g1 = f4{__uint_as_float(G[2] << 16), __uint_as_float(G[2] & 0xffff0000u), __uint_as_float(G[3] << 16), __uint_as_float(G[3] & 0xffff0000u)};
+    f4 m0 = M0 * 0.9f + g0 * 0.1f, m1 = M1 * 0.9f + g1 * 0.1f;
+    f4 v0 = V0 * 0.95f + g0 * g0 * 0.05f, v1 = V1 * 0.95f + g1 * g1 * 0.05f;
+    f4 w0 = W0 - m0 * 0.001f, w1 = W1 - m1 * 0.001f;
+    u4 P = u4{(__float_as_uint(w0[0]) >> 16) | (__float_as_uint(w0[1]) & 0xffff0000u), (__float_as_uint(w0[2]) >> 16) | (__float_as_uint(w0[3]) & 0xffff0000u),
+              (__float_as_uint(w1[0]) >> 16) | (__float_as_uint(w1[1]) & 0xffff0000u), (__float_as_uint(w1[2]) >> 16) | (__float_as_uint(w1[3]) & 0xffff0000u)};
+    if (NT) {
+      __builtin_nontemporal_store(w0, &w[2 * i]); __builtin_nontemporal_store(w1, &w[2 * i + 1]);
+      __builtin_nontemporal_store(m0, &m[2 * i]); __builtin_nontemporal_store(m1, &m[2 * i + 1]);
+      __builtin_nontemporal_store(v0, &v[2 * i]); __builtin_nontemporal_store(v1, &v[2 * i + 1]);
+      __builtin_nontemporal_store(P, &p[i]);
+    } else {
+      w[2 * i] = w0; w[2 * i + 1] = w1; m[2 * i] = m0; m[2 * i + 1] = m1; v[2 * i] = v0; v[2 * i + 1] = v1; p[i] = P;
+    }
+  }
+}
+
 template <typename F>
 float time_ms(F launch, int reps) {
   hipEvent_t a, b; CHECK(hipEventCreate(&a)); CHECK(hipEventCreate(&b));
@@ -99,6 +148,14 @@ int main(int argc, char** argv) {
     RUN(adam_like, 2, false, n * 112.0, w, m, v, g, n);
     RUN(adam_like, 2, true, n * 112.0, w, m, v, g, n);
     RUN(adam_like, 4, false, n * 112.0, w, m, v, g, n);
+    // bf16 gradient + copy: n f32x4 groups of w, m, v; g and the copy reuse
+    // the first halves of the g and b buffers (8 B per group of four).
+    {
+      float ms = time_ms([&]{ adam_bf16_quads<true><<<grid, 256>>>(w, m, v, (const u2*)g, (u2*)b, n); }, reps);
+      printf("%-10s NT=1 blocks/CU=%2d  %8.1f us  %7.0f GB/s\n", "bf16_quads", bpc, ms * 1e3, n * 4 * 30.0 / (ms * 1e-3) / 1e9); fflush(stdout);
+      ms = time_ms([&]{ adam_bf16_octets<true><<<grid, 256>>>(w, m, v, (const u4*)g, (u4*)b, n / 2); }, reps);
+      printf("%-10s NT=1 blocks/CU=%2d  %8.1f us  %7.0f GB/s\n", "bf16_octets", bpc, ms * 1e3, n * 4 * 30.0 / (ms * 1e-3) / 1e9); fflush(stdout);
+    }
   }
   return 0;
 }
