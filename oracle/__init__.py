@@ -16,6 +16,10 @@ from . import build as _build
 
 _c_f32p = ctypes.POINTER(ctypes.c_float)
 _c_u16p = ctypes.POINTER(ctypes.c_uint16)
+_c_u8p = ctypes.POINTER(ctypes.c_uint8)
+
+E4M3, E5M2 = 0, 1   # 8-bit formats of the moment state: m, v
+QBLOCK = 32         # elements per shared scale
 
 
 class Scalars(ctypes.Structure):
@@ -58,6 +62,23 @@ class Oracle:
         lib.oracle_adamw_step.restype = None
         lib.oracle_adamw_step.argtypes = [
             _c_f32p, _c_f32p, _c_f32p, ctypes.c_void_p, ctypes.c_int, _c_u16p,
+            ctypes.c_int64, ctypes.c_float, ctypes.c_int64, ctypes.c_double,
+            ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double]
+        lib.oracle_fp8_value.restype = ctypes.c_double
+        lib.oracle_fp8_value.argtypes = [ctypes.c_uint8, ctypes.c_int]
+        lib.oracle_fp8_round.restype = ctypes.c_uint8
+        lib.oracle_fp8_round.argtypes = [ctypes.c_double, ctypes.c_int]
+        lib.oracle_fp8_round_array.restype = None
+        lib.oracle_fp8_round_array.argtypes = [_c_f32p, ctypes.c_int64, ctypes.c_int, _c_u8p]
+        lib.oracle_block_exponent.restype = ctypes.c_int
+        lib.oracle_block_exponent.argtypes = [ctypes.c_double, ctypes.c_int]
+        lib.oracle_quantize.restype = None
+        lib.oracle_quantize.argtypes = [_c_f32p, ctypes.c_int64, ctypes.c_int, _c_u8p, _c_u8p]
+        lib.oracle_dequantize.restype = None
+        lib.oracle_dequantize.argtypes = [_c_u8p, _c_u8p, ctypes.c_int64, ctypes.c_int, _c_f32p]
+        lib.oracle_adamw8_step.restype = None
+        lib.oracle_adamw8_step.argtypes = [
+            _c_f32p, _c_u8p, _c_u8p, _c_u8p, _c_u8p, ctypes.c_void_p, ctypes.c_int, _c_u16p,
             ctypes.c_int64, ctypes.c_float, ctypes.c_int64, ctypes.c_double,
             ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double]
 
@@ -134,12 +155,75 @@ class Oracle:
             n, float(clip), int(t), lr, beta1, beta2, eps, wd)
 
 
+    # -- 8-bit moment state -------------------------------------------------
+    def fp8_value(self, codes, fmt) -> np.ndarray:
+        """Values (float64) of 8-bit codes in format `fmt` (E4M3 or E5M2)."""
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        return np.array([self.lib.oracle_fp8_value(int(c), fmt) for c in codes.ravel()],
+                        dtype=np.float64).reshape(codes.shape)
+
+    def fp8_round(self, x, fmt) -> np.ndarray:
+        """Nearest 8-bit code (ties to even) of each float32 in `x`."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, dtype=np.uint8)
+        self.lib.oracle_fp8_round_array(_f32(x), x.size, fmt, _u8(out))
+        return out
+
+    def block_exponent(self, absmax: float, fmt) -> int:
+        return self.lib.oracle_block_exponent(float(absmax), fmt)
+
+    def quantize(self, x, fmt):
+        """(codes uint8[n], scales uint8[ceil(n/32)]) of float32 `x`."""
+        x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+        codes = np.empty(x.size, dtype=np.uint8)
+        scales = np.empty((x.size + QBLOCK - 1) // QBLOCK, dtype=np.uint8)
+        self.lib.oracle_quantize(_f32(x), x.size, fmt, _u8(codes), _u8(scales))
+        return codes, scales
+
+    def dequantize(self, codes, scales, fmt) -> np.ndarray:
+        codes = np.ascontiguousarray(codes, dtype=np.uint8).ravel()
+        scales = np.ascontiguousarray(scales, dtype=np.uint8).ravel()
+        if scales.size != (codes.size + QBLOCK - 1) // QBLOCK:
+            raise ValueError("scales: one byte per 32 codes")
+        out = np.empty(codes.size, dtype=np.float32)
+        self.lib.oracle_dequantize(_u8(codes), _u8(scales), codes.size, fmt, _f32(out))
+        return out
+
+    def adamw8_step(self, master, m_codes, m_scales, v_codes, v_scales, grad, param_bf16,
+                    clip, t, lr, beta1, beta2, eps, wd) -> None:
+        """In-place step on one tensor whose moments are 8-bit (m: E4M3,
+        v: E5M2, one scale byte per 32 elements)."""
+        n = master.size
+        if master.dtype != np.float32 or not master.flags.c_contiguous:
+            raise ValueError("master: contiguous float32")
+        nb = (n + QBLOCK - 1) // QBLOCK
+        for a, size in ((m_codes, n), (v_codes, n), (m_scales, nb), (v_scales, nb)):
+            if a.dtype != np.uint8 or not a.flags.c_contiguous or a.size != size:
+                raise ValueError("codes: contiguous uint8[n]; scales: contiguous uint8[ceil(n/32)]")
+        grad = np.ascontiguousarray(grad)
+        if grad.size != n or grad.dtype not in (np.float32, np.uint16):
+            raise ValueError("grad: float32 or uint16 (bf16), same size")
+        if param_bf16 is not None and (param_bf16.dtype != np.uint16 or
+                                       param_bf16.size != n or
+                                       not param_bf16.flags.c_contiguous):
+            raise ValueError("param_bf16: contiguous uint16 of the same size")
+        self.lib.oracle_adamw8_step(
+            _f32(master), _u8(m_codes), _u8(m_scales), _u8(v_codes), _u8(v_scales),
+            grad.ctypes.data_as(ctypes.c_void_p), int(grad.dtype == np.uint16),
+            _u16(param_bf16) if param_bf16 is not None else None,
+            n, float(clip), int(t), lr, beta1, beta2, eps, wd)
+
+
 def _f32(a):
     return a.ctypes.data_as(_c_f32p)
 
 
 def _u16(a):
     return a.ctypes.data_as(_c_u16p)
+
+
+def _u8(a):
+    return a.ctypes.data_as(_c_u8p)
 
 
 _default = None

@@ -220,3 +220,152 @@ void oracle_adamw_step(float* master, float* exp_avg, float* exp_avg_sq,
         if (param_bf16) param_bf16[i] = oracle_f32_to_bf16(master[i]);
     }
 }
+
+/* ------------------------------------------------- 8-bit moment state --- */
+
+/* The 10N variant of the state (Lecture 9 exercises page: the third row of
+ * the three-basis table and the 7B answer, where 8-bit optimizer state takes
+ * the 16N of mixed-precision Adam down to 10N, 112 GB to 70 GB): m and v are
+ * stored in one byte per element.  The page names no encoding.  The reading
+ * taken here:
+ *   - element codes are OCP 8-bit floats: E4M3 (finite only, largest 448)
+ *     for m and E5M2 (largest finite 57344) for v, whose wider exponent range
+ *     holds v's squared magnitudes;
+ *   - each run of 32 consecutive elements of a tensor (the last run may be
+ *     shorter) shares a power-of-two scale 2^e, stored as the byte e + 127;
+ *     an element's value is code * 2^e;
+ *   - e is the smallest integer >= -127 for which the run's largest magnitude
+ *     is at most the format's largest finite value times 2^e, so scaling
+ *     never overflows and is exact;
+ *   - a scaled value is rounded to the nearest code, ties to the even code;
+ *   - a run holding a NaN or an infinity is stored as scale byte 255 with
+ *     every code 255 and reads back as NaN;
+ *   - a step decodes m and v, applies the fp32 update above unchanged (the
+ *     new master comes from the unrounded fp32 moments) and stores the new
+ *     moments re-encoded with fresh scales. */
+
+#define ORACLE_QBLOCK 32
+#define ORACLE_E4M3 0
+#define ORACLE_E5M2 1
+
+/* Value of one 8-bit code (sign, exponent field, mantissa field). */
+double oracle_fp8_value(uint8_t code, int format)
+{
+    const int mbits = format == ORACLE_E4M3 ? 3 : 2;
+    const int ebits = 7 - mbits;
+    const int bias = (1 << (ebits - 1)) - 1;
+    const int E = (code >> mbits) & ((1 << ebits) - 1);
+    const int M = code & ((1 << mbits) - 1);
+    double mag;
+    if (format == ORACLE_E4M3 && E == 15 && M == 7) return NAN;
+    if (format == ORACLE_E5M2 && E == 31) {
+        if (M != 0) return NAN;
+        mag = INFINITY;
+    } else if (E == 0) {
+        mag = ldexp((double)M, 1 - bias - mbits);            /* subnormal */
+    } else {
+        mag = ldexp((double)((1 << mbits) + M), E - bias - mbits);
+    }
+    return (code & 0x80) ? -mag : mag;
+}
+
+/* Nearest code to x, ties to the even code.  The candidates are every finite
+ * non-negative code and the code one above the largest, standing for the
+ * next step of the grid: in E4M3 that code is NaN (480), in E5M2 infinity
+ * (65536), so values past the halfway point to it overflow the way the
+ * format's own conversion rule says. */
+uint8_t oracle_fp8_round(double x, int format)
+{
+    if (isnan(x)) return signbit(x) ? 0xFF : 0x7F;
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    const int top = format == ORACLE_E4M3 ? 0x7E : 0x7B;
+    const double next = format == ORACLE_E4M3 ? 480.0 : 65536.0;
+    const double a = fabs(x);
+    /* At or past the next grid point, that point is the nearest candidate
+     * (the test keeps the distances below exact in double). */
+    if (a >= next) return (uint8_t)(sign | (top + 1));
+    int best = 0;
+    double best_d = a;
+    for (int c = 1; c <= top + 1; ++c) {
+        const double v = c <= top ? oracle_fp8_value((uint8_t)c, format) : next;
+        const double d = fabs(a - v);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+void oracle_fp8_round_array(const float* x, int64_t n, int format, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_fp8_round((double)x[i], format);
+}
+
+/* Smallest e >= -127 with absmax <= largest * 2^e. */
+int oracle_block_exponent(double absmax, int format)
+{
+    const double largest = format == ORACLE_E4M3 ? 448.0 : 57344.0;
+    int e = -127;
+    while (ldexp(largest, e) < absmax) ++e;
+    return e;
+}
+
+/* Encode x[0..n) run by run: codes[n], scales[ceil(n / 32)]. */
+void oracle_quantize(const float* x, int64_t n, int format, uint8_t* codes, uint8_t* scales)
+{
+    for (int64_t b0 = 0; b0 < n; b0 += ORACLE_QBLOCK) {
+        const int64_t len = n - b0 < ORACLE_QBLOCK ? n - b0 : ORACLE_QBLOCK;
+        int finite = 1;
+        double absmax = 0.0;
+        for (int64_t i = 0; i < len; ++i) {
+            const double a = fabs((double)x[b0 + i]);
+            if (!isfinite(a)) finite = 0;
+            else if (a > absmax) absmax = a;
+        }
+        if (!finite) {
+            scales[b0 / ORACLE_QBLOCK] = 255;
+            memset(codes + b0, 255, (size_t)len);
+            continue;
+        }
+        const int e = oracle_block_exponent(absmax, format);
+        scales[b0 / ORACLE_QBLOCK] = (uint8_t)(e + 127);
+        for (int64_t i = 0; i < len; ++i) {
+            codes[b0 + i] = oracle_fp8_round(ldexp((double)x[b0 + i], -e), format);
+        }
+    }
+}
+
+void oracle_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n, int format, float* x)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        const int s = scales[i / ORACLE_QBLOCK];
+        x[i] = s == 255 ? NAN : (float)ldexp(oracle_fp8_value(codes[i], format), s - 127);
+    }
+}
+
+/* The step over one tensor with 8-bit moments, run by run. */
+void oracle_adamw8_step(float* master, uint8_t* m_codes, uint8_t* m_scales, uint8_t* v_codes,
+                        uint8_t* v_scales, const void* grad, int grad_is_bf16,
+                        uint16_t* param_bf16, int64_t n, float clip, int64_t t, double lr,
+                        double beta1, double beta2, double eps, double wd)
+{
+    oracle_scalars s;
+    oracle_step_scalars(t, lr, beta1, beta2, eps, wd, &s);
+    float m[ORACLE_QBLOCK], v[ORACLE_QBLOCK];
+    for (int64_t b0 = 0; b0 < n; b0 += ORACLE_QBLOCK) {
+        const int64_t len = n - b0 < ORACLE_QBLOCK ? n - b0 : ORACLE_QBLOCK;
+        const int64_t blk = b0 / ORACLE_QBLOCK;
+        oracle_dequantize(m_codes + b0, m_scales + blk, len, ORACLE_E4M3, m);
+        oracle_dequantize(v_codes + b0, v_scales + blk, len, ORACLE_E5M2, v);
+        for (int64_t i = 0; i < len; ++i) {
+            const int64_t k = b0 + i;
+            const float g = grad_is_bf16 ? oracle_bf16_to_f32(((const uint16_t*)grad)[k])
+                                         : ((const float*)grad)[k];
+            oracle_update_one(&master[k], &m[i], &v[i], g, clip, &s);
+            if (param_bf16) param_bf16[k] = oracle_f32_to_bf16(master[k]);
+        }
+        oracle_quantize(m, len, ORACLE_E4M3, m_codes + b0, m_scales + blk);
+        oracle_quantize(v, len, ORACLE_E5M2, v_codes + b0, v_scales + blk);
+    }
+}

@@ -510,4 +510,250 @@ def pin_nonfinite_propagation(o):
     assert np.array_equal(m1[rest], (np.float32(B1) * m[rest]) + np.float32(0.0))
 
 
+# ------------------------------------------------- 8-bit moment state ---
+# Codes of m are E4M3, codes of v E5M2; 32 elements share a power-of-two
+# scale.  The library routine pinned against is torch's fp32 -> float8 cast
+# (round to nearest even) and its float8 -> fp32 widening; the block
+# exponent is re-derived here from frexp.
+
+Q_E4M3, Q_E5M2 = 0, 1
+Q_LARGEST = {Q_E4M3: 448.0, Q_E5M2: 57344.0}
+Q_TORCH = {Q_E4M3: torch.float8_e4m3fn, Q_E5M2: torch.float8_e5m2}
+Q_HALF_STEP = {Q_E4M3: (2.0 ** -4, 2.0 ** -10), Q_E5M2: (2.0 ** -3, 2.0 ** -17)}
+
+
+def q8_exponent_ref(absmax: float, fmt) -> int:
+    """Smallest e >= -127 with absmax <= largest * 2^e, from frexp."""
+    if absmax == 0.0:
+        return -127
+    mant, ex = math.frexp(absmax)                 # absmax = mant 2^ex, mant in [0.5, 1)
+    lmant, lex = math.frexp(Q_LARGEST[fmt])      # 448 = 0.875 2^9, 57344 = 0.875 2^16
+    e = ex - lex if mant <= lmant else ex - lex + 1
+    return max(e, -127)
+
+
+def q8_quantize_ref(x, fmt):
+    """Independent quantizer: frexp exponent, codes from torch's float8 cast."""
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    codes = np.empty(x.size, np.uint8)
+    scales = np.empty((x.size + 31) // 32, np.uint8)
+    for b in range(0, x.size, 32):
+        blk = x[b:b + 32]
+        if not np.isfinite(blk).all():
+            scales[b // 32] = 255
+            codes[b:b + 32] = 255
+            continue
+        e = q8_exponent_ref(float(np.max(np.abs(blk))), fmt)
+        scales[b // 32] = e + 127
+        scaled = (blk.astype(np.float64) * 2.0 ** -e).astype(np.float32)
+        codes[b:b + 32] = torch.from_numpy(scaled).to(Q_TORCH[fmt]).view(torch.uint8).numpy()
+    return codes, scales
+
+
+def q8_state(o, m, v):
+    mc, ms = o.quantize(m, Q_E4M3)
+    vc, vs = o.quantize(v, Q_E5M2)
+    return mc, ms, vc, vs
+
+
+def q8_step(o, w, state, g, c, t, copy=True, **hp):
+    h = dict(lr=LR, beta1=B1, beta2=B2, eps=EPS, wd=WD)
+    h.update(hp)
+    w = w.copy()
+    mc, ms, vc, vs = (a.copy() for a in state)
+    p = np.zeros(w.size, np.uint16) if copy else None
+    o.adamw8_step(w, mc, ms, vc, vs, g, p, c, t, h["lr"], h["beta1"], h["beta2"], h["eps"], h["wd"])
+    return w, (mc, ms, vc, vs), p
+
+
+def q8_blocks(n, seed):
+    """Values spread over many magnitudes, ragged, with special blocks."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(n) * 10.0 ** rng.integers(-40, 30, size=(n + 31) // 32).repeat(32)[:n]
+    x = x.astype(np.float32)
+    x[32:64] = 0.0                                  # all-zero block
+    x[64:96] *= np.float32(1e-4)
+    x[70] = np.float32(3.0)                         # one large value, the rest flush
+    x[96:128] = (rng.standard_normal(32) * 1e-39).astype(np.float32)   # fp32 subnormals
+    x[128] = -0.0
+    x[160:192] = np.float32(448.0) * np.float32(2.0 ** -30)            # exactly on a boundary
+    return x
+
+
+def pin_q8_codes_decode_like_torch(o):
+    for fmt in (Q_E4M3, Q_E5M2):
+        ours = o.fp8_value(np.arange(256), fmt)
+        ref = torch.arange(256, dtype=torch.uint8).view(Q_TORCH[fmt]).double().numpy()
+        assert np.array_equal(np.isnan(ours), np.isnan(ref)), fmt
+        keep = ~np.isnan(ref)
+        assert np.array_equal(ours[keep], ref[keep]), fmt
+
+
+def q8_probe_values() -> np.ndarray:
+    """Every bf16-grid fp32 value, every code value and midpoint of both
+    formats (and the overflow points), each with its fp32 neighbours."""
+    grid = (np.arange(1 << 16, dtype=np.uint32) << 16).view(np.float32)
+    pts = [np.float32([464.0, 480.0, 61440.0, 65536.0, 2.0 ** -10, 2.0 ** -17])]
+    for fmt in (Q_E4M3, Q_E5M2):
+        v = torch.arange(128, dtype=torch.uint8).view(Q_TORCH[fmt]).double().numpy()
+        v = np.unique(v[np.isfinite(v)])
+        pts += [v.astype(np.float32), ((v[:-1] + v[1:]) / 2).astype(np.float32)]
+    p = np.concatenate(pts)
+    up = np.nextafter(p, np.float32(np.inf))
+    down = np.nextafter(p, np.float32(-np.inf))
+    p = np.concatenate([p, up, down])
+    return np.concatenate([grid, p, -p, np.float32([np.inf, -np.inf, np.nan, -np.nan])])
+
+
+def pin_q8_rounding_matches_torch(o):
+    x = q8_probe_values()
+    for fmt in (Q_E4M3, Q_E5M2):
+        ours = o.fp8_round(x, fmt)
+        ref = torch.from_numpy(x).to(Q_TORCH[fmt]).view(torch.uint8).numpy()
+        bad = np.nonzero(ours != ref)[0]
+        assert bad.size == 0, (fmt, [(float(x[i]), int(ours[i]), int(ref[i])) for i in bad[:5]])
+
+
+def pin_q8_block_exponent(o):
+    rng = np.random.default_rng(21)
+    bits = rng.integers(0, 0x7F7FFFFF, size=4000, dtype=np.uint32)
+    samples = [0.0] + [float(a) for a in bits.view(np.float32)]
+    for fmt in (Q_E4M3, Q_E5M2):
+        edges = []
+        for k in range(-140, 122):
+            if Q_LARGEST[fmt] * 2.0 ** k > 3.4e38:
+                break
+            b = np.float32(Q_LARGEST[fmt] * 2.0 ** k)
+            if b > 0:
+                edges += [float(b), float(np.nextafter(b, np.float32(np.inf))),
+                          float(np.nextafter(b, np.float32(0)))]
+        for a in samples + edges:
+            e = o.block_exponent(a, fmt)
+            assert e == q8_exponent_ref(a, fmt), (fmt, a, e)
+            assert a <= math.ldexp(Q_LARGEST[fmt], e)
+            assert e == -127 or a > math.ldexp(Q_LARGEST[fmt], e - 1)
+
+
+def pin_q8_quantize_matches_reference(o):
+    x = q8_blocks(32 * 41 + 13, 22)
+    xn = x.copy()
+    xn[200] = np.nan
+    xn[260] = -np.inf
+    for fmt in (Q_E4M3, Q_E5M2):
+        for arr in (x, xn, x[:17], x[:0]):
+            codes, scales = o.quantize(arr, fmt)
+            rc, rs = q8_quantize_ref(arr, fmt)
+            assert np.array_equal(scales, rs), fmt
+            assert np.array_equal(codes, rc), fmt
+
+
+def pin_q8_roundtrip_error_bound(o):
+    x = q8_blocks(32 * 60 + 7, 23)
+    for fmt in (Q_E4M3, Q_E5M2):
+        codes, scales = o.quantize(x, fmt)
+        y = o.dequantize(codes, scales, fmt)
+        e = scales.astype(np.int64).repeat(32)[:x.size] - 127
+        rel, sub = Q_HALF_STEP[fmt]
+        bound = np.maximum(rel * np.abs(x.astype(np.float64)), sub * np.exp2(e.astype(np.float64)))
+        assert_within(y, x, bound, f"round trip, format {fmt}")
+        # The largest element of every block sits in the top binade: its code
+        # is at least half the largest code, unless the exponent is clamped.
+        for b in range(0, x.size, 32):
+            blk = np.abs(x[b:b + 32])
+            if blk.max() > 0 and scales[b // 32] > 0:
+                top = np.abs(y[b:b + 32]).max() * 2.0 ** -(int(scales[b // 32]) - 127)
+                assert Q_LARGEST[fmt] / 2 <= top <= Q_LARGEST[fmt], (fmt, b)
+    # Values already on a block's grid come back exactly.
+    rng = np.random.default_rng(24)
+    for fmt in (Q_E4M3, Q_E5M2):
+        codes = rng.integers(0, 0x78 if fmt == Q_E5M2 else 0x7E, size=320).astype(np.uint8)
+        codes |= rng.integers(0, 2, size=320).astype(np.uint8) << 7
+        codes[::32] = 0x7E if fmt == Q_E4M3 else 0x7B            # the block maximum
+        scales = rng.integers(1, 200, size=10).astype(np.uint8)
+        x = o.dequantize(codes, scales, fmt)
+        c2, s2 = o.quantize(x, fmt)
+        assert np.array_equal(s2, scales) and np.array_equal(o.dequantize(c2, s2, fmt), x)
+
+
+def pin_q8_step_is_fp32_step_on_decoded_state(o):
+    n = 32 * 9 + 5
+    w, m, v, g = rand_state(n, 25, warm=True)
+    g[::17] *= np.float32(100.0)
+    state = q8_state(o, m, v)
+    m_dec = o.dequantize(state[0], state[1], Q_E4M3)
+    v_dec = o.dequantize(state[2], state[3], Q_E5M2)
+    for grad in (g, o.f32_to_bf16(g)):
+        for c, t in ((np.float32(0.37), 7), (np.float32(1.0), 1)):
+            w8, (mc, ms, vc, vs), p8 = q8_step(o, w, state, grad, c, t)
+            w32, m32, v32, p32 = run_step(o, w, m_dec, v_dec, grad, c, t, copy=True)
+            assert np.array_equal(w8.view(np.uint32), w32.view(np.uint32))
+            assert np.array_equal(p8, p32)
+            rc, rs = q8_quantize_ref(m32, Q_E4M3)
+            assert np.array_equal(mc, rc) and np.array_equal(ms, rs)
+            rc, rs = q8_quantize_ref(v32, Q_E5M2)
+            assert np.array_equal(vc, rc) and np.array_equal(vs, rs)
+
+
+def pin_q8_zero_state_zero_gradient(o):
+    w, _, _, _ = rand_state(100, 26, warm=False)
+    zeros = np.zeros(100, np.float32)
+    state = (np.zeros(100, np.uint8), np.zeros(4, np.uint8), np.zeros(100, np.uint8),
+             np.zeros(4, np.uint8))
+    w1, st1, _ = q8_step(o, w, state, zeros, np.float32(1.0), 1)
+    decay = round_f32(1 - dec("3e-4") * dec("0.1"))
+    assert np.array_equal(w1.view(np.uint32), (w * decay).view(np.uint32))
+    for a in st1:
+        assert not a.any()
+
+
+def pin_q8_first_step_closed_form(o):
+    """From zero state the master follows the fp32 closed form and the stored
+    moments are (1 - b1) g and (1 - b2) g^2 within half a code step."""
+    w, _, _, g = rand_state(32 * 20, 27, warm=False)
+    state = (np.zeros(w.size, np.uint8), np.zeros(20, np.uint8)) * 2
+    c = np.float32(0.5)
+    w1, (mc, ms, vc, vs), _ = q8_step(o, w, state, g, c, 1)
+    gc = g.astype(np.float64) * float(c)
+    want = w.astype(np.float64) * (1 - LR * WD) - LR * gc / (np.abs(gc) + EPS)
+    assert_within(w1, want, 8 * U32 * (np.abs(w) + LR) + 1e-12, "first-step w (8-bit)")
+    for codes, scales, fmt, exact in ((mc, ms, Q_E4M3, (1 - B1) * gc),
+                                      (vc, vs, Q_E5M2, (1 - B2) * gc * gc)):
+        y = o.dequantize(codes, scales, fmt)
+        e = scales.astype(np.float64).repeat(32) - 127
+        rel, sub = Q_HALF_STEP[fmt]
+        bound = (rel * np.abs(exact) + sub * np.exp2(e)) * (1 + 1e-6) + 4 * U32 * np.abs(exact)
+        assert_within(y, exact, bound, f"stored moment, format {fmt}")
+
+
+def pin_q8_nonfinite_block(o):
+    """A NaN gradient poisons its own block of 32 (stored as NaN), nothing else."""
+    w, m, v, g = rand_state(96, 28, warm=True)
+    state = q8_state(o, m, v)
+    g[40] = np.nan
+    w1, st1, _ = q8_step(o, w, state, g, np.float32(1.0), 2)
+    assert np.isnan(w1[40]) and np.isfinite(np.delete(w1, 40)).all()
+    for codes, scales in ((st1[0], st1[1]), (st1[2], st1[3])):
+        assert scales[1] == 255 and (codes[32:64] == 255).all()
+        assert scales[0] != 255 and scales[2] != 255
+    g[40] = 0.0
+    w2, st2, _ = q8_step(o, w1, st1, g, np.float32(1.0), 3)
+    assert np.isnan(w2[32:64]).all()
+    assert np.isfinite(w2[:32]).all() and np.isfinite(w2[64:]).all()
+
+
+def pin_q8_list_equals_flat_on_block_multiples(o):
+    w, m, v, g = rand_state(32 * 30, 29, warm=True)
+    state = q8_state(o, m, v)
+    whole = q8_step(o, w, state, g, np.float32(0.8), 4)
+    cut = 32 * 11
+    parts = []
+    for lo, hi in ((0, cut), (cut, w.size)):
+        sub = (state[0][lo:hi], state[1][lo // 32:hi // 32], state[2][lo:hi], state[3][lo // 32:hi // 32])
+        parts.append(q8_step(o, w[lo:hi], tuple(np.ascontiguousarray(a) for a in sub), g[lo:hi],
+                             np.float32(0.8), 4))
+    assert np.array_equal(whole[0], np.concatenate([parts[0][0], parts[1][0]]))
+    for k in range(4):
+        assert np.array_equal(whole[1][k], np.concatenate([parts[0][1][k], parts[1][1][k]]))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

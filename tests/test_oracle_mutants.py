@@ -41,6 +41,27 @@ MUTANTS = {
     "scale_not_applied": ("return (float)(grad_scale * clip);", "return (float)clip;"),
     "scale_squared_in_norm": ("double norm = grad_scale * sqrt(sumsq);",
                               "double norm = grad_scale * grad_scale * sqrt(sumsq);"),
+    # 8-bit moment state
+    "q8_subnormal_exponent": ("mag = ldexp((double)M, 1 - bias - mbits);",
+                              "mag = ldexp((double)M, -bias - mbits);"),
+    "q8_ties_away": ("(d == best_d && (c & 1) == 0)", "(d == best_d)"),
+    "q8_saturates": ("if (a >= next) return (uint8_t)(sign | (top + 1));",
+                     "if (a >= next) return (uint8_t)(sign | top);"),
+    "q8_no_overflow_candidate": ("for (int c = 1; c <= top + 1; ++c) {", "for (int c = 1; c <= top; ++c) {"),
+    "q8_largest_e4m3": ("const double largest = format == ORACLE_E4M3 ? 448.0 : 57344.0;",
+                        "const double largest = format == ORACLE_E4M3 ? 480.0 : 57344.0;"),
+    "q8_exponent_floor": ("int e = -127;\n    while", "int e = -126;\n    while"),
+    "q8_exponent_inclusive": ("while (ldexp(largest, e) < absmax) ++e;",
+                              "while (ldexp(largest, e) <= absmax) ++e;"),
+    "q8_scale_bias": ("(float)ldexp(oracle_fp8_value(codes[i], format), s - 127);",
+                      "(float)ldexp(oracle_fp8_value(codes[i], format), s - 126);"),
+    "q8_scale_index": ("const int s = scales[i / ORACLE_QBLOCK];",
+                       "const int s = scales[i / (2 * ORACLE_QBLOCK)];"),
+    "q8_step_one_scale": ("const int64_t blk = b0 / ORACLE_QBLOCK;", "const int64_t blk = 0;"),
+    "q8_m_decoded_as_e5m2": ("oracle_dequantize(m_codes + b0, m_scales + blk, len, ORACLE_E4M3, m);",
+                             "oracle_dequantize(m_codes + b0, m_scales + blk, len, ORACLE_E5M2, m);"),
+    "q8_nan_block_codes": ("memset(codes + b0, 255, (size_t)len);", "memset(codes + b0, 0, (size_t)len);"),
+    "q8_nan_block_ignored": ("if (!isfinite(a)) finite = 0;", "if (!isfinite(a)) finite = 1;"),
 }
 
 
