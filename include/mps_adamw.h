@@ -224,6 +224,91 @@ int adamw_fused_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dt
                      double beta1, double beta2, double eps, double weight_decay,
                      void* d_workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------- 8-bit moment state ---
+ *
+ * The 10N variant of the state (Lecture 9 exercises page: the third row of
+ * the three-basis table, mixed precision with an 8-bit optimizer, and the 7B
+ * answer, 70 GB instead of 112 GB): m and v are kept in one byte per element.
+ * The page gives no encoding; this library's is
+ *   - m: one OCP FP8 E4M3 code per element (largest finite value 448);
+ *   - v: one OCP FP8 E5M2 code per element (largest finite value 57344);
+ *   - every run of MPS_Q8_BLOCK = 32 consecutive elements of a tensor (the
+ *     last run may be shorter) shares one scale byte b per moment, and an
+ *     element's value is code * 2^(b - 127).  b = 255 marks a run that held a
+ *     NaN or an infinity: its codes are all 0xFF and it reads back as NaN;
+ *   - a run is written with the smallest exponent e = b - 127 >= -127 for
+ *     which its largest magnitude is at most the format's largest value times
+ *     2^e; each value is multiplied by 2^-e (exact) and rounded to the
+ *     nearest code, ties to the even code.
+ * Codes and scale bytes that are all zero are a valid zero state (m = v = 0).
+ * State per parameter: fp32 master 4 B + codes 2 B + scale bytes 2/32 B, so
+ * with bf16 gradients and a bf16 copy the accounting is 10.0625N.
+ */
+#define MPS_Q8_BLOCK 32
+
+typedef enum mps_q8_format {
+    MPS_Q8_E4M3 = 0, /* first moment m  */
+    MPS_Q8_E5M2 = 1  /* second moment v */
+} mps_q8_format;
+
+/* One parameter tensor with 8-bit moments.  Device pointers; any
+ * element-aligned start is accepted.  Whole runs of a tensor whose master,
+ * gradient and copy are 16-byte aligned and whose code arrays are 8-byte
+ * aligned take the vector path; other tensors are processed element-wise
+ * (same results). */
+typedef struct mps_tensor8 {
+    float* master;              /* fp32 master weights, updated in place          */
+    uint8_t* exp_avg_codes;     /* m: E4M3 codes [numel], updated in place         */
+    uint8_t* exp_avg_scales;    /* m: scale bytes [ceil(numel / 32)], in place     */
+    uint8_t* exp_avg_sq_codes;  /* v: E5M2 codes [numel], updated in place         */
+    uint8_t* exp_avg_sq_scales; /* v: scale bytes [ceil(numel / 32)], in place     */
+    const void* grad;           /* fp32 or bf16 gradient, read only                */
+    uint16_t* param_bf16;       /* bf16 copy of the new master (written), or NULL */
+    int64_t numel;              /* >= 0; a tensor with numel == 0 is skipped       */
+} mps_tensor8;
+
+/* Workspace size for adamw8_grad_norm_sq and adamw8_multi_tensor_step on this
+ * list (same rules as adamw_workspace_bytes; release it with
+ * adamw_workspace_release).  Returns 0 and sets the last error if the list
+ * is invalid. */
+size_t adamw8_workspace_bytes(const mps_tensor8* tensors, int n_tensors);
+
+/* grad_norm_sq for a list of 8-bit-state tensors: the same result and
+ * arguments (only grad and numel are read; pass the same list as to the
+ * step so that the workspace tables are shared). */
+int adamw8_grad_norm_sq(const mps_tensor8* tensors, int n_tensors, mps_dtype grad_dtype,
+                        double* d_sumsq, double max_norm, double grad_scale, float* d_coef,
+                        void* d_workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * adamw8_multi_tensor_step — adamw_multi_tensor_step with 8-bit moments.
+ * Per run of 32 elements: m and v are decoded to fp32, every element takes
+ * exactly the fp32 update of adamw_multi_tensor_step (the new master and its
+ * bf16 copy come from the unrounded fp32 moments), and the new m and v are
+ * encoded with fresh scale bytes as described above.  Arguments, step
+ * counter, skip rule and errors as adamw_multi_tensor_step.
+ */
+int adamw8_multi_tensor_step(const mps_tensor8* tensors, int n_tensors,
+                             mps_dtype grad_dtype, const float* d_coef,
+                             const double* d_skip_if_nonfinite, int32_t* d_step,
+                             double lr, double beta1, double beta2, double eps,
+                             double weight_decay, void* d_workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * adamw8_quantize — encode n fp32 values (e.g. fp32 moments from a
+ * checkpoint) as 8-bit state: d_codes[n] and d_scales[ceil(n / 32)], with
+ * the encoding rule above; runs start at d_x[0].
+ * adamw8_dequantize — the values the state stands for, as fp32 (scale byte
+ * 255 gives NaN).
+ *   format : MPS_Q8_E4M3 for m, MPS_Q8_E5M2 for v.
+ *   n >= 0 (n == 0 enqueues nothing); pointers non-NULL when n > 0.
+ */
+int adamw8_quantize(const float* d_x, int64_t n, mps_q8_format format, uint8_t* d_codes,
+                    uint8_t* d_scales, void* stream);
+int adamw8_dequantize(const uint8_t* d_codes, const uint8_t* d_scales, int64_t n,
+                      mps_q8_format format, float* d_x, void* stream);
+
 /* The calling thread's last error message ("" if none). */
 const char* adamw_last_error(void);
 

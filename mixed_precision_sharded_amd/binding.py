@@ -16,6 +16,9 @@ LIB_PATH = os.path.join(HERE, "libmps_adamw.so")
 MPS_OK = 0
 MPS_DTYPE_F32 = 0
 MPS_DTYPE_BF16 = 1
+MPS_Q8_E4M3 = 0   # 8-bit format of m
+MPS_Q8_E5M2 = 1   # 8-bit format of v
+MPS_Q8_BLOCK = 32
 WORKSPACE_ALIGN = 256
 
 
@@ -25,6 +28,20 @@ class MpsTensor(ctypes.Structure):
         ("master", ctypes.c_void_p),
         ("exp_avg", ctypes.c_void_p),
         ("exp_avg_sq", ctypes.c_void_p),
+        ("grad", ctypes.c_void_p),
+        ("param_bf16", ctypes.c_void_p),
+        ("numel", ctypes.c_int64),
+    ]
+
+
+class MpsTensor8(ctypes.Structure):
+    """Mirror of `mps_tensor8`."""
+    _fields_ = [
+        ("master", ctypes.c_void_p),
+        ("exp_avg_codes", ctypes.c_void_p),
+        ("exp_avg_scales", ctypes.c_void_p),
+        ("exp_avg_sq_codes", ctypes.c_void_p),
+        ("exp_avg_sq_scales", ctypes.c_void_p),
         ("grad", ctypes.c_void_p),
         ("param_bf16", ctypes.c_void_p),
         ("numel", ctypes.c_int64),
@@ -69,6 +86,20 @@ def lib() -> ctypes.CDLL:
             ctypes.POINTER(MpsTensor), ctypes.c_int, ctypes.c_int, ctypes.c_double,
             ctypes.c_double, ctypes.c_int, P, P, P, ctypes.c_double, ctypes.c_double,
             ctypes.c_double, ctypes.c_double, ctypes.c_double, P, ctypes.c_size_t, P]
+        T8 = ctypes.POINTER(MpsTensor8)
+        L.adamw8_workspace_bytes.restype = ctypes.c_size_t
+        L.adamw8_workspace_bytes.argtypes = [T8, ctypes.c_int]
+        L.adamw8_grad_norm_sq.restype = ctypes.c_int
+        L.adamw8_grad_norm_sq.argtypes = [T8, ctypes.c_int, ctypes.c_int, P, ctypes.c_double,
+                                          ctypes.c_double, P, P, ctypes.c_size_t, P]
+        L.adamw8_multi_tensor_step.restype = ctypes.c_int
+        L.adamw8_multi_tensor_step.argtypes = [
+            T8, ctypes.c_int, ctypes.c_int, P, P, P, ctypes.c_double, ctypes.c_double,
+            ctypes.c_double, ctypes.c_double, ctypes.c_double, P, ctypes.c_size_t, P]
+        L.adamw8_quantize.restype = ctypes.c_int
+        L.adamw8_quantize.argtypes = [P, ctypes.c_int64, ctypes.c_int, P, P, P]
+        L.adamw8_dequantize.restype = ctypes.c_int
+        L.adamw8_dequantize.argtypes = [P, P, ctypes.c_int64, ctypes.c_int, P, P]
         L.adamw_last_error.restype = ctypes.c_char_p
         L.adamw_last_error.argtypes = []
         _lib = L
@@ -131,12 +162,15 @@ class TensorList:
         self.n = n
         self._refs = (list(masters), list(exp_avgs), list(exp_avg_sqs), list(grads),
                       list(params_bf16))
-        self.workspace_bytes = lib().adamw_workspace_bytes(self.array, n)
-        if self.workspace_bytes == 0:
-            raise MpsError(-22, "adamw_workspace_bytes", last_error())
+        self._allocate_workspace(lib().adamw_workspace_bytes(self.array, n), "adamw_workspace_bytes")
+
+    def _allocate_workspace(self, nbytes: int, where: str) -> None:
+        if nbytes == 0:
+            raise MpsError(-22, where, last_error())
+        self.workspace_bytes = nbytes
         # Over-allocate so the base can be rounded up to 256 bytes.
-        self._ws_storage = torch.empty(self.workspace_bytes + WORKSPACE_ALIGN,
-                                       dtype=torch.uint8, device=self.device)
+        self._ws_storage = torch.empty(nbytes + WORKSPACE_ALIGN, dtype=torch.uint8,
+                                       device=self.device)
         base = self._ws_storage.data_ptr()
         self.workspace_ptr = (base + WORKSPACE_ALIGN - 1) // WORKSPACE_ALIGN * WORKSPACE_ALIGN
 
@@ -151,6 +185,63 @@ class TensorList:
             self.release()
         except Exception:
             pass
+
+
+def q8_scale_count(numel: int) -> int:
+    """Scale bytes per moment of a tensor with 8-bit state."""
+    return (numel + MPS_Q8_BLOCK - 1) // MPS_Q8_BLOCK
+
+
+def zeros_q8_state(numel: int, device) -> tuple:
+    """(m codes, m scales, v codes, v scales), all zero: m = v = 0."""
+    nb = q8_scale_count(numel)
+    return (torch.zeros(numel, dtype=torch.uint8, device=device),
+            torch.zeros(nb, dtype=torch.uint8, device=device),
+            torch.zeros(numel, dtype=torch.uint8, device=device),
+            torch.zeros(nb, dtype=torch.uint8, device=device))
+
+
+class TensorList8(TensorList):
+    """The `mps_tensor8` records of a list whose moments are 8-bit, and its
+    workspace.  states[i] = (m codes, m scales, v codes, v scales): uint8
+    CUDA tensors of numel, ceil(numel / 32), numel, ceil(numel / 32)
+    elements (see zeros_q8_state)."""
+
+    def __init__(self, masters: Sequence[torch.Tensor], states: Sequence[tuple],
+                 grads: Sequence[torch.Tensor],
+                 params_bf16: Optional[Sequence[Optional[torch.Tensor]]] = None):
+        n = len(masters)
+        if not (len(states) == len(grads) == n) or n == 0:
+            raise ValueError("masters, states and grads: same non-zero length")
+        if params_bf16 is None:
+            params_bf16 = [None] * n
+        if len(params_bf16) != n:
+            raise ValueError("params_bf16 must have one entry per tensor")
+        gdt = grads[0].dtype
+        if gdt not in (torch.float32, torch.bfloat16):
+            raise TypeError("grads must be float32 or bfloat16")
+        self.grad_dtype = MPS_DTYPE_BF16 if gdt == torch.bfloat16 else MPS_DTYPE_F32
+        self.device = masters[0].device
+        self.array = (MpsTensor8 * n)()
+        for i in range(n):
+            w, g, p = masters[i], grads[i], params_bf16[i]
+            k = w.numel()
+            if len(states[i]) != 4:
+                raise ValueError(f"states[{i}]: (m codes, m scales, v codes, v scales)")
+            mc, ms, vc, vs = states[i]
+            _require(w, torch.float32, k, self.device, f"master[{i}]")
+            _require(g, gdt, k, self.device, f"grad[{i}]")
+            _require(mc, torch.uint8, k, self.device, f"m codes[{i}]")
+            _require(vc, torch.uint8, k, self.device, f"v codes[{i}]")
+            _require(ms, torch.uint8, q8_scale_count(k), self.device, f"m scales[{i}]")
+            _require(vs, torch.uint8, q8_scale_count(k), self.device, f"v scales[{i}]")
+            if p is not None:
+                _require(p, torch.bfloat16, k, self.device, f"param_bf16[{i}]")
+            self.array[i] = MpsTensor8(_ptr(w), _ptr(mc), _ptr(ms), _ptr(vc), _ptr(vs), _ptr(g),
+                                       _ptr(p), k)
+        self.n = n
+        self._refs = (list(masters), [tuple(st) for st in states], list(grads), list(params_bf16))
+        self._allocate_workspace(lib().adamw8_workspace_bytes(self.array, n), "adamw8_workspace_bytes")
 
 
 def _require(t: torch.Tensor, dtype, numel: int, device, name: str) -> None:
@@ -234,3 +325,71 @@ def adamw_fused_step(tl: TensorList, step: torch.Tensor, lr: float, beta1: float
         1 if skip_if_nonfinite else 0, _ptr(sumsq_out), _ptr(coef_out), step.data_ptr(),
         float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), tl.workspace_ptr,
         tl.workspace_bytes, _stream_handle(stream)), "adamw_fused_step")
+
+
+# ------------------------------------------------------ 8-bit moment state ---
+
+def adamw8_grad_norm_sq(tl: TensorList8, out: torch.Tensor, max_norm: Optional[float] = None,
+                        coef_out: Optional[torch.Tensor] = None, grad_scale: float = 1.0,
+                        stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """grad_norm_sq for a TensorList8."""
+    if not isinstance(tl, TensorList8):
+        raise TypeError("adamw8_grad_norm_sq takes a TensorList8")
+    if out.dtype != torch.float64 or out.device != tl.device or out.numel() < 1:
+        raise ValueError("out: float64 tensor on the list's device")
+    if coef_out is not None:
+        if coef_out.dtype != torch.float32 or coef_out.device != tl.device:
+            raise ValueError("coef_out: float32 tensor on the list's device")
+        if max_norm is None:
+            raise ValueError("coef_out needs max_norm")
+    _check(lib().adamw8_grad_norm_sq(tl.array, tl.n, tl.grad_dtype, out.data_ptr(),
+                                     float(max_norm) if max_norm is not None else 0.0,
+                                     float(grad_scale), _ptr(coef_out), tl.workspace_ptr,
+                                     tl.workspace_bytes, _stream_handle(stream)),
+           "adamw8_grad_norm_sq")
+    return out
+
+
+def adamw8_multi_tensor_step(tl: TensorList8, coef: Optional[torch.Tensor], step: torch.Tensor,
+                             lr: float, beta1: float, beta2: float, eps: float,
+                             weight_decay: float, skip_if_nonfinite: Optional[torch.Tensor] = None,
+                             stream: Optional[torch.cuda.Stream] = None) -> None:
+    """adamw_multi_tensor_step with 8-bit moments."""
+    if not isinstance(tl, TensorList8):
+        raise TypeError("adamw8_multi_tensor_step takes a TensorList8")
+    if coef is not None and (coef.dtype != torch.float32 or coef.device != tl.device):
+        raise ValueError("coef: float32 tensor on the list's device, or None")
+    if step.dtype != torch.int32 or step.device != tl.device:
+        raise ValueError("step: int32 tensor on the list's device")
+    if skip_if_nonfinite is not None and (skip_if_nonfinite.dtype != torch.float64 or
+                                          skip_if_nonfinite.device != tl.device):
+        raise ValueError("skip_if_nonfinite: float64 tensor on the list's device, or None")
+    _check(lib().adamw8_multi_tensor_step(
+        tl.array, tl.n, tl.grad_dtype, _ptr(coef), _ptr(skip_if_nonfinite), step.data_ptr(),
+        float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), tl.workspace_ptr,
+        tl.workspace_bytes, _stream_handle(stream)), "adamw8_multi_tensor_step")
+
+
+def adamw8_quantize(x: torch.Tensor, fmt: int, codes: torch.Tensor, scales: torch.Tensor,
+                    stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Encode fp32 `x` into 8-bit codes and scale bytes (fmt MPS_Q8_E4M3 / _E5M2)."""
+    n = x.numel()
+    if x.dtype != torch.float32 or x.device.type != "cuda" or not x.is_contiguous():
+        raise ValueError("x: contiguous float32 CUDA tensor")
+    _require(codes, torch.uint8, n, x.device, "codes")
+    _require(scales, torch.uint8, q8_scale_count(n), x.device, "scales")
+    _check(lib().adamw8_quantize(_ptr(x), n, int(fmt), _ptr(codes), _ptr(scales),
+                                 _stream_handle(stream)), "adamw8_quantize")
+
+
+def adamw8_dequantize(codes: torch.Tensor, scales: torch.Tensor, fmt: int, out: torch.Tensor,
+                      stream: Optional[torch.cuda.Stream] = None) -> None:
+    """The fp32 values that 8-bit codes and scale bytes stand for."""
+    n = codes.numel()
+    if codes.device.type != "cuda":
+        raise ValueError("codes: CUDA tensor")
+    _require(codes, torch.uint8, n, codes.device, "codes")
+    _require(scales, torch.uint8, q8_scale_count(n), codes.device, "scales")
+    _require(out, torch.float32, n, codes.device, "out")
+    _check(lib().adamw8_dequantize(_ptr(codes), _ptr(scales), n, int(fmt), _ptr(out),
+                                   _stream_handle(stream)), "adamw8_dequantize")

@@ -47,6 +47,7 @@ int ok()
 struct Plan {
     std::vector<unsigned char> image;  // header + tensor entries + chunk map
     size_t tensors_off = 0;
+    size_t quant_off = 0;   // 8-bit lists: QuantEntry table (else == chunks_off)
     size_t chunks_off = 0;
     size_t partials_off = 0;
     size_t total_bytes = 0;
@@ -96,6 +97,54 @@ uint64_t fnv1a(const unsigned char* p, size_t n, uint64_t h = 146959810393466560
     return h;
 }
 
+// Chunk the list and build the workspace image: header, tensor entries,
+// the QuantEntry table of an 8-bit list (`quant` non-NULL), chunk map.
+// `entries` carry numel, pointers and head; first_chunk is filled in here.
+int layout_plan(std::vector<TensorEntry>& entries, const std::vector<mps::QuantEntry>* quant,
+                int64_t total, Plan& plan)
+{
+    const int n = static_cast<int>(entries.size());
+    plan.chunk_elems = pick_chunk_elems(total);
+    int64_t n_chunks = 0;
+    for (TensorEntry& e : entries) {
+        e.first_chunk = static_cast<int32_t>(n_chunks);
+        n_chunks += (e.numel + plan.chunk_elems - 1) / plan.chunk_elems;
+        if (n_chunks > INT32_MAX) return fail(MPS_ERR_INVALID_ARGUMENT, "too many chunks");
+    }
+    plan.n_chunks = static_cast<int>(n_chunks);
+
+    plan.tensors_off = sizeof(WorkspaceHeader);
+    plan.quant_off = plan.tensors_off + sizeof(TensorEntry) * static_cast<size_t>(n);
+    plan.chunks_off = plan.quant_off + (quant ? sizeof(mps::QuantEntry) * static_cast<size_t>(n) : 0);
+    plan.partials_off = round_up(plan.chunks_off + sizeof(uint32_t) * n_chunks, 256);
+    plan.total_bytes = plan.partials_off + sizeof(double) * mps::kPartials;
+
+    plan.image.assign(plan.partials_off, 0);
+    unsigned char* base = plan.image.data();
+    std::memcpy(base + plan.tensors_off, entries.data(), sizeof(TensorEntry) * n);
+    if (quant) std::memcpy(base + plan.quant_off, quant->data(), sizeof(mps::QuantEntry) * n);
+    uint32_t* map = reinterpret_cast<uint32_t*>(base + plan.chunks_off);
+    for (int i = 0; i < n; ++i) {
+        const int64_t k = (entries[i].numel + plan.chunk_elems - 1) / plan.chunk_elems;
+        for (int64_t j = 0; j < k; ++j) map[entries[i].first_chunk + j] = static_cast<uint32_t>(i);
+    }
+
+    // The tag identifies the tables; it never equals zero, so freshly
+    // zeroed memory is never mistaken for an upload.
+    uint64_t tag = fnv1a(base + plan.tensors_off, plan.partials_off - plan.tensors_off);
+    tag = fnv1a(reinterpret_cast<const unsigned char*>(&plan.chunk_elems), sizeof plan.chunk_elems, tag);
+    plan.tag = tag ? tag : 1;
+
+    WorkspaceHeader* hdr = reinterpret_cast<WorkspaceHeader*>(base);
+    hdr->norm_ticket = 0;
+    hdr->step_ticket = 0;
+    hdr->tag = plan.tag;
+    hdr->n_tensors = n;
+    hdr->n_chunks = plan.n_chunks;
+    hdr->chunk_elems = plan.chunk_elems;
+    return MPS_OK;
+}
+
 // Validate the list and lay out the workspace.  `need_state` asks for the
 // master / moment pointers (the step); the norm reads gradients only.
 int build_plan(const mps_tensor* tensors, int n, int grad_dtype, bool need_state, Plan& plan)
@@ -133,15 +182,12 @@ int build_plan(const mps_tensor* tensors, int n, int grad_dtype, bool need_state
         total += t.numel;
     }
 
-    plan.chunk_elems = pick_chunk_elems(total);
-    int64_t n_chunks = 0;
     std::vector<TensorEntry> entries(n);
     for (int i = 0; i < n; ++i) {
         const mps_tensor& t = tensors[i];
         TensorEntry& e = entries[i];
         std::memset(&e, 0, sizeof e);
         e.numel = t.numel;
-        e.first_chunk = static_cast<int32_t>(n_chunks);
         if (t.numel == 0) continue;  // no chunks; pointers stay NULL
         e.master = t.master;
         e.exp_avg = t.exp_avg;
@@ -149,39 +195,64 @@ int build_plan(const mps_tensor* tensors, int n, int grad_dtype, bool need_state
         e.grad = t.grad;
         e.param_bf16 = t.param_bf16;  // the same list gives the same tables for both calls
         e.head = common_head(e, bf16);
-        n_chunks += (t.numel + plan.chunk_elems - 1) / plan.chunk_elems;
-        if (n_chunks > INT32_MAX) return fail(MPS_ERR_INVALID_ARGUMENT, "too many chunks");
     }
-    plan.n_chunks = static_cast<int>(n_chunks);
+    return layout_plan(entries, nullptr, total, plan);
+}
 
-    plan.tensors_off = sizeof(WorkspaceHeader);
-    plan.chunks_off = plan.tensors_off + sizeof(TensorEntry) * static_cast<size_t>(n);
-    plan.partials_off = round_up(plan.chunks_off + sizeof(uint32_t) * n_chunks, 256);
-    plan.total_bytes = plan.partials_off + sizeof(double) * mps::kPartials;
+bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
-    plan.image.assign(plan.partials_off, 0);
-    unsigned char* base = plan.image.data();
-    std::memcpy(base + plan.tensors_off, entries.data(), sizeof(TensorEntry) * n);
-    uint32_t* map = reinterpret_cast<uint32_t*>(base + plan.chunks_off);
+// The same for a list with 8-bit moments.  head is 0 when every stream is
+// aligned for the vector path at the tensor's start, -1 otherwise.
+int build_plan8(const mps_tensor8* tensors, int n, int grad_dtype, bool need_state, Plan& plan)
+{
+    if (!tensors) return fail(MPS_ERR_INVALID_ARGUMENT, "tensors is NULL");
+    if (n <= 0) return fail(MPS_ERR_INVALID_ARGUMENT, "n_tensors must be >= 1 (got %d)", n);
+    if (grad_dtype != MPS_DTYPE_F32 && grad_dtype != MPS_DTYPE_BF16) {
+        return fail(MPS_ERR_INVALID_ARGUMENT, "unknown gradient dtype %d", grad_dtype);
+    }
+    const bool bf16 = grad_dtype == MPS_DTYPE_BF16;
+    const int gbytes = bf16 ? 2 : 4;
+
+    int64_t total = 0;
+    std::vector<TensorEntry> entries(n);
+    std::vector<mps::QuantEntry> quant(n);
     for (int i = 0; i < n; ++i) {
-        const int64_t k = (entries[i].numel + plan.chunk_elems - 1) / plan.chunk_elems;
-        for (int64_t j = 0; j < k; ++j) map[entries[i].first_chunk + j] = static_cast<uint32_t>(i);
+        const mps_tensor8& t = tensors[i];
+        if (t.numel < 0) return fail(MPS_ERR_INVALID_ARGUMENT, "tensor %d: numel < 0", i);
+        TensorEntry& e = entries[i];
+        mps::QuantEntry& q = quant[i];
+        std::memset(&e, 0, sizeof e);
+        std::memset(&q, 0, sizeof q);
+        e.numel = t.numel;
+        if (t.numel == 0) continue;
+        if (!t.grad) return fail(MPS_ERR_INVALID_ARGUMENT, "tensor %d: grad is NULL", i);
+        if (!aligned(t.grad, gbytes)) {
+            return fail(MPS_ERR_INVALID_ARGUMENT, "tensor %d: grad not %d-byte aligned", i, gbytes);
+        }
+        if (need_state) {
+            if (!t.master || !t.exp_avg_codes || !t.exp_avg_scales || !t.exp_avg_sq_codes ||
+                !t.exp_avg_sq_scales) {
+                return fail(MPS_ERR_INVALID_ARGUMENT, "tensor %d: master or 8-bit state is NULL", i);
+            }
+            if (!aligned(t.master, 4)) return fail(MPS_ERR_INVALID_ARGUMENT, "tensor %d: master not 4-byte aligned", i);
+            if (!aligned(t.param_bf16, 2)) {
+                return fail(MPS_ERR_INVALID_ARGUMENT, "tensor %d: param_bf16 not 2-byte aligned", i);
+            }
+        }
+        if (total > INT64_MAX - t.numel) return fail(MPS_ERR_INVALID_ARGUMENT, "total numel overflows");
+        total += t.numel;
+        e.master = t.master;
+        e.grad = t.grad;
+        e.param_bf16 = t.param_bf16;
+        q.m_codes = t.exp_avg_codes;
+        q.m_scales = t.exp_avg_scales;
+        q.v_codes = t.exp_avg_sq_codes;
+        q.v_scales = t.exp_avg_sq_scales;
+        const bool vector = aligned(t.master, 16) && aligned(t.grad, 16) && aligned(t.param_bf16, 16) &&
+                            aligned(t.exp_avg_codes, 8) && aligned(t.exp_avg_sq_codes, 8);
+        e.head = vector ? 0 : -1;
     }
-
-    // The tag identifies the tables; it never equals zero, so freshly
-    // zeroed memory is never mistaken for an upload.
-    uint64_t tag = fnv1a(base + plan.tensors_off, plan.partials_off - plan.tensors_off);
-    tag = fnv1a(reinterpret_cast<const unsigned char*>(&plan.chunk_elems), sizeof plan.chunk_elems, tag);
-    plan.tag = tag ? tag : 1;
-
-    WorkspaceHeader* hdr = reinterpret_cast<WorkspaceHeader*>(base);
-    hdr->norm_ticket = 0;
-    hdr->step_ticket = 0;
-    hdr->tag = plan.tag;
-    hdr->n_tensors = n;
-    hdr->n_chunks = plan.n_chunks;
-    hdr->chunk_elems = plan.chunk_elems;
-    return MPS_OK;
+    return layout_plan(entries, &quant, total, plan);
 }
 
 // -------------------------------------------------- workspace upload cache ---
@@ -258,6 +329,45 @@ bool finite_in(double x, double lo, double hi_exclusive)
     return std::isfinite(x) && x >= lo && x < hi_exclusive;
 }
 
+int check_hyperparameters(double lr, double beta1, double beta2, double eps, double weight_decay)
+{
+    if (!(std::isfinite(lr) && lr >= 0.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "lr must be finite and >= 0");
+    if (!finite_in(beta1, 0.0, 1.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "beta1 must be in [0, 1)");
+    if (!finite_in(beta2, 0.0, 1.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "beta2 must be in [0, 1)");
+    if (!(std::isfinite(eps) && eps >= 0.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+    if (!(std::isfinite(weight_decay) && weight_decay >= 0.0)) {
+        return fail(MPS_ERR_INVALID_ARGUMENT, "weight_decay must be finite and >= 0");
+    }
+    return MPS_OK;
+}
+
+int check_clip_arguments(double max_norm, double grad_scale)
+{
+    if (!(std::isfinite(max_norm) && max_norm > 0.0)) {
+        return fail(MPS_ERR_INVALID_ARGUMENT, "max_norm must be finite and > 0");
+    }
+    if (!(std::isfinite(grad_scale) && grad_scale > 0.0)) {
+        return fail(MPS_ERR_INVALID_ARGUMENT, "grad_scale must be finite and > 0");
+    }
+    return MPS_OK;
+}
+
+// Launch the norm (and optionally the clip coefficient) over a planned list.
+int run_grad_norm(Plan& plan, bool bf16, double* d_sumsq, double max_norm,
+                  double grad_scale, float* d_coef, void* d_workspace, size_t workspace_bytes,
+                  void* stream)
+{
+    int rc = check_workspace(d_workspace, workspace_bytes, plan);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
+    const int grid = grid_for(plan.n_chunks, mps::kNormMaxBlocks);
+    hipError_t e = mps::launch_grad_norm(view_of(d_workspace, plan), bf16, grid, d_sumsq, max_norm,
+                                         grad_scale, d_coef, st);
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "grad_norm launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -291,35 +401,19 @@ int grad_norm_sq(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
                  size_t workspace_bytes, void* stream)
 {
     if (!d_sumsq) return fail(MPS_ERR_INVALID_ARGUMENT, "d_sumsq is NULL");
-    if (d_coef && !(std::isfinite(max_norm) && max_norm > 0.0)) {
-        return fail(MPS_ERR_INVALID_ARGUMENT, "max_norm must be finite and > 0");
-    }
-    if (d_coef && !(std::isfinite(grad_scale) && grad_scale > 0.0)) {
-        return fail(MPS_ERR_INVALID_ARGUMENT, "grad_scale must be finite and > 0");
-    }
-    Plan plan;
-    int rc = build_plan(tensors, n_tensors, grad_dtype, false, plan);
+    int rc = d_coef ? check_clip_arguments(max_norm, grad_scale) : MPS_OK;
     if (rc) return rc;
-    if ((rc = check_workspace(d_workspace, workspace_bytes, plan))) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
-    const int grid = grid_for(plan.n_chunks, mps::kNormMaxBlocks);
-    hipError_t e = mps::launch_grad_norm(view_of(d_workspace, plan), grad_dtype == MPS_DTYPE_BF16,
-                                         grid, d_sumsq, max_norm, grad_scale, d_coef, st);
-    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "grad_norm launch: %s", hipGetErrorString(e));
-    return ok();
+    Plan plan;
+    if ((rc = build_plan(tensors, n_tensors, grad_dtype, false, plan))) return rc;
+    return run_grad_norm(plan, grad_dtype == MPS_DTYPE_BF16, d_sumsq, max_norm, grad_scale, d_coef,
+                         d_workspace, workspace_bytes, stream);
 }
 
 int clip_coef(const double* d_sumsq, double max_norm, double grad_scale, float* d_coef,
               void* stream)
 {
     if (!d_sumsq || !d_coef) return fail(MPS_ERR_INVALID_ARGUMENT, "d_sumsq / d_coef is NULL");
-    if (!(std::isfinite(max_norm) && max_norm > 0.0)) {
-        return fail(MPS_ERR_INVALID_ARGUMENT, "max_norm must be finite and > 0");
-    }
-    if (!(std::isfinite(grad_scale) && grad_scale > 0.0)) {
-        return fail(MPS_ERR_INVALID_ARGUMENT, "grad_scale must be finite and > 0");
-    }
+    if (int rc = check_clip_arguments(max_norm, grad_scale)) return rc;
     hipError_t e = mps::launch_clip_coef(d_sumsq, max_norm, grad_scale, d_coef,
                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "clip_coef launch: %s", hipGetErrorString(e));
@@ -333,16 +427,10 @@ int adamw_multi_tensor_step(const mps_tensor* tensors, int n_tensors, mps_dtype 
                             void* stream)
 {
     if (!d_step) return fail(MPS_ERR_INVALID_ARGUMENT, "d_step is NULL");
-    if (!(std::isfinite(lr) && lr >= 0.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "lr must be finite and >= 0");
-    if (!finite_in(beta1, 0.0, 1.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "beta1 must be in [0, 1)");
-    if (!finite_in(beta2, 0.0, 1.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "beta2 must be in [0, 1)");
-    if (!(std::isfinite(eps) && eps >= 0.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
-    if (!(std::isfinite(weight_decay) && weight_decay >= 0.0)) {
-        return fail(MPS_ERR_INVALID_ARGUMENT, "weight_decay must be finite and >= 0");
-    }
-    Plan plan;
-    int rc = build_plan(tensors, n_tensors, grad_dtype, true, plan);
+    int rc = check_hyperparameters(lr, beta1, beta2, eps, weight_decay);
     if (rc) return rc;
+    Plan plan;
+    if ((rc = build_plan(tensors, n_tensors, grad_dtype, true, plan))) return rc;
     if ((rc = check_workspace(d_workspace, workspace_bytes, plan))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
@@ -361,22 +449,11 @@ int adamw_fused_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dt
                      void* stream)
 {
     if (!d_step) return fail(MPS_ERR_INVALID_ARGUMENT, "d_step is NULL");
-    if (!(std::isfinite(max_norm) && max_norm > 0.0)) {
-        return fail(MPS_ERR_INVALID_ARGUMENT, "max_norm must be finite and > 0");
-    }
-    if (!(std::isfinite(grad_scale) && grad_scale > 0.0)) {
-        return fail(MPS_ERR_INVALID_ARGUMENT, "grad_scale must be finite and > 0");
-    }
-    if (!(std::isfinite(lr) && lr >= 0.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "lr must be finite and >= 0");
-    if (!finite_in(beta1, 0.0, 1.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "beta1 must be in [0, 1)");
-    if (!finite_in(beta2, 0.0, 1.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "beta2 must be in [0, 1)");
-    if (!(std::isfinite(eps) && eps >= 0.0)) return fail(MPS_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
-    if (!(std::isfinite(weight_decay) && weight_decay >= 0.0)) {
-        return fail(MPS_ERR_INVALID_ARGUMENT, "weight_decay must be finite and >= 0");
-    }
-    Plan plan;
-    int rc = build_plan(tensors, n_tensors, grad_dtype, true, plan);
+    int rc = check_clip_arguments(max_norm, grad_scale);
+    if (!rc) rc = check_hyperparameters(lr, beta1, beta2, eps, weight_decay);
     if (rc) return rc;
+    Plan plan;
+    if ((rc = build_plan(tensors, n_tensors, grad_dtype, true, plan))) return rc;
     if ((rc = check_workspace(d_workspace, workspace_bytes, plan))) return rc;
     const bool bf16 = grad_dtype == MPS_DTYPE_BF16;
     int resident = 0;
@@ -392,6 +469,82 @@ int adamw_fused_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dt
     e = mps::launch_fused_step(view_of(d_workspace, plan), bf16, grid, max_norm, grad_scale,
                                skip_if_nonfinite ? 1 : 0, d_sumsq, d_coef, d_step, hp, st);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "fused step launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t adamw8_workspace_bytes(const mps_tensor8* tensors, int n_tensors)
+{
+    Plan plan;
+    if (build_plan8(tensors, n_tensors, MPS_DTYPE_BF16, false, plan) != MPS_OK) return 0;
+    ok();
+    return plan.total_bytes;
+}
+
+int adamw8_grad_norm_sq(const mps_tensor8* tensors, int n_tensors, mps_dtype grad_dtype,
+                        double* d_sumsq, double max_norm, double grad_scale, float* d_coef,
+                        void* d_workspace, size_t workspace_bytes, void* stream)
+{
+    if (!d_sumsq) return fail(MPS_ERR_INVALID_ARGUMENT, "d_sumsq is NULL");
+    int rc = d_coef ? check_clip_arguments(max_norm, grad_scale) : MPS_OK;
+    if (rc) return rc;
+    Plan plan;
+    if ((rc = build_plan8(tensors, n_tensors, grad_dtype, false, plan))) return rc;
+    return run_grad_norm(plan, grad_dtype == MPS_DTYPE_BF16, d_sumsq, max_norm, grad_scale, d_coef,
+                         d_workspace, workspace_bytes, stream);
+}
+
+int adamw8_multi_tensor_step(const mps_tensor8* tensors, int n_tensors, mps_dtype grad_dtype,
+                             const float* d_coef, const double* d_skip_if_nonfinite,
+                             int32_t* d_step, double lr, double beta1, double beta2, double eps,
+                             double weight_decay, void* d_workspace, size_t workspace_bytes,
+                             void* stream)
+{
+    if (!d_step) return fail(MPS_ERR_INVALID_ARGUMENT, "d_step is NULL");
+    int rc = check_hyperparameters(lr, beta1, beta2, eps, weight_decay);
+    if (rc) return rc;
+    Plan plan;
+    if ((rc = build_plan8(tensors, n_tensors, grad_dtype, true, plan))) return rc;
+    if ((rc = check_workspace(d_workspace, workspace_bytes, plan))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
+    mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
+    const int grid = grid_for(plan.n_chunks, mps::kStepMaxBlocks);
+    const auto* quant = reinterpret_cast<const mps::QuantEntry*>(static_cast<unsigned char*>(d_workspace) +
+                                                                 plan.quant_off);
+    hipError_t e = mps::launch_adamw8_step(view_of(d_workspace, plan), quant,
+                                           grad_dtype == MPS_DTYPE_BF16, grid, d_coef,
+                                           d_skip_if_nonfinite, d_step, hp, st);
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "adamw8_step launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int adamw8_quantize(const float* d_x, int64_t n, mps_q8_format format, uint8_t* d_codes,
+                    uint8_t* d_scales, void* stream)
+{
+    if (n < 0) return fail(MPS_ERR_INVALID_ARGUMENT, "n < 0");
+    if (format != MPS_Q8_E4M3 && format != MPS_Q8_E5M2) {
+        return fail(MPS_ERR_INVALID_ARGUMENT, "unknown 8-bit format %d", static_cast<int>(format));
+    }
+    if (n == 0) return ok();
+    if (!d_x || !d_codes || !d_scales) return fail(MPS_ERR_INVALID_ARGUMENT, "NULL pointer");
+    hipError_t e = mps::launch_quantize(d_x, n, format == MPS_Q8_E4M3, d_codes, d_scales,
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "quantize launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int adamw8_dequantize(const uint8_t* d_codes, const uint8_t* d_scales, int64_t n,
+                      mps_q8_format format, float* d_x, void* stream)
+{
+    if (n < 0) return fail(MPS_ERR_INVALID_ARGUMENT, "n < 0");
+    if (format != MPS_Q8_E4M3 && format != MPS_Q8_E5M2) {
+        return fail(MPS_ERR_INVALID_ARGUMENT, "unknown 8-bit format %d", static_cast<int>(format));
+    }
+    if (n == 0) return ok();
+    if (!d_x || !d_codes || !d_scales) return fail(MPS_ERR_INVALID_ARGUMENT, "NULL pointer");
+    hipError_t e = mps::launch_dequantize(d_codes, d_scales, n, format == MPS_Q8_E4M3, d_x,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "dequantize launch: %s", hipGetErrorString(e));
     return ok();
 }
 

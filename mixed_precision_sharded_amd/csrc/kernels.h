@@ -39,4 +39,16 @@ hipError_t launch_fused_step(const WorkspaceView& ws, bool grad_bf16, int grid, 
                              float* d_coef, int32_t* d_step, const HyperParams& hp,
                              hipStream_t stream);
 
+// 8-bit moment state (kernels_q8.hip).  `quant` is the QuantEntry table in
+// the same workspace.
+hipError_t launch_adamw8_step(const WorkspaceView& ws, const QuantEntry* quant, bool grad_bf16,
+                              int grid, const float* d_coef, const double* d_skip_if_nonfinite,
+                              int32_t* d_step, const HyperParams& hp, hipStream_t stream);
+
+hipError_t launch_quantize(const float* x, int64_t n, bool e4m3, uint8_t* codes, uint8_t* scales,
+                           hipStream_t stream);
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n, bool e4m3,
+                             float* x, hipStream_t stream);
+
 }  // namespace mps

@@ -25,163 +25,13 @@
 // in source order; division and sqrt are the correctly rounded defaults.
 #include <hip/hip_runtime.h>
 
+#include "device.h"
 #include "kernels.h"
-
-#ifndef MPS_STEP_UNROLL
-#define MPS_STEP_UNROLL 1   // groups of four elements per thread per tile
-#endif
-#ifndef MPS_NORM_UNROLL
-#define MPS_NORM_UNROLL 8   // 16-byte vectors per thread per iteration
-#endif
-// Buffer cache policies (the aux operand of buffer loads and stores):
-// 0 = default, 2 = nontemporal.
-#ifndef MPS_LOAD_POLICY
-#define MPS_LOAD_POLICY 2   // update: master, m, v, gradient
-#endif
-#ifndef MPS_STORE_POLICY
-#define MPS_STORE_POLICY 2  // update: master, m, v, bf16 copy
-#endif
-#ifndef MPS_NORM_POLICY
-#define MPS_NORM_POLICY 0   // norm: gradient (read again by the update)
-#endif
 
 namespace mps {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWave = 64;
-constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kLoadPolicy = MPS_LOAD_POLICY;
-constexpr int kStorePolicy = MPS_STORE_POLICY;
-constexpr int kNormPolicy = MPS_NORM_POLICY;
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
-
-// ------------------------------------------------------ buffer resources ---
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                             kRsrcWord3);
-}
-
-__device__ __forceinline__ f32x4 load_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadPolicy));
-}
-
-template <int kAux>
-__device__ __forceinline__ u32x4 load_u32x4(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAux);
-}
-
-__device__ __forceinline__ u32x2 load_u32x2(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadPolicy);
-}
-
-__device__ __forceinline__ void store_f32x4(f32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kStorePolicy);
-}
-
-__device__ __forceinline__ void store_u32x2(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kStorePolicy);
-}
-
-// ----------------------------------------------------------------- bf16 ---
-
-__device__ __forceinline__ float bf16_lo(uint32_t word) { return __uint_as_float(word << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t word) { return __uint_as_float(word & 0xffff0000u); }
-
-// Round to nearest even: add half an ulp of the kept part, plus one when the
-// kept part is odd, then truncate.  NaN keeps its sign and gets the quiet bit.
-__device__ __forceinline__ uint32_t bf16_bits(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-// ------------------------------------------------------ reductions (fp64) ---
-
-template <int kCtrl>
-__device__ __forceinline__ double dpp_move(double x)
-{
-    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), kCtrl, 0xf, 0xf, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), kCtrl, 0xf, 0xf, false);
-    return __hiloint2double(hi, lo);
-}
-
-// Sum over the 64 lanes of a wavefront; every lane ends with the total.
-// Within each row of 16 lanes the exchange uses DPP (quad permutes, then the
-// half-row and row mirrors); the two cross-row steps use lane shuffles.
-// All lanes must be active.
-__device__ __forceinline__ double wave_sum(double x)
-{
-    constexpr int kQuadSwap1 = 0xb1;   // quad_perm [1,0,3,2]
-    constexpr int kQuadSwap2 = 0x4e;   // quad_perm [2,3,0,1]
-    constexpr int kHalfMirror = 0x141; // row_half_mirror
-    constexpr int kRowMirror = 0x140;  // row_mirror
-    x = x + dpp_move<kQuadSwap1>(x);
-    x = x + dpp_move<kQuadSwap2>(x);
-    x = x + dpp_move<kHalfMirror>(x);
-    x = x + dpp_move<kRowMirror>(x);
-    x = x + __shfl_xor(x, 16, kWave);
-    x = x + __shfl_xor(x, 32, kWave);
-    return x;
-}
-
-// Sum over the block in a fixed order; the result is valid in thread 0.
-// `lds` holds one double per wavefront.  Ends with a barrier so that `lds`
-// may be reused right away.
-__device__ __forceinline__ double block_sum(double x, double* lds)
-{
-    x = wave_sum(x);
-    const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
-    if (lane == 0) lds[wave] = x;
-    __syncthreads();
-    double r = 0.0;
-    if (threadIdx.x == 0) {
-        for (int w = 0; w < kWavesPerBlock; ++w) r = r + lds[w];
-    }
-    __syncthreads();
-    return r;
-}
-
-__device__ __forceinline__ double add_square(double acc, float x)
-{
-    const double d = static_cast<double>(x);
-    return __builtin_fma(d, d, acc);  // d*d is exact in fp64: one rounding
-}
-
-// The multiplier the update applies to the stored gradient g, whose value
-// for the step is s*g (s: 1/K accumulation, 1/world averaging, 1/loss scale):
-//     s * min(1, max_norm / (s * sqrt(S) + 1e-6))
-// in fp64, rounded once to fp32.  With s = 1 it is the plain clip
-// coefficient.  A NaN S gives NaN (the comparison is false), an infinite S
-// gives 0.
-__device__ __forceinline__ float clip_from_sumsq(double sumsq, double max_norm, double grad_scale)
-{
-    const double norm = grad_scale * __builtin_sqrt(sumsq);
-    double clip = max_norm / (norm + 1e-6);
-    clip = (clip > 1.0) ? 1.0 : clip;
-    return static_cast<float>(grad_scale * clip);
-}
-
 // ------------------------------------------------------------ grad norm ---
-
-template <bool kBf16>
-__device__ __forceinline__ float grad_at(const void* p, int64_t i)
-{
-    if (kBf16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
-    return static_cast<const float*>(p)[i];
-}
 
 template <bool kBf16>
 __device__ __forceinline__ double add_vector(double acc, u32x4 v)
@@ -344,61 +194,9 @@ __global__ __launch_bounds__(kWave) void clip_coef_kernel(const double* d_sumsq,
     *d_coef = clip_from_sumsq(*d_sumsq, max_norm, grad_scale);
 }
 
+
 // ---------------------------------------------------------------- update ---
 
-struct StepScalars {
-    float beta1, beta2, one_m_b1, one_m_b2, decay, step_size, bc2_sqrt, eps, clip;
-};
-
-// beta^t, squaring the base and multiplying in the set bits from the lowest.
-__device__ __forceinline__ double power_by_squaring(double beta, int64_t t)
-{
-    double result = 1.0;
-    double base = beta;
-    for (; t > 0; t >>= 1) {
-        if (t & 1) result = result * base;
-        base = base * base;
-    }
-    return result;
-}
-
-__device__ __forceinline__ StepScalars step_scalars(int64_t t, const HyperParams& hp, float clip)
-{
-    StepScalars s;
-    const double p1 = power_by_squaring(hp.beta1, t);
-    const double p2 = power_by_squaring(hp.beta2, t);
-    s.beta1 = static_cast<float>(hp.beta1);
-    s.beta2 = static_cast<float>(hp.beta2);
-    s.one_m_b1 = static_cast<float>(1.0 - hp.beta1);
-    s.one_m_b2 = static_cast<float>(1.0 - hp.beta2);
-    s.decay = static_cast<float>(1.0 - hp.lr * hp.weight_decay);
-    s.step_size = static_cast<float>(hp.lr / (1.0 - p1));
-    s.bc2_sqrt = static_cast<float>(__builtin_sqrt(1.0 - p2));
-    s.eps = static_cast<float>(hp.eps);
-    s.clip = clip;
-    return s;
-}
-
-// One element; each statement is a single correctly rounded fp32 operation.
-__device__ __forceinline__ void adamw_element(float& w, float& m, float& v, float grad,
-                                              const StepScalars& s)
-{
-    const float g = grad * s.clip;
-    const float m_keep = s.beta1 * m;
-    const float m_add = s.one_m_b1 * g;
-    m = m_keep + m_add;
-    const float v_keep = s.beta2 * v;
-    const float g_sq = g * g;
-    const float v_add = s.one_m_b2 * g_sq;
-    v = v_keep + v_add;
-    const float root = __builtin_sqrtf(v);
-    const float root_hat = root / s.bc2_sqrt;
-    const float den = root_hat + s.eps;
-    const float w_decayed = w * s.decay;
-    const float ratio = m / den;
-    const float delta = s.step_size * ratio;
-    w = w_decayed - delta;
-}
 
 template <bool kBf16>
 __device__ __forceinline__ void adamw_scalar_at(const TensorEntry* te, int64_t i, const StepScalars& s)

@@ -1,0 +1,422 @@
+// gfx950 kernels of the AdamW step with 8-bit moment state.
+//
+// m and v are stored as one byte per element: m as OCP FP8 E4M3 codes, v as
+// OCP FP8 E5M2 codes, every run of 32 consecutive elements of a tensor with
+// one power-of-two scale byte (value = code * 2^(byte - 127); 255 marks a
+// run that held a NaN or an infinity and reads back as NaN).  A step decodes
+// the moments, runs the same fp32 update as the fp32-state kernel, takes the
+// new largest magnitude of each run, picks the smallest exponent that fits
+// it under the format's largest code, and re-encodes with the hardware's
+// round-to-nearest-even conversions.
+//
+//   adamw8_step_kernel  the update.  A thread takes eight consecutive
+//                       elements, so the four lanes of a quad hold one run of
+//                       32 and its largest magnitude is two DPP exchanges
+//                       away.  Streams per element: master 4 B in and out,
+//                       codes 1 + 1 B in and out, gradient 2 or 4 B in, bf16
+//                       copy 2 B out, scales 2 B per 32 elements each way.
+//   quantize_kernel /   conversion between fp32 moments and the 8-bit
+//   dequantize_kernel   state (checkpoints, switching a run over).
+//
+// Tensors whose streams are not all aligned for the vector loads, and the
+// last partial run of every tensor, go through an element-per-lane path in
+// which 32 lanes hold one run and reduce it with lane shuffles.
+#include <hip/hip_runtime.h>
+
+#include "device.h"
+#include "kernels.h"
+
+namespace mps {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Largest finite code of each format is 1.75 * 2^k: 448 (E4M3), 57344 (E5M2).
+constexpr int kE4M3TopExp = 8;
+constexpr int kE5M2TopExp = 15;
+constexpr uint32_t kNonFinite = 255;
+
+// ------------------------------------------------------ scales and codes ---
+
+// 2^(byte - 127); byte 0 is the subnormal 2^-127; 255 gives NaN.
+__device__ __forceinline__ float scale_value(uint32_t byte)
+{
+    uint32_t bits = byte << 23;
+    bits = byte == 0 ? 0x00400000u : bits;
+    bits = byte == kNonFinite ? 0x7fc00000u : bits;
+    return __uint_as_float(bits);
+}
+
+// The scale byte of a run whose largest magnitude has the bit pattern
+// `absbits` (sign cleared): the smallest e >= -127 with
+// absmax <= 1.75 * 2^(kTopExp + e), or 255 when the run is not finite.
+template <int kTopExp>
+__device__ __forceinline__ uint32_t scale_byte(uint32_t absbits)
+{
+    if (absbits >= 0x7f800000u) return kNonFinite;
+    int e = static_cast<int>(absbits >> 23) - 127 - kTopExp + ((absbits & 0x7fffffu) > 0x600000u ? 1 : 0);
+    e = e < -127 ? -127 : e;
+    return static_cast<uint32_t>(e + 127);
+}
+
+// 2^-e for a finite scale byte (exact: e <= 120 for any finite fp32 run).
+__device__ __forceinline__ float inverse_scale(uint32_t byte)
+{
+    return __uint_as_float((254u - byte) << 23);
+}
+
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
+
+// The two codes in the low (kHigh false) or high half of `word`, widened.
+template <bool kE4M3, bool kHigh>
+__device__ __forceinline__ f32x2 decode_pair(uint32_t word)
+{
+    return kE4M3 ? __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(word), kHigh)
+                 : __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(word), kHigh);
+}
+
+// Eight codes (two words) to values times `scale`.
+template <bool kE4M3>
+__device__ __forceinline__ void decode8(u32x2 codes, float scale, float (&out)[8])
+{
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const f32x2 lo = decode_pair<kE4M3, false>(codes[h]);
+        const f32x2 hi = decode_pair<kE4M3, true>(codes[h]);
+        out[4 * h] = lo[0] * scale;
+        out[4 * h + 1] = lo[1] * scale;
+        out[4 * h + 2] = hi[0] * scale;
+        out[4 * h + 3] = hi[1] * scale;
+    }
+}
+
+// Round a and b to codes (nearest, ties to even) into the low (kHigh false)
+// or high half of `old`, keeping the other half.
+template <bool kE4M3, bool kHigh>
+__device__ __forceinline__ uint32_t encode_pair(float a, float b, uint32_t old)
+{
+    return static_cast<uint32_t>(kE4M3 ? __builtin_amdgcn_cvt_pk_fp8_f32(a, b, static_cast<int>(old), kHigh)
+                                       : __builtin_amdgcn_cvt_pk_bf8_f32(a, b, static_cast<int>(old), kHigh));
+}
+
+// Eight values to codes at the run's scale byte (all 0xFF for a
+// non-finite run).
+template <bool kE4M3>
+__device__ __forceinline__ u32x2 encode8(const float (&x)[8], uint32_t byte)
+{
+    const float inv = inverse_scale(byte);
+    u32x2 out;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint32_t word = encode_pair<kE4M3, false>(x[4 * h] * inv, x[4 * h + 1] * inv, 0u);
+        word = encode_pair<kE4M3, true>(x[4 * h + 2] * inv, x[4 * h + 3] * inv, word);
+        out[h] = byte == kNonFinite ? 0xffffffffu : word;
+    }
+    return out;
+}
+
+template <bool kE4M3>
+__device__ __forceinline__ uint32_t encode1(float x, uint32_t byte)
+{
+    const uint32_t word = encode_pair<kE4M3, false>(x * inverse_scale(byte), 0.0f, 0u);
+    return byte == kNonFinite ? 0xffu : (word & 0xffu);
+}
+
+template <bool kE4M3>
+__device__ __forceinline__ float decode1(uint32_t code, float scale)
+{
+    return decode_pair<kE4M3, false>(code)[0] * scale;
+}
+
+// Largest of the four lanes of this quad (lanes 4k .. 4k+3).
+__device__ __forceinline__ uint32_t quad_max(uint32_t x)
+{
+    constexpr int kQuadSwap1 = 0xb1;  // quad_perm [1,0,3,2]
+    constexpr int kQuadSwap2 = 0x4e;  // quad_perm [2,3,0,1]
+    x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kQuadSwap1, 0xf, 0xf, false)));
+    x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kQuadSwap2, 0xf, 0xf, false)));
+    return x;
+}
+
+// Largest over the 32 lanes of this half wavefront.  All lanes must be active.
+__device__ __forceinline__ uint32_t half_wave_max(uint32_t x)
+{
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) x = max(x, static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), off, kWave)));
+    return x;
+}
+
+__device__ __forceinline__ uint32_t load_byte(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, kLoadPolicy);
+}
+
+__device__ __forceinline__ void store_byte(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(v), r, off, 0, kStorePolicy);
+}
+
+__device__ __forceinline__ void store_u32x4(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStorePolicy);
+}
+
+// ---------------------------------------------------------------- update ---
+
+// Elements [begin, end) of one tensor, one element per lane; `begin` is a
+// multiple of 32, so each half wavefront holds one run.
+template <bool kBf16>
+__device__ __forceinline__ void adamw8_elements(const TensorEntry* te, const QuantEntry* qe,
+                                                int64_t begin, int64_t end, const StepScalars& s)
+{
+    for (int64_t base = begin; base < end; base += kBlock) {
+        const int64_t i = base + threadIdx.x;
+        const bool valid = i < end;
+        float w = 0.0f, m = 0.0f, v = 0.0f, g = 0.0f;
+        if (valid) {
+            const int64_t run = i / kQuantBlock;
+            w = te->master[i];
+            g = grad_at<kBf16>(te->grad, i);
+            m = decode1<true>(qe->m_codes[i], scale_value(qe->m_scales[run]));
+            v = decode1<false>(qe->v_codes[i], scale_value(qe->v_scales[run]));
+        }
+        adamw_element(w, m, v, g, s);
+        const uint32_t mb = scale_byte<kE4M3TopExp>(half_wave_max(valid ? abs_bits(m) : 0u));
+        const uint32_t vb = scale_byte<kE5M2TopExp>(half_wave_max(valid ? abs_bits(v) : 0u));
+        if (valid) {
+            te->master[i] = w;
+            qe->m_codes[i] = static_cast<uint8_t>(encode1<true>(m, mb));
+            qe->v_codes[i] = static_cast<uint8_t>(encode1<false>(v, vb));
+            if (te->param_bf16) te->param_bf16[i] = static_cast<uint16_t>(bf16_bits(w));
+            if (i % kQuantBlock == 0) {
+                qe->m_scales[i / kQuantBlock] = static_cast<uint8_t>(mb);
+                qe->v_scales[i / kQuantBlock] = static_cast<uint8_t>(vb);
+            }
+        }
+    }
+}
+
+// Whole runs [e0, e0 + 8 * ngroups) of one tensor (ngroups a multiple of 4),
+// every stream aligned for its vector width there.  Thread q of a tile takes
+// elements 8q .. 8q+7.
+template <bool kBf16>
+__device__ __forceinline__ void adamw8_body(const TensorEntry* te, const QuantEntry* qe, int64_t e0,
+                                            int ngroups, const StepScalars& s)
+{
+    const int tid = threadIdx.x;
+    const uint32_t ng = static_cast<uint32_t>(ngroups);
+    const __amdgpu_buffer_rsrc_t W = rsrc(te->master + e0, ng * 32u);
+    const __amdgpu_buffer_rsrc_t G = rsrc(static_cast<const char*>(te->grad) + e0 * (kBf16 ? 2 : 4),
+                                          ng * (kBf16 ? 16u : 32u));
+    const bool copy = te->param_bf16 != nullptr;
+    const __amdgpu_buffer_rsrc_t P = rsrc(copy ? te->param_bf16 + e0 : nullptr, copy ? ng * 16u : 0u);
+    const __amdgpu_buffer_rsrc_t MQ = rsrc(qe->m_codes + e0, ng * 8u);
+    const __amdgpu_buffer_rsrc_t VQ = rsrc(qe->v_codes + e0, ng * 8u);
+    const __amdgpu_buffer_rsrc_t MS = rsrc(qe->m_scales + e0 / kQuantBlock, ng / 4u);
+    const __amdgpu_buffer_rsrc_t VS = rsrc(qe->v_scales + e0 / kQuantBlock, ng / 4u);
+
+    // Two tiles are held in registers in turn, as in the fp32 kernel: the
+    // next tile's loads are in flight while this one is computed.  Groups past
+    // the end read zeros and their stores are dropped; a quad is either wholly
+    // inside or wholly past the end.
+    struct Tile {
+        f32x4 w[2];
+        u32x4 g[2];  // bf16: g[0] holds the eight gradients; fp32: both
+        u32x2 mq, vq;
+        uint32_t ms, vs;
+    };
+    auto load_tile = [&](Tile& t, int base) {
+        const uint32_t q = base + tid;
+        t.w[0] = load_f32x4(W, q * 32u);
+        t.w[1] = load_f32x4(W, q * 32u + 16u);
+        if (kBf16) {
+            t.g[0] = load_u32x4<kLoadPolicy>(G, q * 16u);
+        } else {
+            t.g[0] = load_u32x4<kLoadPolicy>(G, q * 32u);
+            t.g[1] = load_u32x4<kLoadPolicy>(G, q * 32u + 16u);
+        }
+        t.mq = load_u32x2(MQ, q * 8u);
+        t.vq = load_u32x2(VQ, q * 8u);
+        t.ms = load_byte(MS, q / 4u);
+        t.vs = load_byte(VS, q / 4u);
+    };
+    auto update_tile = [&](Tile& t, int base) {
+        const uint32_t q = base + tid;
+        float w[8], m[8], v[8], g[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            w[k] = t.w[0][k];
+            w[4 + k] = t.w[1][k];
+        }
+        if (kBf16) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                g[2 * k] = bf16_lo(t.g[0][k]);
+                g[2 * k + 1] = bf16_hi(t.g[0][k]);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                g[k] = __uint_as_float(t.g[0][k]);
+                g[4 + k] = __uint_as_float(t.g[1][k]);
+            }
+        }
+        decode8<true>(t.mq, scale_value(t.ms), m);
+        decode8<false>(t.vq, scale_value(t.vs), v);
+        uint32_t am = 0, av = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            adamw_element(w[k], m[k], v[k], g[k], s);
+            am = max(am, abs_bits(m[k]));
+            av = max(av, abs_bits(v[k]));
+        }
+        const uint32_t mb = scale_byte<kE4M3TopExp>(quad_max(am));
+        const uint32_t vb = scale_byte<kE5M2TopExp>(quad_max(av));
+        store_f32x4(f32x4{w[0], w[1], w[2], w[3]}, W, q * 32u);
+        store_f32x4(f32x4{w[4], w[5], w[6], w[7]}, W, q * 32u + 16u);
+        store_u32x2(encode8<true>(m, mb), MQ, q * 8u);
+        store_u32x2(encode8<false>(v, vb), VQ, q * 8u);
+        if (copy) {
+            u32x4 packed;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) packed[k] = bf16_bits(w[2 * k]) | (bf16_bits(w[2 * k + 1]) << 16);
+            store_u32x4(packed, P, q * 16u);
+        }
+        if ((tid & 3) == 0) {
+            store_byte(mb, MS, q / 4u);
+            store_byte(vb, VS, q / 4u);
+        }
+    };
+
+    Tile a, b;
+    load_tile(a, 0);
+    for (int base = 0; base < ngroups; base += 2 * kBlock) {
+        load_tile(b, base + kBlock);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+        update_tile(a, base);
+        if (base + kBlock >= ngroups) break;  // uniform: the other tile is empty
+        load_tile(a, base + 2 * kBlock);
+        __builtin_amdgcn_sched_barrier(0);
+        update_tile(b, base + kBlock);
+    }
+}
+
+// Chunks b, b + G, ... of this block, as in the fp32 kernel.  Within a chunk
+// the whole runs of an aligned tensor take the vector body and the tensor's
+// last partial run the element path.
+template <bool kBf16>
+__device__ __forceinline__ void update8_chunks(const TensorEntry* tensors, const QuantEntry* quant,
+                                               const uint32_t* chunk_map, int n_chunks,
+                                               int64_t chunk_elems, const StepScalars& s)
+{
+    for (int c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+        const uint32_t k = chunk_map[c];
+        const TensorEntry te = tensors[k];
+        const QuantEntry qe = quant[k];
+        const int64_t begin = static_cast<int64_t>(c - te.first_chunk) * chunk_elems;
+        const int64_t end = min(begin + chunk_elems, te.numel);
+        if (te.head < 0) {
+            adamw8_elements<kBf16>(&te, &qe, begin, end, s);
+            continue;
+        }
+        const int64_t whole = te.numel - te.numel % kQuantBlock;
+        const int64_t vend = max(begin, min(end, whole));
+        if (vend > begin) adamw8_body<kBf16>(&te, &qe, begin, static_cast<int>((vend - begin) / 8), s);
+        if (end > vend) adamw8_elements<kBf16>(&te, &qe, vend, end, s);
+    }
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(kBlock) void adamw8_step_kernel(
+    WorkspaceHeader* header, const TensorEntry* tensors, const QuantEntry* quant,
+    const uint32_t* chunk_map, int n_chunks, int64_t chunk_elems, uint64_t tag,
+    const float* d_coef, const double* d_skip_if_nonfinite, int32_t* d_step, HyperParams hp)
+{
+    if (header->tag != tag) return;  // tables overwritten: touch nothing
+    if (d_skip_if_nonfinite && !__builtin_isfinite(*d_skip_if_nonfinite)) return;
+
+    const int64_t t = static_cast<int64_t>(*d_step) + 1;
+    const StepScalars s = step_scalars(t, hp, d_coef ? *d_coef : 1.0f);
+    update8_chunks<kBf16>(tensors, quant, chunk_map, n_chunks, chunk_elems, s);
+    // Step counter: the last block to take a ticket stores it (the fp32
+    // kernel explains why no release fence is needed).
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const unsigned prev = atomicInc(&header->step_ticket, gridDim.x - 1);
+        if (prev == gridDim.x - 1) *d_step = static_cast<int32_t>(t);
+    }
+}
+
+// ------------------------------------------------------------ conversion ---
+
+// One element per lane; each half wavefront holds one run of 32.
+template <bool kE4M3>
+__global__ __launch_bounds__(kBlock) void quantize_kernel(const float* x, int64_t n, uint8_t* codes,
+                                                          uint8_t* scales)
+{
+    constexpr int kTop = kE4M3 ? kE4M3TopExp : kE5M2TopExp;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock; base < n; base += stride) {
+        const int64_t i = base + threadIdx.x;
+        const bool valid = i < n;
+        const float xi = valid ? x[i] : 0.0f;
+        const uint32_t byte = scale_byte<kTop>(half_wave_max(abs_bits(xi)));
+        if (valid) {
+            codes[i] = static_cast<uint8_t>(encode1<kE4M3>(xi, byte));
+            if (i % kQuantBlock == 0) scales[i / kQuantBlock] = static_cast<uint8_t>(byte);
+        }
+    }
+}
+
+template <bool kE4M3>
+__global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* codes, const uint8_t* scales,
+                                                            int64_t n, float* x)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride) {
+        x[i] = decode1<kE4M3>(codes[i], scale_value(scales[i / kQuantBlock]));
+    }
+}
+
+}  // namespace
+
+// --------------------------------------------------------------- launchers ---
+
+hipError_t launch_adamw8_step(const WorkspaceView& ws, const QuantEntry* quant, bool grad_bf16,
+                              int grid, const float* d_coef, const double* d_skip_if_nonfinite,
+                              int32_t* d_step, const HyperParams& hp, hipStream_t stream)
+{
+    if (grad_bf16) {
+        adamw8_step_kernel<true><<<grid, kBlock, 0, stream>>>(
+            ws.header, ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag, d_coef,
+            d_skip_if_nonfinite, d_step, hp);
+    } else {
+        adamw8_step_kernel<false><<<grid, kBlock, 0, stream>>>(
+            ws.header, ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag, d_coef,
+            d_skip_if_nonfinite, d_step, hp);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(const float* x, int64_t n, bool e4m3, uint8_t* codes, uint8_t* scales,
+                           hipStream_t stream)
+{
+    const int64_t blocks = (n + kBlock - 1) / kBlock;
+    const int grid = static_cast<int>(blocks < 4096 ? blocks : 4096);
+    if (e4m3) quantize_kernel<true><<<grid, kBlock, 0, stream>>>(x, n, codes, scales);
+    else quantize_kernel<false><<<grid, kBlock, 0, stream>>>(x, n, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n, bool e4m3,
+                             float* x, hipStream_t stream)
+{
+    const int64_t blocks = (n + kBlock - 1) / kBlock;
+    const int grid = static_cast<int>(blocks < 4096 ? blocks : 4096);
+    if (e4m3) dequantize_kernel<true><<<grid, kBlock, 0, stream>>>(codes, scales, n, x);
+    else dequantize_kernel<false><<<grid, kBlock, 0, stream>>>(codes, scales, n, x);
+    return hipGetLastError();
+}
+
+}  // namespace mps

@@ -3,8 +3,9 @@
 // Workspace layout (256-byte aligned base):
 //   [0, 64)                      WorkspaceHeader
 //   [64, 64 + 64*T)              TensorEntry[T]
-//   [.., + 4*K rounded to 8)     uint32 chunk -> tensor index, K chunks
-//   [.., + 8*kPartials)          fp64 per-block partial sums of the norm
+//   [.., + 32*T)                 QuantEntry[T] (8-bit moment lists only)
+//   [.., + 4*K)                  uint32 chunk -> tensor index, K chunks
+//   [.. rounded to 256, + 8*kPartials)  fp64 per-block partial sums of the norm
 // Everything before the partials is written by one host-to-device copy when
 // the list changes; the partials need no initial value.
 #pragma once
@@ -78,6 +79,19 @@ struct alignas(64) TensorEntry {
                             // four, 0..3; -1 when the streams share no alignment
 };
 static_assert(sizeof(TensorEntry) == 64, "tensor entry is one 64-byte record");
+
+// The 8-bit moment state of one tensor: codes (one byte per element; m in
+// E4M3, v in E5M2) and one scale byte per 32 elements (2^(byte - 127); 255
+// marks a block holding a non-finite value).
+constexpr int kQuantBlock = 32;
+
+struct QuantEntry {
+    uint8_t* m_codes;
+    uint8_t* m_scales;
+    uint8_t* v_codes;
+    uint8_t* v_scales;
+};
+static_assert(sizeof(QuantEntry) == 32, "quant entry is one 32-byte record");
 
 // Hyperparameters as passed by the caller (fp64, before rounding).
 struct HyperParams {

@@ -37,7 +37,9 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "adamw_workspace_bytes", "adamw_workspace_release", "grad_norm_sq", "clip_coef",
-        "adamw_multi_tensor_step", "adamw_fused_step", "adamw_last_error"])
+        "adamw_multi_tensor_step", "adamw_fused_step", "adamw_last_error",
+        "adamw8_workspace_bytes", "adamw8_grad_norm_sq", "adamw8_multi_tensor_step",
+        "adamw8_quantize", "adamw8_dequantize"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -172,3 +174,65 @@ def test_clip_argument_errors(lib):
 
 def test_release_unknown_workspace_is_harmless(lib):
     assert lib.adamw_workspace_release(ctypes.c_void_p(0x1234500)) == 0
+
+
+def fake_list8(n=2, numel=1000, base=0x7f0000000000, misalign=0):
+    arr = (binding.MpsTensor8 * n)()
+    for i in range(n):
+        off = base + i * (1 << 26) + misalign
+        arr[i] = binding.MpsTensor8(off, off + (8 << 20), off + (16 << 20), off + (24 << 20),
+                                    off + (32 << 20), off + (40 << 20), None, numel)
+    return arr
+
+
+def test_8bit_workspace_bytes(lib):
+    size8 = lib.adamw8_workspace_bytes(fake_list8(3, 5000), 3)
+    size = lib.adamw_workspace_bytes(fake_list(3, 5000), 3)
+    # one more 32-byte record per tensor for the 8-bit state (tables are padded to 256 bytes)
+    assert size <= size8 <= size + 3 * 32 + 256
+    many = lib.adamw8_workspace_bytes(fake_list8(40, 5000), 40)
+    assert many >= lib.adamw_workspace_bytes(fake_list(40, 5000), 40) + 40 * 32 - 256
+    assert lib.adamw8_workspace_bytes(None, 1) == 0
+    bad = fake_list8(1)
+    bad[0].numel = -5
+    assert lib.adamw8_workspace_bytes(bad, 1) == 0 and "numel" in binding.last_error()
+
+
+def test_8bit_argument_errors(lib):
+    arr = fake_list8(1, 4096)
+    ws = ctypes.c_void_p(0x7e0000000000)
+    step = ctypes.c_void_p(0x7d0000000000)
+
+    def call(a=arr, dtype=0, step=step, b1=0.9, wd=0.1, ws=ws, size=1 << 30):
+        return lib.adamw8_multi_tensor_step(a, 1, dtype, None, None, step, 3e-4, b1, 0.95, 1e-8,
+                                            wd, ws, size, None)
+
+    assert call(step=None) == EINVAL
+    assert call(b1=1.0) == EINVAL
+    assert call(wd=float("nan")) == EINVAL
+    assert call(dtype=5) == EINVAL
+    for field in ("master", "exp_avg_codes", "exp_avg_scales", "exp_avg_sq_codes",
+                  "exp_avg_sq_scales", "grad"):
+        broken = fake_list8(1, 4096)
+        setattr(broken[0], field, None)
+        assert call(a=broken) == EINVAL, field
+    assert call(a=fake_list8(1, 4096, misalign=2)) == EINVAL       # fp32 master
+    assert call(ws=None) == EWORKSPACE
+    assert call(size=64) == EWORKSPACE
+    out = ctypes.c_void_p(0x7d0000000000)
+    assert lib.adamw8_grad_norm_sq(fake_list8(1, 10, misalign=1), 1, 1, out, 0.0, 1.0, None, ws,
+                                   1 << 30, None) == EINVAL      # bf16 gradient, odd address
+    assert lib.adamw8_grad_norm_sq(arr, 1, 0, None, 1.0, 1.0, None, ws, 1 << 30, None) == EINVAL
+    assert lib.adamw8_grad_norm_sq(arr, 1, 0, out, 0.0, 1.0, out, ws, 1 << 30, None) == EINVAL
+
+
+def test_8bit_conversion_argument_errors(lib):
+    p = ctypes.c_void_p(0x7d0000000000)
+    assert lib.adamw8_quantize(p, -1, 0, p, p, None) == EINVAL
+    assert lib.adamw8_quantize(p, 10, 2, p, p, None) == EINVAL
+    assert lib.adamw8_quantize(None, 10, 0, p, p, None) == EINVAL
+    assert lib.adamw8_dequantize(p, None, 10, 1, p, None) == EINVAL
+    assert lib.adamw8_dequantize(p, p, 10, -1, p, None) == EINVAL
+    # nothing to do: no pointer is needed and nothing is enqueued
+    assert lib.adamw8_quantize(None, 0, 0, None, None, None) == 0
+    assert lib.adamw8_dequantize(None, None, 0, 1, None, None) == 0
