@@ -9,7 +9,11 @@ dominant kernel (the update) its roofline against MI355X's 8 TB/s HBM peak,
 timed live with events on the launch stream; plus the CPU oracle timed on a
 bounded sample on the host (single thread).
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--rotate R]
+    python bench.py [--steps K] [--warmup W] [--config 2] [--rotate R] [--state8]
+
+--state8 times the same workload with 8-bit moments (adamw8_grad_norm_sq,
+then adamw8_multi_tensor_step): m and v are the workload's, encoded once
+before the timed region.
 """
 import argparse
 import hashlib
@@ -21,7 +25,13 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "mixed_precision_sharded_amd", "csrc", "kernels.hip")
+CSRC = os.path.join(ROOT, "mixed_precision_sharded_amd", "csrc")
+# The sources each timed kernel is built from (its counter record is valid
+# only for these exact sources).
+KERNEL_SOURCES = {
+    "adamw_step_kernel": ("kernels.hip", "device.h", "layout.h"),
+    "adamw8_step_kernel": ("kernels_q8.hip", "device.h", "layout.h"),
+}
 
 
 def log(*a):
@@ -43,27 +53,32 @@ def parse():
     p.add_argument("--fused", action="store_true",
                    help="time the single-launch step (adamw_fused_step) instead of the "
                         "two launches (grad_norm_sq with the clip output, then the update)")
+    p.add_argument("--state8", action="store_true",
+                   help="8-bit moment state (m: E4M3, v: E5M2, a scale byte per 32 elements)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="after the measurement, run 5 plain device copies of this many MiB "
                         "(known bytes, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
-def kernel_source_digest():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def kernel_source_digest(kernel):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def stored_traffic(workload_name):
-    """HBM bytes per update launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
+def stored_traffic(kernel, workload_name):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             table = json.load(f)
     except (OSError, ValueError):
         return None
-    rec = table.get(workload_name)
-    if not rec or rec.get("kernel_source_sha256") != kernel_source_digest():
+    rec = table.get(f"{kernel} {workload_name}")
+    if not rec or rec.get("kernel_source_sha256") != kernel_source_digest(kernel):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -89,14 +104,31 @@ def main():
     w = WORKLOADS[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.state8 and args.fused:
+        print("--state8 has no single-launch form", file=sys.stderr)
+        sys.exit(2)
     log(f"workload {w.cfg} {w.name}: {w.numel:,} params in {w.n_tensors} tensors, "
-        f"{'bf16' if w.grad_bf16 else 'fp32'} grads, copy={w.copy_bf16}, rotate={args.rotate}")
+        f"{'bf16' if w.grad_bf16 else 'fp32'} grads, copy={w.copy_bf16}, rotate={args.rotate}, "
+        f"moments={'8-bit' if args.state8 else 'fp32'}")
 
     sets = []
     for r in range(args.rotate):
         cols = synth.workload_inputs(w, dev, cfg_key=w.cfg * 1000 + r if r else None)
-        tl = binding.TensorList(cols["master"], cols["exp_avg"], cols["exp_avg_sq"], cols["grad"],
-                                cols["param_bf16"])
+        if args.state8:
+            states = []
+            for m, v in zip(cols["exp_avg"], cols["exp_avg_sq"]):
+                st = binding.zeros_q8_state(m.numel(), dev)
+                if m.numel():
+                    binding.adamw8_quantize(m, binding.MPS_Q8_E4M3, st[0], st[1])
+                    binding.adamw8_quantize(v, binding.MPS_Q8_E5M2, st[2], st[3])
+                states.append(st)
+            torch.cuda.synchronize()
+            cols["exp_avg"] = cols["exp_avg_sq"] = None  # only the 8-bit state stays resident
+            cols["q8_state"] = states
+            tl = binding.TensorList8(cols["master"], states, cols["grad"], cols["param_bf16"])
+        else:
+            tl = binding.TensorList(cols["master"], cols["exp_avg"], cols["exp_avg_sq"],
+                                    cols["grad"], cols["param_bf16"])
         sets.append((cols, tl))
     sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
     coef = torch.zeros(1, dtype=torch.float32, device=dev)
@@ -111,6 +143,15 @@ def main():
                                      w.max_norm, sumsq_out=sumsq, coef_out=coef)
             if ev is not None:
                 ev[1].record()
+                ev[2].record()
+            return
+        if args.state8:
+            binding.adamw8_grad_norm_sq(tl, sumsq, w.max_norm, coef)
+            if ev is not None:
+                ev[1].record()
+            binding.adamw8_multi_tensor_step(tl, coef, step, w.lr, w.beta1, w.beta2, w.eps,
+                                             w.weight_decay)
+            if ev is not None:
                 ev[2].record()
             return
         binding.grad_norm_sq(tl, sumsq, w.max_norm, coef)  # norm + clip coefficient
@@ -151,11 +192,15 @@ def main():
         upd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
         if args.fused:
             kern_us = {"adamw_fused_step": norm_ms * 1e3}
+        elif args.state8:
+            kern_us = {"adamw8_grad_norm_sq+clip": norm_ms * 1e3,
+                       "adamw8_multi_tensor_step": upd_ms * 1e3}
         else:
             kern_us = {"grad_norm_sq+clip": norm_ms * 1e3, "adamw_multi_tensor_step": upd_ms * 1e3}
 
     n = w.numel
-    step_bytes = w.algorithmic_bytes_per_param() * n
+    bytes_per_param = w.algorithmic8_bytes_per_param() if args.state8 else w.algorithmic_bytes_per_param()
+    step_bytes = bytes_per_param * n
     params_per_s = n / (ms_per_step * 1e-3)
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"{ms_per_step * 1e3:.1f} us/step, {params_per_s:.3e} params/s, {step_gbps:.0f} GB/s "
@@ -165,6 +210,9 @@ def main():
     if kern_us is not None:
         if args.fused:  # one kernel does the whole step
             name, launch_bytes, us = "adamw_fused_kernel", step_bytes, kern_us["adamw_fused_step"]
+        elif args.state8:
+            name, launch_bytes = "adamw8_step_kernel", w.update8_bytes_per_param() * n
+            us = kern_us["adamw8_multi_tensor_step"]
         else:
             name, launch_bytes = "adamw_step_kernel", w.update_bytes_per_param() * n
             us = kern_us["adamw_multi_tensor_step"]
@@ -172,7 +220,7 @@ def main():
         roofline = {"bound": "hbm", "kernel": name,
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": None if args.fused else stored_traffic(w.name),
+                    "traffic": None if args.fused else stored_traffic(name, w.name),
                     "algorithmic_bytes_per_launch": launch_bytes,
                     "avg_launch_us": round(us, 2)}
         log(f"kernels (us): " + ", ".join(f"{k} {v:.1f}" for k, v in kern_us.items()))
@@ -187,7 +235,10 @@ def main():
         log(f"copy calibration: 5 copies of {args.copy_calibration_mib} MiB")
         del src, dst
 
-    cpu = cpu_baseline(w, sets[0][0], args.cpu_seconds) if args.cpu_seconds > 0 else None
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = (cpu_baseline8(w, sets[0][0], args.cpu_seconds) if args.state8
+               else cpu_baseline(w, sets[0][0], args.cpu_seconds))
 
     out = {
         "metric": "params updated/sec and achieved HBM GB/s (fraction of peak) per AdamW step",
@@ -204,7 +255,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "params": n, "tensors": w.n_tensors,
                    "grad_dtype": "bf16" if w.grad_bf16 else "f32", "bf16_copy": w.copy_bf16,
-                   "step": w.step, "algorithmic_bytes_per_param": w.algorithmic_bytes_per_param(),
+                   "step": w.step, "algorithmic_bytes_per_param": bytes_per_param,
+                   "moments": "8-bit (m E4M3, v E5M2, scale byte per 32)" if args.state8 else "f32",
                    "buffer_sets": args.rotate, "launches": "fused" if args.fused else "two",
                    "parallelism": "one GPU's shard"},
         "step_gbps": round(step_gbps, 1),
@@ -261,6 +313,54 @@ def cpu_baseline(w, cols, budget_s):
     return {"value": taken * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"{what} ({taken:,} params): norm + clip + update, {steps} consecutive "
                       f"steps, 1 thread, {dt:.1f} s",
+            "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
+
+
+CPU_SAMPLE_MAX_ELEMS_Q8 = 2 << 20
+
+
+def cpu_baseline8(w, cols, budget_s):
+    """The oracle's 8-bit-moment step, as cpu_baseline, on the first tensors
+    of the workload up to CPU_SAMPLE_MAX_ELEMS_Q8 elements (its nearest-code
+    search is much slower per element than the fp32 update)."""
+    import oracle
+    from mixed_precision_sharded_amd.synth import to_numpy
+
+    o = oracle.default()
+    host = []
+    taken = 0
+    for i in range(w.n_tensors):
+        n = min(w.tensors[i][1], CPU_SAMPLE_MAX_ELEMS_Q8 - taken)
+        if n <= 0:
+            break
+        nb = (n + 31) // 32
+        mc, ms, vc, vs = cols["q8_state"][i]
+        p = cols["param_bf16"][i]
+        host.append(dict(w=to_numpy(cols["master"][i][:n]).copy(), g=to_numpy(cols["grad"][i][:n]).copy(),
+                         mc=mc[:n].cpu().numpy().copy(), ms=ms[:nb].cpu().numpy().copy(),
+                         vc=vc[:n].cpu().numpy().copy(), vs=vs[:nb].cpu().numpy().copy(),
+                         p=None if p is None else to_numpy(p[:n]).copy()))
+        taken += n
+    t_done = w.step
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        S = o.grad_norm_sq([h["g"] for h in host])
+        c = o.clip_coef(S, w.max_norm)
+        for h in host:
+            o.adamw8_step(h["w"], h["mc"], h["ms"], h["vc"], h["vs"], h["g"], h["p"], c, t_done,
+                          w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
+        t_done += 1
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    what = (f"whole {w.name} shard" if taken == w.numel else
+            f"first {len(host)} of {w.n_tensors} tensors of {w.name}")
+    log(f"cpu oracle (8-bit moments): {steps} steps of {taken:,} params in {dt:.2f} s")
+    return {"value": taken * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{what}, first {taken:,} params: norm + clip + 8-bit-moment update, "
+                      f"{steps} consecutive steps, 1 thread, {dt:.1f} s",
             "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
 
 

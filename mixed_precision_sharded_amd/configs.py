@@ -56,6 +56,22 @@ class Workload:
         g = 2 if self.grad_bf16 else 4
         return 12 + g + 12 + (2 if self.copy_bf16 else 0)
 
+    # With 8-bit moments (one code byte each for m and v, one scale byte per
+    # 32 elements for each) the update moves master 4 + codes 2 + scales
+    # 2/32 bytes each way instead of 12.
+    def update8_bytes_per_param(self) -> float:
+        g = 2 if self.grad_bf16 else 4
+        return g + 2 * (4 + 2 + 2 / 32) + (2 if self.copy_bf16 else 0)
+
+    def algorithmic8_bytes_per_param(self) -> float:
+        return (2 if self.grad_bf16 else 4) + self.update8_bytes_per_param()
+
+    def state8_bytes_per_param(self) -> float:
+        """Resident state with 8-bit moments: the 10N row of the accounting
+        (plus the scale bytes) on the mixed basis."""
+        g = 2 if self.grad_bf16 else 4
+        return 4 + 2 + 2 / 32 + g + (2 if self.copy_bf16 else 0)
+
     def state_bytes_per_param(self) -> int:
         """Resident state per parameter under the 16N accounting: fp32
         master, m and v (12 B) plus the gradient and the parameter copy.
