@@ -355,7 +355,7 @@ int check_clip_arguments(double max_norm, double grad_scale)
 // Launch the norm (and optionally the clip coefficient) over a planned list.
 int run_grad_norm(Plan& plan, bool bf16, double* d_sumsq, double max_norm,
                   double grad_scale, float* d_coef, void* d_workspace, size_t workspace_bytes,
-                  void* stream)
+                  void* stream, mps::NormBefore next)
 {
     int rc = check_workspace(d_workspace, workspace_bytes, plan);
     if (rc) return rc;
@@ -363,7 +363,7 @@ int run_grad_norm(Plan& plan, bool bf16, double* d_sumsq, double max_norm,
     if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
     const int grid = grid_for(plan.n_chunks, mps::kNormMaxBlocks);
     hipError_t e = mps::launch_grad_norm(view_of(d_workspace, plan), bf16, grid, d_sumsq, max_norm,
-                                         grad_scale, d_coef, st);
+                                         grad_scale, d_coef, st, next);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "grad_norm launch: %s", hipGetErrorString(e));
     return ok();
 }
@@ -406,7 +406,7 @@ int grad_norm_sq(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
     Plan plan;
     if ((rc = build_plan(tensors, n_tensors, grad_dtype, false, plan))) return rc;
     return run_grad_norm(plan, grad_dtype == MPS_DTYPE_BF16, d_sumsq, max_norm, grad_scale, d_coef,
-                         d_workspace, workspace_bytes, stream);
+                         d_workspace, workspace_bytes, stream, mps::NormBefore::kUpdate);
 }
 
 int clip_coef(const double* d_sumsq, double max_norm, double grad_scale, float* d_coef,
@@ -490,7 +490,7 @@ int adamw8_grad_norm_sq(const mps_tensor8* tensors, int n_tensors, mps_dtype gra
     Plan plan;
     if ((rc = build_plan8(tensors, n_tensors, grad_dtype, false, plan))) return rc;
     return run_grad_norm(plan, grad_dtype == MPS_DTYPE_BF16, d_sumsq, max_norm, grad_scale, d_coef,
-                         d_workspace, workspace_bytes, stream);
+                         d_workspace, workspace_bytes, stream, mps::NormBefore::kQ8Update);
 }
 
 int adamw8_multi_tensor_step(const mps_tensor8* tensors, int n_tensors, mps_dtype grad_dtype,
@@ -508,7 +508,7 @@ int adamw8_multi_tensor_step(const mps_tensor8* tensors, int n_tensors, mps_dtyp
     hipStream_t st = static_cast<hipStream_t>(stream);
     if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
     mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
-    const int grid = grid_for(plan.n_chunks, mps::kStepMaxBlocks);
+    const int grid = grid_for(plan.n_chunks, mps::kQ8MaxBlocks);
     const auto* quant = reinterpret_cast<const mps::QuantEntry*>(static_cast<unsigned char*>(d_workspace) +
                                                                  plan.quant_off);
     hipError_t e = mps::launch_adamw8_step(view_of(d_workspace, plan), quant,

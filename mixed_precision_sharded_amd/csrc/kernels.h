@@ -18,9 +18,12 @@ struct WorkspaceView {
     uint64_t tag;
 };
 
+// Which update the norm precedes (selects the gradient cache policy).
+enum class NormBefore { kUpdate, kQ8Update };
+
 hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid,
                             double* d_sumsq, double max_norm, double grad_scale,
-                            float* d_coef, hipStream_t stream);
+                            float* d_coef, hipStream_t stream, NormBefore next);
 
 hipError_t launch_clip_coef(const double* d_sumsq, double max_norm, double grad_scale,
                             float* d_coef, hipStream_t stream);

@@ -52,7 +52,7 @@ __device__ __forceinline__ double add_vector(double acc, u32x4 v)
 // run_stop), in a fixed order.  Consecutive chunks of one tensor are one
 // contiguous stretch of memory, streamed as a single body so the load
 // pipeline only restarts at tensor boundaries.
-template <bool kBf16, int kUnroll>
+template <bool kBf16, int kUnroll, int kPolicy>
 __device__ __forceinline__ double norm_of_run(const TensorEntry* tensors, const uint32_t* chunk_map,
                                               int64_t chunk_elems, int run_first, int run_stop)
 {
@@ -97,18 +97,18 @@ __device__ __forceinline__ double norm_of_run(const TensorEntry* tensors, const 
             constexpr int kStride = kBlock * kUnroll;
             u32x4 x[kUnroll], y[kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) x[u] = load_u32x4<kNormPolicy>(g, (u * kBlock + tid) * 16u);
+            for (int u = 0; u < kUnroll; ++u) x[u] = load_u32x4<kPolicy>(g, (u * kBlock + tid) * 16u);
             for (int base = 0; base < nvec; base += 2 * kStride) {
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
-                    y[u] = load_u32x4<kNormPolicy>(g, (base + kStride + u * kBlock + tid) * 16u);
+                    y[u] = load_u32x4<kPolicy>(g, (base + kStride + u * kBlock + tid) * 16u);
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) acc[u] = add_vector<kBf16>(acc[u], x[u]);
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
-                    x[u] = load_u32x4<kNormPolicy>(g, (base + 2 * kStride + u * kBlock + tid) * 16u);
+                    x[u] = load_u32x4<kPolicy>(g, (base + 2 * kStride + u * kBlock + tid) * 16u);
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (base + kStride < nvec) {  // uniform: skip the math of an empty tile
@@ -133,7 +133,7 @@ __device__ __forceinline__ int run_begin(int b, int n_chunks)
     return static_cast<int>(static_cast<int64_t>(b) * n_chunks / gridDim.x);
 }
 
-template <bool kBf16, int kUnroll>
+template <bool kBf16, int kUnroll, int kPolicy>
 __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
     WorkspaceHeader* header, const TensorEntry* tensors, const uint32_t* chunk_map,
     double* partials, int n_chunks, int64_t chunk_elems, uint64_t tag, double* d_sumsq,
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
     }
 
     const int tid = threadIdx.x;
-    const double mine = norm_of_run<kBf16, kUnroll>(tensors, chunk_map, chunk_elems,
+    const double mine = norm_of_run<kBf16, kUnroll, kPolicy>(tensors, chunk_map, chunk_elems,
                                                     run_begin(blockIdx.x, n_chunks),
                                                     run_begin(blockIdx.x + 1, n_chunks));
 
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(kBlock) void adamw_fused_kernel(
     const int64_t t = static_cast<int64_t>(*d_step) + 1;
 
     // Phase 1: this block's partial of S.
-    const double mine = norm_of_run<kBf16, kNormUnroll>(tensors, chunk_map, chunk_elems,
+    const double mine = norm_of_run<kBf16, kNormUnroll, kNormPolicy>(tensors, chunk_map, chunk_elems,
                                                         run_begin(blockIdx.x, n_chunks),
                                                         run_begin(blockIdx.x + 1, n_chunks));
     __shared__ double lds[kWavesPerBlock];
@@ -446,17 +446,39 @@ __global__ __launch_bounds__(kBlock) void adamw_fused_kernel(
 
 // --------------------------------------------------------------- launchers ---
 
-hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid, double* d_sumsq,
-                            double max_norm, double grad_scale, float* d_coef, hipStream_t stream)
+namespace {
+
+template <int kPolicy>
+void grad_norm_launch(const WorkspaceView& ws, bool grad_bf16, int grid, double* d_sumsq,
+                      double max_norm, double grad_scale, float* d_coef, hipStream_t stream)
 {
     if (grad_bf16) {
-        grad_norm_kernel<true, MPS_NORM_UNROLL><<<grid, kBlock, 0, stream>>>(
+        grad_norm_kernel<true, MPS_NORM_UNROLL, kPolicy><<<grid, kBlock, 0, stream>>>(
             ws.header, ws.tensors, ws.chunk_map, ws.partials, ws.n_chunks, ws.chunk_elems, ws.tag,
             d_sumsq, max_norm, grad_scale, d_coef);
     } else {
-        grad_norm_kernel<false, MPS_NORM_UNROLL><<<grid, kBlock, 0, stream>>>(
+        grad_norm_kernel<false, MPS_NORM_UNROLL, kPolicy><<<grid, kBlock, 0, stream>>>(
             ws.header, ws.tensors, ws.chunk_map, ws.partials, ws.n_chunks, ws.chunk_elems, ws.tag,
             d_sumsq, max_norm, grad_scale, d_coef);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid, double* d_sumsq,
+                            double max_norm, double grad_scale, float* d_coef, hipStream_t stream,
+                            NormBefore next)
+{
+    // The gradient cache policy that suits the update that follows: the fp32
+    // update re-reads the gradients soon after and benefits from the ones the
+    // norm left in the caches; the 8-bit update streams its own data through
+    // the caches, so there the norm reads nontemporally (measured on MI355X).
+    if (next == NormBefore::kQ8Update) {
+        grad_norm_launch<kQ8NormPolicy>(ws, grad_bf16, grid, d_sumsq, max_norm, grad_scale, d_coef,
+                                        stream);
+    } else {
+        grad_norm_launch<kNormPolicy>(ws, grad_bf16, grid, d_sumsq, max_norm, grad_scale, d_coef,
+                                      stream);
     }
     return hipGetLastError();
 }

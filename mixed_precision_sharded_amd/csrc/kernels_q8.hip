@@ -26,10 +26,30 @@
 #include "device.h"
 #include "kernels.h"
 
+// Cache policies of the 8-bit update's streams (aux operand: 0 default,
+// 2 nontemporal).
+#ifndef MPS_Q8_W_POLICY
+#define MPS_Q8_W_POLICY 0       // master and gradient loads
+#endif
+#ifndef MPS_Q8_CODE_POLICY
+#define MPS_Q8_CODE_POLICY 2    // code loads
+#endif
+#ifndef MPS_Q8_SCALE_POLICY
+#define MPS_Q8_SCALE_POLICY 0   // scale-byte loads
+#endif
+#ifndef MPS_Q8_STORE_POLICY
+#define MPS_Q8_STORE_POLICY 0   // every store
+#endif
+
 namespace mps {
 namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kQ8WPolicy = MPS_Q8_W_POLICY;
+constexpr int kQ8CodePolicy = MPS_Q8_CODE_POLICY;
+constexpr int kQ8ScalePolicy = MPS_Q8_SCALE_POLICY;
+constexpr int kQ8StorePolicy = MPS_Q8_STORE_POLICY;
 
 // Largest finite code of each format is 1.75 * 2^k: 448 (E4M3), 57344 (E5M2).
 constexpr int kE4M3TopExp = 8;
@@ -146,19 +166,31 @@ __device__ __forceinline__ uint32_t half_wave_max(uint32_t x)
     return x;
 }
 
+template <int kAux>
 __device__ __forceinline__ uint32_t load_byte(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, kLoadPolicy);
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, kAux);
+}
+
+template <int kAux>
+__device__ __forceinline__ u32x2 load_u32x2_policy(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kAux);
 }
 
 __device__ __forceinline__ void store_byte(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-    __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(v), r, off, 0, kStorePolicy);
+    __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(v), r, off, 0, kQ8StorePolicy);
 }
 
-__device__ __forceinline__ void store_u32x4(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+__device__ __forceinline__ void store8_u32x2(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStorePolicy);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kQ8StorePolicy);
+}
+
+__device__ __forceinline__ void store8_u32x4(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kQ8StorePolicy);
 }
 
 // ---------------------------------------------------------------- update ---
@@ -227,18 +259,18 @@ __device__ __forceinline__ void adamw8_body(const TensorEntry* te, const QuantEn
     };
     auto load_tile = [&](Tile& t, int base) {
         const uint32_t q = base + tid;
-        t.w[0] = load_f32x4(W, q * 32u);
-        t.w[1] = load_f32x4(W, q * 32u + 16u);
+        t.w[0] = __builtin_bit_cast(f32x4, load_u32x4<kQ8WPolicy>(W, q * 32u));
+        t.w[1] = __builtin_bit_cast(f32x4, load_u32x4<kQ8WPolicy>(W, q * 32u + 16u));
         if (kBf16) {
-            t.g[0] = load_u32x4<kLoadPolicy>(G, q * 16u);
+            t.g[0] = load_u32x4<kQ8WPolicy>(G, q * 16u);
         } else {
-            t.g[0] = load_u32x4<kLoadPolicy>(G, q * 32u);
-            t.g[1] = load_u32x4<kLoadPolicy>(G, q * 32u + 16u);
+            t.g[0] = load_u32x4<kQ8WPolicy>(G, q * 32u);
+            t.g[1] = load_u32x4<kQ8WPolicy>(G, q * 32u + 16u);
         }
-        t.mq = load_u32x2(MQ, q * 8u);
-        t.vq = load_u32x2(VQ, q * 8u);
-        t.ms = load_byte(MS, q / 4u);
-        t.vs = load_byte(VS, q / 4u);
+        t.mq = load_u32x2_policy<kQ8CodePolicy>(MQ, q * 8u);
+        t.vq = load_u32x2_policy<kQ8CodePolicy>(VQ, q * 8u);
+        t.ms = load_byte<kQ8ScalePolicy>(MS, q / 4u);
+        t.vs = load_byte<kQ8ScalePolicy>(VS, q / 4u);
     };
     auto update_tile = [&](Tile& t, int base) {
         const uint32_t q = base + tid;
@@ -272,15 +304,17 @@ __device__ __forceinline__ void adamw8_body(const TensorEntry* te, const QuantEn
         }
         const uint32_t mb = scale_byte<kE4M3TopExp>(quad_max(am));
         const uint32_t vb = scale_byte<kE5M2TopExp>(quad_max(av));
-        store_f32x4(f32x4{w[0], w[1], w[2], w[3]}, W, q * 32u);
-        store_f32x4(f32x4{w[4], w[5], w[6], w[7]}, W, q * 32u + 16u);
-        store_u32x2(encode8<true>(m, mb), MQ, q * 8u);
-        store_u32x2(encode8<false>(v, vb), VQ, q * 8u);
+        store8_u32x4(u32x4{__float_as_uint(w[0]), __float_as_uint(w[1]), __float_as_uint(w[2]),
+                           __float_as_uint(w[3])}, W, q * 32u);
+        store8_u32x4(u32x4{__float_as_uint(w[4]), __float_as_uint(w[5]), __float_as_uint(w[6]),
+                           __float_as_uint(w[7])}, W, q * 32u + 16u);
+        store8_u32x2(encode8<true>(m, mb), MQ, q * 8u);
+        store8_u32x2(encode8<false>(v, vb), VQ, q * 8u);
         if (copy) {
             u32x4 packed;
 #pragma unroll
             for (int k = 0; k < 4; ++k) packed[k] = bf16_bits(w[2 * k]) | (bf16_bits(w[2 * k + 1]) << 16);
-            store_u32x4(packed, P, q * 16u);
+            store8_u32x4(packed, P, q * 16u);
         }
         if ((tid & 3) == 0) {
             store_byte(mb, MS, q / 4u);
@@ -301,18 +335,31 @@ __device__ __forceinline__ void adamw8_body(const TensorEntry* te, const QuantEn
     }
 }
 
-// Chunks b, b + G, ... of this block, as in the fp32 kernel.  Within a chunk
-// the whole runs of an aligned tensor take the vector body and the tensor's
-// last partial run the element path.
+// Chunks b, b + G, ... of this block, as in the fp32 kernel (the next
+// chunk's table entries are fetched before this chunk streams).  Within a
+// chunk the whole runs of an aligned tensor take the vector body and the
+// tensor's last partial run the element path.
 template <bool kBf16>
-__device__ __forceinline__ void update8_chunks(const TensorEntry* tensors, const QuantEntry* quant,
-                                               const uint32_t* chunk_map, int n_chunks,
+__device__ __forceinline__ void update8_chunks(const TensorEntry* __restrict__ tensors,
+                                               const QuantEntry* __restrict__ quant,
+                                               const uint32_t* __restrict__ chunk_map, int n_chunks,
                                                int64_t chunk_elems, const StepScalars& s)
 {
+    TensorEntry next{};
+    QuantEntry next_q{};
+    if (static_cast<int>(blockIdx.x) < n_chunks) {
+        const uint32_t k = chunk_map[blockIdx.x];
+        next = tensors[k];
+        next_q = quant[k];
+    }
     for (int c = blockIdx.x; c < n_chunks; c += gridDim.x) {
-        const uint32_t k = chunk_map[c];
-        const TensorEntry te = tensors[k];
-        const QuantEntry qe = quant[k];
+        const TensorEntry te = next;
+        const QuantEntry qe = next_q;
+        if (c + static_cast<int>(gridDim.x) < n_chunks) {
+            const uint32_t k = chunk_map[c + gridDim.x];
+            next = tensors[k];
+            next_q = quant[k];
+        }
         const int64_t begin = static_cast<int64_t>(c - te.first_chunk) * chunk_elems;
         const int64_t end = min(begin + chunk_elems, te.numel);
         if (te.head < 0) {
@@ -328,8 +375,9 @@ __device__ __forceinline__ void update8_chunks(const TensorEntry* tensors, const
 
 template <bool kBf16>
 __global__ __launch_bounds__(kBlock) void adamw8_step_kernel(
-    WorkspaceHeader* header, const TensorEntry* tensors, const QuantEntry* quant,
-    const uint32_t* chunk_map, int n_chunks, int64_t chunk_elems, uint64_t tag,
+    WorkspaceHeader* header, const TensorEntry* __restrict__ tensors,
+    const QuantEntry* __restrict__ quant, const uint32_t* __restrict__ chunk_map, int n_chunks,
+    int64_t chunk_elems, uint64_t tag,
     const float* d_coef, const double* d_skip_if_nonfinite, int32_t* d_step, HyperParams hp)
 {
     if (header->tag != tag) return;  // tables overwritten: touch nothing

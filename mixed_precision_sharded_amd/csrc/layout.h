@@ -35,6 +35,10 @@ namespace mps {
 #define MPS_CHUNK_TARGET 3072       // aim for about this many chunks
 #endif
 
+#ifndef MPS_Q8_MAX_BLOCKS
+#define MPS_Q8_MAX_BLOCKS 768      // 8-bit-moment update grid cap
+#endif
+
 #ifndef MPS_FUSED_MAX_BLOCKS
 #define MPS_FUSED_MAX_BLOCKS 512   // single-launch step grid cap (all co-resident)
 #endif
@@ -43,6 +47,7 @@ constexpr int kBlock = 256;                        // threads per block, all ker
 constexpr int kNormMaxBlocks = MPS_NORM_MAX_BLOCKS;
 constexpr int kStepMaxBlocks = MPS_STEP_MAX_BLOCKS;
 constexpr int kFusedMaxBlocks = MPS_FUSED_MAX_BLOCKS;
+constexpr int kQ8MaxBlocks = MPS_Q8_MAX_BLOCKS;
 constexpr int kPartials = kNormMaxBlocks > kFusedMaxBlocks ? kNormMaxBlocks : kFusedMaxBlocks;
 constexpr int64_t kChunkQuantum = 2048;            // chunk sizes are multiples of this
 constexpr int64_t kChunkMin = MPS_CHUNK_MIN;
