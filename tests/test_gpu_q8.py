@@ -316,3 +316,109 @@ def test_q8_empty_and_single_tensor_lists():
     say("q8 empty tensors in the list")
     host = make_host([0, 45, 0], 110, bf16=True, copy_every=1)
     step_and_compare(host, "empty")
+
+
+# ------------------------------------------------------- full sizes ---
+
+def random_q8_state(n, rng, warm):
+    """A valid seeded 8-bit state without the encoder: random finite codes and
+    scale bytes near those of m ~ N(0, 1e-4) and v = |N(0, 1e-8)| (warm), or
+    all zero."""
+    nb = (n + 31) // 32
+    if not warm:
+        return (np.zeros(n, np.uint8), np.zeros(nb, np.uint8), np.zeros(n, np.uint8),
+                np.zeros(nb, np.uint8))
+    mc = rng.integers(0, 0x7F, size=n, dtype=np.uint8) | (rng.integers(0, 2, size=n, dtype=np.uint8) << 7)
+    vc = rng.integers(0, 0x7C, size=n, dtype=np.uint8)
+    ms = rng.integers(105, 109, size=nb, dtype=np.uint8)
+    vs = rng.integers(85, 89, size=nb, dtype=np.uint8)
+    return mc, ms, vc, vs
+
+
+def sampled_runs(n, k, rng):
+    """Run indices: the first and last run, runs at chunk edges, k random."""
+    nr = (n + 31) // 32
+    fixed = {0, nr - 1} | {r for q in range(64, min(nr, 2048) + 1, 64) for r in (q - 1, q) if r < nr}
+    return sorted(fixed | set(rng.integers(0, nr, size=min(k, nr)).tolist()))
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_q8_full_size_sampled(cfg):
+    """The bench's workload and launches with 8-bit moments: the sum of
+    squares over every gradient, and sampled runs of 32 recomputed by the
+    oracle from their inputs gathered before the step."""
+    from mixed_precision_sharded_amd import synth
+    from mixed_precision_sharded_amd.configs import WORKLOADS
+    from mixed_precision_sharded_amd.synth import to_numpy
+
+    w = WORKLOADS[cfg]
+    warm = w.m_std is not None
+    say(f"q8 full size: {w.name}, {w.numel:,} params in {w.n_tensors} tensors, warm={warm}")
+    cols = synth.workload_inputs(w, "cuda")
+    del cols["exp_avg"], cols["exp_avg_sq"]
+    rng = np.random.default_rng(200 + cfg)
+    states, picks, before = [], [], []
+    per_tensor = max(4, 6000 // w.n_tensors)
+    for i, (_, n) in enumerate(w.tensors):
+        st = tuple(torch.from_numpy(a).cuda() for a in random_q8_state(n, rng, warm))
+        states.append(st)
+        runs = sampled_runs(n, per_tensor, rng)
+        elems = torch.tensor([e for r in runs for e in range(32 * r, min(32 * r + 32, n))],
+                             dtype=torch.int64, device="cuda")
+        rix = torch.tensor(runs, dtype=torch.int64, device="cuda")
+        picks.append((runs, elems, rix))
+        before.append(dict(w=to_numpy(cols["master"][i][elems]), g=to_numpy(cols["grad"][i][elems]),
+                           mc=st[0][elems].cpu().numpy(), ms=st[1][rix].cpu().numpy(),
+                           vc=st[2][elems].cpu().numpy(), vs=st[3][rix].cpu().numpy()))
+    torch.cuda.synchronize()
+    say("oracle sum of squares over every gradient")
+    o = oracle.default()
+    S_ref = o.grad_norm_sq(to_numpy(g) for g in cols["grad"])
+
+    say("GPU step (8-bit moments)")
+    tl = binding.TensorList8(cols["master"], states, cols["grad"], cols["param_bf16"])
+    sumsq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    coef = torch.zeros(1, dtype=torch.float32, device="cuda")
+    step = torch.tensor([w.step - 1], dtype=torch.int32, device="cuda")
+    binding.adamw8_grad_norm_sq(tl, sumsq, w.max_norm, coef)
+    binding.adamw8_multi_tensor_step(tl, coef, step, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
+    torch.cuda.synchronize()
+    S, c, t = float(sumsq.item()), np.float32(coef.item()), int(step.item())
+    assert t == w.step
+    assert abs(S - S_ref) <= NORM_REL_TOL * S_ref, (S, S_ref)
+    assert c == o.clip_coef(S, w.max_norm)
+    say(f"S={S:.9e} oracle {S_ref:.9e} c={float(c)}")
+
+    n_runs = nbit = 0
+    for i, (_, n) in enumerate(w.tensors):
+        runs, elems, rix = picks[i]
+        b = before[i]
+        got_w = to_numpy(cols["master"][i][elems])
+        got = [states[i][0][elems].cpu().numpy(), states[i][1][rix].cpu().numpy(),
+               states[i][2][elems].cpu().numpy(), states[i][3][rix].cpu().numpy()]
+        got_p = to_numpy(cols["param_bf16"][i][elems]) if w.copy_bf16 else None
+        off = 0
+        for j, r in enumerate(runs):
+            k = min(32 * r + 32, n) - 32 * r
+            sl = slice(off, off + k)
+            ww = b["w"][sl].copy()
+            mc, vc = b["mc"][sl].copy(), b["vc"][sl].copy()
+            ms, vs = b["ms"][j:j + 1].copy(), b["vs"][j:j + 1].copy()
+            pv = np.zeros(k, np.uint16) if w.copy_bf16 else None
+            o.adamw8_step(ww, mc, ms, vc, vs, np.ascontiguousarray(b["g"][sl]), pv, c, w.step,
+                          w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
+            nb, _ = check_f32(got_w[sl], ww, f"{w.name} tensor {i} run {r} master")
+            nbit += nb
+            assert np.array_equal(got[0][sl], mc), (i, r, "m codes")
+            assert got[1][j] == ms[0], (i, r, "m scale")
+            assert np.array_equal(got[2][sl], vc), (i, r, "v codes")
+            assert got[3][j] == vs[0], (i, r, "v scale")
+            if w.copy_bf16:
+                check_bf16(got_p[sl], pv, f"{w.name} tensor {i} run {r} copy")
+            off += k
+            n_runs += 1
+        assert bool(torch.isfinite(cols["master"][i]).all()), i
+    say(f"{n_runs:,} sampled runs checked; {nbit} master elements not bitwise equal")
+    tl.release()
+    del tl, cols, states
+    torch.cuda.empty_cache()
