@@ -87,13 +87,20 @@ __device__ __forceinline__ void store_u32x2(u32x2 v, __amdgpu_buffer_rsrc_t r, u
 __device__ __forceinline__ float bf16_lo(uint32_t word) { return __uint_as_float(word << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t word) { return __uint_as_float(word & 0xffff0000u); }
 
-// Round to nearest even: add half an ulp of the kept part, plus one when the
-// kept part is odd, then truncate.  NaN keeps its sign and gets the quiet bit.
-__device__ __forceinline__ uint32_t bf16_bits(float f)
+// bf16 copies use the chip's conversion (v_cvt_pk_bf16_f32 on gfx950): round
+// to nearest, ties to even, two values per instruction.  A NaN stays a NaN.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// a in the low half, b in the high half.
+__device__ __forceinline__ uint32_t bf16_pack2(float a, float b)
 {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2));
+}
+
+__device__ __forceinline__ uint16_t bf16_one(float f)
+{
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // ------------------------------------------------------ reductions (fp64) ---

@@ -207,7 +207,7 @@ __device__ __forceinline__ void adamw_scalar_at(const TensorEntry* te, int64_t i
     te->master[i] = w;
     te->exp_avg[i] = m;
     te->exp_avg_sq[i] = v;
-    if (te->param_bf16) te->param_bf16[i] = static_cast<uint16_t>(bf16_bits(w));
+    if (te->param_bf16) te->param_bf16[i] = bf16_one(w);
 }
 
 // The aligned body of one chunk: `nquad` groups of four elements starting at
@@ -265,8 +265,8 @@ __device__ __forceinline__ void adamw_body(const TensorEntry* te, int64_t q0, in
             store_f32x4(t.v[u], V, q * 16u);
             if (copy) {
                 u32x2 packed;
-                packed[0] = bf16_bits(t.w[u][0]) | (bf16_bits(t.w[u][1]) << 16);
-                packed[1] = bf16_bits(t.w[u][2]) | (bf16_bits(t.w[u][3]) << 16);
+                packed[0] = bf16_pack2(t.w[u][0], t.w[u][1]);
+                packed[1] = bf16_pack2(t.w[u][2], t.w[u][3]);
                 store_u32x2(packed, P, q * 8u);
             }
         }

@@ -219,7 +219,7 @@ __device__ __forceinline__ void adamw8_elements(const TensorEntry* te, const Qua
             te->master[i] = w;
             qe->m_codes[i] = static_cast<uint8_t>(encode1<true>(m, mb));
             qe->v_codes[i] = static_cast<uint8_t>(encode1<false>(v, vb));
-            if (te->param_bf16) te->param_bf16[i] = static_cast<uint16_t>(bf16_bits(w));
+            if (te->param_bf16) te->param_bf16[i] = bf16_one(w);
             if (i % kQuantBlock == 0) {
                 qe->m_scales[i / kQuantBlock] = static_cast<uint8_t>(mb);
                 qe->v_scales[i / kQuantBlock] = static_cast<uint8_t>(vb);
@@ -313,7 +313,7 @@ __device__ __forceinline__ void adamw8_body(const TensorEntry* te, const QuantEn
         if (copy) {
             u32x4 packed;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) packed[k] = bf16_bits(w[2 * k]) | (bf16_bits(w[2 * k + 1]) << 16);
+            for (int k = 0; k < 4; ++k) packed[k] = bf16_pack2(w[2 * k], w[2 * k + 1]);
             store8_u32x4(packed, P, q * 16u);
         }
         if ((tid & 3) == 0) {

@@ -155,3 +155,23 @@ def sample_indices(n, k, gen):
         fixed += [q - 1, q] if q < n else [q - 1]
     rnd = torch.randint(0, n, (min(k, n),), generator=gen).tolist() if n else []
     return sorted(set(i for i in fixed + rnd if 0 <= i < n))
+
+
+def crafted_bf16_masters(rng, n_random=4000):
+    """fp32 values at the corners of bf16 rounding: exact ties below odd and
+    even kept halves, one unit either side of a tie, fp32 subnormals (also at
+    ties), the largest finite values (which round up to infinity), signed
+    zeros, infinities and NaNs."""
+    hi = rng.integers(0, 1 << 16, size=n_random, dtype=np.uint32) << 16
+    lows = np.array([0x8000, 0x7FFF, 0x8001, 0x0000, 0xFFFF], dtype=np.uint32)
+    bits = (hi[:, None] | lows[None, :]).ravel()
+    sub = rng.integers(1, 0x00800000, size=500, dtype=np.uint32)
+    sub_ties = (rng.integers(0, 0x80, size=500, dtype=np.uint32) << 16) | 0x8000
+    special = np.array([0x7F7FFFFF, 0x7F7F8000, 0x7F7F7FFF, 0xFF7FFFFF, 0x00000000, 0x80000000,
+                        0x7F800000, 0xFF800000, 0x7FC00001, 0xFFA00000, 0x00008000, 0x80018000],
+                       dtype=np.uint32)
+    bits = np.concatenate([bits, sub, sub | 0x80000000, sub_ties, special])
+    # keep the exponent field away from all-ones except for the specials
+    body = bits[:-special.size]
+    body = np.where((body & 0x7F800000) == 0x7F800000, body & 0xBFFFFFFF, body)
+    return np.concatenate([body, special]).view(np.float32)

@@ -361,3 +361,37 @@ def test_workload_70b_share_full_parity():
     run_and_check(cols, t=w.step, max_norm=w.max_norm, what=w.name,
                   hp=dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, wd=w.weight_decay))
     del cols
+
+
+def test_bf16_copy_rounds_to_nearest_even():
+    """lr = 0 and zero moments and gradients keep every master as it is, so
+    the copy is exactly the bf16 rounding of the crafted masters: ties, one
+    unit off a tie, subnormals, overflow to infinity, zeros, infinities, NaN;
+    aligned (vector path) and one element off (scalar peel)."""
+    from gpu_harness import crafted_bf16_masters
+    from mixed_precision_sharded_amd.synth import to_numpy
+    w = crafted_bf16_masters(np.random.default_rng(31))
+    n = w.size
+    buf = torch.zeros(n + 1, dtype=torch.float32, device=DEV)
+    buf[1:] = torch.from_numpy(w).to(DEV)
+    masters = [torch.from_numpy(w).to(DEV), buf[1:]]
+    cols = {"master": masters,
+            "exp_avg": [torch.zeros(n, device=DEV) for _ in range(2)],
+            "exp_avg_sq": [torch.zeros(n, device=DEV) for _ in range(2)],
+            "grad": [torch.zeros(n, dtype=torch.bfloat16, device=DEV) for _ in range(2)],
+            "param_bf16": [torch.zeros(n, dtype=torch.bfloat16, device=DEV) for _ in range(2)]}
+    st = Step(cols).norm_clip(1.0).update(0.0, HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+    S, c, _ = st.results()
+    assert S == 0.0 and c == np.float32(1.0)
+    want = oracle.default().f32_to_bf16(w)
+    nan = np.isnan(w)
+    for i in range(2):
+        got = to_numpy(cols["param_bf16"][i])
+        assert ((got & 0x7FFF) > 0x7F80)[nan].all(), f"tensor {i}: NaN copies"
+        bad = np.nonzero(got[~nan] != want[~nan])[0]
+        assert bad.size == 0, (f"tensor {i}: {bad.size} copies differ, e.g. "
+                               f"{w[~nan][bad[0]].view(np.uint32):#010x} -> {got[~nan][bad[0]]:#06x}"
+                               f" vs {want[~nan][bad[0]]:#06x}")
+        kept = to_numpy(cols["master"][i])
+        assert np.array_equal(kept[~nan].view(np.uint32), w[~nan].view(np.uint32))
+    say(f"bf16 copy: {n} crafted values, every non-NaN copy bitwise equal to the oracle's")

@@ -318,6 +318,33 @@ def test_q8_empty_and_single_tensor_lists():
     step_and_compare(host, "empty")
 
 
+def test_q8_bf16_copy_rounds_to_nearest_even():
+    """The 8-bit kernel's copy on crafted masters (lr = 0, zero state and
+    gradients keep the master): vector path and element path."""
+    from gpu_harness import crafted_bf16_masters
+    w = crafted_bf16_masters(np.random.default_rng(32))
+    n = w.size - w.size % 32            # whole runs: vector path ...
+    w = w[:n]
+    host = []
+    for extra in (0, 5):                # ... and a partial run: element path
+        m = w.size + extra
+        wm = np.concatenate([w, np.float32([1.0, -2.5, 3e-39, 0.1, 7.0])[:extra]]).astype(np.float32)
+        host.append(dict(w=wm, mc=np.zeros(m, np.uint8), ms=np.zeros((m + 31) // 32, np.uint8),
+                         vc=np.zeros(m, np.uint8), vs=np.zeros((m + 31) // 32, np.uint8),
+                         g=np.zeros(m, np.float32), p=np.zeros(m, np.uint16)))
+    s8 = Step8(host)
+    S_gpu, c, t = s8.run(1.0, dict(HP, lr=0.0))
+    assert S_gpu == 0.0 and c == np.float32(1.0)
+    o = oracle.default()
+    for d, h in zip(s8.dev, host):
+        want = o.f32_to_bf16(h["w"])
+        got = to_host(d["p"])
+        nan = np.isnan(h["w"])
+        assert ((got & 0x7FFF) > 0x7F80)[nan].all()
+        assert np.array_equal(got[~nan], want[~nan])
+    s8.tl.release()
+
+
 # ------------------------------------------------------- full sizes ---
 
 def random_q8_state(n, rng, warm):
