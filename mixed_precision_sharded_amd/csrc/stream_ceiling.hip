@@ -109,6 +109,36 @@ __global__ __launch_bounds__(256) void adam_bf16_octets(f4* __restrict__ w, f4* 
   }
 }
 
+// The 8-bit-moment update's streams, eight elements per lane: fp32 w in and
+// out (two 16 B accesses), bf16 g in (16 B), bf16 copy out (16 B), m and v
+// codes in and out (8 B each), one scale byte per 32 elements for each
+// moment in (every lane) and out (one lane in four).  16.125 B per element.
+template <bool NT>
+__global__ __launch_bounds__(256) void adam_q8_octets(f4* __restrict__ w, const u4* __restrict__ g, u4* __restrict__ p,
+                                                      u2* __restrict__ mq, u2* __restrict__ vq,
+                                                      unsigned char* __restrict__ ms, unsigned char* __restrict__ vs, long n8) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)gridDim.x * 256) {
+    f4 W0 = NT ? __builtin_nontemporal_load(&w[2 * i]) : w[2 * i], W1 = NT ? __builtin_nontemporal_load(&w[2 * i + 1]) : w[2 * i + 1];
+    u4 G = NT ? __builtin_nontemporal_load(&g[i]) : g[i];
+    u2 M = NT ? __builtin_nontemporal_load(&mq[i]) : mq[i];
+    u2 V = NT ? __builtin_nontemporal_load(&vq[i]) : vq[i];
+    unsigned sm = ms[i / 4], sv = vs[i / 4];
+    f4 g0 = f4{__uint_as_float(G[0] << 16), __uint_as_float(G[0] & 0xffff0000u), __uint_as_float(G[1] << 16), __uint_as_float(G[1] & 0xffff0000u)};
+    f4 g1 = f4{__uint_as_float(G[2] << 16), __uint_as_float(G[2] & 0xffff0000u), __uint_as_float(G[3] << 16), __uint_as_float(G[3] & 0xffff0000u)};
+    f4 w0 = W0 - g0 * 0.001f, w1 = W1 - g1 * 0.001f;
+    u2 M2 = M ^ (u2)(sm * 0x01010101u), V2 = V ^ (u2)(sv * 0x01010101u);
+    u4 P = u4{(__float_as_uint(w0[0]) >> 16) | (__float_as_uint(w0[1]) & 0xffff0000u), (__float_as_uint(w0[2]) >> 16) | (__float_as_uint(w0[3]) & 0xffff0000u),
+              (__float_as_uint(w1[0]) >> 16) | (__float_as_uint(w1[1]) & 0xffff0000u), (__float_as_uint(w1[2]) >> 16) | (__float_as_uint(w1[3]) & 0xffff0000u)};
+    if (NT) {
+      __builtin_nontemporal_store(w0, &w[2 * i]); __builtin_nontemporal_store(w1, &w[2 * i + 1]);
+      __builtin_nontemporal_store(M2, &mq[i]); __builtin_nontemporal_store(V2, &vq[i]); __builtin_nontemporal_store(P, &p[i]);
+    } else {
+      w[2 * i] = w0; w[2 * i + 1] = w1; mq[i] = M2; vq[i] = V2; p[i] = P;
+    }
+    if ((threadIdx.x & 3) == 0) { ms[i / 4] = (unsigned char)(sm + 1); vs[i / 4] = (unsigned char)(sv + 1); }
+  }
+}
+
 template <typename F>
 float time_ms(F launch, int reps) {
   hipEvent_t a, b; CHECK(hipEventCreate(&a)); CHECK(hipEventCreate(&b));
@@ -155,6 +185,17 @@ int main(int argc, char** argv) {
       printf("%-10s NT=1 blocks/CU=%2d  %8.1f us  %7.0f GB/s\n", "bf16_quads", bpc, ms * 1e3, n * 4 * 30.0 / (ms * 1e-3) / 1e9); fflush(stdout);
       ms = time_ms([&]{ adam_bf16_octets<true><<<grid, 256>>>(w, m, v, (const u4*)g, (u4*)b, n / 2); }, reps);
       printf("%-10s NT=1 blocks/CU=%2d  %8.1f us  %7.0f GB/s\n", "bf16_octets", bpc, ms * 1e3, n * 4 * 30.0 / (ms * 1e-3) / 1e9); fflush(stdout);
+    }
+    // 8-bit moments: 4n elements; codes in the m and v buffers (4n bytes
+    // each), scale bytes after them (n/2 bytes each).
+    for (int nt = 0; nt < 2; ++nt) {
+      unsigned char* mb = (unsigned char*)m; unsigned char* vb = (unsigned char*)v;
+      auto launch = [&]{
+        if (nt) adam_q8_octets<true><<<grid, 256>>>(w, (const u4*)g, (u4*)b, (u2*)mb, (u2*)vb, mb + 4 * n, vb + 4 * n, n / 2);
+        else adam_q8_octets<false><<<grid, 256>>>(w, (const u4*)g, (u4*)b, (u2*)mb, (u2*)vb, mb + 4 * n, vb + 4 * n, n / 2);
+      };
+      float ms = time_ms(launch, reps);
+      printf("%-10s NT=%d blocks/CU=%2d  %8.1f us  %7.0f GB/s\n", "q8_octets", nt, bpc, ms * 1e3, n * 4 * 16.125 / (ms * 1e-3) / 1e9); fflush(stdout);
     }
   }
   return 0;
