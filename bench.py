@@ -182,6 +182,7 @@ def main():
     # Per-kernel durations: the same K steps again with events between the
     # launches, on the stream the kernels run on.
     kern_us = None
+    spread = None
     if not args.no_kernel_events:
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
         torch.cuda.synchronize()
@@ -190,6 +191,9 @@ def main():
         torch.cuda.synchronize()
         norm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
         upd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+        per_step = sorted(e[0].elapsed_time(e[2]) * 1e3 for e in evs)
+        spread = {f"p{q}": round(per_step[min(len(per_step) - 1, int(q / 100 * len(per_step)))], 2)
+                  for q in (10, 50, 90)}
         if args.fused:
             kern_us = {"adamw_fused_step": norm_ms * 1e3}
         elif args.state8:
@@ -262,6 +266,7 @@ def main():
         "step_gbps": round(step_gbps, 1),
         "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "kernel_us": kern_us,
+        "step_us_spread": spread,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
