@@ -139,6 +139,33 @@ __global__ __launch_bounds__(256) void adam_q8_octets(f4* __restrict__ w, const 
   }
 }
 
+// The same bytes with the codes of m and v interleaved per eight elements
+// (16 B per thread, one load and one store) and the two scale bytes of a run
+// side by side (2 B per 32 elements): four read and four write streams.
+template <bool NT>
+__global__ __launch_bounds__(256) void adam_q8_interleaved(f4* __restrict__ w, const u4* __restrict__ g, u4* __restrict__ p,
+                                                           u4* __restrict__ mv, unsigned short* __restrict__ sc, long n8) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)gridDim.x * 256) {
+    f4 W0 = NT ? __builtin_nontemporal_load(&w[2 * i]) : w[2 * i], W1 = NT ? __builtin_nontemporal_load(&w[2 * i + 1]) : w[2 * i + 1];
+    u4 G = NT ? __builtin_nontemporal_load(&g[i]) : g[i];
+    u4 C = NT ? __builtin_nontemporal_load(&mv[i]) : mv[i];
+    unsigned s = sc[i / 4];
+    f4 g0 = f4{__uint_as_float(G[0] << 16), __uint_as_float(G[0] & 0xffff0000u), __uint_as_float(G[1] << 16), __uint_as_float(G[1] & 0xffff0000u)};
+    f4 g1 = f4{__uint_as_float(G[2] << 16), __uint_as_float(G[2] & 0xffff0000u), __uint_as_float(G[3] << 16), __uint_as_float(G[3] & 0xffff0000u)};
+    f4 w0 = W0 - g0 * 0.001f, w1 = W1 - g1 * 0.001f;
+    u4 C2 = C ^ (u4)(s * 0x00010001u);
+    u4 P = u4{(__float_as_uint(w0[0]) >> 16) | (__float_as_uint(w0[1]) & 0xffff0000u), (__float_as_uint(w0[2]) >> 16) | (__float_as_uint(w0[3]) & 0xffff0000u),
+              (__float_as_uint(w1[0]) >> 16) | (__float_as_uint(w1[1]) & 0xffff0000u), (__float_as_uint(w1[2]) >> 16) | (__float_as_uint(w1[3]) & 0xffff0000u)};
+    if (NT) {
+      __builtin_nontemporal_store(w0, &w[2 * i]); __builtin_nontemporal_store(w1, &w[2 * i + 1]);
+      __builtin_nontemporal_store(C2, &mv[i]); __builtin_nontemporal_store(P, &p[i]);
+    } else {
+      w[2 * i] = w0; w[2 * i + 1] = w1; mv[i] = C2; p[i] = P;
+    }
+    if ((threadIdx.x & 3) == 0) sc[i / 4] = (unsigned short)(s + 1);
+  }
+}
+
 template <typename F>
 float time_ms(F launch, int reps) {
   hipEvent_t a, b; CHECK(hipEventCreate(&a)); CHECK(hipEventCreate(&b));
@@ -196,6 +223,13 @@ int main(int argc, char** argv) {
       };
       float ms = time_ms(launch, reps);
       printf("%-10s NT=%d blocks/CU=%2d  %8.1f us  %7.0f GB/s\n", "q8_octets", nt, bpc, ms * 1e3, n * 4 * 16.125 / (ms * 1e-3) / 1e9); fflush(stdout);
+      // interleaved codes (8n bytes) in the m buffer, scale pairs after them
+      auto launch2 = [&]{
+        if (nt) adam_q8_interleaved<true><<<grid, 256>>>(w, (const u4*)g, (u4*)b, (u4*)mb, (unsigned short*)(mb + 8 * n), n / 2);
+        else adam_q8_interleaved<false><<<grid, 256>>>(w, (const u4*)g, (u4*)b, (u4*)mb, (unsigned short*)(mb + 8 * n), n / 2);
+      };
+      ms = time_ms(launch2, reps);
+      printf("%-10s NT=%d blocks/CU=%2d  %8.1f us  %7.0f GB/s\n", "q8_interl", nt, bpc, ms * 1e3, n * 4 * 16.125 / (ms * 1e-3) / 1e9); fflush(stdout);
     }
   }
   return 0;
