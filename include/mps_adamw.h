@@ -40,6 +40,11 @@
  *   - Buffers of different tensors, and master / exp_avg / exp_avg_sq /
  *     grad / param_bf16 of one tensor, must not overlap.
  *   - Concurrent calls must use distinct workspaces.
+ *   - Graph capture: once a list's tables are in a workspace (after any
+ *     call with that list and workspace, e.g. the norm, which changes no
+ *     state), the calls enqueue kernel launches only and may be recorded in
+ *     a HIP graph and replayed; the first call on a list also enqueues the
+ *     host-to-device copy of its tables and must not be captured.
  */
 #ifndef MPS_ADAMW_H
 #define MPS_ADAMW_H
