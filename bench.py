@@ -86,9 +86,9 @@ def stored_traffic(kernel, workload_name):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's shard only; multi-GPU runs are not part of this "
-              "build (the path needs one scalar all-reduce per step across ranks, see the "
-              "design notes)", file=sys.stderr)
+        print("bench.py times one GPU's shard only: over several GPUs each rank runs the same "
+              "step on its own shard, with one all-reduce of the 8-byte sum of squares "
+              "between the norm and the clip, which the caller performs", file=sys.stderr)
         sys.exit(2)
 
     import torch
