@@ -98,7 +98,10 @@ def check_f32(got, want, what, rel=REL_TOL):
     assert got.shape == want.shape, what
     gn, wn = np.isnan(got), np.isnan(want)
     assert np.array_equal(gn, wn), f"{what}: NaN positions differ"
-    ok = ~wn
+    wi = np.isinf(want)
+    assert np.array_equal(got[wi], want[wi]) and not np.isinf(got[~wi & ~wn]).any(), \
+        f"{what}: infinities differ"
+    ok = ~wn & ~wi
     g64, w64 = got[ok].astype(np.float64), want[ok].astype(np.float64)
     diff = np.abs(g64 - w64)
     zero = w64 == 0

@@ -345,6 +345,22 @@ def test_q8_bf16_copy_rounds_to_nearest_even():
     s8.tl.release()
 
 
+@pytest.mark.parametrize("t", [1, 2, 10, 1000, 123456])
+def test_q8_step_counter_and_bias_corrections(t):
+    say(f"q8 bias corrections at t = {t}")
+    step_and_compare(make_host([4099, 64], 111, bf16=True, copy_every=1), f"t={t}",
+                     completed=t - 1)
+
+
+@pytest.mark.parametrize("hp", [dict(lr=0.0, beta1=0.9, beta2=0.95, eps=1e-8, wd=0.1),
+                                dict(lr=1e-2, beta1=0.0, beta2=0.0, eps=1e-6, wd=0.0),
+                                dict(lr=1e-3, beta1=0.5, beta2=0.999, eps=0.0, wd=1.0)])
+def test_q8_hyperparameter_corners(hp):
+    say(f"q8 hyperparameters {hp}")
+    step_and_compare(make_host([3000, 33], 112, bf16=False, copy_every=1), "hp", hp=hp,
+                     completed=4)
+
+
 # ------------------------------------------------------- full sizes ---
 
 def random_q8_state(n, rng, warm):
