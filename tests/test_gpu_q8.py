@@ -390,22 +390,39 @@ def test_q8_full_size_sampled(cfg):
     """The bench's workload and launches with 8-bit moments: the sum of
     squares over every gradient, and sampled runs of 32 recomputed by the
     oracle from their inputs gathered before the step."""
-    from mixed_precision_sharded_amd import synth
     from mixed_precision_sharded_amd.configs import WORKLOADS
+    q8_sampled_parity(WORKLOADS[cfg], seed=200 + cfg)
+
+
+def test_q8_single_tensor_over_2g_elements_sampled():
+    """One tensor of 2^31 + 1003 elements (runs around element 2^31
+    included): 64-bit offsets throughout."""
+    from mixed_precision_sharded_amd.configs import Workload
+    w = Workload(cfg=91, name="single_tensor_2g", tensors=(("huge", (1 << 31) + 1003),),
+                 grad_bf16=True, copy_bf16=True, step=5, m_std=1e-4, v_std=1e-8)
+    free, _ = torch.cuda.mem_get_info()
+    need = w.numel * 16 + (8 << 30)
+    if free < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB free, {free / 2**30:.0f} GiB available")
+    q8_sampled_parity(w, seed=210, extra_runs=[((1 << 31) >> 5) + d for d in range(-3, 4)])
+
+
+def q8_sampled_parity(w, seed, extra_runs=()):
+    from mixed_precision_sharded_amd import synth
     from mixed_precision_sharded_amd.synth import to_numpy
 
-    w = WORKLOADS[cfg]
     warm = w.m_std is not None
     say(f"q8 full size: {w.name}, {w.numel:,} params in {w.n_tensors} tensors, warm={warm}")
     cols = synth.workload_inputs(w, "cuda")
     del cols["exp_avg"], cols["exp_avg_sq"]
-    rng = np.random.default_rng(200 + cfg)
+    rng = np.random.default_rng(seed)
     states, picks, before = [], [], []
     per_tensor = max(4, 6000 // w.n_tensors)
     for i, (_, n) in enumerate(w.tensors):
         st = tuple(torch.from_numpy(a).cuda() for a in random_q8_state(n, rng, warm))
         states.append(st)
-        runs = sampled_runs(n, per_tensor, rng)
+        runs = sorted(set(sampled_runs(n, per_tensor, rng)) |
+                      {r for r in extra_runs if 0 <= r < (n + 31) // 32})
         elems = torch.tensor([e for r in runs for e in range(32 * r, min(32 * r + 32, n))],
                              dtype=torch.int64, device="cuda")
         rix = torch.tensor(runs, dtype=torch.int64, device="cuda")

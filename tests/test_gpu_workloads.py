@@ -14,7 +14,7 @@ import torch
 import oracle
 from gpu_harness import NORM_REL_TOL, Step, check_bf16, check_f32, sample_indices, say
 from mixed_precision_sharded_amd import synth
-from mixed_precision_sharded_amd.configs import WORKLOADS, warm
+from mixed_precision_sharded_amd.configs import WORKLOADS, Workload, warm
 from mixed_precision_sharded_amd.synth import to_numpy
 
 pytestmark = pytest.mark.gpu
@@ -31,12 +31,14 @@ def _gpu_only():
     torch.cuda.empty_cache()
 
 
-def sampled_parity(w, per_tensor, seed):
+def sampled_parity(w, per_tensor, seed, extra=()):
+    """`extra`: more element indices to check in every tensor (where they exist)."""
     say(f"workload {w.name}: {w.numel:,} params in {w.n_tensors} tensors; generating")
     cols = synth.workload_inputs(w, "cuda")
     torch.cuda.synchronize()
     gen = torch.Generator().manual_seed(seed)
-    idx = [sample_indices(n, per_tensor, gen) for _, n in w.tensors]
+    idx = [sorted(set(sample_indices(n, per_tensor, gen)) | {e for e in extra if 0 <= e < n})
+           for _, n in w.tensors]
     idx_dev = [torch.tensor(ix, dtype=torch.int64, device="cuda") for ix in idx]
     before = {k: [to_numpy(t[ix]) for t, ix in zip(cols[k], idx_dev)] for k in FIELDS + ("grad",)}
 
@@ -88,3 +90,18 @@ def test_llama8b_full_list_sampled():
     if free < need:
         pytest.skip(f"needs {need / 2**30:.0f} GiB free, {free / 2**30:.0f} GiB available")
     sampled_parity(WORKLOADS[3], per_tensor=20000, seed=52)
+
+
+# A single tensor of more than 2^31 elements: element offsets, chunk indices
+# and buffer pieces must not wrap at 32 bits.
+HUGE = Workload(cfg=90, name="single_tensor_2g", tensors=(("huge", (1 << 31) + 1003),),
+                grad_bf16=True, copy_bf16=True, step=5, m_std=1e-4, v_std=1e-8)
+AROUND_2G = [(1 << 31) + d for d in range(-40, 41)] + [(1 << 30) + d for d in range(-8, 9)]
+
+
+def test_single_tensor_over_2g_elements_sampled():
+    free, _ = torch.cuda.mem_get_info()
+    need = HUGE.numel * (HUGE.state_bytes_per_param() + 4) + (8 << 30)
+    if free < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB free, {free / 2**30:.0f} GiB available")
+    sampled_parity(HUGE, per_tensor=20000, seed=53, extra=AROUND_2G)
