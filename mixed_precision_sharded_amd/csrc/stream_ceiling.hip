@@ -60,6 +60,22 @@ __global__ __launch_bounds__(256) void adam_like(f4* __restrict__ w, f4* __restr
   }
 }
 
+// The same bytes with w, m and v interleaved per group of four (48 B per
+// thread, three 16 B loads and stores of one contiguous piece): one
+// read-write state stream and the gradient stream instead of four streams.
+template <bool NT>
+__global__ __launch_bounds__(256) void adam_aos(f4* __restrict__ s, const f4* __restrict__ g, long n) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    f4 W = NT ? __builtin_nontemporal_load(&s[3 * i]) : s[3 * i];
+    f4 M = NT ? __builtin_nontemporal_load(&s[3 * i + 1]) : s[3 * i + 1];
+    f4 V = NT ? __builtin_nontemporal_load(&s[3 * i + 2]) : s[3 * i + 2];
+    f4 G = NT ? __builtin_nontemporal_load(&g[i]) : g[i];
+    f4 mm = M * 0.9f + G * 0.1f; f4 vv = V * 0.95f + G * G * 0.05f; f4 ww = W - mm * 0.001f;
+    if (NT) { __builtin_nontemporal_store(ww, &s[3 * i]); __builtin_nontemporal_store(mm, &s[3 * i + 1]); __builtin_nontemporal_store(vv, &s[3 * i + 2]); }
+    else { s[3 * i] = ww; s[3 * i + 1] = mm; s[3 * i + 2] = vv; }
+  }
+}
+
 typedef unsigned int u2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 
@@ -183,7 +199,9 @@ int main(int argc, char** argv) {
   long n = 62736416 / 4;  // f32x4 per buffer (the 8B / 128 shard)
   if (argc > 1) n = atol(argv[1]) / 4;
   f4 *w, *m, *v, *g, *b; float* out;
-  CHECK(hipMalloc(&w, n * 16)); CHECK(hipMalloc(&m, n * 16)); CHECK(hipMalloc(&v, n * 16));
+  // w, m and v in one allocation, back to back, so the interleaved pattern
+  // can use all three as one 3n-vector state buffer.
+  CHECK(hipMalloc(&w, n * 48)); m = w + n; v = w + 2 * n;
   CHECK(hipMalloc(&g, n * 16)); CHECK(hipMalloc(&b, n * 16)); CHECK(hipMalloc(&out, 16));
   CHECK(hipMemset(w, 0, n * 16)); CHECK(hipMemset(m, 0, n * 16)); CHECK(hipMemset(v, 0, n * 16));
   CHECK(hipMemset(g, 0, n * 16)); CHECK(hipMemset(b, 0, n * 16));
@@ -205,6 +223,11 @@ int main(int argc, char** argv) {
     RUN(adam_like, 2, false, n * 112.0, w, m, v, g, n);
     RUN(adam_like, 2, true, n * 112.0, w, m, v, g, n);
     RUN(adam_like, 4, false, n * 112.0, w, m, v, g, n);
+    // interleaved state: n groups of four in the 3n f32x4 of w, m, v
+    for (int nt = 0; nt < 2; ++nt) {
+      float ms = time_ms([&]{ if (nt) adam_aos<true><<<grid, 256>>>(w, g, n); else adam_aos<false><<<grid, 256>>>(w, g, n); }, reps);
+      printf("%-10s NT=%d blocks/CU=%2d  %8.1f us  %7.0f GB/s\n", "adam_aos", nt, bpc, ms * 1e3, n * 112.0 / (ms * 1e-3) / 1e9); fflush(stdout);
+    }
     // bf16 gradient + copy: n f32x4 groups of w, m, v; g and the copy reuse
     // the first halves of the g and b buffers (8 B per group of four).
     {
