@@ -236,3 +236,31 @@ def test_8bit_conversion_argument_errors(lib):
     # nothing to do: no pointer is needed and nothing is enqueued
     assert lib.adamw8_quantize(None, 0, 0, None, None, None) == 0
     assert lib.adamw8_dequantize(None, None, 0, 1, None, None) == 0
+
+
+def test_header_is_plain_c(tmp_path):
+    """The header compiles as C99 and C++17 on its own, with every warning,
+    and its entry points have the declared C types."""
+    src = tmp_path / "use.c"
+    src.write_text(
+        '#include "mps_adamw.h"\n'
+        "size_t (*f0)(const mps_tensor*, int) = adamw_workspace_bytes;\n"
+        "int (*f1)(const mps_tensor*, int, mps_dtype, double*, double, double, float*, void*,"
+        " size_t, void*) = grad_norm_sq;\n"
+        "int (*f2)(const double*, double, double, float*, void*) = clip_coef;\n"
+        "int (*f3)(const mps_tensor8*, int, mps_dtype, const float*, const double*, int32_t*,"
+        " double, double, double, double, double, void*, size_t, void*) = adamw8_multi_tensor_step;\n"
+        "int (*f4)(const float*, int64_t, mps_q8_format, uint8_t*, uint8_t*, void*) = adamw8_quantize;\n"
+        "const char* (*f5)(void) = adamw_last_error;\n"
+        "int main(void) { return sizeof(mps_tensor) == 48 && sizeof(mps_tensor8) == 64 &&"
+        " MPS_Q8_BLOCK == 32 ? 0 : 1; }\n")
+    inc = os.path.join(ROOT, "include")
+    for compiler, std in (("gcc", "-std=c99"), ("g++", "-std=c++17")):
+        args = [compiler, std, "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only",
+                "-I", inc, str(src)]
+        if compiler == "g++":
+            args[-1:] = ["-x", "c++", str(src)]
+        r = subprocess.run(args, capture_output=True, text=True)
+        assert r.returncode == 0, (compiler, r.stderr)
+    # the ctypes mirrors have the C layout
+    assert ctypes.sizeof(binding.MpsTensor) == 48 and ctypes.sizeof(binding.MpsTensor8) == 64
