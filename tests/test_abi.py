@@ -252,8 +252,9 @@ def test_header_is_plain_c(tmp_path):
         " double, double, double, double, double, void*, size_t, void*) = adamw8_multi_tensor_step;\n"
         "int (*f4)(const float*, int64_t, mps_q8_format, uint8_t*, uint8_t*, void*) = adamw8_quantize;\n"
         "const char* (*f5)(void) = adamw_last_error;\n"
-        "int main(void) { return sizeof(mps_tensor) == 48 && sizeof(mps_tensor8) == 64 &&"
-        " MPS_Q8_BLOCK == 32 ? 0 : 1; }\n")
+        "typedef char size_check[(sizeof(mps_tensor) == 48 && sizeof(mps_tensor8) == 64 &&"
+        " MPS_Q8_BLOCK == 32) ? 1 : -1];\n"
+        "int main(void) { return (int)sizeof(size_check) - 1; }\n")
     inc = os.path.join(ROOT, "include")
     for compiler, std in (("gcc", "-std=c99"), ("g++", "-std=c++17")):
         args = [compiler, std, "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only",
