@@ -228,12 +228,22 @@ __device__ __forceinline__ void adamw8_elements(const TensorEntry* te, const Qua
     }
 }
 
-// Whole runs [e0, e0 + 8 * ngroups) of one tensor (ngroups a multiple of 4),
-// every stream aligned for its vector width there.  Thread q of a tile takes
-// elements 8q .. 8q+7.
+// Scale bytes of one body are collected in LDS (a run's quad leader writes
+// its byte) and stored after the body's last tile by consecutive threads, so
+// each wavefront writes 64 contiguous bytes per moment instead of 16-byte
+// pieces.  Two buffers alternate between consecutive bodies of a block: the
+// barrier that ends one body also separates the readers of a buffer from the
+// writers of the body after next.
+constexpr int kMaxRunsPerBody = MPS_CHUNK_MAX / kQuantBlock;
+
+// Whole runs [e0, e0 + 8 * ngroups) of one tensor (ngroups a multiple of 4,
+// at most one chunk), every stream aligned for its vector width there.
+// Thread q of a tile takes elements 8q .. 8q+7.  `lds_m` and `lds_v` hold
+// kMaxRunsPerBody bytes each.
 template <bool kBf16>
 __device__ __forceinline__ void adamw8_body(const TensorEntry* te, const QuantEntry* qe, int64_t e0,
-                                            int ngroups, const StepScalars& s)
+                                            int ngroups, const StepScalars& s, uint8_t* lds_m,
+                                            uint8_t* lds_v)
 {
     const int tid = threadIdx.x;
     const uint32_t ng = static_cast<uint32_t>(ngroups);
@@ -316,9 +326,9 @@ __device__ __forceinline__ void adamw8_body(const TensorEntry* te, const QuantEn
             for (int k = 0; k < 4; ++k) packed[k] = bf16_pack2(w[2 * k], w[2 * k + 1]);
             store8_u32x4(packed, P, q * 16u);
         }
-        if ((tid & 3) == 0) {
-            store_byte(mb, MS, q / 4u);
-            store_byte(vb, VS, q / 4u);
+        if ((tid & 3) == 0 && q < ng) {
+            lds_m[q / 4u] = static_cast<uint8_t>(mb);
+            lds_v[q / 4u] = static_cast<uint8_t>(vb);
         }
     };
 
@@ -333,6 +343,11 @@ __device__ __forceinline__ void adamw8_body(const TensorEntry* te, const QuantEn
         __builtin_amdgcn_sched_barrier(0);
         update_tile(b, base + kBlock);
     }
+    __syncthreads();
+    for (uint32_t r = tid; r < ng / 4u; r += kBlock) {
+        store_byte(lds_m[r], MS, r);
+        store_byte(lds_v[r], VS, r);
+    }
 }
 
 // Chunks b, b + G, ... of this block, as in the fp32 kernel (the next
@@ -345,6 +360,8 @@ __device__ __forceinline__ void update8_chunks(const TensorEntry* __restrict__ t
                                                const uint32_t* __restrict__ chunk_map, int n_chunks,
                                                int64_t chunk_elems, const StepScalars& s)
 {
+    __shared__ uint8_t scale_lds[2][2][kMaxRunsPerBody];
+    int parity = 0;
     TensorEntry next{};
     QuantEntry next_q{};
     if (static_cast<int>(blockIdx.x) < n_chunks) {
@@ -368,7 +385,11 @@ __device__ __forceinline__ void update8_chunks(const TensorEntry* __restrict__ t
         }
         const int64_t whole = te.numel - te.numel % kQuantBlock;
         const int64_t vend = max(begin, min(end, whole));
-        if (vend > begin) adamw8_body<kBf16>(&te, &qe, begin, static_cast<int>((vend - begin) / 8), s);
+        if (vend > begin) {
+            adamw8_body<kBf16>(&te, &qe, begin, static_cast<int>((vend - begin) / 8), s,
+                               scale_lds[parity][0], scale_lds[parity][1]);
+            parity ^= 1;
+        }
         if (end > vend) adamw8_elements<kBf16>(&te, &qe, vend, end, s);
     }
 }
