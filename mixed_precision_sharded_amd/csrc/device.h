@@ -29,7 +29,7 @@
 #define MPS_NORM_POLICY 0   // norm before the fp32 update: gradient (read again by the update)
 #endif
 #ifndef MPS_Q8_NORM_POLICY
-#define MPS_Q8_NORM_POLICY 2  // norm before the 8-bit update
+#define MPS_Q8_NORM_POLICY 0  // norm before the 8-bit update
 #endif
 
 

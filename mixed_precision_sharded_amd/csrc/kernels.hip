@@ -469,10 +469,9 @@ hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid, d
                             double max_norm, double grad_scale, float* d_coef, hipStream_t stream,
                             NormBefore next)
 {
-    // The gradient cache policy that suits the update that follows: the fp32
-    // update re-reads the gradients soon after and benefits from the ones the
-    // norm left in the caches; the 8-bit update streams its own data through
-    // the caches, so there the norm reads nontemporally (measured on MI355X).
+    // The gradient cache policy can be chosen per following update (both
+    // updates re-read the gradients soon after and, measured on MI355X,
+    // benefit from the ones a default-policy norm leaves in the caches).
     if (next == NormBefore::kQ8Update) {
         grad_norm_launch<kQ8NormPolicy>(ws, grad_bf16, grid, d_sumsq, max_norm, grad_scale, d_coef,
                                         stream);

@@ -9,10 +9,11 @@
 // it under the format's largest code, and re-encodes with the hardware's
 // round-to-nearest-even conversions.
 //
-//   adamw8_step_kernel  the update.  A thread takes eight consecutive
-//                       elements, so the four lanes of a quad hold one run of
-//                       32 and its largest magnitude is two DPP exchanges
-//                       away.  Streams per element: master 4 B in and out,
+//   adamw8_step_kernel  the update.  A thread takes four consecutive
+//                       elements, so eight lanes hold one run of 32 and its
+//                       largest magnitude is three DPP exchanges away, and
+//                       every access of an instruction is contiguous across
+//                       the wavefront.  Streams per element: master 4 B in and out,
 //                       codes 1 + 1 B in and out, gradient 2 or 4 B in, bf16
 //                       copy 2 B out, scales 2 B per 32 elements each way.
 //   quantize_kernel /   conversion between fp32 moments and the 8-bit
@@ -29,16 +30,16 @@
 // Cache policies of the 8-bit update's streams (aux operand: 0 default,
 // 2 nontemporal).
 #ifndef MPS_Q8_W_POLICY
-#define MPS_Q8_W_POLICY 0       // master and gradient loads
+#define MPS_Q8_W_POLICY 2       // master and gradient loads
 #endif
 #ifndef MPS_Q8_CODE_POLICY
 #define MPS_Q8_CODE_POLICY 2    // code loads
 #endif
 #ifndef MPS_Q8_SCALE_POLICY
-#define MPS_Q8_SCALE_POLICY 0   // scale-byte loads
+#define MPS_Q8_SCALE_POLICY 2   // scale-byte loads
 #endif
 #ifndef MPS_Q8_STORE_POLICY
-#define MPS_Q8_STORE_POLICY 0   // every store
+#define MPS_Q8_STORE_POLICY 2   // every store
 #endif
 
 namespace mps {
@@ -95,19 +96,16 @@ __device__ __forceinline__ f32x2 decode_pair(uint32_t word)
                  : __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(word), kHigh);
 }
 
-// Eight codes (two words) to values times `scale`.
+// Four codes (one word) to values times `scale`.
 template <bool kE4M3>
-__device__ __forceinline__ void decode8(u32x2 codes, float scale, float (&out)[8])
+__device__ __forceinline__ void decode4(uint32_t codes, float scale, float (&out)[4])
 {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const f32x2 lo = decode_pair<kE4M3, false>(codes[h]);
-        const f32x2 hi = decode_pair<kE4M3, true>(codes[h]);
-        out[4 * h] = lo[0] * scale;
-        out[4 * h + 1] = lo[1] * scale;
-        out[4 * h + 2] = hi[0] * scale;
-        out[4 * h + 3] = hi[1] * scale;
-    }
+    const f32x2 lo = decode_pair<kE4M3, false>(codes);
+    const f32x2 hi = decode_pair<kE4M3, true>(codes);
+    out[0] = lo[0] * scale;
+    out[1] = lo[1] * scale;
+    out[2] = hi[0] * scale;
+    out[3] = hi[1] * scale;
 }
 
 // Round a and b to codes (nearest, ties to even) into the low (kHigh false)
@@ -119,20 +117,15 @@ __device__ __forceinline__ uint32_t encode_pair(float a, float b, uint32_t old)
                                        : __builtin_amdgcn_cvt_pk_bf8_f32(a, b, static_cast<int>(old), kHigh));
 }
 
-// Eight values to codes at the run's scale byte (all 0xFF for a
-// non-finite run).
+// Four values to codes at the run's scale byte (all 0xFF for a non-finite
+// run).
 template <bool kE4M3>
-__device__ __forceinline__ u32x2 encode8(const float (&x)[8], uint32_t byte)
+__device__ __forceinline__ uint32_t encode4(const float (&x)[4], uint32_t byte)
 {
     const float inv = inverse_scale(byte);
-    u32x2 out;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint32_t word = encode_pair<kE4M3, false>(x[4 * h] * inv, x[4 * h + 1] * inv, 0u);
-        word = encode_pair<kE4M3, true>(x[4 * h + 2] * inv, x[4 * h + 3] * inv, word);
-        out[h] = byte == kNonFinite ? 0xffffffffu : word;
-    }
-    return out;
+    uint32_t word = encode_pair<kE4M3, false>(x[0] * inv, x[1] * inv, 0u);
+    word = encode_pair<kE4M3, true>(x[2] * inv, x[3] * inv, word);
+    return byte == kNonFinite ? 0xffffffffu : word;
 }
 
 template <bool kE4M3>
@@ -148,13 +141,17 @@ __device__ __forceinline__ float decode1(uint32_t code, float scale)
     return decode_pair<kE4M3, false>(code)[0] * scale;
 }
 
-// Largest of the four lanes of this quad (lanes 4k .. 4k+3).
-__device__ __forceinline__ uint32_t quad_max(uint32_t x)
+// Largest over the eight lanes 8k .. 8k+7 (one run of 32 elements): two
+// exchanges within each quad, then the half-row mirror (lane i with lane
+// 7 - i of the eight), which meets the other quad.
+__device__ __forceinline__ uint32_t run_max(uint32_t x)
 {
-    constexpr int kQuadSwap1 = 0xb1;  // quad_perm [1,0,3,2]
-    constexpr int kQuadSwap2 = 0x4e;  // quad_perm [2,3,0,1]
+    constexpr int kQuadSwap1 = 0xb1;   // quad_perm [1,0,3,2]
+    constexpr int kQuadSwap2 = 0x4e;   // quad_perm [2,3,0,1]
+    constexpr int kHalfMirror = 0x141; // row_half_mirror
     x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kQuadSwap1, 0xf, 0xf, false)));
     x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kQuadSwap2, 0xf, 0xf, false)));
+    x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kHalfMirror, 0xf, 0xf, false)));
     return x;
 }
 
@@ -178,6 +175,12 @@ __device__ __forceinline__ u32x2 load_u32x2_policy(__amdgpu_buffer_rsrc_t r, uin
     return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kAux);
 }
 
+template <int kAux>
+__device__ __forceinline__ uint32_t load_u32(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kAux);
+}
+
 __device__ __forceinline__ void store_byte(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(v), r, off, 0, kQ8StorePolicy);
@@ -191,6 +194,11 @@ __device__ __forceinline__ void store8_u32x2(u32x2 v, __amdgpu_buffer_rsrc_t r, 
 __device__ __forceinline__ void store8_u32x4(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kQ8StorePolicy);
+}
+
+__device__ __forceinline__ void store8_u32(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kQ8StorePolicy);
 }
 
 // ---------------------------------------------------------------- update ---
@@ -236,10 +244,11 @@ __device__ __forceinline__ void adamw8_elements(const TensorEntry* te, const Qua
 // writers of the body after next.
 constexpr int kMaxRunsPerBody = MPS_CHUNK_MAX / kQuantBlock;
 
-// Whole runs [e0, e0 + 8 * ngroups) of one tensor (ngroups a multiple of 4,
+// Whole runs [e0, e0 + 4 * ngroups) of one tensor (ngroups a multiple of 8,
 // at most one chunk), every stream aligned for its vector width there.
-// Thread q of a tile takes elements 8q .. 8q+7.  `lds_m` and `lds_v` hold
-// kMaxRunsPerBody bytes each.
+// Thread q of a tile takes elements 4q .. 4q+3, so eight consecutive lanes
+// hold one run of 32 and every load and store of a tile is contiguous across
+// the wavefront.  `lds_m` and `lds_v` hold kMaxRunsPerBody bytes each.
 template <bool kBf16>
 __device__ __forceinline__ void adamw8_body(const TensorEntry* te, const QuantEntry* qe, int64_t e0,
                                             int ngroups, const StepScalars& s, uint8_t* lds_m,
@@ -247,88 +256,72 @@ __device__ __forceinline__ void adamw8_body(const TensorEntry* te, const QuantEn
 {
     const int tid = threadIdx.x;
     const uint32_t ng = static_cast<uint32_t>(ngroups);
-    const __amdgpu_buffer_rsrc_t W = rsrc(te->master + e0, ng * 32u);
+    const __amdgpu_buffer_rsrc_t W = rsrc(te->master + e0, ng * 16u);
     const __amdgpu_buffer_rsrc_t G = rsrc(static_cast<const char*>(te->grad) + e0 * (kBf16 ? 2 : 4),
-                                          ng * (kBf16 ? 16u : 32u));
+                                          ng * (kBf16 ? 8u : 16u));
     const bool copy = te->param_bf16 != nullptr;
-    const __amdgpu_buffer_rsrc_t P = rsrc(copy ? te->param_bf16 + e0 : nullptr, copy ? ng * 16u : 0u);
-    const __amdgpu_buffer_rsrc_t MQ = rsrc(qe->m_codes + e0, ng * 8u);
-    const __amdgpu_buffer_rsrc_t VQ = rsrc(qe->v_codes + e0, ng * 8u);
-    const __amdgpu_buffer_rsrc_t MS = rsrc(qe->m_scales + e0 / kQuantBlock, ng / 4u);
-    const __amdgpu_buffer_rsrc_t VS = rsrc(qe->v_scales + e0 / kQuantBlock, ng / 4u);
+    const __amdgpu_buffer_rsrc_t P = rsrc(copy ? te->param_bf16 + e0 : nullptr, copy ? ng * 8u : 0u);
+    const __amdgpu_buffer_rsrc_t MQ = rsrc(qe->m_codes + e0, ng * 4u);
+    const __amdgpu_buffer_rsrc_t VQ = rsrc(qe->v_codes + e0, ng * 4u);
+    const __amdgpu_buffer_rsrc_t MS = rsrc(qe->m_scales + e0 / kQuantBlock, ng / 8u);
+    const __amdgpu_buffer_rsrc_t VS = rsrc(qe->v_scales + e0 / kQuantBlock, ng / 8u);
 
     // Two tiles are held in registers in turn, as in the fp32 kernel: the
     // next tile's loads are in flight while this one is computed.  Groups past
-    // the end read zeros and their stores are dropped; a quad is either wholly
-    // inside or wholly past the end.
+    // the end read zeros and their stores are dropped; the eight lanes of a
+    // run are either all inside or all past the end.
     struct Tile {
-        f32x4 w[2];
-        u32x4 g[2];  // bf16: g[0] holds the eight gradients; fp32: both
-        u32x2 mq, vq;
-        uint32_t ms, vs;
+        f32x4 w;
+        u32x4 g;  // bf16: g[0..1] hold the four gradients; fp32: all four
+        uint32_t mq, vq, ms, vs;
     };
     auto load_tile = [&](Tile& t, int base) {
         const uint32_t q = base + tid;
-        t.w[0] = __builtin_bit_cast(f32x4, load_u32x4<kQ8WPolicy>(W, q * 32u));
-        t.w[1] = __builtin_bit_cast(f32x4, load_u32x4<kQ8WPolicy>(W, q * 32u + 16u));
+        t.w = __builtin_bit_cast(f32x4, load_u32x4<kQ8WPolicy>(W, q * 16u));
         if (kBf16) {
-            t.g[0] = load_u32x4<kQ8WPolicy>(G, q * 16u);
+            const u32x2 h = load_u32x2_policy<kQ8WPolicy>(G, q * 8u);
+            t.g = u32x4{h[0], h[1], 0u, 0u};
         } else {
-            t.g[0] = load_u32x4<kQ8WPolicy>(G, q * 32u);
-            t.g[1] = load_u32x4<kQ8WPolicy>(G, q * 32u + 16u);
+            t.g = load_u32x4<kQ8WPolicy>(G, q * 16u);
         }
-        t.mq = load_u32x2_policy<kQ8CodePolicy>(MQ, q * 8u);
-        t.vq = load_u32x2_policy<kQ8CodePolicy>(VQ, q * 8u);
-        t.ms = load_byte<kQ8ScalePolicy>(MS, q / 4u);
-        t.vs = load_byte<kQ8ScalePolicy>(VS, q / 4u);
+        t.mq = load_u32<kQ8CodePolicy>(MQ, q * 4u);
+        t.vq = load_u32<kQ8CodePolicy>(VQ, q * 4u);
+        t.ms = load_byte<kQ8ScalePolicy>(MS, q / 8u);
+        t.vs = load_byte<kQ8ScalePolicy>(VS, q / 8u);
     };
     auto update_tile = [&](Tile& t, int base) {
         const uint32_t q = base + tid;
-        float w[8], m[8], v[8], g[8];
+        float w[4], m[4], v[4], g[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            w[k] = t.w[0][k];
-            w[4 + k] = t.w[1][k];
-        }
+        for (int k = 0; k < 4; ++k) w[k] = t.w[k];
         if (kBf16) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                g[2 * k] = bf16_lo(t.g[0][k]);
-                g[2 * k + 1] = bf16_hi(t.g[0][k]);
-            }
+            g[0] = bf16_lo(t.g[0]);
+            g[1] = bf16_hi(t.g[0]);
+            g[2] = bf16_lo(t.g[1]);
+            g[3] = bf16_hi(t.g[1]);
         } else {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                g[k] = __uint_as_float(t.g[0][k]);
-                g[4 + k] = __uint_as_float(t.g[1][k]);
-            }
+            for (int k = 0; k < 4; ++k) g[k] = __uint_as_float(t.g[k]);
         }
-        decode8<true>(t.mq, scale_value(t.ms), m);
-        decode8<false>(t.vq, scale_value(t.vs), v);
+        decode4<true>(t.mq, scale_value(t.ms), m);
+        decode4<false>(t.vq, scale_value(t.vs), v);
         uint32_t am = 0, av = 0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < 4; ++k) {
             adamw_element(w[k], m[k], v[k], g[k], s);
             am = max(am, abs_bits(m[k]));
             av = max(av, abs_bits(v[k]));
         }
-        const uint32_t mb = scale_byte<kE4M3TopExp>(quad_max(am));
-        const uint32_t vb = scale_byte<kE5M2TopExp>(quad_max(av));
+        const uint32_t mb = scale_byte<kE4M3TopExp>(run_max(am));
+        const uint32_t vb = scale_byte<kE5M2TopExp>(run_max(av));
         store8_u32x4(u32x4{__float_as_uint(w[0]), __float_as_uint(w[1]), __float_as_uint(w[2]),
-                           __float_as_uint(w[3])}, W, q * 32u);
-        store8_u32x4(u32x4{__float_as_uint(w[4]), __float_as_uint(w[5]), __float_as_uint(w[6]),
-                           __float_as_uint(w[7])}, W, q * 32u + 16u);
-        store8_u32x2(encode8<true>(m, mb), MQ, q * 8u);
-        store8_u32x2(encode8<false>(v, vb), VQ, q * 8u);
-        if (copy) {
-            u32x4 packed;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) packed[k] = bf16_pack2(w[2 * k], w[2 * k + 1]);
-            store8_u32x4(packed, P, q * 16u);
-        }
-        if ((tid & 3) == 0 && q < ng) {
-            lds_m[q / 4u] = static_cast<uint8_t>(mb);
-            lds_v[q / 4u] = static_cast<uint8_t>(vb);
+                           __float_as_uint(w[3])}, W, q * 16u);
+        store8_u32(encode4<true>(m, mb), MQ, q * 4u);
+        store8_u32(encode4<false>(v, vb), VQ, q * 4u);
+        if (copy) store8_u32x2(u32x2{bf16_pack2(w[0], w[1]), bf16_pack2(w[2], w[3])}, P, q * 8u);
+        if ((tid & 7) == 0 && q < ng) {
+            lds_m[q / 8u] = static_cast<uint8_t>(mb);
+            lds_v[q / 8u] = static_cast<uint8_t>(vb);
         }
     };
 
@@ -344,7 +337,7 @@ __device__ __forceinline__ void adamw8_body(const TensorEntry* te, const QuantEn
         update_tile(b, base + kBlock);
     }
     __syncthreads();
-    for (uint32_t r = tid; r < ng / 4u; r += kBlock) {
+    for (uint32_t r = tid; r < ng / 8u; r += kBlock) {
         store_byte(lds_m[r], MS, r);
         store_byte(lds_v[r], VS, r);
     }
@@ -386,7 +379,7 @@ __device__ __forceinline__ void update8_chunks(const TensorEntry* __restrict__ t
         const int64_t whole = te.numel - te.numel % kQuantBlock;
         const int64_t vend = max(begin, min(end, whole));
         if (vend > begin) {
-            adamw8_body<kBf16>(&te, &qe, begin, static_cast<int>((vend - begin) / 8), s,
+            adamw8_body<kBf16>(&te, &qe, begin, static_cast<int>((vend - begin) / 4), s,
                                scale_lds[parity][0], scale_lds[parity][1]);
             parity ^= 1;
         }

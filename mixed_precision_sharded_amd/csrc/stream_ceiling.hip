@@ -155,6 +155,33 @@ __global__ __launch_bounds__(256) void adam_q8_octets(f4* __restrict__ w, const 
   }
 }
 
+// The 8-bit-moment streams with four elements per lane: fp32 w in and out
+// (16 B), bf16 g in and bf16 copy out (8 B), m and v codes (4 B each), a
+// scale byte per 32 elements (eight lanes) per moment.  Every access of one
+// instruction is contiguous across the wavefront.
+template <bool NT>
+__global__ __launch_bounds__(256) void adam_q8_quads(f4* __restrict__ w, const u2* __restrict__ g, u2* __restrict__ p,
+                                                     unsigned* __restrict__ mq, unsigned* __restrict__ vq,
+                                                     unsigned char* __restrict__ ms, unsigned char* __restrict__ vs, long n4) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+    f4 W = NT ? __builtin_nontemporal_load(&w[i]) : w[i];
+    u2 G = NT ? __builtin_nontemporal_load(&g[i]) : g[i];
+    unsigned M = NT ? __builtin_nontemporal_load(&mq[i]) : mq[i];
+    unsigned V = NT ? __builtin_nontemporal_load(&vq[i]) : vq[i];
+    unsigned sm = ms[i / 8], sv = vs[i / 8];
+    f4 gf = f4{__uint_as_float(G[0] << 16), __uint_as_float(G[0] & 0xffff0000u), __uint_as_float(G[1] << 16), __uint_as_float(G[1] & 0xffff0000u)};
+    f4 ww = W - gf * 0.001f;
+    unsigned M2 = M ^ (sm * 0x01010101u), V2 = V ^ (sv * 0x01010101u);
+    u2 P = u2{(__float_as_uint(ww[0]) >> 16) | (__float_as_uint(ww[1]) & 0xffff0000u), (__float_as_uint(ww[2]) >> 16) | (__float_as_uint(ww[3]) & 0xffff0000u)};
+    if (NT) {
+      __builtin_nontemporal_store(ww, &w[i]); __builtin_nontemporal_store(M2, &mq[i]); __builtin_nontemporal_store(V2, &vq[i]); __builtin_nontemporal_store(P, &p[i]);
+    } else {
+      w[i] = ww; mq[i] = M2; vq[i] = V2; p[i] = P;
+    }
+    if ((threadIdx.x & 7) == 0) { ms[i / 8] = (unsigned char)(sm + 1); vs[i / 8] = (unsigned char)(sv + 1); }
+  }
+}
+
 // The same bytes with the codes of m and v interleaved per eight elements
 // (16 B per thread, one load and one store) and the two scale bytes of a run
 // side by side (2 B per 32 elements): four read and four write streams.
@@ -253,6 +280,12 @@ int main(int argc, char** argv) {
       };
       ms = time_ms(launch2, reps);
       printf("%-10s NT=%d blocks/CU=%2d  %8.1f us  %7.0f GB/s\n", "q8_interl", nt, bpc, ms * 1e3, n * 4 * 16.125 / (ms * 1e-3) / 1e9); fflush(stdout);
+      auto launch3 = [&]{
+        if (nt) adam_q8_quads<true><<<grid, 256>>>(w, (const u2*)g, (u2*)b, (unsigned*)mb, (unsigned*)vb, mb + 4 * n, vb + 4 * n, n);
+        else adam_q8_quads<false><<<grid, 256>>>(w, (const u2*)g, (u2*)b, (unsigned*)mb, (unsigned*)vb, mb + 4 * n, vb + 4 * n, n);
+      };
+      ms = time_ms(launch3, reps);
+      printf("%-10s NT=%d blocks/CU=%2d  %8.1f us  %7.0f GB/s\n", "q8_quads", nt, bpc, ms * 1e3, n * 4 * 16.125 / (ms * 1e-3) / 1e9); fflush(stdout);
     }
   }
   return 0;
