@@ -97,6 +97,25 @@ __global__ __launch_bounds__(256) void adam_bf16_quads(f4* __restrict__ w, f4* _
   }
 }
 
+// bf16_quads with the library's work split: block b walks chunks b, b + G,
+// ... of `kChunk` groups of four, each chunk streamed front to back.
+template <int kChunk>
+__global__ __launch_bounds__(256) void adam_bf16_quads_chunked(f4* __restrict__ w, f4* __restrict__ m, f4* __restrict__ v,
+                                                               const u2* __restrict__ g, u2* __restrict__ p, long n) {
+  const long n_chunks = (n + kChunk - 1) / kChunk;
+  for (long c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+    const long end = c * kChunk + kChunk < n ? c * kChunk + kChunk : n;
+    for (long i = c * kChunk + threadIdx.x; i < end; i += 256) {
+      f4 W = __builtin_nontemporal_load(&w[i]), M = __builtin_nontemporal_load(&m[i]), V = __builtin_nontemporal_load(&v[i]);
+      u2 G = __builtin_nontemporal_load(&g[i]);
+      f4 gf = f4{__uint_as_float(G[0] << 16), __uint_as_float(G[0] & 0xffff0000u), __uint_as_float(G[1] << 16), __uint_as_float(G[1] & 0xffff0000u)};
+      f4 mm = M * 0.9f + gf * 0.1f; f4 vv = V * 0.95f + gf * gf * 0.05f; f4 ww = W - mm * 0.001f;
+      u2 P = u2{(__float_as_uint(ww[0]) >> 16) | (__float_as_uint(ww[1]) & 0xffff0000u), (__float_as_uint(ww[2]) >> 16) | (__float_as_uint(ww[3]) & 0xffff0000u)};
+      __builtin_nontemporal_store(ww, &w[i]); __builtin_nontemporal_store(mm, &m[i]); __builtin_nontemporal_store(vv, &v[i]); __builtin_nontemporal_store(P, &p[i]);
+    }
+  }
+}
+
 // Same streams, eight elements per lane: bf16 g and copy as 16 B accesses,
 // fp32 w, m, v as two 16 B accesses each (lanes 32 B apart).
 template <bool NT>
@@ -260,6 +279,10 @@ int main(int argc, char** argv) {
     {
       float ms = time_ms([&]{ adam_bf16_quads<true><<<grid, 256>>>(w, m, v, (const u2*)g, (u2*)b, n); }, reps);
       printf("%-10s NT=1 blocks/CU=%2d  %8.1f us  %7.0f GB/s\n", "bf16_quads", bpc, ms * 1e3, n * 4 * 30.0 / (ms * 1e-3) / 1e9); fflush(stdout);
+      ms = time_ms([&]{ adam_bf16_quads_chunked<512><<<grid, 256>>>(w, m, v, (const u2*)g, (u2*)b, n); }, reps);
+      printf("%-10s NT=1 blocks/CU=%2d  %8.1f us  %7.0f GB/s\n", "bf16_ch2k", bpc, ms * 1e3, n * 4 * 30.0 / (ms * 1e-3) / 1e9); fflush(stdout);
+      ms = time_ms([&]{ adam_bf16_quads_chunked<4096><<<grid, 256>>>(w, m, v, (const u2*)g, (u2*)b, n); }, reps);
+      printf("%-10s NT=1 blocks/CU=%2d  %8.1f us  %7.0f GB/s\n", "bf16_ch16k", bpc, ms * 1e3, n * 4 * 30.0 / (ms * 1e-3) / 1e9); fflush(stdout);
       ms = time_ms([&]{ adam_bf16_octets<true><<<grid, 256>>>(w, m, v, (const u4*)g, (u4*)b, n / 2); }, reps);
       printf("%-10s NT=1 blocks/CU=%2d  %8.1f us  %7.0f GB/s\n", "bf16_octets", bpc, ms * 1e3, n * 4 * 30.0 / (ms * 1e-3) / 1e9); fflush(stdout);
     }
