@@ -39,7 +39,11 @@
  *     caller's next synchronization, as with any HIP launch.
  *   - Buffers of different tensors, and master / exp_avg / exp_avg_sq /
  *     grad / param_bf16 of one tensor, must not overlap.
- *   - Concurrent calls must use distinct workspaces.
+ *   - Concurrent calls must use distinct workspaces, and calls that share a
+ *     workspace must be ordered on the device (one stream, or streams the
+ *     caller orders with events): a call may upload new tables into it.
+ *     Calls from several host threads are safe (the library's host state is
+ *     locked).
  *   - Graph capture: once a list's tables are in a workspace (after any
  *     call with that list and workspace, e.g. the norm, which changes no
  *     state), the calls enqueue kernel launches only and may be recorded in

@@ -123,3 +123,41 @@ def test_two_lists_on_two_streams(q8):
     same(seq_b.state(), con_b.state(), "list b")
     for r in (seq_a, seq_b, con_a, con_b):
         r.tl.release()
+
+
+def test_host_threads_with_their_own_workspaces():
+    """Three host threads, each with its own list, workspace and stream,
+    stepping at once (the binding's calls release the interpreter lock):
+    every list ends bitwise where a sequential run ends."""
+    import threading
+    say("three host threads")
+    bases = [inputs([50000 + 17 * k, 4096], 70 + k) for k in range(3)]
+    seq = [Runner(clone(b), False) for b in bases]
+    for r in seq:
+        for _ in range(4):
+            r.norm(); r.update()
+    con = [Runner(clone(b), False) for b in bases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in con]
+    errors = []
+
+    def work(r, st):
+        try:
+            with torch.cuda.stream(st):
+                for _ in range(4):
+                    r.norm(st); r.update(st)
+            st.synchronize()
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(r, st)) for r, st in zip(con, streams)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for k, (a, b) in enumerate(zip(seq, con)):
+        same(a.state(), b.state(), f"thread {k}")
+    for r in seq + con:
+        r.tl.release()
