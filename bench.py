@@ -50,15 +50,21 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="host time budget of the oracle baseline (0 = skip)")
     p.add_argument("--no-kernel-events", action="store_true")
-    p.add_argument("--fused", action="store_true",
-                   help="time the single-launch step (adamw_fused_step) instead of the "
-                        "two launches (grad_norm_sq with the clip output, then the update)")
+    p.add_argument("--launches", choices=("separate", "clipped", "fused"), default="separate",
+                   help="separate: grad_norm_sq with the clip output, then "
+                        "adamw_multi_tensor_step; clipped: adamw_clipped_step (the norm's "
+                        "partials finished inside the update); fused: adamw_fused_step "
+                        "(one cooperative launch)")
+    p.add_argument("--fused", action="store_true", help="same as --launches fused")
     p.add_argument("--state8", action="store_true",
                    help="8-bit moment state (m: E4M3, v: E5M2, a scale byte per 32 elements)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="after the measurement, run 5 plain device copies of this many MiB "
                         "(known bytes, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
-    return p.parse_args()
+    args = p.parse_args()
+    if args.fused:
+        args.launches = "fused"
+    return args
 
 
 def kernel_source_digest(kernel):
@@ -104,8 +110,8 @@ def main():
     w = WORKLOADS[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.state8 and args.fused:
-        print("--state8 has no single-launch form", file=sys.stderr)
+    if args.state8 and args.launches != "separate":
+        print("--state8 runs as two separate calls only", file=sys.stderr)
         sys.exit(2)
     log(f"workload {w.cfg} {w.name}: {w.numel:,} params in {w.n_tensors} tensors, "
         f"{'bf16' if w.grad_bf16 else 'fp32'} grads, copy={w.copy_bf16}, rotate={args.rotate}, "
@@ -138,9 +144,17 @@ def main():
     def one_step(tl, ev=None):
         if ev is not None:
             ev[0].record()
-        if args.fused:
+        if args.launches == "fused":
             binding.adamw_fused_step(tl, step, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay,
                                      w.max_norm, sumsq_out=sumsq, coef_out=coef)
+            if ev is not None:
+                ev[1].record()
+                ev[2].record()
+            return
+        if args.launches == "clipped":
+            # Two launches inside one call: the events bracket the call.
+            binding.adamw_clipped_step(tl, step, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay,
+                                       w.max_norm, sumsq_out=sumsq, coef_out=coef)
             if ev is not None:
                 ev[1].record()
                 ev[2].record()
@@ -194,8 +208,10 @@ def main():
         per_step = sorted(e[0].elapsed_time(e[2]) * 1e3 for e in evs)
         spread = {f"p{q}": round(per_step[min(len(per_step) - 1, int(q / 100 * len(per_step)))], 2)
                   for q in (10, 50, 90)}
-        if args.fused:
+        if args.launches == "fused":
             kern_us = {"adamw_fused_step": norm_ms * 1e3}
+        elif args.launches == "clipped":
+            kern_us = {"adamw_clipped_step": norm_ms * 1e3}
         elif args.state8:
             kern_us = {"adamw8_grad_norm_sq+clip": norm_ms * 1e3,
                        "adamw8_multi_tensor_step": upd_ms * 1e3}
@@ -212,8 +228,11 @@ def main():
 
     roofline = None
     if kern_us is not None:
-        if args.fused:  # one kernel does the whole step
+        if args.launches == "fused":  # one kernel does the whole step
             name, launch_bytes, us = "adamw_fused_kernel", step_bytes, kern_us["adamw_fused_step"]
+        elif args.launches == "clipped":  # both launches of the call, all of the step's bytes
+            name, launch_bytes = "adamw_clipped_step", step_bytes
+            us = kern_us["adamw_clipped_step"]
         elif args.state8:
             name, launch_bytes = "adamw8_step_kernel", w.update8_bytes_per_param() * n
             us = kern_us["adamw8_multi_tensor_step"]
@@ -224,7 +243,8 @@ def main():
         roofline = {"bound": "hbm", "kernel": name,
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": None if args.fused else stored_traffic(name, w.name),
+                    "traffic": (stored_traffic(name, w.name) if name in KERNEL_SOURCES
+                                else None),
                     "algorithmic_bytes_per_launch": launch_bytes,
                     "avg_launch_us": round(us, 2)}
         log(f"kernels (us): " + ", ".join(f"{k} {v:.1f}" for k, v in kern_us.items()))
@@ -261,7 +281,7 @@ def main():
                    "grad_dtype": "bf16" if w.grad_bf16 else "f32", "bf16_copy": w.copy_bf16,
                    "step": w.step, "algorithmic_bytes_per_param": bytes_per_param,
                    "moments": "8-bit (m E4M3, v E5M2, scale byte per 32)" if args.state8 else "f32",
-                   "buffer_sets": args.rotate, "launches": "fused" if args.fused else "two",
+                   "buffer_sets": args.rotate, "launches": args.launches,
                    "parallelism": "one GPU's shard"},
         "step_gbps": round(step_gbps, 1),
         "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),

@@ -200,6 +200,37 @@ int adamw_multi_tensor_step(const mps_tensor* tensors, int n_tensors,
                             size_t workspace_bytes, void* stream);
 
 /*
+ * adamw_clipped_step — the whole step (sum of squares, clip coefficient with
+ * grad_scale folded in, optional skip on non-finite gradients, update of
+ * every tensor, counter) in two plain launches; the fastest way to run it.
+ * Results are bitwise those of grad_norm_sq(..., d_coef) followed by
+ * adamw_multi_tensor_step with that coefficient (and d_sumsq as the skip
+ * value when skip_if_nonfinite is set): the same norm blocks, the same
+ * summation order, the same per-element arithmetic (the norm and the update
+ * follow the same pages as those two calls).
+ *
+ * The first launch leaves one partial sum per block in the workspace; the
+ * update launch finishes the sum in every block (all blocks add the partials
+ * in the same order, so they agree on S), so no block of the norm waits for
+ * the others.
+ *
+ *   tensors, n_tensors, grad_dtype : as adamw_multi_tensor_step.
+ *   max_norm, grad_scale : finite, > 0 (grad_scale 1.0 for none).
+ *   skip_if_nonfinite : non-zero: if S is NaN or inf, no element is written
+ *                       and *d_step is left as it is.
+ *   d_sumsq, d_coef  : device double / float receiving S and the
+ *                      coefficient, or NULL.
+ *   d_step, lr, beta1, beta2, eps, weight_decay : as adamw_multi_tensor_step.
+ *   d_workspace, workspace_bytes : see adamw_workspace_bytes; the same
+ *                      workspace may serve all entry points.
+ */
+int adamw_clipped_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
+                       double max_norm, double grad_scale, int skip_if_nonfinite,
+                       double* d_sumsq, float* d_coef, int32_t* d_step, double lr,
+                       double beta1, double beta2, double eps, double weight_decay,
+                       void* d_workspace, size_t workspace_bytes, void* stream);
+
+/*
  * adamw_fused_step — the whole step in ONE launch: the sum of squares, the
  * clip coefficient (with grad_scale folded in, exactly as clip_coef), the
  * optional skip on non-finite gradients, and the update of every tensor,

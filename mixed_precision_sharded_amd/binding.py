@@ -81,11 +81,14 @@ def lib() -> ctypes.CDLL:
             ctypes.POINTER(MpsTensor), ctypes.c_int, ctypes.c_int, P, P, P,
             ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double,
             ctypes.c_double, P, ctypes.c_size_t, P]
-        L.adamw_fused_step.restype = ctypes.c_int
-        L.adamw_fused_step.argtypes = [
+        whole_step = [
             ctypes.POINTER(MpsTensor), ctypes.c_int, ctypes.c_int, ctypes.c_double,
             ctypes.c_double, ctypes.c_int, P, P, P, ctypes.c_double, ctypes.c_double,
             ctypes.c_double, ctypes.c_double, ctypes.c_double, P, ctypes.c_size_t, P]
+        L.adamw_clipped_step.restype = ctypes.c_int
+        L.adamw_clipped_step.argtypes = whole_step
+        L.adamw_fused_step.restype = ctypes.c_int
+        L.adamw_fused_step.argtypes = whole_step
         T8 = ctypes.POINTER(MpsTensor8)
         L.adamw8_workspace_bytes.restype = ctypes.c_size_t
         L.adamw8_workspace_bytes.argtypes = [T8, ctypes.c_int]
@@ -308,23 +311,42 @@ def adamw_multi_tensor_step(tl: TensorList, coef: Optional[torch.Tensor], step: 
         tl.workspace_bytes, _stream_handle(stream)), "adamw_multi_tensor_step")
 
 
-def adamw_fused_step(tl: TensorList, step: torch.Tensor, lr: float, beta1: float, beta2: float,
-                     eps: float, weight_decay: float, max_norm: float, grad_scale: float = 1.0,
-                     skip_if_nonfinite: bool = False, sumsq_out: Optional[torch.Tensor] = None,
-                     coef_out: Optional[torch.Tensor] = None,
-                     stream: Optional[torch.cuda.Stream] = None) -> None:
-    """Norm, clip and update in one launch (see adamw_fused_step in the header)."""
+def _whole_step(name: str, tl: TensorList, step: torch.Tensor, lr: float, beta1: float,
+                beta2: float, eps: float, weight_decay: float, max_norm: float, grad_scale: float,
+                skip_if_nonfinite: bool, sumsq_out: Optional[torch.Tensor],
+                coef_out: Optional[torch.Tensor], stream: Optional[torch.cuda.Stream]) -> None:
     if step.dtype != torch.int32 or step.device != tl.device:
         raise ValueError("step: int32 tensor on the list's device")
     if sumsq_out is not None and (sumsq_out.dtype != torch.float64 or sumsq_out.device != tl.device):
         raise ValueError("sumsq_out: float64 tensor on the list's device, or None")
     if coef_out is not None and (coef_out.dtype != torch.float32 or coef_out.device != tl.device):
         raise ValueError("coef_out: float32 tensor on the list's device, or None")
-    _check(lib().adamw_fused_step(
+    _check(getattr(lib(), name)(
         tl.array, tl.n, tl.grad_dtype, float(max_norm), float(grad_scale),
         1 if skip_if_nonfinite else 0, _ptr(sumsq_out), _ptr(coef_out), step.data_ptr(),
         float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), tl.workspace_ptr,
-        tl.workspace_bytes, _stream_handle(stream)), "adamw_fused_step")
+        tl.workspace_bytes, _stream_handle(stream)), name)
+
+
+def adamw_clipped_step(tl: TensorList, step: torch.Tensor, lr: float, beta1: float, beta2: float,
+                       eps: float, weight_decay: float, max_norm: float, grad_scale: float = 1.0,
+                       skip_if_nonfinite: bool = False, sumsq_out: Optional[torch.Tensor] = None,
+                       coef_out: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Norm, clip and update in two plain launches, the clip finished inside
+    the update (see adamw_clipped_step in the header)."""
+    _whole_step("adamw_clipped_step", tl, step, lr, beta1, beta2, eps, weight_decay, max_norm,
+                grad_scale, skip_if_nonfinite, sumsq_out, coef_out, stream)
+
+
+def adamw_fused_step(tl: TensorList, step: torch.Tensor, lr: float, beta1: float, beta2: float,
+                     eps: float, weight_decay: float, max_norm: float, grad_scale: float = 1.0,
+                     skip_if_nonfinite: bool = False, sumsq_out: Optional[torch.Tensor] = None,
+                     coef_out: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Norm, clip and update in one launch (see adamw_fused_step in the header)."""
+    _whole_step("adamw_fused_step", tl, step, lr, beta1, beta2, eps, weight_decay, max_norm,
+                grad_scale, skip_if_nonfinite, sumsq_out, coef_out, stream)
 
 
 # ------------------------------------------------------ 8-bit moment state ---

@@ -52,6 +52,7 @@ struct Plan {
     size_t partials_off = 0;
     size_t total_bytes = 0;
     int n_chunks = 0;
+    int solo_tensor = -1;   // the one tensor with elements, else -1
     int64_t chunk_elems = 0;
     uint64_t tag = 0;
 };
@@ -112,11 +113,23 @@ int layout_plan(std::vector<TensorEntry>& entries, const std::vector<mps::QuantE
         if (n_chunks > INT32_MAX) return fail(MPS_ERR_INVALID_ARGUMENT, "too many chunks");
     }
     plan.n_chunks = static_cast<int>(n_chunks);
+    plan.solo_tensor = -1;
+    for (int i = 0; i < n; ++i) {
+        if (entries[i].numel == 0) continue;
+        if (plan.solo_tensor >= 0) {
+            plan.solo_tensor = -1;
+            break;
+        }
+        plan.solo_tensor = i;
+    }
 
     plan.tensors_off = sizeof(WorkspaceHeader);
     plan.quant_off = plan.tensors_off + sizeof(TensorEntry) * static_cast<size_t>(n);
     plan.chunks_off = plan.quant_off + (quant ? sizeof(mps::QuantEntry) * static_cast<size_t>(n) : 0);
-    plan.partials_off = round_up(plan.chunks_off + sizeof(uint32_t) * n_chunks, 256);
+    // At least one chunk-map slot (zero for a list without elements), so
+    // that the kernels' first lookup is always in the table.
+    const int64_t map_slots = n_chunks > 0 ? n_chunks : 1;
+    plan.partials_off = round_up(plan.chunks_off + sizeof(uint32_t) * map_slots, 256);
     plan.total_bytes = plan.partials_off + sizeof(double) * mps::kPartials;
 
     plan.image.assign(plan.partials_off, 0);
@@ -310,6 +323,7 @@ mps::WorkspaceView view_of(void* ws, const Plan& plan)
     v.chunk_map = reinterpret_cast<const uint32_t*>(base + plan.chunks_off);
     v.partials = reinterpret_cast<double*>(base + plan.partials_off);
     v.n_chunks = plan.n_chunks;
+    v.solo_tensor = plan.solo_tensor;
     v.chunk_elems = plan.chunk_elems;
     v.tag = plan.tag;
     return v;
@@ -469,6 +483,35 @@ int adamw_fused_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dt
     e = mps::launch_fused_step(view_of(d_workspace, plan), bf16, grid, max_norm, grad_scale,
                                skip_if_nonfinite ? 1 : 0, d_sumsq, d_coef, d_step, hp, st);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "fused step launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int adamw_clipped_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
+                       double max_norm, double grad_scale, int skip_if_nonfinite, double* d_sumsq,
+                       float* d_coef, int32_t* d_step, double lr, double beta1, double beta2,
+                       double eps, double weight_decay, void* d_workspace, size_t workspace_bytes,
+                       void* stream)
+{
+    if (!d_step) return fail(MPS_ERR_INVALID_ARGUMENT, "d_step is NULL");
+    int rc = check_clip_arguments(max_norm, grad_scale);
+    if (!rc) rc = check_hyperparameters(lr, beta1, beta2, eps, weight_decay);
+    if (rc) return rc;
+    Plan plan;
+    if ((rc = build_plan(tensors, n_tensors, grad_dtype, true, plan))) return rc;
+    if ((rc = check_workspace(d_workspace, workspace_bytes, plan))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
+    const bool bf16 = grad_dtype == MPS_DTYPE_BF16;
+    const mps::WorkspaceView ws = view_of(d_workspace, plan);
+    // The same norm grid as grad_norm_sq, so the partials and S match it.
+    const int norm_grid = grid_for(plan.n_chunks, mps::kNormMaxBlocks);
+    hipError_t e = mps::launch_grad_norm_partials(ws, bf16, norm_grid, d_step, st);
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "grad_norm launch: %s", hipGetErrorString(e));
+    mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
+    const int grid = grid_for(plan.n_chunks, mps::kStepMaxBlocks);
+    e = mps::launch_clipped_step(ws, bf16, grid, norm_grid, max_norm, grad_scale,
+                                 skip_if_nonfinite ? 1 : 0, d_sumsq, d_coef, d_step, hp, st);
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "clipped step launch: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -132,9 +132,9 @@ __device__ __forceinline__ double wave_sum(double x)
     return x;
 }
 
-// Sum over the block in a fixed order; the result is valid in thread 0.
-// `lds` holds one double per wavefront.  Ends with a barrier so that `lds`
-// may be reused right away.
+// Sum over the block in a fixed order, returned to every thread (each
+// computes the same bits).  `lds` holds one double per wavefront.  Ends with
+// a barrier so that `lds` may be reused right away.
 __device__ __forceinline__ double block_sum(double x, double* lds)
 {
     x = wave_sum(x);
@@ -143,9 +143,7 @@ __device__ __forceinline__ double block_sum(double x, double* lds)
     if (lane == 0) lds[wave] = x;
     __syncthreads();
     double r = 0.0;
-    if (threadIdx.x == 0) {
-        for (int w = 0; w < kWavesPerBlock; ++w) r = r + lds[w];
-    }
+    for (int w = 0; w < kWavesPerBlock; ++w) r = r + lds[w];
     __syncthreads();
     return r;
 }

@@ -14,6 +14,7 @@ struct WorkspaceView {
     const uint32_t* chunk_map;
     double* partials;
     int n_chunks;
+    int solo_tensor;  // the index every chunk maps to, or -1 (several tensors)
     int64_t chunk_elems;
     uint64_t tag;
 };
@@ -25,12 +26,24 @@ hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid,
                             double* d_sumsq, double max_norm, double grad_scale,
                             float* d_coef, hipStream_t stream, NormBefore next);
 
+// The norm's first stage only: one partial sum per block, and the step
+// number *d_step + 1, in the workspace for a following launch_clipped_step.
+hipError_t launch_grad_norm_partials(const WorkspaceView& ws, bool grad_bf16, int grid,
+                                     const int32_t* d_step, hipStream_t stream);
+
 hipError_t launch_clip_coef(const double* d_sumsq, double max_norm, double grad_scale,
                             float* d_coef, hipStream_t stream);
 
 hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, int grid,
                              const float* d_coef, const double* d_skip_if_nonfinite,
                              int32_t* d_step, const HyperParams& hp, hipStream_t stream);
+
+// The update that finishes the norm from the `n_partials` partials a
+// launch_grad_norm_partials of grid n_partials left in the workspace.
+hipError_t launch_clipped_step(const WorkspaceView& ws, bool grad_bf16, int grid, int n_partials,
+                               double max_norm, double grad_scale, int skip_if_nonfinite,
+                               double* d_sumsq, float* d_coef, int32_t* d_step,
+                               const HyperParams& hp, hipStream_t stream);
 
 // Largest grid of the single-launch step whose blocks can all be resident.
 hipError_t fused_grid_limit(bool grad_bf16, int* max_blocks);

@@ -48,14 +48,46 @@ __device__ __forceinline__ double add_vector(double acc, u32x4 v)
     return acc;
 }
 
+// The run of chunks of block b among G: the first n % G blocks take
+// n / G + 1 chunks, the others n / G (32-bit arithmetic only).
+struct ChunkRun {
+    int first, stop;
+};
+
+__device__ __forceinline__ ChunkRun block_run(int n_chunks)
+{
+    const uint32_t n = static_cast<uint32_t>(n_chunks);
+    const uint32_t g = gridDim.x, b = blockIdx.x;
+    const uint32_t per = n / g, rem = n % g;
+    const uint32_t first = b * per + min(b, rem);
+    return {static_cast<int>(first), static_cast<int>(first + per + (b < rem ? 1u : 0u))};
+}
+
+// The tensor index of chunk c.  A list whose chunks all belong to one tensor
+// needs no chunk-map read.
+__device__ __forceinline__ uint32_t tensor_of_chunk(const WorkspaceView& ws, int c)
+{
+    return ws.solo_tensor >= 0 ? static_cast<uint32_t>(ws.solo_tensor) : ws.chunk_map[c];
+}
+
+// The tensor index of chunk c for a kernel's prologue: c is clamped into the
+// map, which has at least one slot (a block without chunks never uses the
+// result).
+__device__ __forceinline__ uint32_t prologue_tensor(const WorkspaceView& ws, int c)
+{
+    return tensor_of_chunk(ws, min(c, max(ws.n_chunks - 1, 0)));
+}
+
 // This thread's share of the sum of g^2 over the chunks [run_first,
 // run_stop), in a fixed order.  Consecutive chunks of one tensor are one
 // contiguous stretch of memory, streamed as a single body so the load
 // pipeline only restarts at tensor boundaries.
 template <bool kBf16, int kUnroll, int kPolicy>
-__device__ __forceinline__ double norm_of_run(const TensorEntry* tensors, const uint32_t* chunk_map,
-                                              int64_t chunk_elems, int run_first, int run_stop)
+__device__ __forceinline__ double norm_of_run(const WorkspaceView& ws, uint32_t first_tensor,
+                                              int run_first, int run_stop)
 {
+    const TensorEntry* tensors = ws.tensors;
+    const int64_t chunk_elems = ws.chunk_elems;
     constexpr int64_t kElemBytes = kBf16 ? 2 : 4;
     constexpr int64_t kPerVec = 16 / kElemBytes;
     const int tid = threadIdx.x;
@@ -64,7 +96,7 @@ __device__ __forceinline__ double norm_of_run(const TensorEntry* tensors, const 
     for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
 
     for (int c = run_first; c < run_stop;) {
-        const TensorEntry te = tensors[chunk_map[c]];
+        const TensorEntry te = tensors[c == run_first ? first_tensor : tensor_of_chunk(ws, c)];
         const int tensor_chunks = static_cast<int>((te.numel + chunk_elems - 1) / chunk_elems);
         const int c_lo = c;  // this body: chunks [c_lo, c_hi) of one tensor
         const int c_hi = min(run_stop, te.first_chunk + tensor_chunks);
@@ -127,34 +159,59 @@ __device__ __forceinline__ double norm_of_run(const TensorEntry* tensors, const 
     return mine;
 }
 
-// The run of chunks of block b among G: [b*n/G, (b+1)*n/G).
-__device__ __forceinline__ int run_begin(int b, int n_chunks)
+// S from the n per-block partials, in block-index order: each thread sums
+// its strided share (partials[tid], [tid + kBlock], ...), then the block
+// combines the threads in a fixed tree.  Every thread returns the same bits,
+// and so does every block that calls this on the same partials.  kAtomic:
+// the partials were written by other blocks of this launch (agent-scope
+// loads after an acquire fence); otherwise by an earlier launch.
+template <bool kAtomic>
+__device__ __forceinline__ double sum_partials(const double* partials, int n, double* lds)
 {
-    return static_cast<int>(static_cast<int64_t>(b) * n_chunks / gridDim.x);
+    if (kAtomic) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    double q = 0.0;
+    for (int i = threadIdx.x; i < n; i += kBlock) {
+        q = q + (kAtomic ? __hip_atomic_load(&partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : partials[i]);
+    }
+    return block_sum(q, lds);
 }
 
-template <bool kBf16, int kUnroll, int kPolicy>
+// kFinish: the last block to finish sums the partials and writes S (and the
+// clip coefficient).  Otherwise the launch ends with one partial per block in
+// the workspace, and the step number t = *d_step + 1 in the header, for the
+// clipped update to finish.
+template <bool kBf16, int kUnroll, int kPolicy, bool kFinish>
 __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
-    WorkspaceHeader* header, const TensorEntry* tensors, const uint32_t* chunk_map,
-    double* partials, int n_chunks, int64_t chunk_elems, uint64_t tag, double* d_sumsq,
-    double max_norm, double grad_scale, float* d_coef)
+    WorkspaceView ws, double* d_sumsq, double max_norm, double grad_scale, float* d_coef,
+    const int32_t* d_step)
 {
-    if (header->tag != tag) {  // tables overwritten: touch nothing, report NaN
-        if (blockIdx.x == 0 && threadIdx.x == 0) {
+    const int tid = threadIdx.x;
+    const ChunkRun run = block_run(ws.n_chunks);
+    // The tag and the first chunk's tensor index are independent loads, in
+    // flight together.
+    const uint64_t seen = ws.header->tag;
+    const uint32_t first_tensor = prologue_tensor(ws, run.first);
+    if (seen != ws.tag) {  // tables overwritten: touch nothing, report NaN
+        if (kFinish && blockIdx.x == 0 && tid == 0) {
             *d_sumsq = __builtin_nan("");
             if (d_coef) *d_coef = __builtin_nanf("");
         }
         return;
     }
 
-    const int tid = threadIdx.x;
-    const double mine = norm_of_run<kBf16, kUnroll, kPolicy>(tensors, chunk_map, chunk_elems,
-                                                    run_begin(blockIdx.x, n_chunks),
-                                                    run_begin(blockIdx.x + 1, n_chunks));
+    const double mine = norm_of_run<kBf16, kUnroll, kPolicy>(ws, first_tensor, run.first, run.stop);
 
     __shared__ double lds[kWavesPerBlock];
     __shared__ bool is_last;
     const double block_total = block_sum(mine, lds);
+    if (!kFinish) {
+        if (tid == 0) ws.partials[blockIdx.x] = block_total;
+        // The step the following clipped update will take (it reads t here,
+        // so its own block 0 may store the counter at any time).
+        if (blockIdx.x == 0 && tid == 0) ws.header->pending_step = *d_step + 1;
+        return;
+    }
     // Hand-off to the last block.  The partial is written with an agent-scope
     // atomic store, which goes through to the device's coherence point, and
     // the ticket is taken only once that store is acknowledged (s_waitcnt on
@@ -163,22 +220,17 @@ __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
     // previous update's state.  The last block reads the partials with
     // agent-scope atomic loads, after an acquire fence.
     if (tid == 0) {
-        __hip_atomic_store(&partials[blockIdx.x], block_total, __ATOMIC_RELAXED,
+        __hip_atomic_store(&ws.partials[blockIdx.x], block_total, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_s_waitcnt(0);
-        const unsigned prev = atomicInc(&header->norm_ticket, gridDim.x - 1);
+        const unsigned prev = atomicInc(&ws.header->norm_ticket, gridDim.x - 1);
         is_last = (prev == gridDim.x - 1);  // the ticket wraps back to 0 here
     }
     __syncthreads();
     if (!is_last) return;
 
     // Second stage: the last block sums the partials in block-index order.
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    double q = 0.0;
-    for (int i = tid; i < static_cast<int>(gridDim.x); i += kBlock) {
-        q = q + __hip_atomic_load(&partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    const double total = block_sum(q, lds);
+    const double total = sum_partials<true>(ws.partials, gridDim.x, lds);
     if (tid == 0) {
         *d_sumsq = total;
         if (d_coef) *d_coef = clip_from_sumsq(total, max_norm, grad_scale);
@@ -287,20 +339,21 @@ __device__ __forceinline__ void adamw_body(const TensorEntry* te, int64_t q0, in
 }
 
 // Update the chunks b, b + G, b + 2G, ... of this block (G = gridDim.x): at
-// any moment the blocks stream neighbouring chunks.  The next chunk's table
-// entry is fetched before the current chunk streams, so the two dependent
-// scalar lookups overlap the data loads.
+// any moment the blocks stream neighbouring chunks.  `next` is the table
+// entry of chunk b, fetched by the caller's prologue; the entry of each
+// following chunk is fetched before the current chunk streams, so the two
+// dependent scalar lookups overlap the data loads.
 template <bool kBf16, int kUnroll>
-__device__ __forceinline__ void update_chunks(const TensorEntry* tensors, const uint32_t* chunk_map,
-                                              int n_chunks, int64_t chunk_elems,
+__device__ __forceinline__ void update_chunks(const WorkspaceView& ws, TensorEntry next,
                                               const StepScalars& s)
 {
     const int tid = threadIdx.x;
-    TensorEntry next{};
-    if (static_cast<int>(blockIdx.x) < n_chunks) next = tensors[chunk_map[blockIdx.x]];
+    const int n_chunks = ws.n_chunks;
+    const int64_t chunk_elems = ws.chunk_elems;
     for (int c = blockIdx.x; c < n_chunks; c += gridDim.x) {
         const TensorEntry entry = next;
-        if (c + static_cast<int>(gridDim.x) < n_chunks) next = tensors[chunk_map[c + gridDim.x]];
+        const int c_next = c + static_cast<int>(gridDim.x);
+        if (ws.solo_tensor < 0 && c_next < n_chunks) next = ws.tensors[ws.chunk_map[c_next]];
         const TensorEntry* te = &entry;
         const int64_t begin = static_cast<int64_t>(c - te->first_chunk) * chunk_elems;
         const int64_t end = min(begin + chunk_elems, te->numel);
@@ -318,36 +371,89 @@ __device__ __forceinline__ void update_chunks(const TensorEntry* tensors, const 
     }
 }
 
-template <bool kBf16, int kUnroll>
-__global__ __launch_bounds__(kBlock) void adamw_step_kernel(
-    WorkspaceHeader* header, const TensorEntry* tensors, const uint32_t* chunk_map,
-    int n_chunks, int64_t chunk_elems, uint64_t tag, const float* d_coef,
-    const double* d_skip_if_nonfinite, int32_t* d_step, HyperParams hp)
+// The step counter.  Every wave reads the completed-step count in its
+// prologue; at its end each block takes a ticket, and the block that takes
+// the last one stores the new count.  The only order this needs is that
+// every read comes before that store: the barrier puts all of a block's waves
+// (each past its read) before its ticket, and the last block stores only
+// after seeing every other ticket.  No block reads data that another block of
+// the launch wrote, so there is no release fence (on this chip an agent-scope
+// release writes back the whole L2, which cost ~20 us per launch on a
+// 62.7M-parameter shard).  Tickets at the end also reach the counter spread
+// over the blocks' finishing times; taken at the start they all arrive at
+// once and queue (measured: the update got slower).
+__device__ __forceinline__ void advance_step(WorkspaceHeader* header, int32_t* d_step, int64_t t)
 {
-    if (header->tag != tag) return;  // tables overwritten: touch nothing
-    // A skipped step writes nothing and leaves the counter (no block takes a
-    // ticket).  The value is uniform, so every block makes the same choice.
-    if (d_skip_if_nonfinite && !__builtin_isfinite(*d_skip_if_nonfinite)) return;
-
-    const int tid = threadIdx.x;
-    const int64_t t = static_cast<int64_t>(*d_step) + 1;
-    const StepScalars s = step_scalars(t, hp, d_coef ? *d_coef : 1.0f);
-    update_chunks<kBf16, kUnroll>(tensors, chunk_map, n_chunks, chunk_elems, s);
-    // The last block to take a ticket stores the new step count.  The only
-    // order this needs is that every block's read of the old count comes
-    // before that store: a block with work consumed the count in its
-    // arithmetic before reaching its ticket, and the last block stores only
-    // after seeing every other ticket (a block without work writes nothing,
-    // so when its read happens does not matter).  No block reads data that
-    // another block of this launch wrote, so there is no release fence here:
-    // on this chip an agent-scope release writes back the whole L2, which
-    // cost ~20 us per launch on a 62.7M-parameter shard.
     __syncthreads();
-    if (tid == 0) {
+    if (threadIdx.x == 0) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the compiler keeps the ticket last
         const unsigned prev = atomicInc(&header->step_ticket, gridDim.x - 1);
         if (prev == gridDim.x - 1) *d_step = static_cast<int32_t>(t);
     }
+}
+
+template <bool kBf16, int kUnroll>
+__global__ __launch_bounds__(kBlock) void adamw_step_kernel(
+    WorkspaceView ws, const float* d_coef, const double* d_skip_if_nonfinite, int32_t* d_step,
+    HyperParams hp)
+{
+    // Independent loads, in flight together (the first chunk is chunk
+    // blockIdx.x of the strided walk).
+    const uint64_t seen = ws.header->tag;
+    const int32_t count = *d_step;
+    const float coef = d_coef ? *d_coef : 1.0f;
+    const double skip_value = d_skip_if_nonfinite ? *d_skip_if_nonfinite : 0.0;
+    const TensorEntry first = ws.tensors[prologue_tensor(ws, blockIdx.x)];
+    if (seen != ws.tag) return;  // tables overwritten: touch nothing
+    // A skipped step writes nothing and leaves the counter.  The value is
+    // uniform, so every block makes the same choice.
+    if (!__builtin_isfinite(skip_value)) return;
+
+    const int64_t t = static_cast<int64_t>(count) + 1;
+    update_chunks<kBf16, kUnroll>(ws, first, step_scalars(t, hp, coef));
+    advance_step(ws.header, d_step, t);
+}
+
+// The update with the end of the norm folded in.  A norm launch without the
+// finish left one partial per block (n_partials of them) and the step number
+// in the workspace; every block here sums the partials exactly as the norm's
+// own last block would (same order, same tree: S is the same bits), forms the
+// clip coefficient, and skips a step whose S is not finite if asked to.
+// Block 0 publishes S, the coefficient and the new step count: the blocks
+// take t from the header, not from the counter, so the store needs no ticket.
+// Against the three-call step this saves the norm's hand-off between its
+// blocks (a store, an atomic and a load, each a trip to the device's
+// coherence point) and the update's end-of-launch ticket, whose atomics all
+// reach one counter at once on a small shard (measured: 4 us of 17 on a
+// 2^20-parameter shard); it costs a 2 KB read per block that overlaps the
+// other prologue loads.
+template <bool kBf16, int kUnroll>
+__global__ __launch_bounds__(kBlock) void adamw_clipped_kernel(
+    WorkspaceView ws, int n_partials, double max_norm, double grad_scale, int skip_if_nonfinite,
+    double* d_sumsq, float* d_coef, int32_t* d_step, HyperParams hp)
+{
+    const int tid = threadIdx.x;
+    const uint64_t seen = ws.header->tag;
+    const int32_t t = ws.header->pending_step;
+    const TensorEntry first = ws.tensors[prologue_tensor(ws, blockIdx.x)];
+    if (seen != ws.tag) {  // tables overwritten: touch nothing, report NaN
+        if (blockIdx.x == 0 && tid == 0) {
+            if (d_sumsq) *d_sumsq = __builtin_nan("");
+            if (d_coef) *d_coef = __builtin_nanf("");
+        }
+        return;
+    }
+    __shared__ double lds[kWavesPerBlock];
+    const double total = sum_partials<false>(ws.partials, n_partials, lds);
+    const float clip = clip_from_sumsq(total, max_norm, grad_scale);
+    const bool skip = skip_if_nonfinite && !__builtin_isfinite(total);
+    if (blockIdx.x == 0 && tid == 0) {
+        if (d_sumsq) *d_sumsq = total;
+        if (d_coef) *d_coef = clip;
+        if (!skip) *d_step = t;
+    }
+    if (skip) return;
+    update_chunks<kBf16, kUnroll>(ws, first, step_scalars(t, hp, clip));
 }
 
 // ------------------------------------------------------ single launch ---
@@ -360,34 +466,35 @@ constexpr uint32_t kSpinLimit = 1u << 23;  // x s_sleep(2): about 1 s, never rea
 // and the waiting block stops without writing state).
 template <bool kBf16, int kNormUnroll, int kStepUnroll>
 __global__ __launch_bounds__(kBlock) void adamw_fused_kernel(
-    WorkspaceHeader* header, const TensorEntry* tensors, const uint32_t* chunk_map,
-    double* partials, int n_chunks, int64_t chunk_elems, uint64_t tag, double max_norm,
-    double grad_scale, int skip_if_nonfinite, double* d_sumsq, float* d_coef, int32_t* d_step,
-    HyperParams hp)
+    WorkspaceView ws, double max_norm, double grad_scale, int skip_if_nonfinite, double* d_sumsq,
+    float* d_coef, int32_t* d_step, HyperParams hp)
 {
-    if (header->tag != tag) {  // tables overwritten: touch nothing, report NaN
-        if (blockIdx.x == 0 && threadIdx.x == 0) {
+    const int tid = threadIdx.x;
+    const int grid = gridDim.x;
+    WorkspaceHeader* header = ws.header;
+    const ChunkRun run = block_run(ws.n_chunks);
+    const uint64_t seen = header->tag;
+    const uint32_t first_tensor = prologue_tensor(ws, run.first);
+    if (seen != ws.tag) {  // tables overwritten: touch nothing, report NaN
+        if (blockIdx.x == 0 && tid == 0) {
             if (d_sumsq) *d_sumsq = __builtin_nan("");
             if (d_coef) *d_coef = __builtin_nanf("");
         }
         return;
     }
-    const int tid = threadIdx.x;
-    const int grid = gridDim.x;
     // Every block reads the step count before it arrives at the barrier; the
     // last block to arrive is therefore free to store the new count.
     const int64_t t = static_cast<int64_t>(*d_step) + 1;
 
     // Phase 1: this block's partial of S.
-    const double mine = norm_of_run<kBf16, kNormUnroll, kNormPolicy>(tensors, chunk_map, chunk_elems,
-                                                        run_begin(blockIdx.x, n_chunks),
-                                                        run_begin(blockIdx.x + 1, n_chunks));
+    const double mine = norm_of_run<kBf16, kNormUnroll, kNormPolicy>(ws, first_tensor, run.first,
+                                                                     run.stop);
     __shared__ double lds[kWavesPerBlock];
     __shared__ uint64_t launch;
     __shared__ bool last, failed;
     const double block_total = block_sum(mine, lds);
     if (tid == 0) {
-        __hip_atomic_store(&partials[blockIdx.x], block_total, __ATOMIC_RELAXED,
+        __hip_atomic_store(&ws.partials[blockIdx.x], block_total, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_s_waitcnt(0);  // the partial is visible device-wide
         const uint64_t arrival = __hip_atomic_fetch_add(&header->fused_arrived, uint64_t{1},
@@ -401,12 +508,7 @@ __global__ __launch_bounds__(kBlock) void adamw_fused_kernel(
     // Barrier.  The last block to arrive sums the partials in block order,
     // publishes S and the new step count, then releases the others.
     if (last) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        double q = 0.0;
-        for (int i = tid; i < grid; i += kBlock) {
-            q = q + __hip_atomic_load(&partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        const double total = block_sum(q, lds);
+        const double total = sum_partials<true>(ws.partials, grid, lds);
         if (tid == 0) {
             const bool skip = skip_if_nonfinite && !__builtin_isfinite(total);
             __hip_atomic_store(&header->fused_sumsq, total, __ATOMIC_RELAXED,
@@ -439,7 +541,7 @@ __global__ __launch_bounds__(kBlock) void adamw_fused_kernel(
                                            __HIP_MEMORY_SCOPE_AGENT);
     if (skip_if_nonfinite && !__builtin_isfinite(total)) return;
     const StepScalars s = step_scalars(t, hp, clip_from_sumsq(total, max_norm, grad_scale));
-    update_chunks<kBf16, kStepUnroll>(tensors, chunk_map, n_chunks, chunk_elems, s);
+    update_chunks<kBf16, kStepUnroll>(ws, ws.tensors[prologue_tensor(ws, blockIdx.x)], s);
 }
 
 }  // namespace
@@ -448,18 +550,17 @@ __global__ __launch_bounds__(kBlock) void adamw_fused_kernel(
 
 namespace {
 
-template <int kPolicy>
+template <int kPolicy, bool kFinish>
 void grad_norm_launch(const WorkspaceView& ws, bool grad_bf16, int grid, double* d_sumsq,
-                      double max_norm, double grad_scale, float* d_coef, hipStream_t stream)
+                      double max_norm, double grad_scale, float* d_coef, const int32_t* d_step,
+                      hipStream_t stream)
 {
     if (grad_bf16) {
-        grad_norm_kernel<true, MPS_NORM_UNROLL, kPolicy><<<grid, kBlock, 0, stream>>>(
-            ws.header, ws.tensors, ws.chunk_map, ws.partials, ws.n_chunks, ws.chunk_elems, ws.tag,
-            d_sumsq, max_norm, grad_scale, d_coef);
+        grad_norm_kernel<true, MPS_NORM_UNROLL, kPolicy, kFinish><<<grid, kBlock, 0, stream>>>(
+            ws, d_sumsq, max_norm, grad_scale, d_coef, d_step);
     } else {
-        grad_norm_kernel<false, MPS_NORM_UNROLL, kPolicy><<<grid, kBlock, 0, stream>>>(
-            ws.header, ws.tensors, ws.chunk_map, ws.partials, ws.n_chunks, ws.chunk_elems, ws.tag,
-            d_sumsq, max_norm, grad_scale, d_coef);
+        grad_norm_kernel<false, MPS_NORM_UNROLL, kPolicy, kFinish><<<grid, kBlock, 0, stream>>>(
+            ws, d_sumsq, max_norm, grad_scale, d_coef, d_step);
     }
 }
 
@@ -473,12 +574,20 @@ hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid, d
     // updates re-read the gradients soon after and, measured on MI355X,
     // benefit from the ones a default-policy norm leaves in the caches).
     if (next == NormBefore::kQ8Update) {
-        grad_norm_launch<kQ8NormPolicy>(ws, grad_bf16, grid, d_sumsq, max_norm, grad_scale, d_coef,
-                                        stream);
+        grad_norm_launch<kQ8NormPolicy, true>(ws, grad_bf16, grid, d_sumsq, max_norm, grad_scale,
+                                              d_coef, nullptr, stream);
     } else {
-        grad_norm_launch<kNormPolicy>(ws, grad_bf16, grid, d_sumsq, max_norm, grad_scale, d_coef,
-                                      stream);
+        grad_norm_launch<kNormPolicy, true>(ws, grad_bf16, grid, d_sumsq, max_norm, grad_scale,
+                                            d_coef, nullptr, stream);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_grad_norm_partials(const WorkspaceView& ws, bool grad_bf16, int grid,
+                                     const int32_t* d_step, hipStream_t stream)
+{
+    grad_norm_launch<kNormPolicy, false>(ws, grad_bf16, grid, nullptr, 0.0, 0.0, nullptr, d_step,
+                                         stream);
     return hipGetLastError();
 }
 
@@ -495,12 +604,25 @@ hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, int grid,
 {
     if (grad_bf16) {
         adamw_step_kernel<true, MPS_STEP_UNROLL><<<grid, kBlock, 0, stream>>>(
-            ws.header, ws.tensors, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag, d_coef,
-            d_skip_if_nonfinite, d_step, hp);
+            ws, d_coef, d_skip_if_nonfinite, d_step, hp);
     } else {
         adamw_step_kernel<false, MPS_STEP_UNROLL><<<grid, kBlock, 0, stream>>>(
-            ws.header, ws.tensors, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag, d_coef,
-            d_skip_if_nonfinite, d_step, hp);
+            ws, d_coef, d_skip_if_nonfinite, d_step, hp);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_clipped_step(const WorkspaceView& ws, bool grad_bf16, int grid, int n_partials,
+                               double max_norm, double grad_scale, int skip_if_nonfinite,
+                               double* d_sumsq, float* d_coef, int32_t* d_step,
+                               const HyperParams& hp, hipStream_t stream)
+{
+    if (grad_bf16) {
+        adamw_clipped_kernel<true, MPS_STEP_UNROLL><<<grid, kBlock, 0, stream>>>(
+            ws, n_partials, max_norm, grad_scale, skip_if_nonfinite, d_sumsq, d_coef, d_step, hp);
+    } else {
+        adamw_clipped_kernel<false, MPS_STEP_UNROLL><<<grid, kBlock, 0, stream>>>(
+            ws, n_partials, max_norm, grad_scale, skip_if_nonfinite, d_sumsq, d_coef, d_step, hp);
     }
     return hipGetLastError();
 }
@@ -535,17 +657,10 @@ hipError_t launch_fused_step(const WorkspaceView& ws, bool grad_bf16, int grid, 
                              float* d_coef, int32_t* d_step, const HyperParams& hp,
                              hipStream_t stream)
 {
-    WorkspaceHeader* header = ws.header;
-    const TensorEntry* tensors = ws.tensors;
-    const uint32_t* chunk_map = ws.chunk_map;
-    double* partials = ws.partials;
-    int n_chunks = ws.n_chunks;
-    int64_t chunk_elems = ws.chunk_elems;
-    uint64_t tag = ws.tag;
+    WorkspaceView view = ws;
     HyperParams params = hp;
-    void* args[] = {&header,     &tensors,   &chunk_map,         &partials, &n_chunks,
-                    &chunk_elems, &tag,      &max_norm,          &grad_scale, &skip_if_nonfinite,
-                    &d_sumsq,    &d_coef,    &d_step,            &params};
+    void* args[] = {&view,     &max_norm, &grad_scale, &skip_if_nonfinite,
+                    &d_sumsq,  &d_coef,   &d_step,     &params};
     const void* fn = grad_bf16 ? reinterpret_cast<const void*>(fused_kernel<true>())
                                : reinterpret_cast<const void*>(fused_kernel<false>());
     // Cooperative: the runtime refuses the launch unless every block can be

@@ -4,7 +4,7 @@
 //   [0, 64)                      WorkspaceHeader
 //   [64, 64 + 64*T)              TensorEntry[T]
 //   [.., + 32*T)                 QuantEntry[T] (8-bit moment lists only)
-//   [.., + 4*K)                  uint32 chunk -> tensor index, K chunks
+//   [.., + 4*max(K, 1))          uint32 chunk -> tensor index, K chunks
 //   [.. rounded to 256, + 8*kPartials)  fp64 per-block partial sums of the norm
 // Everything before the partials is written by one host-to-device copy when
 // the list changes; the partials need no initial value.
@@ -68,7 +68,8 @@ struct alignas(64) WorkspaceHeader {
     uint64_t fused_released;
     double fused_sumsq;     // S, published by the last block to arrive
     uint32_t fused_error;   // set if a barrier wait ever ran out (never expected)
-    uint32_t reserved;
+    int32_t pending_step;   // the clipped step: t, written by its norm launch
+                            // for its update launch
 };
 static_assert(sizeof(WorkspaceHeader) == 64, "header is one 64-byte record");
 

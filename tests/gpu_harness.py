@@ -57,6 +57,15 @@ class Step:
                                  sumsq_out=self.sumsq, coef_out=self.coef)
         return self
 
+    def clipped(self, max_norm, lr, beta1, beta2, eps, wd, grad_scale=1.0,
+                skip_if_nonfinite=False):
+        """Norm, clip and update in two launches, the clip finished inside the
+        update (adamw_clipped_step)."""
+        binding.adamw_clipped_step(self.tl, self.step, lr, beta1, beta2, eps, wd, max_norm,
+                                   grad_scale=grad_scale, skip_if_nonfinite=skip_if_nonfinite,
+                                   sumsq_out=self.sumsq, coef_out=self.coef)
+        return self
+
     def header_words(self):
         """The workspace header as 64-bit words (for the barrier counters)."""
         torch.cuda.synchronize()

@@ -37,7 +37,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "adamw_workspace_bytes", "adamw_workspace_release", "grad_norm_sq", "clip_coef",
-        "adamw_multi_tensor_step", "adamw_fused_step", "adamw_last_error",
+        "adamw_multi_tensor_step", "adamw_clipped_step", "adamw_fused_step", "adamw_last_error",
         "adamw8_workspace_bytes", "adamw8_grad_norm_sq", "adamw8_multi_tensor_step",
         "adamw8_quantize", "adamw8_dequantize"])
 
@@ -141,7 +141,8 @@ def test_workspace_errors(lib):
                             need, None) == EINVAL
 
 
-def test_fused_step_argument_errors(lib):
+@pytest.mark.parametrize("entry", ["adamw_clipped_step", "adamw_fused_step"])
+def test_whole_step_argument_errors(lib, entry):
     arr = fake_list(1, 4096)
     ws = ctypes.c_void_p(0x7e0000000000)
     step = ctypes.c_void_p(0x7d0000000000)
@@ -150,9 +151,9 @@ def test_fused_step_argument_errors(lib):
         a = dict(mn=1.0, scale=1.0, step=step, lr=3e-4, b1=0.9, b2=0.95, eps=1e-8, wd=0.1,
                  ws=ws, size=1 << 30)
         a.update(kw)
-        return lib.adamw_fused_step(arr, 1, 0, a["mn"], a["scale"], 0, None, None, a["step"],
-                                    a["lr"], a["b1"], a["b2"], a["eps"], a["wd"], a["ws"],
-                                    a["size"], None)
+        return getattr(lib, entry)(arr, 1, 0, a["mn"], a["scale"], 0, None, None, a["step"],
+                                   a["lr"], a["b1"], a["b2"], a["eps"], a["wd"], a["ws"],
+                                   a["size"], None)
 
     assert call(step=None) == EINVAL
     assert call(mn=0.0) == EINVAL

@@ -23,8 +23,9 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout.strip() == ""
 
 
-def test_fused_and_8bit_together_are_refused_or_need_a_gpu():
-    r = run("--fused", "--state8")
+@pytest.mark.parametrize("launches", ["fused", "clipped"])
+def test_one_call_steps_and_8bit_together_are_refused_or_need_a_gpu(launches):
+    r = run("--launches", launches, "--state8")
     assert r.returncode != 0 and r.stdout.strip() == ""
 
 
