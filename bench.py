@@ -1,13 +1,15 @@
 """Throughput of the fused, clipped, mixed-precision AdamW step on one GPU.
 
-A step is one pass of the whole path over one shard: grad_norm_sq (sum of
-g^2 and, in the same launch, the clip coefficient), then
-adamw_multi_tensor_step (update + optional bf16 copy + step counter), on one
-stream, inputs resident in HBM.  Prints ONE JSON line:
-params updated per second (value), the step's algorithmic GB/s, and for the
-dominant kernel (the update) its roofline against MI355X's 8 TB/s HBM peak,
-timed live with events on the launch stream; plus the CPU oracle timed on a
-bounded sample on the host (single thread).
+A step is one pass of the whole path over one shard, on one stream, inputs
+resident in HBM.  By default it is one adamw_clipped_step call: a norm launch
+(per-block partial sums of g^2), then the update launch, which finishes the
+sum, forms the clip coefficient and updates (+ optional bf16 copy + step
+counter).  --launches separate times grad_norm_sq (sum and clip coefficient
+in one launch) followed by adamw_multi_tensor_step instead.  Prints ONE JSON
+line: params updated per second (value), the step's algorithmic GB/s, and for
+the dominant kernel (the update) its roofline against MI355X's 8 TB/s HBM
+peak, timed live with events on the launch stream; plus the CPU oracle timed
+on a bounded sample on the host (single thread).
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--rotate R] [--state8]
 
@@ -30,7 +32,9 @@ CSRC = os.path.join(ROOT, "mixed_precision_sharded_amd", "csrc")
 # only for these exact sources).
 KERNEL_SOURCES = {
     "adamw_step_kernel": ("kernels.hip", "device.h", "layout.h"),
+    "adamw_clipped_kernel": ("kernels.hip", "device.h", "layout.h"),
     "adamw8_step_kernel": ("kernels_q8.hip", "device.h", "layout.h"),
+    "adamw8_clipped_kernel": ("kernels_q8.hip", "device.h", "layout.h"),
 }
 
 
@@ -50,7 +54,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="host time budget of the oracle baseline (0 = skip)")
     p.add_argument("--no-kernel-events", action="store_true")
-    p.add_argument("--launches", choices=("separate", "clipped", "fused"), default="separate",
+    p.add_argument("--launches", choices=("separate", "clipped", "fused"), default="clipped",
                    help="separate: grad_norm_sq with the clip output, then "
                         "adamw_multi_tensor_step; clipped: adamw_clipped_step (the norm's "
                         "partials finished inside the update); fused: adamw_fused_step "
@@ -110,8 +114,8 @@ def main():
     w = WORKLOADS[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.state8 and args.launches != "separate":
-        print("--state8 runs as two separate calls only", file=sys.stderr)
+    if args.state8 and args.launches == "fused":
+        print("--state8 has no single-launch form", file=sys.stderr)
         sys.exit(2)
     log(f"workload {w.cfg} {w.name}: {w.numel:,} params in {w.n_tensors} tensors, "
         f"{'bf16' if w.grad_bf16 else 'fp32'} grads, copy={w.copy_bf16}, rotate={args.rotate}, "
@@ -152,11 +156,11 @@ def main():
                 ev[2].record()
             return
         if args.launches == "clipped":
-            # Two launches inside one call: the events bracket the call.
-            binding.adamw_clipped_step(tl, step, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay,
-                                       w.max_norm, sumsq_out=sumsq, coef_out=coef)
+            # Two launches inside one call; the library records ev[1] between them.
+            fn = binding.adamw8_clipped_step if args.state8 else binding.adamw_clipped_step
+            fn(tl, step, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.max_norm,
+               sumsq_out=sumsq, coef_out=coef, mid_event=None if ev is None else ev[1])
             if ev is not None:
-                ev[1].record()
                 ev[2].record()
             return
         if args.state8:
@@ -199,6 +203,8 @@ def main():
     spread = None
     if not args.no_kernel_events:
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for e in evs:
+            e[1].record()  # creates the event the library records between its launches
         torch.cuda.synchronize()
         for i in range(args.steps):
             one_step(sets[i % len(sets)][1], evs[i])
@@ -211,7 +217,7 @@ def main():
         if args.launches == "fused":
             kern_us = {"adamw_fused_step": norm_ms * 1e3}
         elif args.launches == "clipped":
-            kern_us = {"adamw_clipped_step": norm_ms * 1e3}
+            kern_us = {"grad_norm partials": norm_ms * 1e3, "clipped update": upd_ms * 1e3}
         elif args.state8:
             kern_us = {"adamw8_grad_norm_sq+clip": norm_ms * 1e3,
                        "adamw8_multi_tensor_step": upd_ms * 1e3}
@@ -230,9 +236,12 @@ def main():
     if kern_us is not None:
         if args.launches == "fused":  # one kernel does the whole step
             name, launch_bytes, us = "adamw_fused_kernel", step_bytes, kern_us["adamw_fused_step"]
-        elif args.launches == "clipped":  # both launches of the call, all of the step's bytes
-            name, launch_bytes = "adamw_clipped_step", step_bytes
-            us = kern_us["adamw_clipped_step"]
+        elif args.launches == "clipped" and args.state8:
+            name, launch_bytes = "adamw8_clipped_kernel", w.update8_bytes_per_param() * n
+            us = kern_us["clipped update"]
+        elif args.launches == "clipped":
+            name, launch_bytes = "adamw_clipped_kernel", w.update_bytes_per_param() * n
+            us = kern_us["clipped update"]
         elif args.state8:
             name, launch_bytes = "adamw8_step_kernel", w.update8_bytes_per_param() * n
             us = kern_us["adamw8_multi_tensor_step"]

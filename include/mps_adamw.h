@@ -223,12 +223,15 @@ int adamw_multi_tensor_step(const mps_tensor* tensors, int n_tensors,
  *   d_step, lr, beta1, beta2, eps, weight_decay : as adamw_multi_tensor_step.
  *   d_workspace, workspace_bytes : see adamw_workspace_bytes; the same
  *                      workspace may serve all entry points.
+ *   mid_event        : a hipEvent_t to record on `stream` between the two
+ *                      launches (to time the update alone), or NULL.
  */
 int adamw_clipped_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
                        double max_norm, double grad_scale, int skip_if_nonfinite,
                        double* d_sumsq, float* d_coef, int32_t* d_step, double lr,
                        double beta1, double beta2, double eps, double weight_decay,
-                       void* d_workspace, size_t workspace_bytes, void* stream);
+                       void* d_workspace, size_t workspace_bytes, void* stream,
+                       void* mid_event);
 
 /*
  * adamw_fused_step — the whole step in ONE launch: the sum of squares, the
@@ -336,6 +339,19 @@ int adamw8_multi_tensor_step(const mps_tensor8* tensors, int n_tensors,
                              double lr, double beta1, double beta2, double eps,
                              double weight_decay, void* d_workspace,
                              size_t workspace_bytes, void* stream);
+
+/* adamw8_clipped_step — the whole step on 8-bit moment state in two plain
+ * launches, as adamw_clipped_step: bitwise the results of
+ * adamw8_grad_norm_sq(..., d_coef) followed by adamw8_multi_tensor_step with
+ * that coefficient (and d_sumsq as the skip value when skip_if_nonfinite is
+ * set).  Arguments as adamw_clipped_step, with the 8-bit list and its
+ * workspace (adamw8_workspace_bytes). */
+int adamw8_clipped_step(const mps_tensor8* tensors, int n_tensors, mps_dtype grad_dtype,
+                        double max_norm, double grad_scale, int skip_if_nonfinite,
+                        double* d_sumsq, float* d_coef, int32_t* d_step, double lr,
+                        double beta1, double beta2, double eps, double weight_decay,
+                        void* d_workspace, size_t workspace_bytes, void* stream,
+                        void* mid_event);
 
 /*
  * adamw8_quantize — encode n fp32 values (e.g. fp32 moments from a

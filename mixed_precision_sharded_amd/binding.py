@@ -86,7 +86,7 @@ def lib() -> ctypes.CDLL:
             ctypes.c_double, ctypes.c_int, P, P, P, ctypes.c_double, ctypes.c_double,
             ctypes.c_double, ctypes.c_double, ctypes.c_double, P, ctypes.c_size_t, P]
         L.adamw_clipped_step.restype = ctypes.c_int
-        L.adamw_clipped_step.argtypes = whole_step
+        L.adamw_clipped_step.argtypes = whole_step + [P]
         L.adamw_fused_step.restype = ctypes.c_int
         L.adamw_fused_step.argtypes = whole_step
         T8 = ctypes.POINTER(MpsTensor8)
@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.adamw8_multi_tensor_step.argtypes = [
             T8, ctypes.c_int, ctypes.c_int, P, P, P, ctypes.c_double, ctypes.c_double,
             ctypes.c_double, ctypes.c_double, ctypes.c_double, P, ctypes.c_size_t, P]
+        L.adamw8_clipped_step.restype = ctypes.c_int
+        L.adamw8_clipped_step.argtypes = [T8] + whole_step[1:] + [P]
         L.adamw8_quantize.restype = ctypes.c_int
         L.adamw8_quantize.argtypes = [P, ctypes.c_int64, ctypes.c_int, P, P, P]
         L.adamw8_dequantize.restype = ctypes.c_int
@@ -314,7 +316,8 @@ def adamw_multi_tensor_step(tl: TensorList, coef: Optional[torch.Tensor], step: 
 def _whole_step(name: str, tl: TensorList, step: torch.Tensor, lr: float, beta1: float,
                 beta2: float, eps: float, weight_decay: float, max_norm: float, grad_scale: float,
                 skip_if_nonfinite: bool, sumsq_out: Optional[torch.Tensor],
-                coef_out: Optional[torch.Tensor], stream: Optional[torch.cuda.Stream]) -> None:
+                coef_out: Optional[torch.Tensor], stream: Optional[torch.cuda.Stream],
+                *extra) -> None:
     if step.dtype != torch.int32 or step.device != tl.device:
         raise ValueError("step: int32 tensor on the list's device")
     if sumsq_out is not None and (sumsq_out.dtype != torch.float64 or sumsq_out.device != tl.device):
@@ -325,18 +328,32 @@ def _whole_step(name: str, tl: TensorList, step: torch.Tensor, lr: float, beta1:
         tl.array, tl.n, tl.grad_dtype, float(max_norm), float(grad_scale),
         1 if skip_if_nonfinite else 0, _ptr(sumsq_out), _ptr(coef_out), step.data_ptr(),
         float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), tl.workspace_ptr,
-        tl.workspace_bytes, _stream_handle(stream)), name)
+        tl.workspace_bytes, _stream_handle(stream), *extra), name)
 
 
 def adamw_clipped_step(tl: TensorList, step: torch.Tensor, lr: float, beta1: float, beta2: float,
                        eps: float, weight_decay: float, max_norm: float, grad_scale: float = 1.0,
                        skip_if_nonfinite: bool = False, sumsq_out: Optional[torch.Tensor] = None,
                        coef_out: Optional[torch.Tensor] = None,
-                       stream: Optional[torch.cuda.Stream] = None) -> None:
+                       stream: Optional[torch.cuda.Stream] = None,
+                       mid_event: Optional[torch.cuda.Event] = None) -> None:
     """Norm, clip and update in two plain launches, the clip finished inside
-    the update (see adamw_clipped_step in the header)."""
+    the update (see adamw_clipped_step in the header).  `mid_event`, if given,
+    is recorded between the two launches (it must have been recorded once
+    before, so that it exists)."""
+    if isinstance(tl, TensorList8):
+        raise TypeError("adamw_clipped_step takes a TensorList (8-bit state: adamw8_clipped_step)")
     _whole_step("adamw_clipped_step", tl, step, lr, beta1, beta2, eps, weight_decay, max_norm,
-                grad_scale, skip_if_nonfinite, sumsq_out, coef_out, stream)
+                grad_scale, skip_if_nonfinite, sumsq_out, coef_out, stream,
+                _event_handle(mid_event))
+
+
+def _event_handle(event: Optional[torch.cuda.Event]):
+    if event is None:
+        return None
+    if not event.cuda_event:
+        raise ValueError("mid_event: record it once before passing it")
+    return ctypes.c_void_p(event.cuda_event)
 
 
 def adamw_fused_step(tl: TensorList, step: torch.Tensor, lr: float, beta1: float, beta2: float,
@@ -390,6 +407,21 @@ def adamw8_multi_tensor_step(tl: TensorList8, coef: Optional[torch.Tensor], step
         tl.array, tl.n, tl.grad_dtype, _ptr(coef), _ptr(skip_if_nonfinite), step.data_ptr(),
         float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), tl.workspace_ptr,
         tl.workspace_bytes, _stream_handle(stream)), "adamw8_multi_tensor_step")
+
+
+def adamw8_clipped_step(tl: TensorList8, step: torch.Tensor, lr: float, beta1: float,
+                        beta2: float, eps: float, weight_decay: float, max_norm: float,
+                        grad_scale: float = 1.0, skip_if_nonfinite: bool = False,
+                        sumsq_out: Optional[torch.Tensor] = None,
+                        coef_out: Optional[torch.Tensor] = None,
+                        stream: Optional[torch.cuda.Stream] = None,
+                        mid_event: Optional[torch.cuda.Event] = None) -> None:
+    """adamw_clipped_step with 8-bit moments."""
+    if not isinstance(tl, TensorList8):
+        raise TypeError("adamw8_clipped_step takes a TensorList8")
+    _whole_step("adamw8_clipped_step", tl, step, lr, beta1, beta2, eps, weight_decay, max_norm,
+                grad_scale, skip_if_nonfinite, sumsq_out, coef_out, stream,
+                _event_handle(mid_event))
 
 
 def adamw8_quantize(x: torch.Tensor, fmt: int, codes: torch.Tensor, scales: torch.Tensor,

@@ -382,6 +382,41 @@ int run_grad_norm(Plan& plan, bool bf16, double* d_sumsq, double max_norm,
     return ok();
 }
 
+int check_clipped_arguments(const int32_t* d_step, double max_norm, double grad_scale, double lr,
+                            double beta1, double beta2, double eps, double weight_decay)
+{
+    if (!d_step) return fail(MPS_ERR_INVALID_ARGUMENT, "d_step is NULL");
+    int rc = check_clip_arguments(max_norm, grad_scale);
+    if (!rc) rc = check_hyperparameters(lr, beta1, beta2, eps, weight_decay);
+    return rc;
+}
+
+// The clipped step's two launches over a planned list: the norm's partial
+// sums (and the step number) into the workspace, the optional event, then
+// `update(view, norm grid, stream)`, which finishes the sum.
+template <class Update>
+int run_clipped(Plan& plan, bool bf16, const int32_t* d_step, void* d_workspace,
+                size_t workspace_bytes, void* stream, void* mid_event, mps::NormBefore next,
+                Update update)
+{
+    int rc = check_workspace(d_workspace, workspace_bytes, plan);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
+    const mps::WorkspaceView ws = view_of(d_workspace, plan);
+    // The same norm grid as grad_norm_sq, so the partials and S match it.
+    const int norm_grid = grid_for(plan.n_chunks, mps::kNormMaxBlocks);
+    hipError_t e = mps::launch_grad_norm_partials(ws, bf16, norm_grid, d_step, st, next);
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "grad_norm launch: %s", hipGetErrorString(e));
+    if (mid_event && (e = hipEventRecord(static_cast<hipEvent_t>(mid_event), st)) != hipSuccess) {
+        return fail(MPS_ERR_DEVICE, "hipEventRecord (mid_event): %s", hipGetErrorString(e));
+    }
+    if ((e = update(ws, norm_grid, st)) != hipSuccess) {
+        return fail(MPS_ERR_DEVICE, "clipped update launch: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -462,9 +497,8 @@ int adamw_fused_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dt
                      double eps, double weight_decay, void* d_workspace, size_t workspace_bytes,
                      void* stream)
 {
-    if (!d_step) return fail(MPS_ERR_INVALID_ARGUMENT, "d_step is NULL");
-    int rc = check_clip_arguments(max_norm, grad_scale);
-    if (!rc) rc = check_hyperparameters(lr, beta1, beta2, eps, weight_decay);
+    int rc = check_clipped_arguments(d_step, max_norm, grad_scale, lr, beta1, beta2, eps,
+                                     weight_decay);
     if (rc) return rc;
     Plan plan;
     if ((rc = build_plan(tensors, n_tensors, grad_dtype, true, plan))) return rc;
@@ -490,29 +524,23 @@ int adamw_clipped_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_
                        double max_norm, double grad_scale, int skip_if_nonfinite, double* d_sumsq,
                        float* d_coef, int32_t* d_step, double lr, double beta1, double beta2,
                        double eps, double weight_decay, void* d_workspace, size_t workspace_bytes,
-                       void* stream)
+                       void* stream, void* mid_event)
 {
-    if (!d_step) return fail(MPS_ERR_INVALID_ARGUMENT, "d_step is NULL");
-    int rc = check_clip_arguments(max_norm, grad_scale);
-    if (!rc) rc = check_hyperparameters(lr, beta1, beta2, eps, weight_decay);
+    int rc = check_clipped_arguments(d_step, max_norm, grad_scale, lr, beta1, beta2, eps,
+                                     weight_decay);
     if (rc) return rc;
     Plan plan;
     if ((rc = build_plan(tensors, n_tensors, grad_dtype, true, plan))) return rc;
-    if ((rc = check_workspace(d_workspace, workspace_bytes, plan))) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
     const bool bf16 = grad_dtype == MPS_DTYPE_BF16;
-    const mps::WorkspaceView ws = view_of(d_workspace, plan);
-    // The same norm grid as grad_norm_sq, so the partials and S match it.
-    const int norm_grid = grid_for(plan.n_chunks, mps::kNormMaxBlocks);
-    hipError_t e = mps::launch_grad_norm_partials(ws, bf16, norm_grid, d_step, st);
-    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "grad_norm launch: %s", hipGetErrorString(e));
-    mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
+    const mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
     const int grid = grid_for(plan.n_chunks, mps::kStepMaxBlocks);
-    e = mps::launch_clipped_step(ws, bf16, grid, norm_grid, max_norm, grad_scale,
-                                 skip_if_nonfinite ? 1 : 0, d_sumsq, d_coef, d_step, hp, st);
-    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "clipped step launch: %s", hipGetErrorString(e));
-    return ok();
+    return run_clipped(plan, bf16, d_step, d_workspace, workspace_bytes, stream, mid_event,
+                       mps::NormBefore::kUpdate,
+                       [&](const mps::WorkspaceView& ws, int norm_grid, hipStream_t st) {
+                           return mps::launch_clipped_step(ws, bf16, grid, norm_grid, max_norm,
+                                                           grad_scale, skip_if_nonfinite ? 1 : 0,
+                                                           d_sumsq, d_coef, d_step, hp, st);
+                       });
 }
 
 size_t adamw8_workspace_bytes(const mps_tensor8* tensors, int n_tensors)
@@ -559,6 +587,32 @@ int adamw8_multi_tensor_step(const mps_tensor8* tensors, int n_tensors, mps_dtyp
                                            d_skip_if_nonfinite, d_step, hp, st);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "adamw8_step launch: %s", hipGetErrorString(e));
     return ok();
+}
+
+int adamw8_clipped_step(const mps_tensor8* tensors, int n_tensors, mps_dtype grad_dtype,
+                        double max_norm, double grad_scale, int skip_if_nonfinite, double* d_sumsq,
+                        float* d_coef, int32_t* d_step, double lr, double beta1, double beta2,
+                        double eps, double weight_decay, void* d_workspace,
+                        size_t workspace_bytes, void* stream, void* mid_event)
+{
+    int rc = check_clipped_arguments(d_step, max_norm, grad_scale, lr, beta1, beta2, eps,
+                                     weight_decay);
+    if (rc) return rc;
+    Plan plan;
+    if ((rc = build_plan8(tensors, n_tensors, grad_dtype, true, plan))) return rc;
+    const bool bf16 = grad_dtype == MPS_DTYPE_BF16;
+    const mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
+    const int grid = grid_for(plan.n_chunks, mps::kQ8MaxBlocks);
+    const auto* quant = reinterpret_cast<const mps::QuantEntry*>(static_cast<unsigned char*>(d_workspace) +
+                                                                 plan.quant_off);
+    return run_clipped(plan, bf16, d_step, d_workspace, workspace_bytes, stream, mid_event,
+                       mps::NormBefore::kQ8Update,
+                       [&](const mps::WorkspaceView& ws, int norm_grid, hipStream_t st) {
+                           return mps::launch_adamw8_clipped(ws, quant, bf16, grid, norm_grid,
+                                                             max_norm, grad_scale,
+                                                             skip_if_nonfinite ? 1 : 0, d_sumsq,
+                                                             d_coef, d_step, hp, st);
+                       });
 }
 
 int adamw8_quantize(const float* d_x, int64_t n, mps_q8_format format, uint8_t* d_codes,

@@ -1,7 +1,8 @@
 // Device helpers shared by the gfx950 kernels of the AdamW step: buffer
 // resources and vector loads/stores, bf16 rounding, fp64 wavefront and block
-// reductions, the clip multiplier, the step scalars and the per-element
-// update.  Included by kernels.hip and kernels_q8.hip only.
+// reductions, the norm's second stage, the step counter, the clip
+// multiplier, the step scalars and the per-element update.  Included by
+// kernels.hip and kernels_q8.hip only.
 //
 // Build with -ffp-contract=off: every fp32 operation below must round once,
 // in source order; division and sqrt are the correctly rounded defaults.
@@ -166,6 +167,45 @@ __device__ __forceinline__ float clip_from_sumsq(double sumsq, double max_norm, 
     double clip = max_norm / (norm + 1e-6);
     clip = (clip > 1.0) ? 1.0 : clip;
     return static_cast<float>(grad_scale * clip);
+}
+
+// S from the n per-block partials, in block-index order: each thread sums
+// its strided share (partials[tid], [tid + kBlock], ...), then the block
+// combines the threads in a fixed tree.  Every thread returns the same bits,
+// and so does every block that calls this on the same partials.  kAtomic:
+// the partials were written by other blocks of this launch (agent-scope
+// loads after an acquire fence); otherwise by an earlier launch.
+template <bool kAtomic>
+__device__ __forceinline__ double sum_partials(const double* partials, int n, double* lds)
+{
+    if (kAtomic) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    double q = 0.0;
+    for (int i = threadIdx.x; i < n; i += kBlock) {
+        q = q + (kAtomic ? __hip_atomic_load(&partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : partials[i]);
+    }
+    return block_sum(q, lds);
+}
+
+// The step counter.  Every wave reads the completed-step count in its
+// prologue; at its end each block takes a ticket, and the block that takes
+// the last one stores the new count.  The only order this needs is that
+// every read comes before that store: the barrier puts all of a block's waves
+// (each past its read) before its ticket, and the last block stores only
+// after seeing every other ticket.  No block reads data that another block of
+// the launch wrote, so there is no release fence (on this chip an agent-scope
+// release writes back the whole L2, which cost ~20 us per launch on a
+// 62.7M-parameter shard).  Tickets at the end also reach the counter spread
+// over the blocks' finishing times; taken at the start they all arrive at
+// once and queue (measured: the update got slower).
+__device__ __forceinline__ void advance_step(WorkspaceHeader* header, int32_t* d_step, int64_t t)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the compiler keeps the ticket last
+        const unsigned prev = atomicInc(&header->step_ticket, gridDim.x - 1);
+        if (prev == gridDim.x - 1) *d_step = static_cast<int32_t>(t);
+    }
 }
 
 // ------------------------------------------------------------ gradients ---

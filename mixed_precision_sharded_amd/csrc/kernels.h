@@ -29,7 +29,7 @@ hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid,
 // The norm's first stage only: one partial sum per block, and the step
 // number *d_step + 1, in the workspace for a following launch_clipped_step.
 hipError_t launch_grad_norm_partials(const WorkspaceView& ws, bool grad_bf16, int grid,
-                                     const int32_t* d_step, hipStream_t stream);
+                                     const int32_t* d_step, hipStream_t stream, NormBefore next);
 
 hipError_t launch_clip_coef(const double* d_sumsq, double max_norm, double grad_scale,
                             float* d_coef, hipStream_t stream);
@@ -60,6 +60,12 @@ hipError_t launch_fused_step(const WorkspaceView& ws, bool grad_bf16, int grid, 
 hipError_t launch_adamw8_step(const WorkspaceView& ws, const QuantEntry* quant, bool grad_bf16,
                               int grid, const float* d_coef, const double* d_skip_if_nonfinite,
                               int32_t* d_step, const HyperParams& hp, hipStream_t stream);
+
+// The 8-bit update that finishes the norm (as launch_clipped_step).
+hipError_t launch_adamw8_clipped(const WorkspaceView& ws, const QuantEntry* quant, bool grad_bf16,
+                                 int grid, int n_partials, double max_norm, double grad_scale,
+                                 int skip_if_nonfinite, double* d_sumsq, float* d_coef,
+                                 int32_t* d_step, const HyperParams& hp, hipStream_t stream);
 
 hipError_t launch_quantize(const float* x, int64_t n, bool e4m3, uint8_t* codes, uint8_t* scales,
                            hipStream_t stream);

@@ -159,24 +159,6 @@ __device__ __forceinline__ double norm_of_run(const WorkspaceView& ws, uint32_t 
     return mine;
 }
 
-// S from the n per-block partials, in block-index order: each thread sums
-// its strided share (partials[tid], [tid + kBlock], ...), then the block
-// combines the threads in a fixed tree.  Every thread returns the same bits,
-// and so does every block that calls this on the same partials.  kAtomic:
-// the partials were written by other blocks of this launch (agent-scope
-// loads after an acquire fence); otherwise by an earlier launch.
-template <bool kAtomic>
-__device__ __forceinline__ double sum_partials(const double* partials, int n, double* lds)
-{
-    if (kAtomic) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    double q = 0.0;
-    for (int i = threadIdx.x; i < n; i += kBlock) {
-        q = q + (kAtomic ? __hip_atomic_load(&partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                         : partials[i]);
-    }
-    return block_sum(q, lds);
-}
-
 // kFinish: the last block to finish sums the partials and writes S (and the
 // clip coefficient).  Otherwise the launch ends with one partial per block in
 // the workspace, and the step number t = *d_step + 1 in the header, for the
@@ -368,27 +350,6 @@ __device__ __forceinline__ void update_chunks(const WorkspaceView& ws, TensorEnt
         adamw_body<kBf16, kUnroll>(te, qbegin, nquad, s);
         const int64_t tail = qbegin + static_cast<int64_t>(nquad) * 4;
         if (tid < end - tail) adamw_scalar_at<kBf16>(te, tail + tid, s);
-    }
-}
-
-// The step counter.  Every wave reads the completed-step count in its
-// prologue; at its end each block takes a ticket, and the block that takes
-// the last one stores the new count.  The only order this needs is that
-// every read comes before that store: the barrier puts all of a block's waves
-// (each past its read) before its ticket, and the last block stores only
-// after seeing every other ticket.  No block reads data that another block of
-// the launch wrote, so there is no release fence (on this chip an agent-scope
-// release writes back the whole L2, which cost ~20 us per launch on a
-// 62.7M-parameter shard).  Tickets at the end also reach the counter spread
-// over the blocks' finishing times; taken at the start they all arrive at
-// once and queue (measured: the update got slower).
-__device__ __forceinline__ void advance_step(WorkspaceHeader* header, int32_t* d_step, int64_t t)
-{
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the compiler keeps the ticket last
-        const unsigned prev = atomicInc(&header->step_ticket, gridDim.x - 1);
-        if (prev == gridDim.x - 1) *d_step = static_cast<int32_t>(t);
     }
 }
 
@@ -584,10 +545,15 @@ hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid, d
 }
 
 hipError_t launch_grad_norm_partials(const WorkspaceView& ws, bool grad_bf16, int grid,
-                                     const int32_t* d_step, hipStream_t stream)
+                                     const int32_t* d_step, hipStream_t stream, NormBefore next)
 {
-    grad_norm_launch<kNormPolicy, false>(ws, grad_bf16, grid, nullptr, 0.0, 0.0, nullptr, d_step,
-                                         stream);
+    if (next == NormBefore::kQ8Update) {
+        grad_norm_launch<kQ8NormPolicy, false>(ws, grad_bf16, grid, nullptr, 0.0, 0.0, nullptr,
+                                               d_step, stream);
+    } else {
+        grad_norm_launch<kNormPolicy, false>(ws, grad_bf16, grid, nullptr, 0.0, 0.0, nullptr,
+                                             d_step, stream);
+    }
     return hipGetLastError();
 }
 

@@ -400,14 +400,44 @@ __global__ __launch_bounds__(kBlock) void adamw8_step_kernel(
     const int64_t t = static_cast<int64_t>(*d_step) + 1;
     const StepScalars s = step_scalars(t, hp, d_coef ? *d_coef : 1.0f);
     update8_chunks<kBf16>(tensors, quant, chunk_map, n_chunks, chunk_elems, s);
-    // Step counter: the last block to take a ticket stores it (the fp32
-    // kernel explains why no release fence is needed).
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        const unsigned prev = atomicInc(&header->step_ticket, gridDim.x - 1);
-        if (prev == gridDim.x - 1) *d_step = static_cast<int32_t>(t);
+    advance_step(header, d_step, t);
+}
+
+// The update with the end of the norm folded in, as the fp32 state's clipped
+// kernel: every block sums the norm launch's partials in block order (the
+// same bits as the norm's own second stage), forms the coefficient, and takes
+// t from the header, where the norm launch left it; block 0 publishes S, the
+// coefficient and the new count.
+template <bool kBf16>
+__global__ __launch_bounds__(kBlock) void adamw8_clipped_kernel(
+    WorkspaceHeader* header, const TensorEntry* __restrict__ tensors,
+    const QuantEntry* __restrict__ quant, const uint32_t* __restrict__ chunk_map, int n_chunks,
+    int64_t chunk_elems, uint64_t tag, const double* __restrict__ partials, int n_partials,
+    double max_norm, double grad_scale, int skip_if_nonfinite, double* d_sumsq, float* d_coef,
+    int32_t* d_step, HyperParams hp)
+{
+    const int tid = threadIdx.x;
+    const uint64_t seen = header->tag;
+    const int32_t t = header->pending_step;
+    if (seen != tag) {  // tables overwritten: touch nothing, report NaN
+        if (blockIdx.x == 0 && tid == 0) {
+            if (d_sumsq) *d_sumsq = __builtin_nan("");
+            if (d_coef) *d_coef = __builtin_nanf("");
+        }
+        return;
     }
+    __shared__ double lds[kWavesPerBlock];
+    const double total = sum_partials<false>(partials, n_partials, lds);
+    const float clip = clip_from_sumsq(total, max_norm, grad_scale);
+    const bool skip = skip_if_nonfinite && !__builtin_isfinite(total);
+    if (blockIdx.x == 0 && tid == 0) {
+        if (d_sumsq) *d_sumsq = total;
+        if (d_coef) *d_coef = clip;
+        if (!skip) *d_step = t;
+    }
+    if (skip) return;
+    update8_chunks<kBf16>(tensors, quant, chunk_map, n_chunks, chunk_elems,
+                          step_scalars(t, hp, clip));
 }
 
 // ------------------------------------------------------------ conversion ---
@@ -457,6 +487,25 @@ hipError_t launch_adamw8_step(const WorkspaceView& ws, const QuantEntry* quant, 
         adamw8_step_kernel<false><<<grid, kBlock, 0, stream>>>(
             ws.header, ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag, d_coef,
             d_skip_if_nonfinite, d_step, hp);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_adamw8_clipped(const WorkspaceView& ws, const QuantEntry* quant, bool grad_bf16,
+                                 int grid, int n_partials, double max_norm, double grad_scale,
+                                 int skip_if_nonfinite, double* d_sumsq, float* d_coef,
+                                 int32_t* d_step, const HyperParams& hp, hipStream_t stream)
+{
+    if (grad_bf16) {
+        adamw8_clipped_kernel<true><<<grid, kBlock, 0, stream>>>(
+            ws.header, ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag,
+            ws.partials, n_partials, max_norm, grad_scale, skip_if_nonfinite, d_sumsq, d_coef,
+            d_step, hp);
+    } else {
+        adamw8_clipped_kernel<false><<<grid, kBlock, 0, stream>>>(
+            ws.header, ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag,
+            ws.partials, n_partials, max_norm, grad_scale, skip_if_nonfinite, d_sumsq, d_coef,
+            d_step, hp);
     }
     return hipGetLastError();
 }

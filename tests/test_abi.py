@@ -39,6 +39,7 @@ def test_header_declares_the_boundary():
         "adamw_workspace_bytes", "adamw_workspace_release", "grad_norm_sq", "clip_coef",
         "adamw_multi_tensor_step", "adamw_clipped_step", "adamw_fused_step", "adamw_last_error",
         "adamw8_workspace_bytes", "adamw8_grad_norm_sq", "adamw8_multi_tensor_step",
+        "adamw8_clipped_step",
         "adamw8_quantize", "adamw8_dequantize"])
 
 
@@ -151,9 +152,10 @@ def test_whole_step_argument_errors(lib, entry):
         a = dict(mn=1.0, scale=1.0, step=step, lr=3e-4, b1=0.9, b2=0.95, eps=1e-8, wd=0.1,
                  ws=ws, size=1 << 30)
         a.update(kw)
+        extra = (None,) if entry == "adamw_clipped_step" else ()
         return getattr(lib, entry)(arr, 1, 0, a["mn"], a["scale"], 0, None, None, a["step"],
                                    a["lr"], a["b1"], a["b2"], a["eps"], a["wd"], a["ws"],
-                                   a["size"], None)
+                                   a["size"], None, *extra)
 
     assert call(step=None) == EINVAL
     assert call(mn=0.0) == EINVAL

@@ -72,11 +72,19 @@ class Step8:
         self.coef = torch.zeros(1, dtype=torch.float32, device="cuda")
         self.step = torch.tensor([completed_steps], dtype=torch.int32, device="cuda")
 
-    def run(self, max_norm, hp=HP, skip_if_nonfinite=False):
-        binding.adamw8_grad_norm_sq(self.tl, self.sumsq, max_norm, self.coef)
-        binding.adamw8_multi_tensor_step(self.tl, self.coef, self.step, hp["lr"], hp["beta1"],
-                                         hp["beta2"], hp["eps"], hp["wd"],
-                                         skip_if_nonfinite=self.sumsq if skip_if_nonfinite else None)
+    def run(self, max_norm, hp=HP, skip_if_nonfinite=False, clipped=False):
+        """Three calls (norm with the clip output, update), or one
+        adamw8_clipped_step."""
+        if clipped:
+            binding.adamw8_clipped_step(self.tl, self.step, hp["lr"], hp["beta1"], hp["beta2"],
+                                        hp["eps"], hp["wd"], max_norm,
+                                        skip_if_nonfinite=skip_if_nonfinite,
+                                        sumsq_out=self.sumsq, coef_out=self.coef)
+        else:
+            binding.adamw8_grad_norm_sq(self.tl, self.sumsq, max_norm, self.coef)
+            binding.adamw8_multi_tensor_step(
+                self.tl, self.coef, self.step, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                hp["wd"], skip_if_nonfinite=self.sumsq if skip_if_nonfinite else None)
         torch.cuda.synchronize()
         return float(self.sumsq.item()), np.float32(self.coef.item()), int(self.step.item())
 
@@ -112,10 +120,11 @@ def compare(step8, host, what):
     return nbit
 
 
-def step_and_compare(host, what, max_norm=1.0, hp=HP, offset=0, steps=1, completed=0):
+def step_and_compare(host, what, max_norm=1.0, hp=HP, offset=0, steps=1, completed=0,
+                     clipped=False):
     s8 = Step8(host, offset=offset, completed_steps=completed)
     for k in range(steps):
-        S_gpu, c, t = s8.run(max_norm, hp)
+        S_gpu, c, t = s8.run(max_norm, hp, clipped=clipped)
         check_norm(S_gpu, host, f"{what} step {k}")
         assert t == completed + k + 1
         oracle_step(host, c, t, hp)
@@ -136,6 +145,43 @@ def test_q8_ragged_list_bf16_grads_with_copy():
     say("q8 ragged list, bf16 gradients, copy, cold start, two steps")
     step_and_compare(make_host(SIZES, 102, bf16=True, copy_every=2, warm=False), "bf16",
                      steps=2)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_q8_clipped_ragged_two_steps(bf16):
+    say(f"q8 clipped step, ragged list, bf16 gradients={bf16}")
+    step_and_compare(make_host(SIZES, 105 + bf16, bf16=bf16, copy_every=2), f"clipped bf16={bf16}",
+                     steps=2, completed=4, clipped=True)
+
+
+def test_q8_clipped_is_bitwise_the_three_call_step():
+    host = make_host(SIZES + [0, 250000], 107, bf16=True, copy_every=1)
+    a, b = Step8(host, completed_steps=2), Step8(host, completed_steps=2)
+    for _ in range(2):
+        ra = a.run(1.0, clipped=True, skip_if_nonfinite=True)
+        rb = b.run(1.0, clipped=False, skip_if_nonfinite=True)
+        assert np.float64(ra[0]).tobytes() == np.float64(rb[0]).tobytes()
+        assert np.float32(ra[1]).tobytes() == np.float32(rb[1]).tobytes() and ra[2] == rb[2]
+    for da, db in zip(a.dev, b.dev):
+        for k, x in da.items():
+            if x is not None and x.numel():
+                assert torch.equal(x.view(torch.uint8), db[k].view(torch.uint8)), k
+    a.tl.release()
+    b.tl.release()
+
+
+def test_q8_clipped_skip_if_nonfinite():
+    host = make_host([5000, 77], 108, bf16=True, copy_every=1)
+    host[1]["g"][10] = 0x7FC0  # a bf16 NaN
+    s8 = Step8(host, completed_steps=6)
+    before = [{k: x.clone() for k, x in d.items() if x is not None} for d in s8.dev]
+    S, _, t = s8.run(1.0, clipped=True, skip_if_nonfinite=True)
+    assert np.isnan(S) and t == 6
+    for d, b in zip(s8.dev, before):
+        for k, x in b.items():
+            if x.numel():
+                assert torch.equal(d[k].view(torch.uint8), x.view(torch.uint8)), k
+    s8.tl.release()
 
 
 def test_q8_misaligned_views_take_the_element_path():
@@ -385,13 +431,14 @@ def sampled_runs(n, k, rng):
     return sorted(fixed | set(rng.integers(0, nr, size=min(k, nr)).tolist()))
 
 
-@pytest.mark.parametrize("cfg", [2, 5])
-def test_q8_full_size_sampled(cfg):
-    """The bench's workload and launches with 8-bit moments: the sum of
-    squares over every gradient, and sampled runs of 32 recomputed by the
-    oracle from their inputs gathered before the step."""
+@pytest.mark.parametrize("cfg,clipped", [(2, True), (5, True), (2, False)])
+def test_q8_full_size_sampled(cfg, clipped):
+    """The bench's workload and launches with 8-bit moments (the clipped
+    step; once also the three-call step): the sum of squares over every
+    gradient, and sampled runs of 32 recomputed by the oracle from their
+    inputs gathered before the step."""
     from mixed_precision_sharded_amd.configs import WORKLOADS
-    q8_sampled_parity(WORKLOADS[cfg], seed=200 + cfg)
+    q8_sampled_parity(WORKLOADS[cfg], seed=200 + cfg, clipped=clipped)
 
 
 def test_q8_single_tensor_over_2g_elements_sampled():
@@ -407,7 +454,7 @@ def test_q8_single_tensor_over_2g_elements_sampled():
     q8_sampled_parity(w, seed=210, extra_runs=[((1 << 31) >> 5) + d for d in range(-3, 4)])
 
 
-def q8_sampled_parity(w, seed, extra_runs=()):
+def q8_sampled_parity(w, seed, extra_runs=(), clipped=True):
     from mixed_precision_sharded_amd import synth
     from mixed_precision_sharded_amd.synth import to_numpy
 
@@ -440,8 +487,13 @@ def q8_sampled_parity(w, seed, extra_runs=()):
     sumsq = torch.zeros(1, dtype=torch.float64, device="cuda")
     coef = torch.zeros(1, dtype=torch.float32, device="cuda")
     step = torch.tensor([w.step - 1], dtype=torch.int32, device="cuda")
-    binding.adamw8_grad_norm_sq(tl, sumsq, w.max_norm, coef)
-    binding.adamw8_multi_tensor_step(tl, coef, step, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
+    if clipped:
+        binding.adamw8_clipped_step(tl, step, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay,
+                                    w.max_norm, sumsq_out=sumsq, coef_out=coef)
+    else:
+        binding.adamw8_grad_norm_sq(tl, sumsq, w.max_norm, coef)
+        binding.adamw8_multi_tensor_step(tl, coef, step, w.lr, w.beta1, w.beta2, w.eps,
+                                         w.weight_decay)
     torch.cuda.synchronize()
     S, c, t = float(sumsq.item()), np.float32(coef.item()), int(step.item())
     assert t == w.step

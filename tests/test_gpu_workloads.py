@@ -1,5 +1,6 @@
 """GPU parity at the full sizes of the two largest workloads, in the launch
-configuration bench.py times (same library calls on the same list).
+configuration bench.py times (adamw_clipped_step on the same list; one case
+runs the three-call step instead).
 
 The sum of squares is checked against the oracle over every gradient; the
 update is checked element by element on sampled positions (random ones, the
@@ -31,8 +32,10 @@ def _gpu_only():
     torch.cuda.empty_cache()
 
 
-def sampled_parity(w, per_tensor, seed, extra=()):
-    """`extra`: more element indices to check in every tensor (where they exist)."""
+def sampled_parity(w, per_tensor, seed, extra=(), clipped=True):
+    """`extra`: more element indices to check in every tensor (where they
+    exist).  `clipped`: one adamw_clipped_step call, else grad_norm_sq with
+    the clip output followed by adamw_multi_tensor_step."""
     say(f"workload {w.name}: {w.numel:,} params in {w.n_tensors} tensors; generating")
     cols = synth.workload_inputs(w, "cuda")
     torch.cuda.synchronize()
@@ -46,8 +49,12 @@ def sampled_parity(w, per_tensor, seed, extra=()):
     o = oracle.default()
     S_ref = o.grad_norm_sq(to_numpy(g) for g in cols["grad"])  # one tensor on the host at a time
 
-    say("GPU step")
-    st = Step(cols, completed_steps=w.step - 1).full(w)
+    say(f"GPU step ({'clipped' if clipped else 'three calls'})")
+    st = Step(cols, completed_steps=w.step - 1)
+    if clipped:
+        st.clipped(w.max_norm, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
+    else:
+        st.full(w)
     S, c, step = st.results()
     assert step == w.step
     assert abs(S - S_ref) <= NORM_REL_TOL * S_ref, (S, S_ref)
@@ -80,7 +87,7 @@ def test_llama405b_share_sampled():
 
 
 def test_llama405b_share_warm_moments_sampled():
-    sampled_parity(warm(WORKLOADS[5]), per_tensor=2000, seed=51)
+    sampled_parity(warm(WORKLOADS[5]), per_tensor=2000, seed=51, clipped=False)
 
 
 def test_llama8b_full_list_sampled():
