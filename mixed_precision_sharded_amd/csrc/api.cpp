@@ -49,6 +49,7 @@ struct Plan {
     size_t tensors_off = 0;
     size_t quant_off = 0;   // 8-bit lists: QuantEntry table (else == chunks_off)
     size_t chunks_off = 0;
+    size_t tickets_off = 0;
     size_t partials_off = 0;
     size_t total_bytes = 0;
     int n_chunks = 0;
@@ -129,7 +130,9 @@ int layout_plan(std::vector<TensorEntry>& entries, const std::vector<mps::QuantE
     // At least one chunk-map slot (zero for a list without elements), so
     // that the kernels' first lookup is always in the table.
     const int64_t map_slots = n_chunks > 0 ? n_chunks : 1;
-    plan.partials_off = round_up(plan.chunks_off + sizeof(uint32_t) * map_slots, 256);
+    plan.tickets_off = round_up(plan.chunks_off + sizeof(uint32_t) * map_slots, 128);
+    plan.partials_off = round_up(plan.tickets_off + sizeof(uint32_t) * mps::kTicketStride *
+                                                        (mps::kTicketGroups + 1), 256);
     plan.total_bytes = plan.partials_off + sizeof(double) * mps::kPartials;
 
     plan.image.assign(plan.partials_off, 0);
@@ -149,8 +152,6 @@ int layout_plan(std::vector<TensorEntry>& entries, const std::vector<mps::QuantE
     plan.tag = tag ? tag : 1;
 
     WorkspaceHeader* hdr = reinterpret_cast<WorkspaceHeader*>(base);
-    hdr->norm_ticket = 0;
-    hdr->step_ticket = 0;
     hdr->tag = plan.tag;
     hdr->n_tensors = n;
     hdr->n_chunks = plan.n_chunks;
@@ -321,6 +322,7 @@ mps::WorkspaceView view_of(void* ws, const Plan& plan)
     v.header = reinterpret_cast<WorkspaceHeader*>(base);
     v.tensors = reinterpret_cast<const TensorEntry*>(base + plan.tensors_off);
     v.chunk_map = reinterpret_cast<const uint32_t*>(base + plan.chunks_off);
+    v.tickets = reinterpret_cast<uint32_t*>(base + plan.tickets_off);
     v.partials = reinterpret_cast<double*>(base + plan.partials_off);
     v.n_chunks = plan.n_chunks;
     v.solo_tensor = plan.solo_tensor;

@@ -12,6 +12,7 @@ struct WorkspaceView {
     WorkspaceHeader* header;
     const TensorEntry* tensors;
     const uint32_t* chunk_map;
+    uint32_t* tickets;  // the update's step-ticket tree (kTicketGroups + 1 lines)
     double* partials;
     int n_chunks;
     int solo_tensor;  // the index every chunk maps to, or -1 (several tensors)

@@ -205,8 +205,7 @@ __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
         __hip_atomic_store(&ws.partials[blockIdx.x], block_total, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_s_waitcnt(0);
-        const unsigned prev = atomicInc(&ws.header->norm_ticket, gridDim.x - 1);
-        is_last = (prev == gridDim.x - 1);  // the ticket wraps back to 0 here
+        is_last = last_ticket(ws.tickets);
     }
     __syncthreads();
     if (!is_last) return;
@@ -372,7 +371,7 @@ __global__ __launch_bounds__(kBlock) void adamw_step_kernel(
 
     const int64_t t = static_cast<int64_t>(count) + 1;
     update_chunks<kBf16, kUnroll>(ws, first, step_scalars(t, hp, coef));
-    advance_step(ws.header, d_step, t);
+    advance_step(ws.tickets, d_step, t);
 }
 
 // The update with the end of the norm folded in.  A norm launch without the

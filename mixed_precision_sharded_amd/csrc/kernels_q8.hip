@@ -391,7 +391,7 @@ template <bool kBf16>
 __global__ __launch_bounds__(kBlock) void adamw8_step_kernel(
     WorkspaceHeader* header, const TensorEntry* __restrict__ tensors,
     const QuantEntry* __restrict__ quant, const uint32_t* __restrict__ chunk_map, int n_chunks,
-    int64_t chunk_elems, uint64_t tag,
+    int64_t chunk_elems, uint64_t tag, uint32_t* tickets,
     const float* d_coef, const double* d_skip_if_nonfinite, int32_t* d_step, HyperParams hp)
 {
     if (header->tag != tag) return;  // tables overwritten: touch nothing
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(kBlock) void adamw8_step_kernel(
     const int64_t t = static_cast<int64_t>(*d_step) + 1;
     const StepScalars s = step_scalars(t, hp, d_coef ? *d_coef : 1.0f);
     update8_chunks<kBf16>(tensors, quant, chunk_map, n_chunks, chunk_elems, s);
-    advance_step(header, d_step, t);
+    advance_step(tickets, d_step, t);
 }
 
 // The update with the end of the norm folded in, as the fp32 state's clipped
@@ -481,12 +481,12 @@ hipError_t launch_adamw8_step(const WorkspaceView& ws, const QuantEntry* quant, 
 {
     if (grad_bf16) {
         adamw8_step_kernel<true><<<grid, kBlock, 0, stream>>>(
-            ws.header, ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag, d_coef,
-            d_skip_if_nonfinite, d_step, hp);
+            ws.header, ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag,
+            ws.tickets, d_coef, d_skip_if_nonfinite, d_step, hp);
     } else {
         adamw8_step_kernel<false><<<grid, kBlock, 0, stream>>>(
-            ws.header, ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag, d_coef,
-            d_skip_if_nonfinite, d_step, hp);
+            ws.header, ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag,
+            ws.tickets, d_coef, d_skip_if_nonfinite, d_step, hp);
     }
     return hipGetLastError();
 }

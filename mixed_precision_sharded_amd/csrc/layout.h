@@ -5,9 +5,12 @@
 //   [64, 64 + 64*T)              TensorEntry[T]
 //   [.., + 32*T)                 QuantEntry[T] (8-bit moment lists only)
 //   [.., + 4*max(K, 1))          uint32 chunk -> tensor index, K chunks
+//   [.. rounded to 128, + 128*(kTicketGroups + 1))  the update's step tickets,
+//                                one uint32 per 128-byte line
 //   [.. rounded to 256, + 8*kPartials)  fp64 per-block partial sums of the norm
 // Everything before the partials is written by one host-to-device copy when
-// the list changes; the partials need no initial value.
+// the list changes (the tickets start at zero and every complete launch
+// brings them back to zero); the partials need no initial value.
 #pragma once
 
 #include <stdint.h>
@@ -49,14 +52,15 @@ constexpr int kStepMaxBlocks = MPS_STEP_MAX_BLOCKS;
 constexpr int kFusedMaxBlocks = MPS_FUSED_MAX_BLOCKS;
 constexpr int kQ8MaxBlocks = MPS_Q8_MAX_BLOCKS;
 constexpr int kPartials = kNormMaxBlocks > kFusedMaxBlocks ? kNormMaxBlocks : kFusedMaxBlocks;
+constexpr int kTicketGroups = 8;                   // first level of the step-ticket tree
+constexpr int kTicketStride = 32;                  // uint32s between tickets (128 B)
 constexpr int64_t kChunkQuantum = 2048;            // chunk sizes are multiples of this
 constexpr int64_t kChunkMin = MPS_CHUNK_MIN;
 constexpr int64_t kChunkMax = MPS_CHUNK_MAX;
 constexpr int64_t kChunkTarget = MPS_CHUNK_TARGET;
 
 struct alignas(64) WorkspaceHeader {
-    uint32_t norm_ticket;   // blocks of the norm kernel that have finished
-    uint32_t step_ticket;   // blocks of the update kernel that have finished
+    uint32_t reserved[2];
     uint64_t tag;           // identifies the uploaded tables
     int32_t n_tensors;
     int32_t n_chunks;

@@ -148,6 +148,29 @@ def _hp():
     return dict(lr=HP["lr"], beta1=HP["beta1"], beta2=HP["beta2"], eps=HP["eps"], wd=HP["wd"])
 
 
+@pytest.mark.parametrize("blocks", [1, 2, 7, 8, 9, 15, 17, 100])
+def test_ticket_tree_at_every_group_shape(blocks):
+    """One tensor of `blocks` chunks of 2048 elements: both the norm and the
+    three-call update run `blocks` blocks, so their ticket trees have groups
+    of equal and unequal sizes, or fewer groups than eight.  Four steps in a
+    row: the norm's last block must finish S every time and the counter must
+    advance by exactly one per update."""
+    n = blocks * 2048
+    cols = make_cols([n], True, True, seed=400 + blocks)
+    host = host_copy(cols)
+    st = Step(cols, completed_steps=10)
+    o = oracle.default()
+    S_ref = o.grad_norm_sq(host["grad"])
+    for t in range(11, 15):
+        st.norm_clip(1.0).update(HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+        S, c, step = st.results()
+        assert step == t, (blocks, t, step)
+        assert abs(S - S_ref) <= NORM_REL_TOL * S_ref, (blocks, S, S_ref)
+        oracle_step(host, c, t, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+    stats = compare_state(cols, host, f"{blocks} blocks")
+    assert stats["w"][0] == stats["m"][0] == stats["v"][0] == 0
+
+
 def test_no_coef_means_no_clipping():
     cols = make_cols([5000, 77], False, True, seed=6, grad_std=1.0)
     run_and_check(cols, t=1, what="no coef", use_coef=False)
