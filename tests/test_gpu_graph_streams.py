@@ -2,7 +2,8 @@
 several times (with unrelated eager work and synchronizations between the
 replays) equals the same steps run eagerly, bitwise; two lists with their own
 workspaces stepped on two streams at once equal the same steps run one after
-the other.  Both for fp32 and for 8-bit moments.
+the other.  For fp32 and 8-bit moments, and for both two-launch forms of the
+step (three calls, and the one clipped-step call).
 
 A list's tables are uploaded by its first call (a host-to-device copy), so a
 caller records a graph after one eager call on the list; the norm alone
@@ -42,8 +43,9 @@ def clone(d):
 
 
 class Runner:
-    def __init__(self, d, q8):
+    def __init__(self, d, q8, clipped=False):
         self.q8 = q8
+        self.clipped = clipped
         self.d = d
         if q8:
             self.tl = binding.TensorList8(d["w"], d["st"], d["g"], d["p"])
@@ -60,6 +62,15 @@ class Runner:
     def update(self, stream=None):
         f = binding.adamw8_multi_tensor_step if self.q8 else binding.adamw_multi_tensor_step
         f(self.tl, self.coef, self.step, *HP, stream=stream)
+
+    def full_step(self, stream=None):
+        if self.clipped:
+            f = binding.adamw8_clipped_step if self.q8 else binding.adamw_clipped_step
+            f(self.tl, self.step, *HP, 1.0, sumsq_out=self.sumsq, coef_out=self.coef,
+              stream=stream)
+        else:
+            self.norm(stream)
+            self.update(stream)
 
     def state(self):
         torch.cuda.synchronize()
@@ -79,22 +90,25 @@ def same(a, b, what):
         assert torch.equal(xb, yb), f"{what}: buffer {i} differs"
 
 
+FORMS = [False, True]
+FORM_IDS = ["three_calls", "clipped"]
+
+
+@pytest.mark.parametrize("clipped", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("q8", [False, True], ids=["fp32_moments", "8bit_moments"])
-def test_graph_replays_equal_eager_steps(q8):
-    say(f"graph capture, 8-bit={q8}")
+def test_graph_replays_equal_eager_steps(q8, clipped):
+    say(f"graph capture, 8-bit={q8}, clipped={clipped}")
     sizes = [5, 4096 + 3, 100000]
     base = inputs(sizes, 61, q8)
-    eager, graphed = Runner(clone(base), q8), Runner(clone(base), q8)
+    eager, graphed = Runner(clone(base), q8, clipped), Runner(clone(base), q8, clipped)
     graphed.norm()                      # uploads the tables; changes no state
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        graphed.norm()
-        graphed.update()
+        graphed.full_step()
     scratch = torch.randn(1 << 20, device="cuda")
     for k in range(3):
-        eager.norm()
-        eager.update()
+        eager.full_step()
         g.replay()
         scratch.mul_(1.0001).add_(1.0)  # unrelated eager work between replays
         torch.cuda.synchronize()
@@ -104,20 +118,24 @@ def test_graph_replays_equal_eager_steps(q8):
     graphed.tl.release()
 
 
+@pytest.mark.parametrize("clipped", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("q8", [False, True], ids=["fp32_moments", "8bit_moments"])
-def test_two_lists_on_two_streams(q8):
-    say(f"two streams, 8-bit={q8}")
+def test_two_lists_on_two_streams(q8, clipped):
+    say(f"two streams, 8-bit={q8}, clipped={clipped}")
     a0, b0 = inputs([70000, 33], 62, q8), inputs([123457], 63, q8)
-    seq_a, seq_b = Runner(clone(a0), q8), Runner(clone(b0), q8)
+    seq_a, seq_b = Runner(clone(a0), q8, clipped), Runner(clone(b0), q8, clipped)
     for _ in range(3):
-        seq_a.norm(); seq_a.update()
-        seq_b.norm(); seq_b.update()
-    con_a, con_b = Runner(clone(a0), q8), Runner(clone(b0), q8)
+        seq_a.full_step()
+        seq_b.full_step()
+    con_a, con_b = Runner(clone(a0), q8, clipped), Runner(clone(b0), q8, clipped)
     torch.cuda.synchronize()
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     for _ in range(3):
-        con_a.norm(s1); con_b.norm(s2)
-        con_a.update(s1); con_b.update(s2)
+        if clipped:
+            con_a.full_step(s1); con_b.full_step(s2)
+        else:
+            con_a.norm(s1); con_b.norm(s2)
+            con_a.update(s1); con_b.update(s2)
     torch.cuda.synchronize()
     same(seq_a.state(), con_a.state(), "list a")
     same(seq_b.state(), con_b.state(), "list b")
