@@ -275,6 +275,13 @@ struct Uploaded {
     uint64_t tag = 0;
     std::vector<unsigned char> image;  // source of the last upload, kept alive
     hipEvent_t done = nullptr;         // recorded after that upload
+    // The call that last planned this workspace: list kind, gradient dtype
+    // and the caller's tensor array, byte for byte; whether its state
+    // pointers were checked (a norm-only call leaves them unchecked); and its
+    // plan without the image.
+    std::vector<unsigned char> key;
+    bool state_checked = false;
+    Plan meta;
 };
 
 std::mutex g_cache_mutex;
@@ -312,6 +319,58 @@ int ensure_uploaded(void* ws, Plan& plan, hipStream_t stream)
     e = hipEventRecord(u.done, stream);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "hipEventRecord: %s", hipGetErrorString(e));
     u.tag = plan.tag;
+    return MPS_OK;
+}
+
+int plan_list(const mps_tensor* t, int n, int grad_dtype, bool need_state, Plan& plan)
+{
+    return build_plan(t, n, grad_dtype, need_state, plan);
+}
+
+int plan_list(const mps_tensor8* t, int n, int grad_dtype, bool need_state, Plan& plan)
+{
+    return build_plan8(t, n, grad_dtype, need_state, plan);
+}
+
+// The plan of a call, with its tables in the workspace.  When the workspace
+// was last planned for this very list (same kind, gradient dtype and tensor
+// array, byte for byte, and the state pointers checked if this call needs
+// them), that plan is reused: validating, chunking and hashing a list costs
+// the host 7 us for one tensor and 0.4 ms for 1137 (3 ms for the 8B-parameter
+// list of 291 tensors, 490K chunks), on every call.  Otherwise the list is
+// validated, planned and, if its tables differ from the workspace's,
+// uploaded.  The device still compares the table tag, so a workspace written
+// behind the library's back is never trusted.
+template <class Tensor>
+int prepare(const Tensor* tensors, int n, int grad_dtype, bool need_state, void* ws,
+            size_t ws_bytes, hipStream_t stream, Plan& plan)
+{
+    std::vector<unsigned char> key;
+    if (tensors && n > 0) {
+        const unsigned char head[2] = {static_cast<unsigned char>(sizeof(Tensor)),
+                                       static_cast<unsigned char>(grad_dtype)};
+        key.assign(head, head + 2);
+        const auto* raw = reinterpret_cast<const unsigned char*>(tensors);
+        key.insert(key.end(), raw, raw + sizeof(Tensor) * static_cast<size_t>(n));
+        std::lock_guard<std::mutex> lock(g_cache_mutex);
+        auto it = g_cache.find(ws);
+        if (it != g_cache.end() && it->second.done && it->second.key == key &&
+            (!need_state || it->second.state_checked)) {
+            plan = it->second.meta;
+            return check_workspace(ws, ws_bytes, plan);
+        }
+    }
+    int rc = plan_list(tensors, n, grad_dtype, need_state, plan);
+    if (rc) return rc;
+    if ((rc = check_workspace(ws, ws_bytes, plan))) return rc;
+    if ((rc = ensure_uploaded(ws, plan, stream))) return rc;
+    std::lock_guard<std::mutex> lock(g_cache_mutex);
+    Uploaded& u = g_cache[ws];
+    u.key.swap(key);
+    u.state_checked = need_state;
+    u.meta = plan;
+    u.meta.image.clear();
+    u.meta.image.shrink_to_fit();
     return MPS_OK;
 }
 
@@ -369,14 +428,10 @@ int check_clip_arguments(double max_norm, double grad_scale)
 }
 
 // Launch the norm (and optionally the clip coefficient) over a planned list.
-int run_grad_norm(Plan& plan, bool bf16, double* d_sumsq, double max_norm,
-                  double grad_scale, float* d_coef, void* d_workspace, size_t workspace_bytes,
-                  void* stream, mps::NormBefore next)
+int run_grad_norm(const Plan& plan, bool bf16, double* d_sumsq, double max_norm,
+                  double grad_scale, float* d_coef, void* d_workspace, hipStream_t st,
+                  mps::NormBefore next)
 {
-    int rc = check_workspace(d_workspace, workspace_bytes, plan);
-    if (rc) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
     const int grid = grid_for(plan.n_chunks, mps::kNormMaxBlocks);
     hipError_t e = mps::launch_grad_norm(view_of(d_workspace, plan), bf16, grid, d_sumsq, max_norm,
                                          grad_scale, d_coef, st, next);
@@ -397,14 +452,9 @@ int check_clipped_arguments(const int32_t* d_step, double max_norm, double grad_
 // sums (and the step number) into the workspace, the optional event, then
 // `update(view, norm grid, stream)`, which finishes the sum.
 template <class Update>
-int run_clipped(Plan& plan, bool bf16, const int32_t* d_step, void* d_workspace,
-                size_t workspace_bytes, void* stream, void* mid_event, mps::NormBefore next,
-                Update update)
+int run_clipped(const Plan& plan, bool bf16, const int32_t* d_step, void* d_workspace,
+                hipStream_t st, void* mid_event, mps::NormBefore next, Update update)
 {
-    int rc = check_workspace(d_workspace, workspace_bytes, plan);
-    if (rc) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
     const mps::WorkspaceView ws = view_of(d_workspace, plan);
     // The same norm grid as grad_norm_sq, so the partials and S match it.
     const int norm_grid = grid_for(plan.n_chunks, mps::kNormMaxBlocks);
@@ -455,9 +505,13 @@ int grad_norm_sq(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
     int rc = d_coef ? check_clip_arguments(max_norm, grad_scale) : MPS_OK;
     if (rc) return rc;
     Plan plan;
-    if ((rc = build_plan(tensors, n_tensors, grad_dtype, false, plan))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = prepare(tensors, n_tensors, grad_dtype, false, d_workspace, workspace_bytes, st,
+                      plan))) {
+        return rc;
+    }
     return run_grad_norm(plan, grad_dtype == MPS_DTYPE_BF16, d_sumsq, max_norm, grad_scale, d_coef,
-                         d_workspace, workspace_bytes, stream, mps::NormBefore::kUpdate);
+                         d_workspace, st, mps::NormBefore::kUpdate);
 }
 
 int clip_coef(const double* d_sumsq, double max_norm, double grad_scale, float* d_coef,
@@ -481,10 +535,11 @@ int adamw_multi_tensor_step(const mps_tensor* tensors, int n_tensors, mps_dtype 
     int rc = check_hyperparameters(lr, beta1, beta2, eps, weight_decay);
     if (rc) return rc;
     Plan plan;
-    if ((rc = build_plan(tensors, n_tensors, grad_dtype, true, plan))) return rc;
-    if ((rc = check_workspace(d_workspace, workspace_bytes, plan))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
+    if ((rc = prepare(tensors, n_tensors, grad_dtype, true, d_workspace, workspace_bytes, st,
+                      plan))) {
+        return rc;
+    }
     mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
     const int grid = grid_for(plan.n_chunks, mps::kStepMaxBlocks);
     hipError_t e = mps::launch_adamw_step(view_of(d_workspace, plan), grad_dtype == MPS_DTYPE_BF16,
@@ -503,16 +558,17 @@ int adamw_fused_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dt
                                      weight_decay);
     if (rc) return rc;
     Plan plan;
-    if ((rc = build_plan(tensors, n_tensors, grad_dtype, true, plan))) return rc;
-    if ((rc = check_workspace(d_workspace, workspace_bytes, plan))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = prepare(tensors, n_tensors, grad_dtype, true, d_workspace, workspace_bytes, st,
+                      plan))) {
+        return rc;
+    }
     const bool bf16 = grad_dtype == MPS_DTYPE_BF16;
     int resident = 0;
     hipError_t e = mps::fused_grid_limit(bf16, &resident);
     if (e != hipSuccess || resident < 1) {
         return fail(MPS_ERR_DEVICE, "fused step occupancy query: %s", hipGetErrorString(e));
     }
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
     const int cap = resident < mps::kFusedMaxBlocks ? resident : mps::kFusedMaxBlocks;
     const int grid = grid_for(plan.n_chunks, cap);
     mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
@@ -532,11 +588,15 @@ int adamw_clipped_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_
                                      weight_decay);
     if (rc) return rc;
     Plan plan;
-    if ((rc = build_plan(tensors, n_tensors, grad_dtype, true, plan))) return rc;
+    hipStream_t stream_ = static_cast<hipStream_t>(stream);
+    if ((rc = prepare(tensors, n_tensors, grad_dtype, true, d_workspace, workspace_bytes, stream_,
+                      plan))) {
+        return rc;
+    }
     const bool bf16 = grad_dtype == MPS_DTYPE_BF16;
     const mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
     const int grid = grid_for(plan.n_chunks, mps::kStepMaxBlocks);
-    return run_clipped(plan, bf16, d_step, d_workspace, workspace_bytes, stream, mid_event,
+    return run_clipped(plan, bf16, d_step, d_workspace, stream_, mid_event,
                        mps::NormBefore::kUpdate,
                        [&](const mps::WorkspaceView& ws, int norm_grid, hipStream_t st) {
                            return mps::launch_clipped_step(ws, bf16, grid, norm_grid, max_norm,
@@ -561,9 +621,13 @@ int adamw8_grad_norm_sq(const mps_tensor8* tensors, int n_tensors, mps_dtype gra
     int rc = d_coef ? check_clip_arguments(max_norm, grad_scale) : MPS_OK;
     if (rc) return rc;
     Plan plan;
-    if ((rc = build_plan8(tensors, n_tensors, grad_dtype, false, plan))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = prepare(tensors, n_tensors, grad_dtype, false, d_workspace, workspace_bytes, st,
+                      plan))) {
+        return rc;
+    }
     return run_grad_norm(plan, grad_dtype == MPS_DTYPE_BF16, d_sumsq, max_norm, grad_scale, d_coef,
-                         d_workspace, workspace_bytes, stream, mps::NormBefore::kQ8Update);
+                         d_workspace, st, mps::NormBefore::kQ8Update);
 }
 
 int adamw8_multi_tensor_step(const mps_tensor8* tensors, int n_tensors, mps_dtype grad_dtype,
@@ -576,10 +640,11 @@ int adamw8_multi_tensor_step(const mps_tensor8* tensors, int n_tensors, mps_dtyp
     int rc = check_hyperparameters(lr, beta1, beta2, eps, weight_decay);
     if (rc) return rc;
     Plan plan;
-    if ((rc = build_plan8(tensors, n_tensors, grad_dtype, true, plan))) return rc;
-    if ((rc = check_workspace(d_workspace, workspace_bytes, plan))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((rc = ensure_uploaded(d_workspace, plan, st))) return rc;
+    if ((rc = prepare(tensors, n_tensors, grad_dtype, true, d_workspace, workspace_bytes, st,
+                      plan))) {
+        return rc;
+    }
     mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
     const int grid = grid_for(plan.n_chunks, mps::kQ8MaxBlocks);
     const auto* quant = reinterpret_cast<const mps::QuantEntry*>(static_cast<unsigned char*>(d_workspace) +
@@ -601,13 +666,17 @@ int adamw8_clipped_step(const mps_tensor8* tensors, int n_tensors, mps_dtype gra
                                      weight_decay);
     if (rc) return rc;
     Plan plan;
-    if ((rc = build_plan8(tensors, n_tensors, grad_dtype, true, plan))) return rc;
+    hipStream_t stream_ = static_cast<hipStream_t>(stream);
+    if ((rc = prepare(tensors, n_tensors, grad_dtype, true, d_workspace, workspace_bytes, stream_,
+                      plan))) {
+        return rc;
+    }
     const bool bf16 = grad_dtype == MPS_DTYPE_BF16;
     const mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
     const int grid = grid_for(plan.n_chunks, mps::kQ8MaxBlocks);
     const auto* quant = reinterpret_cast<const mps::QuantEntry*>(static_cast<unsigned char*>(d_workspace) +
                                                                  plan.quant_off);
-    return run_clipped(plan, bf16, d_step, d_workspace, workspace_bytes, stream, mid_event,
+    return run_clipped(plan, bf16, d_step, d_workspace, stream_, mid_event,
                        mps::NormBefore::kQ8Update,
                        [&](const mps::WorkspaceView& ws, int norm_grid, hipStream_t st) {
                            return mps::launch_adamw8_clipped(ws, quant, bf16, grid, norm_grid,

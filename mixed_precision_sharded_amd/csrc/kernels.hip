@@ -7,13 +7,22 @@
 //
 //   grad_norm_kernel  sum of g^2 over the tensor list: exact squares summed in
 //                     fp64 per thread, a DPP/cross-lane wavefront reduction, an
-//                     LDS combine per block, and a deterministic second stage
-//                     run by the last block to finish (atomic ticket).
+//                     LDS combine per block; then either a deterministic
+//                     second stage run by the last block to finish (ticket
+//                     tree), or, for the clipped step, nothing more: the
+//                     per-block partials stay in the workspace.
 //   clip_coef_kernel  c = min(1, max_norm / (sqrt(S) + 1e-6)), fp64, one lane.
-//   adamw_step_kernel the fused update: clip scaling, both moments, decoupled
-//                     weight decay, bias corrections derived on the device from
-//                     the step counter, the optional bf16 copy, and the
-//                     counter write-back by the last block.
+//   adamw_clipped_kernel  the clipped step's update: every block first sums
+//                     the norm's partials (the same order and bits as the
+//                     second stage) and forms the clip coefficient; block 0
+//                     stores the step counter.
+//   adamw_step_kernel the three-call step's update, given the coefficient;
+//                     the counter is stored by the block with the last ticket.
+//                     Both updates share one body: clip scaling, both
+//                     moments, decoupled weight decay, bias corrections
+//                     derived on the device from the step counter, the
+//                     optional bf16 copy.
+//   adamw_fused_kernel the whole step in one cooperative launch.
 //
 // Memory access: each chunk's aligned body is addressed through buffer
 // resources (base and size in scalar registers, 32-bit per-lane offsets).

@@ -9,7 +9,10 @@
 // it under the format's largest code, and re-encodes with the hardware's
 // round-to-nearest-even conversions.
 //
-//   adamw8_step_kernel  the update.  A thread takes four consecutive
+//   adamw8_clipped_kernel / adamw8_step_kernel
+//                       the update, in the clipped step (finishing the norm's
+//                       partials first) or given the coefficient, as the
+//                       fp32-state pair.  A thread takes four consecutive
 //                       elements, so eight lanes hold one run of 32 and its
 //                       largest magnitude is three DPP exchanges away, and
 //                       every access of an instruction is contiguous across

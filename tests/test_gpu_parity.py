@@ -357,6 +357,66 @@ def test_overwritten_workspace_is_detected():
     assert torch.equal(cols["master"][0], before[0])
 
 
+def test_one_workspace_shared_by_two_lists():
+    """Two lists step in turn on one workspace, in both two-launch forms: each
+    call finds the other list's tables there, so the library's cached plan
+    must not be reused; every step matches the oracle bitwise."""
+    a = make_cols([300000, 5, 77], True, True, seed=90)
+    b = make_cols([70001], False, True, seed=91)
+    ha, hb = host_copy(a), host_copy(b)
+    sa, sb = Step(a, completed_steps=0), Step(b, completed_steps=5)
+    assert sa.tl.workspace_bytes >= sb.tl.workspace_bytes
+    sb.tl.release()
+    sb.tl._ws_storage = sa.tl._ws_storage
+    sb.tl.workspace_ptr, sb.tl.workspace_bytes = sa.tl.workspace_ptr, sa.tl.workspace_bytes
+    hp = (HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+    for k in range(4):
+        for st, h in ((sa, ha), (sb, hb)):
+            t_next = int(st.step.item()) + 1
+            if k % 2:
+                st.clipped(1.0, *hp)
+            else:
+                st.norm_clip(1.0).update(*hp)
+            S, c, t = st.results()
+            assert t == t_next, (k, t, t_next)
+            S_ref = oracle_norm(h["grad"])
+            assert abs(S - S_ref) <= NORM_REL_TOL * S_ref, (k, S, S_ref)
+            oracle_step(h, c, t, *hp)
+    for cols, h, what in ((a, ha, "list a"), (b, hb, "list b")):
+        stats = compare_state(cols, h, what)
+        assert stats["w"][0] == stats["m"][0] == stats["v"][0] == 0, what
+
+
+def test_norm_only_list_then_step_still_checks_state_pointers():
+    """A list without state pointers is valid for the norm; the same tensor
+    array passed to a step on the same workspace must still be refused,
+    although the library has a plan for it."""
+    L = binding.lib()
+    g = torch.randn(4096, device=DEV) * 1e-2
+    arr = (binding.MpsTensor * 1)()
+    arr[0] = binding.MpsTensor(None, None, None, g.data_ptr(), None, 4096)
+    nbytes = L.adamw_workspace_bytes(arr, 1)
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=DEV)
+    ws = (buf.data_ptr() + 255) // 256 * 256
+    S = torch.zeros(1, dtype=torch.float64, device=DEV)
+    step = torch.zeros(1, dtype=torch.int32, device=DEV)
+    assert L.grad_norm_sq(arr, 1, binding.MPS_DTYPE_F32, S.data_ptr(), 1.0, 1.0, None, ws,
+                          nbytes, None) == 0
+    torch.cuda.synchronize()
+    assert abs(S.item() - float((g.double() ** 2).sum())) <= 1e-12 * S.item()
+    assert L.adamw_multi_tensor_step(arr, 1, binding.MPS_DTYPE_F32, None, None, step.data_ptr(),
+                                     3e-4, 0.9, 0.95, 1e-8, 0.1, ws, nbytes, None) == -22
+    assert "NULL" in binding.last_error()
+    assert L.adamw_clipped_step(arr, 1, binding.MPS_DTYPE_F32, 1.0, 1.0, 0, None, None,
+                                step.data_ptr(), 3e-4, 0.9, 0.95, 1e-8, 0.1, ws, nbytes, None,
+                                None) == -22
+    assert L.grad_norm_sq(arr, 1, binding.MPS_DTYPE_F32, S.data_ptr(), 1.0, 1.0, None, ws,
+                          nbytes, None) == 0
+    torch.cuda.synchronize()
+    assert int(step.item()) == 0
+    L.adamw_workspace_release(ws)
+
+
 # ------------------------------------------------------------- workloads ---
 
 def _workload_cols(w):
