@@ -14,7 +14,14 @@
  * (2N, mixed basis) or fp32 (4N, pure-fp32 basis), and a bf16 parameter copy
  * (2N) that is only ever written from the fp32 master.
  *
- * A step is two or three calls on one stream, none of which waits on the host:
+ * A step is one call, none of which waits on the host:
+ *
+ *     adamw_clipped_step(list, ..., max_norm, grad_scale, ..., d_step, ..., ws, ...)
+ *                      two launches: the norm's per-block partial sums, then
+ *                      the update, which finishes S and the clip coefficient
+ *
+ * or, where the caller combines S itself first (e.g. across the ranks of a
+ * sharded group), two or three calls on one stream:
  *
  *     grad_norm_sq(list, ..., d_sumsq, max_norm, grad_scale, d_coef, ws, ...)
  *                      S = sum of g^2, and (optionally, same launch)
@@ -85,16 +92,18 @@ typedef struct mps_tensor {
 } mps_tensor;
 
 /*
- * Size in bytes of the device workspace that grad_norm_sq and
- * adamw_multi_tensor_step need for this list (a header, the per-tensor and
- * per-chunk tables, and one fp64 partial per norm block).  It grows with the
- * number of tensors and chunks, not with the bytes of state.  Returns 0 and
- * sets the last error if the list is invalid.
+ * Size in bytes of the device workspace that the fp32-state entry points need
+ * for this list (a header, the per-tensor and per-chunk tables, the lines of
+ * the blocks' ticket counters, and one fp64 partial per norm block).  It
+ * grows with the number of tensors and chunks, not with the bytes of state.
+ * Returns 0 and sets the last error if the list is invalid.
  *
  * The workspace must be 256-byte aligned.  It carries the list's tables from
  * one call to the next: the library uploads them (a host-to-device copy on
  * the call's stream) only when the list differs from the one it last
- * uploaded into that workspace.  Before freeing a workspace, or handing its
+ * uploaded into that workspace, and when a call passes the same tensor array
+ * (byte for byte) as the call that last planned the workspace, it reuses
+ * that plan without validating and chunking the list again.  Before freeing a workspace, or handing its
  * memory to another user, call adamw_workspace_release on it.  A workspace
  * whose tables were overwritten behind the library's back is detected by the
  * kernels, which then leave every buffer untouched (grad_norm_sq writes NaN).
