@@ -90,11 +90,23 @@ int common_head(const mps::TensorEntry& e, bool grad_bf16)
     return -1;
 }
 
-uint64_t fnv1a(const unsigned char* p, size_t n, uint64_t h = 1469598103934665603ull)
+// A 64-bit digest of the tables, eight bytes per step (a byte-at-a-time hash
+// cost the host ~1 ns per byte: 2 ms per call for the 8B model's 2 MB chunk
+// map).  Each word is folded in with a multiply by an odd constant and a
+// shift-xor; it only has to tell one set of tables from another.
+uint64_t digest(const unsigned char* p, size_t n, uint64_t h)
 {
-    for (size_t i = 0; i < n; ++i) {
-        h ^= p[i];
-        h *= 1099511628211ull;
+    constexpr uint64_t kOdd = 0x9E3779B97F4A7C15ull;
+    size_t i = 0;
+    for (; i + 8 <= n; i += 8) {
+        uint64_t w;
+        std::memcpy(&w, p + i, 8);
+        h = (h ^ w) * kOdd;
+        h ^= h >> 29;
+    }
+    for (; i < n; ++i) {
+        h = (h ^ p[i]) * kOdd;
+        h ^= h >> 29;
     }
     return h;
 }
@@ -147,8 +159,10 @@ int layout_plan(std::vector<TensorEntry>& entries, const std::vector<mps::QuantE
 
     // The tag identifies the tables; it never equals zero, so freshly
     // zeroed memory is never mistaken for an upload.
-    uint64_t tag = fnv1a(base + plan.tensors_off, plan.partials_off - plan.tensors_off);
-    tag = fnv1a(reinterpret_cast<const unsigned char*>(&plan.chunk_elems), sizeof plan.chunk_elems, tag);
+    uint64_t tag = digest(base + plan.tensors_off, plan.partials_off - plan.tensors_off,
+                          0x6D70735F74616273ull);
+    tag = digest(reinterpret_cast<const unsigned char*>(&plan.chunk_elems), sizeof plan.chunk_elems,
+                 tag);
     plan.tag = tag ? tag : 1;
 
     WorkspaceHeader* hdr = reinterpret_cast<WorkspaceHeader*>(base);
