@@ -45,7 +45,7 @@ int ok()
 // Host image of everything the kernels read from the workspace, plus where
 // each part sits.
 struct Plan {
-    std::vector<unsigned char> image;  // header + tensor entries + chunk map
+    std::vector<unsigned char> image;  // header, tensor entries, chunk map, ticket lines
     size_t tensors_off = 0;
     size_t quant_off = 0;   // 8-bit lists: QuantEntry table (else == chunks_off)
     size_t chunks_off = 0;
@@ -327,6 +327,7 @@ int ensure_uploaded(void* ws, Plan& plan, hipStream_t stream)
         if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "hipEventCreate: %s", hipGetErrorString(e));
     }
     u.tag = 0;
+    u.key.clear();  // until this upload is enqueued, no plan matches the workspace
     u.image.swap(plan.image);
     hipError_t e = hipMemcpyAsync(ws, u.image.data(), u.image.size(), hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "table upload: %s", hipGetErrorString(e));

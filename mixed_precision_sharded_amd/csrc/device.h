@@ -187,30 +187,6 @@ __device__ __forceinline__ double sum_partials(const double* partials, int n, do
     return block_sum(q, lds);
 }
 
-// The step counter.  Every wave reads the completed-step count in its
-// prologue; at its end each block takes a ticket, and the block that takes
-// the last one stores the new count.  The only order this needs is that
-// every read comes before that store: the barrier puts all of a block's waves
-// (each past its read) before its ticket, and the last block stores only
-// after seeing every other ticket.  No block reads data that another block of
-// the launch wrote, so there is no release fence (on this chip an agent-scope
-// release writes back the whole L2, which cost ~20 us per launch on a
-// 62.7M-parameter shard).
-//
-// The tickets form a two-level tree (`last_ticket`).  Taking them at the
-// start of the block instead was measured slower: the atomics then queue
-// before any data moves.
-__device__ __forceinline__ bool last_ticket(uint32_t* tickets);
-
-__device__ __forceinline__ void advance_step(uint32_t* tickets, int32_t* d_step, int64_t t)
-{
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the compiler keeps the ticket last
-        if (last_ticket(tickets)) *d_step = static_cast<int32_t>(t);
-    }
-}
-
 // One ticket per block (called by one thread of each block of a launch);
 // true in the block that takes the last one.  Two levels, each counter on
 // its own 128-byte line: block b counts in group b mod 8, and the last block
@@ -230,6 +206,25 @@ __device__ __forceinline__ bool last_ticket(uint32_t* tickets)
     const uint32_t members = grid / groups + (g < grid % groups ? 1u : 0u);
     return atomicInc(&tickets[kTicketStride * g], members - 1) == members - 1 &&
            atomicInc(&tickets[kTicketStride * kTicketGroups], groups - 1) == groups - 1;
+}
+
+// The step counter.  Every wave reads the completed-step count in its
+// prologue; at its end each block takes a ticket, and the block that takes
+// the last one stores the new count.  The only order this needs is that
+// every read comes before that store: the barrier puts all of a block's waves
+// (each past its read) before its ticket, and the last block stores only
+// after seeing every other ticket.  No block reads data that another block of
+// the launch wrote, so there is no release fence (on this chip an agent-scope
+// release writes back the whole L2, which cost ~20 us per launch on a
+// 62.7M-parameter shard).  Taking the tickets at the start of the block
+// instead was measured slower: the atomics then queue before any data moves.
+__device__ __forceinline__ void advance_step(uint32_t* tickets, int32_t* d_step, int64_t t)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the compiler keeps the ticket last
+        if (last_ticket(tickets)) *d_step = static_cast<int32_t>(t);
+    }
 }
 
 // ------------------------------------------------------------ gradients ---
