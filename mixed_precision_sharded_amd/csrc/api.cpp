@@ -3,6 +3,7 @@
 // kernel launches.  Declared in include/mps_adamw.h.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -442,14 +443,28 @@ int check_clip_arguments(double max_norm, double grad_scale)
     return MPS_OK;
 }
 
+// How many leading blocks of a norm grid read their gradients with the
+// default cache policy: as many whole block runs (the longest run, for a
+// bound) as fit the cache budget.  Those gradients are still in the
+// Infinity Cache when the update reads them again; the other blocks stream
+// theirs nontemporally, which is faster and leaves the cache to the first.
+// A list within the budget is read the default way throughout.
+int norm_cached_blocks(const Plan& plan, bool bf16, int grid)
+{
+    const int64_t run_chunks = (static_cast<int64_t>(plan.n_chunks) + grid - 1) / grid;
+    const int64_t run_bytes = run_chunks * plan.chunk_elems * (bf16 ? 2 : 4);
+    if (run_bytes <= 0) return grid;
+    return static_cast<int>(std::min<int64_t>(grid, mps::kNormCacheBudget / run_bytes));
+}
+
 // Launch the norm (and optionally the clip coefficient) over a planned list.
 int run_grad_norm(const Plan& plan, bool bf16, double* d_sumsq, double max_norm,
-                  double grad_scale, float* d_coef, void* d_workspace, hipStream_t st,
-                  mps::NormBefore next)
+                  double grad_scale, float* d_coef, void* d_workspace, hipStream_t st)
 {
     const int grid = grid_for(plan.n_chunks, mps::kNormMaxBlocks);
-    hipError_t e = mps::launch_grad_norm(view_of(d_workspace, plan), bf16, grid, d_sumsq, max_norm,
-                                         grad_scale, d_coef, st, next);
+    hipError_t e = mps::launch_grad_norm(view_of(d_workspace, plan), bf16, grid,
+                                         norm_cached_blocks(plan, bf16, grid), d_sumsq, max_norm,
+                                         grad_scale, d_coef, st);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "grad_norm launch: %s", hipGetErrorString(e));
     return ok();
 }
@@ -468,12 +483,14 @@ int check_clipped_arguments(const int32_t* d_step, double max_norm, double grad_
 // `update(view, norm grid, stream)`, which finishes the sum.
 template <class Update>
 int run_clipped(const Plan& plan, bool bf16, const int32_t* d_step, void* d_workspace,
-                hipStream_t st, void* mid_event, mps::NormBefore next, Update update)
+                hipStream_t st, void* mid_event, Update update)
 {
     const mps::WorkspaceView ws = view_of(d_workspace, plan);
     // The same norm grid as grad_norm_sq, so the partials and S match it.
     const int norm_grid = grid_for(plan.n_chunks, mps::kNormMaxBlocks);
-    hipError_t e = mps::launch_grad_norm_partials(ws, bf16, norm_grid, d_step, st, next);
+    hipError_t e = mps::launch_grad_norm_partials(ws, bf16, norm_grid,
+                                                  norm_cached_blocks(plan, bf16, norm_grid), d_step,
+                                                  st);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "grad_norm launch: %s", hipGetErrorString(e));
     if (mid_event && (e = hipEventRecord(static_cast<hipEvent_t>(mid_event), st)) != hipSuccess) {
         return fail(MPS_ERR_DEVICE, "hipEventRecord (mid_event): %s", hipGetErrorString(e));
@@ -526,7 +543,7 @@ int grad_norm_sq(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
         return rc;
     }
     return run_grad_norm(plan, grad_dtype == MPS_DTYPE_BF16, d_sumsq, max_norm, grad_scale, d_coef,
-                         d_workspace, st, mps::NormBefore::kUpdate);
+                         d_workspace, st);
 }
 
 int clip_coef(const double* d_sumsq, double max_norm, double grad_scale, float* d_coef,
@@ -587,7 +604,8 @@ int adamw_fused_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dt
     const int cap = resident < mps::kFusedMaxBlocks ? resident : mps::kFusedMaxBlocks;
     const int grid = grid_for(plan.n_chunks, cap);
     mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
-    e = mps::launch_fused_step(view_of(d_workspace, plan), bf16, grid, max_norm, grad_scale,
+    e = mps::launch_fused_step(view_of(d_workspace, plan), bf16, grid,
+                               norm_cached_blocks(plan, bf16, grid), max_norm, grad_scale,
                                skip_if_nonfinite ? 1 : 0, d_sumsq, d_coef, d_step, hp, st);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "fused step launch: %s", hipGetErrorString(e));
     return ok();
@@ -612,7 +630,6 @@ int adamw_clipped_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_
     const mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
     const int grid = grid_for(plan.n_chunks, mps::kStepMaxBlocks);
     return run_clipped(plan, bf16, d_step, d_workspace, stream_, mid_event,
-                       mps::NormBefore::kUpdate,
                        [&](const mps::WorkspaceView& ws, int norm_grid, hipStream_t st) {
                            return mps::launch_clipped_step(ws, bf16, grid, norm_grid, max_norm,
                                                            grad_scale, skip_if_nonfinite ? 1 : 0,
@@ -642,7 +659,7 @@ int adamw8_grad_norm_sq(const mps_tensor8* tensors, int n_tensors, mps_dtype gra
         return rc;
     }
     return run_grad_norm(plan, grad_dtype == MPS_DTYPE_BF16, d_sumsq, max_norm, grad_scale, d_coef,
-                         d_workspace, st, mps::NormBefore::kQ8Update);
+                         d_workspace, st);
 }
 
 int adamw8_multi_tensor_step(const mps_tensor8* tensors, int n_tensors, mps_dtype grad_dtype,
@@ -692,7 +709,6 @@ int adamw8_clipped_step(const mps_tensor8* tensors, int n_tensors, mps_dtype gra
     const auto* quant = reinterpret_cast<const mps::QuantEntry*>(static_cast<unsigned char*>(d_workspace) +
                                                                  plan.quant_off);
     return run_clipped(plan, bf16, d_step, d_workspace, stream_, mid_event,
-                       mps::NormBefore::kQ8Update,
                        [&](const mps::WorkspaceView& ws, int norm_grid, hipStream_t st) {
                            return mps::launch_adamw8_clipped(ws, quant, bf16, grid, norm_grid,
                                                              max_norm, grad_scale,

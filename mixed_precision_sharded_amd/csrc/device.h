@@ -26,12 +26,6 @@
 #ifndef MPS_STORE_POLICY
 #define MPS_STORE_POLICY 2  // update: master, m, v, bf16 copy
 #endif
-#ifndef MPS_NORM_POLICY
-#define MPS_NORM_POLICY 0   // norm before the fp32 update: gradient (read again by the update)
-#endif
-#ifndef MPS_Q8_NORM_POLICY
-#define MPS_Q8_NORM_POLICY 0  // norm before the 8-bit update
-#endif
 
 
 namespace mps {
@@ -45,8 +39,8 @@ constexpr int kWave = 64;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kLoadPolicy = MPS_LOAD_POLICY;
 constexpr int kStorePolicy = MPS_STORE_POLICY;
-constexpr int kNormPolicy = MPS_NORM_POLICY;
-constexpr int kQ8NormPolicy = MPS_Q8_NORM_POLICY;
+constexpr int kPolicyDefault = 0;  // the norm's gradient reads, cached blocks
+constexpr int kPolicyStream = 2;   // the norm's gradient reads, the other blocks
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 
 // ------------------------------------------------------ buffer resources ---

@@ -20,17 +20,17 @@ struct WorkspaceView {
     uint64_t tag;
 };
 
-// Which update the norm precedes (selects the gradient cache policy).
-enum class NormBefore { kUpdate, kQ8Update };
-
-hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid,
+// The norm launches take `cached_blocks`: blocks below it read their
+// gradients with the default cache policy, the others nontemporally.
+hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid, int cached_blocks,
                             double* d_sumsq, double max_norm, double grad_scale,
-                            float* d_coef, hipStream_t stream, NormBefore next);
+                            float* d_coef, hipStream_t stream);
 
 // The norm's first stage only: one partial sum per block, and the step
 // number *d_step + 1, in the workspace for a following launch_clipped_step.
 hipError_t launch_grad_norm_partials(const WorkspaceView& ws, bool grad_bf16, int grid,
-                                     const int32_t* d_step, hipStream_t stream, NormBefore next);
+                                     int cached_blocks, const int32_t* d_step,
+                                     hipStream_t stream);
 
 hipError_t launch_clip_coef(const double* d_sumsq, double max_norm, double grad_scale,
                             float* d_coef, hipStream_t stream);
@@ -51,10 +51,10 @@ hipError_t fused_grid_limit(bool grad_bf16, int* max_blocks);
 
 // The single-launch step (cooperative launch; `grid` must not exceed
 // fused_grid_limit nor kFusedMaxBlocks).
-hipError_t launch_fused_step(const WorkspaceView& ws, bool grad_bf16, int grid, double max_norm,
-                             double grad_scale, int skip_if_nonfinite, double* d_sumsq,
-                             float* d_coef, int32_t* d_step, const HyperParams& hp,
-                             hipStream_t stream);
+hipError_t launch_fused_step(const WorkspaceView& ws, bool grad_bf16, int grid, int cached_blocks,
+                             double max_norm, double grad_scale, int skip_if_nonfinite,
+                             double* d_sumsq, float* d_coef, int32_t* d_step,
+                             const HyperParams& hp, hipStream_t stream);
 
 // 8-bit moment state (kernels_q8.hip).  `quant` is the QuantEntry table in
 // the same workspace.

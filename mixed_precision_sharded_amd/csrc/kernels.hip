@@ -168,14 +168,28 @@ __device__ __forceinline__ double norm_of_run(const WorkspaceView& ws, uint32_t 
     return mine;
 }
 
+// This block's share of S.  Blocks below `cached_blocks` read their
+// gradients with the default cache policy, and what they read stays in the
+// Infinity Cache for the update to hit again; the others stream theirs past
+// the caches, which reads faster and does not fill the cache (a list larger
+// than the cache cannot keep more than one cache's worth anyway).
+template <bool kBf16, int kUnroll>
+__device__ __forceinline__ double norm_share(const WorkspaceView& ws, int cached_blocks,
+                                             uint32_t first_tensor, const ChunkRun& run)
+{
+    return static_cast<int>(blockIdx.x) < cached_blocks
+               ? norm_of_run<kBf16, kUnroll, kPolicyDefault>(ws, first_tensor, run.first, run.stop)
+               : norm_of_run<kBf16, kUnroll, kPolicyStream>(ws, first_tensor, run.first, run.stop);
+}
+
 // kFinish: the last block to finish sums the partials and writes S (and the
 // clip coefficient).  Otherwise the launch ends with one partial per block in
 // the workspace, and the step number t = *d_step + 1 in the header, for the
 // clipped update to finish.
-template <bool kBf16, int kUnroll, int kPolicy, bool kFinish>
+template <bool kBf16, int kUnroll, bool kFinish>
 __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
-    WorkspaceView ws, double* d_sumsq, double max_norm, double grad_scale, float* d_coef,
-    const int32_t* d_step)
+    WorkspaceView ws, int cached_blocks, double* d_sumsq, double max_norm, double grad_scale,
+    float* d_coef, const int32_t* d_step)
 {
     const int tid = threadIdx.x;
     const ChunkRun run = block_run(ws.n_chunks);
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
         return;
     }
 
-    const double mine = norm_of_run<kBf16, kUnroll, kPolicy>(ws, first_tensor, run.first, run.stop);
+    const double mine = norm_share<kBf16, kUnroll>(ws, cached_blocks, first_tensor, run);
 
     __shared__ double lds[kWavesPerBlock];
     __shared__ bool is_last;
@@ -435,8 +449,8 @@ constexpr uint32_t kSpinLimit = 1u << 23;  // x s_sleep(2): about 1 s, never rea
 // and the waiting block stops without writing state).
 template <bool kBf16, int kNormUnroll, int kStepUnroll>
 __global__ __launch_bounds__(kBlock) void adamw_fused_kernel(
-    WorkspaceView ws, double max_norm, double grad_scale, int skip_if_nonfinite, double* d_sumsq,
-    float* d_coef, int32_t* d_step, HyperParams hp)
+    WorkspaceView ws, int cached_blocks, double max_norm, double grad_scale, int skip_if_nonfinite,
+    double* d_sumsq, float* d_coef, int32_t* d_step, HyperParams hp)
 {
     const int tid = threadIdx.x;
     const int grid = gridDim.x;
@@ -456,8 +470,7 @@ __global__ __launch_bounds__(kBlock) void adamw_fused_kernel(
     const int64_t t = static_cast<int64_t>(*d_step) + 1;
 
     // Phase 1: this block's partial of S.
-    const double mine = norm_of_run<kBf16, kNormUnroll, kNormPolicy>(ws, first_tensor, run.first,
-                                                                     run.stop);
+    const double mine = norm_share<kBf16, kNormUnroll>(ws, cached_blocks, first_tensor, run);
     __shared__ double lds[kWavesPerBlock];
     __shared__ uint64_t launch;
     __shared__ bool last, failed;
@@ -519,49 +532,36 @@ __global__ __launch_bounds__(kBlock) void adamw_fused_kernel(
 
 namespace {
 
-template <int kPolicy, bool kFinish>
-void grad_norm_launch(const WorkspaceView& ws, bool grad_bf16, int grid, double* d_sumsq,
-                      double max_norm, double grad_scale, float* d_coef, const int32_t* d_step,
-                      hipStream_t stream)
+template <bool kFinish>
+void grad_norm_launch(const WorkspaceView& ws, bool grad_bf16, int grid, int cached_blocks,
+                      double* d_sumsq, double max_norm, double grad_scale, float* d_coef,
+                      const int32_t* d_step, hipStream_t stream)
 {
     if (grad_bf16) {
-        grad_norm_kernel<true, MPS_NORM_UNROLL, kPolicy, kFinish><<<grid, kBlock, 0, stream>>>(
-            ws, d_sumsq, max_norm, grad_scale, d_coef, d_step);
+        grad_norm_kernel<true, MPS_NORM_UNROLL, kFinish><<<grid, kBlock, 0, stream>>>(
+            ws, cached_blocks, d_sumsq, max_norm, grad_scale, d_coef, d_step);
     } else {
-        grad_norm_kernel<false, MPS_NORM_UNROLL, kPolicy, kFinish><<<grid, kBlock, 0, stream>>>(
-            ws, d_sumsq, max_norm, grad_scale, d_coef, d_step);
+        grad_norm_kernel<false, MPS_NORM_UNROLL, kFinish><<<grid, kBlock, 0, stream>>>(
+            ws, cached_blocks, d_sumsq, max_norm, grad_scale, d_coef, d_step);
     }
 }
 
 }  // namespace
 
-hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid, double* d_sumsq,
-                            double max_norm, double grad_scale, float* d_coef, hipStream_t stream,
-                            NormBefore next)
+hipError_t launch_grad_norm(const WorkspaceView& ws, bool grad_bf16, int grid, int cached_blocks,
+                            double* d_sumsq, double max_norm, double grad_scale, float* d_coef,
+                            hipStream_t stream)
 {
-    // The gradient cache policy can be chosen per following update (both
-    // updates re-read the gradients soon after and, measured on MI355X,
-    // benefit from the ones a default-policy norm leaves in the caches).
-    if (next == NormBefore::kQ8Update) {
-        grad_norm_launch<kQ8NormPolicy, true>(ws, grad_bf16, grid, d_sumsq, max_norm, grad_scale,
-                                              d_coef, nullptr, stream);
-    } else {
-        grad_norm_launch<kNormPolicy, true>(ws, grad_bf16, grid, d_sumsq, max_norm, grad_scale,
-                                            d_coef, nullptr, stream);
-    }
+    grad_norm_launch<true>(ws, grad_bf16, grid, cached_blocks, d_sumsq, max_norm, grad_scale,
+                           d_coef, nullptr, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_grad_norm_partials(const WorkspaceView& ws, bool grad_bf16, int grid,
-                                     const int32_t* d_step, hipStream_t stream, NormBefore next)
+                                     int cached_blocks, const int32_t* d_step, hipStream_t stream)
 {
-    if (next == NormBefore::kQ8Update) {
-        grad_norm_launch<kQ8NormPolicy, false>(ws, grad_bf16, grid, nullptr, 0.0, 0.0, nullptr,
-                                               d_step, stream);
-    } else {
-        grad_norm_launch<kNormPolicy, false>(ws, grad_bf16, grid, nullptr, 0.0, 0.0, nullptr,
-                                             d_step, stream);
-    }
+    grad_norm_launch<false>(ws, grad_bf16, grid, cached_blocks, nullptr, 0.0, 0.0, nullptr, d_step,
+                            stream);
     return hipGetLastError();
 }
 
@@ -626,15 +626,15 @@ hipError_t fused_grid_limit(bool grad_bf16, int* max_blocks)
     return e;
 }
 
-hipError_t launch_fused_step(const WorkspaceView& ws, bool grad_bf16, int grid, double max_norm,
-                             double grad_scale, int skip_if_nonfinite, double* d_sumsq,
-                             float* d_coef, int32_t* d_step, const HyperParams& hp,
-                             hipStream_t stream)
+hipError_t launch_fused_step(const WorkspaceView& ws, bool grad_bf16, int grid, int cached_blocks,
+                             double max_norm, double grad_scale, int skip_if_nonfinite,
+                             double* d_sumsq, float* d_coef, int32_t* d_step,
+                             const HyperParams& hp, hipStream_t stream)
 {
     WorkspaceView view = ws;
     HyperParams params = hp;
-    void* args[] = {&view,     &max_norm, &grad_scale, &skip_if_nonfinite,
-                    &d_sumsq,  &d_coef,   &d_step,     &params};
+    void* args[] = {&view,    &cached_blocks, &max_norm, &grad_scale, &skip_if_nonfinite,
+                    &d_sumsq, &d_coef,        &d_step,   &params};
     const void* fn = grad_bf16 ? reinterpret_cast<const void*>(fused_kernel<true>())
                                : reinterpret_cast<const void*>(fused_kernel<false>());
     // Cooperative: the runtime refuses the launch unless every block can be

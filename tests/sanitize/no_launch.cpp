@@ -15,18 +15,18 @@ namespace {
 }  // namespace
 
 namespace mps {
-hipError_t launch_grad_norm(const WorkspaceView&, bool, int, double*, double, double, float*,
-                            hipStream_t, NormBefore) { reached("grad_norm"); }
-hipError_t launch_grad_norm_partials(const WorkspaceView&, bool, int, const int32_t*, hipStream_t,
-                                     NormBefore) { reached("grad_norm_partials"); }
+hipError_t launch_grad_norm(const WorkspaceView&, bool, int, int, double*, double, double, float*,
+                            hipStream_t) { reached("grad_norm"); }
+hipError_t launch_grad_norm_partials(const WorkspaceView&, bool, int, int, const int32_t*,
+                                     hipStream_t) { reached("grad_norm_partials"); }
 hipError_t launch_clip_coef(const double*, double, double, float*, hipStream_t) { reached("clip"); }
 hipError_t launch_adamw_step(const WorkspaceView&, bool, int, const float*, const double*,
                              int32_t*, const HyperParams&, hipStream_t) { reached("adamw_step"); }
 hipError_t launch_clipped_step(const WorkspaceView&, bool, int, int, double, double, int, double*,
                                float*, int32_t*, const HyperParams&, hipStream_t) { reached("clipped"); }
 hipError_t fused_grid_limit(bool, int*) { reached("fused_grid_limit"); }
-hipError_t launch_fused_step(const WorkspaceView&, bool, int, double, double, int, double*, float*,
-                             int32_t*, const HyperParams&, hipStream_t) { reached("fused"); }
+hipError_t launch_fused_step(const WorkspaceView&, bool, int, int, double, double, int, double*,
+                             float*, int32_t*, const HyperParams&, hipStream_t) { reached("fused"); }
 hipError_t launch_adamw8_step(const WorkspaceView&, const QuantEntry*, bool, int, const float*,
                               const double*, int32_t*, const HyperParams&, hipStream_t) { reached("adamw8"); }
 hipError_t launch_adamw8_clipped(const WorkspaceView&, const QuantEntry*, bool, int, int, double,
