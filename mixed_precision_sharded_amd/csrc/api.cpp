@@ -55,6 +55,8 @@ struct Plan {
     size_t total_bytes = 0;
     int n_chunks = 0;
     int solo_tensor = -1;   // the one tensor with elements, else -1
+    mps::SoloEntry solo{};  // its entry, passed with every launch
+    mps::QuantEntry solo_quant{};  // an 8-bit list: its 8-bit state
     int64_t chunk_elems = 0;
     uint64_t tag = 0;
 };
@@ -135,6 +137,12 @@ int layout_plan(std::vector<TensorEntry>& entries, const std::vector<mps::QuantE
             break;
         }
         plan.solo_tensor = i;
+    }
+    if (plan.solo_tensor >= 0) {
+        const TensorEntry& e = entries[plan.solo_tensor];
+        plan.solo = mps::SoloEntry{e.master, e.exp_avg,    e.exp_avg_sq, e.grad,
+                                   e.param_bf16, e.numel, e.first_chunk, e.head};
+        if (quant) plan.solo_quant = (*quant)[plan.solo_tensor];
     }
 
     plan.tensors_off = sizeof(WorkspaceHeader);
@@ -401,6 +409,8 @@ mps::WorkspaceView view_of(void* ws, const Plan& plan)
     v.partials = reinterpret_cast<double*>(base + plan.partials_off);
     v.n_chunks = plan.n_chunks;
     v.solo_tensor = plan.solo_tensor;
+    v.solo = plan.solo;
+    v.solo_quant = plan.solo_quant;
     v.chunk_elems = plan.chunk_elems;
     v.tag = plan.tag;
     return v;

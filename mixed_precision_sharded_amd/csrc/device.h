@@ -163,22 +163,80 @@ __device__ __forceinline__ float clip_from_sumsq(double sumsq, double max_norm, 
     return static_cast<float>(grad_scale * clip);
 }
 
-// S from the n per-block partials, in block-index order: each thread sums
-// its strided share (partials[tid], [tid + kBlock], ...), then the block
-// combines the threads in a fixed tree.  Every thread returns the same bits,
-// and so does every block that calls this on the same partials.  kAtomic:
+// The two partial slots of this thread, tid and tid + kBlock of the
+// workspace's kPartials, loaded without a condition (no loop, no branch: a
+// kernel can issue these loads early and wait for them alone).  kAtomic:
 // the partials were written by other blocks of this launch (agent-scope
 // loads after an acquire fence); otherwise by an earlier launch.
+static_assert(kPartials <= 2 * kBlock, "at most two partials per thread");
+struct PartialSlots {
+    double first, second;
+};
+
+template <bool kAtomic>
+__device__ __forceinline__ PartialSlots load_partials(const double* partials)
+{
+    const int i = threadIdx.x;
+    if (kAtomic) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        return {__hip_atomic_load(&partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                __hip_atomic_load(&partials[i + kBlock], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+    }
+    // Buffer loads (default cache policy), the same kind as the update's
+    // streams: the compiler counts loads of one kind in issue order, so a
+    // wait for these leaves later stream loads in flight.
+    const __amdgpu_buffer_rsrc_t r = rsrc(partials, sizeof(double) * kPartials);
+    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, i * 8u, 0, 0);
+    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(r, (i + kBlock) * 8u, 0, 0);
+    return {__builtin_bit_cast(double, a), __builtin_bit_cast(double, b)};
+}
+
+// This thread's strided share of the first n partials: 0 + the slots below
+// n.  A slot at or past n is added as +0, which leaves the sum's bits as they
+// are (the share is never -0).
+__device__ __forceinline__ double partial_share(const PartialSlots& p, int n)
+{
+    const int i = threadIdx.x;
+    double q = 0.0;
+    q = q + (i < n ? p.first : 0.0);
+    q = q + (i + kBlock < n ? p.second : 0.0);
+    return q;
+}
+
+// S from the n per-block partials, in block-index order: each thread sums
+// its strided share, then the block combines the threads in a fixed tree.
+// Every thread returns the same bits, and so does every block that calls
+// this on the same partials.
 template <bool kAtomic>
 __device__ __forceinline__ double sum_partials(const double* partials, int n, double* lds)
 {
-    if (kAtomic) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    double q = 0.0;
-    for (int i = threadIdx.x; i < n; i += kBlock) {
-        q = q + (kAtomic ? __hip_atomic_load(&partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                         : partials[i]);
+    return block_sum(partial_share(load_partials<kAtomic>(partials), n), lds);
+}
+
+// A clipped update that finds the workspace tables overwritten writes a NaN
+// S and coefficient (block 0) and nothing else.
+__device__ __forceinline__ void report_stale_clip(double* d_sumsq, float* d_coef)
+{
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (d_sumsq) *d_sumsq = __builtin_nan("");
+        if (d_coef) *d_coef = __builtin_nanf("");
     }
-    return block_sum(q, lds);
+}
+
+// Block 0 of a clipped update publishes S, the coefficient and, unless the
+// step is skipped (S not finite and skipping asked for), the new count t.
+// Returns whether the step is skipped (the same in every block).
+__device__ __forceinline__ bool publish_clip(double total, float clip, int32_t t,
+                                             int skip_if_nonfinite, double* d_sumsq,
+                                             float* d_coef, int32_t* d_step)
+{
+    const bool skip = skip_if_nonfinite && !__builtin_isfinite(total);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (d_sumsq) *d_sumsq = total;
+        if (d_coef) *d_coef = clip;
+        if (!skip) *d_step = t;
+    }
+    return skip;
 }
 
 // One ticket per block (called by one thread of each block of a launch);

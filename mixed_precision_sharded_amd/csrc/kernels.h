@@ -7,6 +7,20 @@
 
 namespace mps {
 
+// The table entry of the one tensor of a list whose elements all sit in one
+// tensor, passed with each launch (the fields of TensorEntry, without its
+// 64-byte record alignment, which a kernel argument does not carry).
+struct SoloEntry {
+    float* master;
+    float* exp_avg;
+    float* exp_avg_sq;
+    const void* grad;
+    uint16_t* param_bf16;
+    int64_t numel;
+    int32_t first_chunk;
+    int32_t head;
+};
+
 // Pointers into one workspace, derived by the host library from its base.
 struct WorkspaceView {
     WorkspaceHeader* header;
@@ -18,6 +32,8 @@ struct WorkspaceView {
     int solo_tensor;  // the index every chunk maps to, or -1 (several tensors)
     int64_t chunk_elems;
     uint64_t tag;
+    SoloEntry solo;          // that tensor's entry (when solo_tensor >= 0)
+    QuantEntry solo_quant;   // and, for an 8-bit-moment list, its 8-bit state
 };
 
 // The norm launches take `cached_blocks`: blocks below it read their

@@ -87,6 +87,74 @@ __device__ __forceinline__ uint32_t prologue_tensor(const WorkspaceView& ws, int
     return tensor_of_chunk(ws, min(c, max(ws.n_chunks - 1, 0)));
 }
 
+// Adds this thread's share of the sum of g^2 over elements [begin, end) of
+// one gradient to acc: a peel to 16-byte alignment, the vector body, the
+// tail.
+template <bool kBf16, int kUnroll, int kPolicy>
+__device__ __forceinline__ void norm_stretch(const void* grad, int64_t begin, int64_t end,
+                                             double (&acc)[kUnroll])
+{
+    constexpr int64_t kElemBytes = kBf16 ? 2 : 4;
+    constexpr int64_t kPerVec = 16 / kElemBytes;
+    const int tid = threadIdx.x;
+
+    // Peel elements until the gradient address is 16-byte aligned.
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(grad) + begin * kElemBytes;
+    int64_t head = static_cast<int64_t>((16 - (addr & 15)) & 15) / kElemBytes;
+    head = min(head, end - begin);
+    if (tid < head) acc[0] = add_square(acc[0], grad_at<kBf16>(grad, begin + tid));
+    int64_t vbegin = begin + head;
+    const int64_t nvec_all = (end - vbegin) / kPerVec;
+    const int64_t tail = vbegin + nvec_all * kPerVec;
+
+    // The body in pieces of at most 2^26 vectors (1 GiB), so that byte
+    // offsets fit the 32-bit buffer addressing.
+    for (int64_t done = 0; done < nvec_all;) {
+        const int nvec = static_cast<int>(min(nvec_all - done, static_cast<int64_t>(1) << 26));
+        const __amdgpu_buffer_rsrc_t g =
+            rsrc(static_cast<const char*>(grad) + (vbegin + done * kPerVec) * kElemBytes,
+                 static_cast<uint32_t>(nvec) * 16u);
+        done += nvec;
+
+        // Two register sets in turn: the loads of one are in flight while
+        // the other is accumulated.  Offsets past the body read zeros
+        // without touching memory, so the loop needs no bounds branches.
+        constexpr int kStride = kBlock * kUnroll;
+        u32x4 x[kUnroll], y[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) x[u] = load_u32x4<kPolicy>(g, (u * kBlock + tid) * 16u);
+        for (int base = 0; base < nvec; base += 2 * kStride) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                y[u] = load_u32x4<kPolicy>(g, (base + kStride + u * kBlock + tid) * 16u);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) acc[u] = add_vector<kBf16>(acc[u], x[u]);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                x[u] = load_u32x4<kPolicy>(g, (base + 2 * kStride + u * kBlock + tid) * 16u);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (base + kStride < nvec) {  // uniform: skip the math of an empty tile
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) acc[u] = add_vector<kBf16>(acc[u], y[u]);
+            }
+        }
+    }
+
+    if (tid < end - tail) acc[0] = add_square(acc[0], grad_at<kBf16>(grad, tail + tid));
+}
+
+template <int kUnroll>
+__device__ __forceinline__ double sum_of(const double (&acc)[kUnroll])
+{
+    double mine = acc[0];
+#pragma unroll
+    for (int u = 1; u < kUnroll; ++u) mine = mine + acc[u];
+    return mine;
+}
+
 // This thread's share of the sum of g^2 over the chunks [run_first,
 // run_stop), in a fixed order.  Consecutive chunks of one tensor are one
 // contiguous stretch of memory, streamed as a single body so the load
@@ -97,9 +165,6 @@ __device__ __forceinline__ double norm_of_run(const WorkspaceView& ws, uint32_t 
 {
     const TensorEntry* tensors = ws.tensors;
     const int64_t chunk_elems = ws.chunk_elems;
-    constexpr int64_t kElemBytes = kBf16 ? 2 : 4;
-    constexpr int64_t kPerVec = 16 / kElemBytes;
-    const int tid = threadIdx.x;
     double acc[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
@@ -107,65 +172,30 @@ __device__ __forceinline__ double norm_of_run(const WorkspaceView& ws, uint32_t 
     for (int c = run_first; c < run_stop;) {
         const TensorEntry te = tensors[c == run_first ? first_tensor : tensor_of_chunk(ws, c)];
         const int tensor_chunks = static_cast<int>((te.numel + chunk_elems - 1) / chunk_elems);
-        const int c_lo = c;  // this body: chunks [c_lo, c_hi) of one tensor
+        const int c_lo = c;  // this stretch: chunks [c_lo, c_hi) of one tensor
         const int c_hi = min(run_stop, te.first_chunk + tensor_chunks);
         c = c_hi;
-        const void* grad = te.grad;
         const int64_t begin = static_cast<int64_t>(c_lo - te.first_chunk) * chunk_elems;
         const int64_t end = min(static_cast<int64_t>(c_hi - te.first_chunk) * chunk_elems, te.numel);
-
-        // Peel elements until the gradient address is 16-byte aligned.
-        const uintptr_t addr = reinterpret_cast<uintptr_t>(grad) + begin * kElemBytes;
-        int64_t head = static_cast<int64_t>((16 - (addr & 15)) & 15) / kElemBytes;
-        head = min(head, end - begin);
-        if (tid < head) acc[0] = add_square(acc[0], grad_at<kBf16>(grad, begin + tid));
-        int64_t vbegin = begin + head;
-        const int64_t nvec_all = (end - vbegin) / kPerVec;
-        const int64_t tail = vbegin + nvec_all * kPerVec;
-
-        // The body in pieces of at most 2^26 vectors (1 GiB), so that byte
-        // offsets fit the 32-bit buffer addressing.
-        for (int64_t done = 0; done < nvec_all;) {
-            const int nvec = static_cast<int>(min(nvec_all - done, static_cast<int64_t>(1) << 26));
-            const __amdgpu_buffer_rsrc_t g =
-                rsrc(static_cast<const char*>(grad) + (vbegin + done * kPerVec) * kElemBytes,
-                     static_cast<uint32_t>(nvec) * 16u);
-            done += nvec;
-
-            // Two register sets in turn: the loads of one are in flight while
-            // the other is accumulated.  Offsets past the body read zeros
-            // without touching memory, so the loop needs no bounds branches.
-            constexpr int kStride = kBlock * kUnroll;
-            u32x4 x[kUnroll], y[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) x[u] = load_u32x4<kPolicy>(g, (u * kBlock + tid) * 16u);
-            for (int base = 0; base < nvec; base += 2 * kStride) {
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    y[u] = load_u32x4<kPolicy>(g, (base + kStride + u * kBlock + tid) * 16u);
-                }
-                __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) acc[u] = add_vector<kBf16>(acc[u], x[u]);
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    x[u] = load_u32x4<kPolicy>(g, (base + 2 * kStride + u * kBlock + tid) * 16u);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                if (base + kStride < nvec) {  // uniform: skip the math of an empty tile
-#pragma unroll
-                    for (int u = 0; u < kUnroll; ++u) acc[u] = add_vector<kBf16>(acc[u], y[u]);
-                }
-            }
-        }
-
-        if (tid < end - tail) acc[0] = add_square(acc[0], grad_at<kBf16>(grad, tail + tid));
+        norm_stretch<kBf16, kUnroll, kPolicy>(te.grad, begin, end, acc);
     }
+    return sum_of(acc);
+}
 
-    double mine = acc[0];
+// The same when every chunk belongs to the one tensor `te` that came with
+// the launch: the run is one stretch, and no table is read.
+template <bool kBf16, int kUnroll, int kPolicy>
+__device__ __forceinline__ double norm_of_solo_run(const SoloEntry& te, int64_t chunk_elems,
+                                                   int run_first, int run_stop)
+{
+    double acc[kUnroll];
 #pragma unroll
-    for (int u = 1; u < kUnroll; ++u) mine = mine + acc[u];
-    return mine;
+    for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
+    const int64_t begin = static_cast<int64_t>(run_first - te.first_chunk) * chunk_elems;
+    const int64_t end =
+        max(begin, min(static_cast<int64_t>(run_stop - te.first_chunk) * chunk_elems, te.numel));
+    norm_stretch<kBf16, kUnroll, kPolicy>(te.grad, begin, end, acc);
+    return sum_of(acc);
 }
 
 // This block's share of S.  Blocks below `cached_blocks` read their
@@ -182,6 +212,17 @@ __device__ __forceinline__ double norm_share(const WorkspaceView& ws, int cached
                : norm_of_run<kBf16, kUnroll, kPolicyStream>(ws, first_tensor, run.first, run.stop);
 }
 
+template <bool kBf16, int kUnroll>
+__device__ __forceinline__ double norm_solo_share(const WorkspaceView& ws, int cached_blocks,
+                                                  const ChunkRun& run)
+{
+    return static_cast<int>(blockIdx.x) < cached_blocks
+               ? norm_of_solo_run<kBf16, kUnroll, kPolicyDefault>(ws.solo, ws.chunk_elems,
+                                                                   run.first, run.stop)
+               : norm_of_solo_run<kBf16, kUnroll, kPolicyStream>(ws.solo, ws.chunk_elems,
+                                                                  run.first, run.stop);
+}
+
 // kFinish: the last block to finish sums the partials and writes S (and the
 // clip coefficient).  Otherwise the launch ends with one partial per block in
 // the workspace, and the step number t = *d_step + 1 in the header, for the
@@ -193,23 +234,37 @@ __global__ __launch_bounds__(kBlock) void grad_norm_kernel(
 {
     const int tid = threadIdx.x;
     const ChunkRun run = block_run(ws.n_chunks);
-    // The tag and the first chunk's tensor index are independent loads, in
-    // flight together.
     const uint64_t seen = ws.header->tag;
-    const uint32_t first_tensor = prologue_tensor(ws, run.first);
-    if (seen != ws.tag) {  // tables overwritten: touch nothing, report NaN
+    auto report_stale = [&] {  // tables overwritten: write nothing but a NaN S
         if (kFinish && blockIdx.x == 0 && tid == 0) {
             *d_sumsq = __builtin_nan("");
             if (d_coef) *d_coef = __builtin_nanf("");
         }
-        return;
+    };
+    double mine;
+    if (ws.solo_tensor >= 0) {
+        // One tensor, which came with the launch: its reads need no table and
+        // start at once; the tag is checked below, before anything is written.
+        mine = norm_solo_share<kBf16, kUnroll>(ws, cached_blocks, run);
+    } else {
+        // The tag and the first chunk's tensor index are independent loads,
+        // in flight together; the table's pointers are used only once the tag
+        // has matched.
+        const uint32_t first_tensor = prologue_tensor(ws, run.first);
+        if (seen != ws.tag) {
+            report_stale();
+            return;
+        }
+        mine = norm_share<kBf16, kUnroll>(ws, cached_blocks, first_tensor, run);
     }
-
-    const double mine = norm_share<kBf16, kUnroll>(ws, cached_blocks, first_tensor, run);
 
     __shared__ double lds[kWavesPerBlock];
     __shared__ bool is_last;
     const double block_total = block_sum(mine, lds);
+    if (seen != ws.tag) {
+        report_stale();
+        return;
+    }
     if (!kFinish) {
         if (tid == 0) ws.partials[blockIdx.x] = block_total;
         // The step the following clipped update will take (it reads t here,
@@ -254,8 +309,8 @@ __global__ __launch_bounds__(kWave) void clip_coef_kernel(const double* d_sumsq,
 // ---------------------------------------------------------------- update ---
 
 
-template <bool kBf16>
-__device__ __forceinline__ void adamw_scalar_at(const TensorEntry* te, int64_t i, const StepScalars& s)
+template <bool kBf16, class Entry>
+__device__ __forceinline__ void adamw_scalar_at(const Entry* te, int64_t i, const StepScalars& s)
 {
     const float grad = grad_at<kBf16>(te->grad, i);
     float w = te->master[i], m = te->exp_avg[i], v = te->exp_avg_sq[i];
@@ -268,31 +323,38 @@ __device__ __forceinline__ void adamw_scalar_at(const TensorEntry* te, int64_t i
 
 // The aligned body of one chunk: `nquad` groups of four elements starting at
 // element `q0` of the tensor, every stream 16-byte (fp32) or 8-byte (bf16)
-// aligned there.
+// aligned there.  One tile = kUnroll groups of four per thread.  Two tiles
+// are held in registers in turn: the loads of the next tile are in flight
+// while the current one is computed and stored.  Lanes past the body read
+// zeros and their stores are dropped, so the tail needs no branches.
 template <bool kBf16, int kUnroll>
-__device__ __forceinline__ void adamw_body(const TensorEntry* te, int64_t q0, int nquad,
-                                           const StepScalars& s)
-{
-    const int tid = threadIdx.x;
-    const __amdgpu_buffer_rsrc_t W = rsrc(te->master + q0, nquad * 16u);
-    const __amdgpu_buffer_rsrc_t M = rsrc(te->exp_avg + q0, nquad * 16u);
-    const __amdgpu_buffer_rsrc_t V = rsrc(te->exp_avg_sq + q0, nquad * 16u);
-    const __amdgpu_buffer_rsrc_t G = rsrc(static_cast<const char*>(te->grad) + q0 * (kBf16 ? 2 : 4),
-                                          nquad * (kBf16 ? 8u : 16u));
-    const bool copy = te->param_bf16 != nullptr;
-    const __amdgpu_buffer_rsrc_t P = rsrc(copy ? te->param_bf16 + q0 : nullptr, copy ? nquad * 8u : 0u);
-
-    // One tile = kUnroll groups of four per thread.  Two tiles are held in
-    // registers in turn: the loads of the next tile are in flight while the
-    // current one is computed and stored.  Lanes past the body read zeros and
-    // their stores are dropped, so the tail needs no branches.
+struct Body {
     struct Tile {
         f32x4 w[kUnroll], m[kUnroll], v[kUnroll], g[kUnroll];
     };
-    auto load_tile = [&](Tile& t, int base) {
+    __amdgpu_buffer_rsrc_t W, M, V, G, P;
+    bool copy;
+    int nquad;
+
+    template <class Entry>
+    __device__ __forceinline__ Body(const Entry* te, int64_t q0, int n)
+        : W(rsrc(te->master + q0, static_cast<uint32_t>(n) * 16u)),
+          M(rsrc(te->exp_avg + q0, static_cast<uint32_t>(n) * 16u)),
+          V(rsrc(te->exp_avg_sq + q0, static_cast<uint32_t>(n) * 16u)),
+          G(rsrc(static_cast<const char*>(te->grad) + q0 * (kBf16 ? 2 : 4),
+                 static_cast<uint32_t>(n) * (kBf16 ? 8u : 16u))),
+          P(rsrc(te->param_bf16 ? te->param_bf16 + q0 : nullptr,
+                 te->param_bf16 ? static_cast<uint32_t>(n) * 8u : 0u)),
+          copy(te->param_bf16 != nullptr),
+          nquad(n)
+    {
+    }
+
+    __device__ __forceinline__ void load(Tile& t, int base) const
+    {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t q = base + u * kBlock + tid;
+            const uint32_t q = base + u * kBlock + threadIdx.x;
             t.w[u] = load_f32x4(W, q * 16u);
             t.m[u] = load_f32x4(M, q * 16u);
             t.v[u] = load_f32x4(V, q * 16u);
@@ -303,11 +365,13 @@ __device__ __forceinline__ void adamw_body(const TensorEntry* te, int64_t q0, in
                 t.g[u] = load_f32x4(G, q * 16u);
             }
         }
-    };
-    auto update_tile = [&](Tile& t, int base) {
+    }
+
+    __device__ __forceinline__ void update(Tile& t, int base, const StepScalars& s) const
+    {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t q = base + u * kBlock + tid;
+            const uint32_t q = base + u * kBlock + threadIdx.x;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 float wk = t.w[u][k], mk = t.m[u][k], vk = t.v[u][k];
@@ -326,20 +390,64 @@ __device__ __forceinline__ void adamw_body(const TensorEntry* te, int64_t q0, in
                 store_u32x2(packed, P, q * 8u);
             }
         }
-    };
-
-    constexpr int kStride = kBlock * kUnroll;
-    Tile a, b;
-    load_tile(a, 0);
-    for (int base = 0; base < nquad; base += 2 * kStride) {
-        load_tile(b, base + kStride);
-        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
-        update_tile(a, base);
-        if (base + kStride >= nquad) break;  // uniform: the other tile is empty
-        load_tile(a, base + 2 * kStride);
-        __builtin_amdgcn_sched_barrier(0);
-        update_tile(b, base + kStride);
     }
+
+    // Streams the body; `a` already holds the loads of its first tile.
+    __device__ __forceinline__ void run(Tile& a, const StepScalars& s) const
+    {
+        constexpr int kStride = kBlock * kUnroll;
+        Tile b;
+        for (int base = 0; base < nquad; base += 2 * kStride) {
+            load(b, base + kStride);
+            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+            update(a, base, s);
+            if (base + kStride >= nquad) break;  // uniform: the other tile is empty
+            load(a, base + 2 * kStride);
+            __builtin_amdgcn_sched_barrier(0);
+            update(b, base + kStride, s);
+        }
+    }
+};
+
+// The element ranges of chunk c of a tensor whose streams share an
+// alignment (head >= 0): scalar [begin, qbegin), nquad groups of four from
+// qbegin, scalar [tail, end).
+struct ChunkSpan {
+    int64_t begin, qbegin, tail, end;
+    int nquad;
+};
+
+template <class Entry>
+__device__ __forceinline__ ChunkSpan chunk_span(const Entry* te, int c, int64_t chunk_elems)
+{
+    ChunkSpan k;
+    k.begin = static_cast<int64_t>(c - te->first_chunk) * chunk_elems;
+    k.end = min(k.begin + chunk_elems, te->numel);
+    k.qbegin = min(k.begin + te->head, k.end);
+    k.nquad = static_cast<int>((k.end - k.qbegin) / 4);
+    k.tail = k.qbegin + static_cast<int64_t>(k.nquad) * 4;
+    return k;
+}
+
+// Chunk c of tensor te in full.
+template <bool kBf16, int kUnroll, class Entry>
+__device__ __forceinline__ void adamw_chunk(const Entry* te, int c, int64_t chunk_elems,
+                                            const StepScalars& s)
+{
+    const int tid = threadIdx.x;
+    if (te->head < 0) {  // streams share no alignment: element-wise
+        const int64_t begin = static_cast<int64_t>(c - te->first_chunk) * chunk_elems;
+        const int64_t end = min(begin + chunk_elems, te->numel);
+        for (int64_t i = begin + tid; i < end; i += kBlock) adamw_scalar_at<kBf16>(te, i, s);
+        return;
+    }
+    const ChunkSpan k = chunk_span(te, c, chunk_elems);
+    if (tid < k.qbegin - k.begin) adamw_scalar_at<kBf16>(te, k.begin + tid, s);
+    const Body<kBf16, kUnroll> body(te, k.qbegin, k.nquad);
+    typename Body<kBf16, kUnroll>::Tile a;
+    body.load(a, 0);
+    body.run(a, s);
+    if (tid < k.end - k.tail) adamw_scalar_at<kBf16>(te, k.tail + tid, s);
 }
 
 // Update the chunks b, b + G, b + 2G, ... of this block (G = gridDim.x): at
@@ -351,27 +459,12 @@ template <bool kBf16, int kUnroll>
 __device__ __forceinline__ void update_chunks(const WorkspaceView& ws, TensorEntry next,
                                               const StepScalars& s)
 {
-    const int tid = threadIdx.x;
     const int n_chunks = ws.n_chunks;
-    const int64_t chunk_elems = ws.chunk_elems;
     for (int c = blockIdx.x; c < n_chunks; c += gridDim.x) {
         const TensorEntry entry = next;
         const int c_next = c + static_cast<int>(gridDim.x);
         if (ws.solo_tensor < 0 && c_next < n_chunks) next = ws.tensors[ws.chunk_map[c_next]];
-        const TensorEntry* te = &entry;
-        const int64_t begin = static_cast<int64_t>(c - te->first_chunk) * chunk_elems;
-        const int64_t end = min(begin + chunk_elems, te->numel);
-
-        if (te->head < 0) {  // streams share no alignment: element-wise
-            for (int64_t i = begin + tid; i < end; i += kBlock) adamw_scalar_at<kBf16>(te, i, s);
-            continue;
-        }
-        const int64_t qbegin = min(begin + te->head, end);
-        if (tid < qbegin - begin) adamw_scalar_at<kBf16>(te, begin + tid, s);
-        const int nquad = static_cast<int>((end - qbegin) / 4);
-        adamw_body<kBf16, kUnroll>(te, qbegin, nquad, s);
-        const int64_t tail = qbegin + static_cast<int64_t>(nquad) * 4;
-        if (tid < end - tail) adamw_scalar_at<kBf16>(te, tail + tid, s);
+        adamw_chunk<kBf16, kUnroll>(&entry, c, ws.chunk_elems, s);
     }
 }
 
@@ -410,32 +503,71 @@ __global__ __launch_bounds__(kBlock) void adamw_step_kernel(
 // 2^20-parameter shard, whose blocks all finish at about the same moment,
 // 4 us of 17 with a single counter); it costs a 2 KB read per block that
 // overlaps the other prologue loads.
+//
+// A list with one tensor brings that tensor's entry with the launch, and
+// the kernel starts by issuing the loads of its first tile, before it reads
+// the tag or the partials: on a small shard the update then waits for one
+// memory round trip before its data moves instead of three.  The tag is
+// checked before anything is stored.
 template <bool kBf16, int kUnroll>
 __global__ __launch_bounds__(kBlock) void adamw_clipped_kernel(
     WorkspaceView ws, int n_partials, double max_norm, double grad_scale, int skip_if_nonfinite,
     double* d_sumsq, float* d_coef, int32_t* d_step, HyperParams hp)
 {
     const int tid = threadIdx.x;
+    // The header first: read before anything else, these are scalar loads,
+    // which the vector-memory counter does not wait for.
     const uint64_t seen = ws.header->tag;
     const int32_t t = ws.header->pending_step;
-    const TensorEntry first = ws.tensors[prologue_tensor(ws, blockIdx.x)];
-    if (seen != ws.tag) {  // tables overwritten: touch nothing, report NaN
-        if (blockIdx.x == 0 && tid == 0) {
-            if (d_sumsq) *d_sumsq = __builtin_nan("");
-            if (d_coef) *d_coef = __builtin_nanf("");
+    __shared__ double lds[kWavesPerBlock];
+
+    if (ws.solo_tensor >= 0) {
+        const SoloEntry& te = ws.solo;
+        const int c0 = blockIdx.x;
+        const bool whole = c0 < ws.n_chunks;
+        const bool vector = whole && te.head >= 0;
+        const ChunkSpan k = chunk_span(&te, min(c0, ws.n_chunks - 1), ws.chunk_elems);
+        // A block without a vector body loads nothing (an empty range).
+        const Body<kBf16, kUnroll> body(&te, vector ? k.qbegin : k.begin, vector ? k.nquad : 0);
+        // The vector-memory counter is waited for in issue order.  All the
+        // address arithmetic comes first, then the loads of the partials,
+        // then the tile's: the sum of the partials can start while the tile
+        // is still in flight.
+        __builtin_amdgcn_sched_barrier(0);
+        const PartialSlots slots = load_partials<false>(ws.partials);
+        __builtin_amdgcn_sched_barrier(0);
+        typename Body<kBf16, kUnroll>::Tile a;
+        body.load(a, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const double total = block_sum(partial_share(slots, n_partials), lds);
+        if (seen != ws.tag) {
+            report_stale_clip(d_sumsq, d_coef);
+            return;
+        }
+        const float clip = clip_from_sumsq(total, max_norm, grad_scale);
+        if (publish_clip(total, clip, t, skip_if_nonfinite, d_sumsq, d_coef, d_step)) return;
+        const StepScalars s = step_scalars(t, hp, clip);
+        if (vector) {
+            if (tid < k.qbegin - k.begin) adamw_scalar_at<kBf16>(&te, k.begin + tid, s);
+            body.run(a, s);
+            if (tid < k.end - k.tail) adamw_scalar_at<kBf16>(&te, k.tail + tid, s);
+        } else if (whole) {
+            adamw_chunk<kBf16, kUnroll>(&te, c0, ws.chunk_elems, s);
+        }
+        for (int c = c0 + static_cast<int>(gridDim.x); c < ws.n_chunks; c += gridDim.x) {
+            adamw_chunk<kBf16, kUnroll>(&te, c, ws.chunk_elems, s);
         }
         return;
     }
-    __shared__ double lds[kWavesPerBlock];
+
+    const TensorEntry first = ws.tensors[prologue_tensor(ws, blockIdx.x)];
+    if (seen != ws.tag) {
+        report_stale_clip(d_sumsq, d_coef);
+        return;
+    }
     const double total = sum_partials<false>(ws.partials, n_partials, lds);
     const float clip = clip_from_sumsq(total, max_norm, grad_scale);
-    const bool skip = skip_if_nonfinite && !__builtin_isfinite(total);
-    if (blockIdx.x == 0 && tid == 0) {
-        if (d_sumsq) *d_sumsq = total;
-        if (d_coef) *d_coef = clip;
-        if (!skip) *d_step = t;
-    }
-    if (skip) return;
+    if (publish_clip(total, clip, t, skip_if_nonfinite, d_sumsq, d_coef, d_step)) return;
     update_chunks<kBf16, kUnroll>(ws, first, step_scalars(t, hp, clip));
 }
 

@@ -208,8 +208,8 @@ __device__ __forceinline__ void store8_u32(uint32_t v, __amdgpu_buffer_rsrc_t r,
 
 // Elements [begin, end) of one tensor, one element per lane; `begin` is a
 // multiple of 32, so each half wavefront holds one run.
-template <bool kBf16>
-__device__ __forceinline__ void adamw8_elements(const TensorEntry* te, const QuantEntry* qe,
+template <bool kBf16, class Entry>
+__device__ __forceinline__ void adamw8_elements(const Entry* te, const QuantEntry* qe,
                                                 int64_t begin, int64_t end, const StepScalars& s)
 {
     for (int64_t base = begin; base < end; base += kBlock) {
@@ -247,39 +247,52 @@ __device__ __forceinline__ void adamw8_elements(const TensorEntry* te, const Qua
 // writers of the body after next.
 constexpr int kMaxRunsPerBody = MPS_CHUNK_MAX / kQuantBlock;
 
+// The two pairs of scale-byte buffers (m, v) that consecutive bodies of a
+// block alternate between, one LDS allocation however often this is inlined.
+__device__ __forceinline__ uint8_t (*scale_lds())[2][kMaxRunsPerBody]
+{
+    __shared__ uint8_t buffers[2][2][kMaxRunsPerBody];
+    return buffers;
+}
+
 // Whole runs [e0, e0 + 4 * ngroups) of one tensor (ngroups a multiple of 8,
 // at most one chunk), every stream aligned for its vector width there.
 // Thread q of a tile takes elements 4q .. 4q+3, so eight consecutive lanes
 // hold one run of 32 and every load and store of a tile is contiguous across
-// the wavefront.  `lds_m` and `lds_v` hold kMaxRunsPerBody bytes each.
+// the wavefront.  Two tiles are held in registers in turn, as in the fp32
+// kernel: the next tile's loads are in flight while this one is computed.
+// Groups past the end read zeros and their stores are dropped; the eight
+// lanes of a run are either all inside or all past the end.
 template <bool kBf16>
-__device__ __forceinline__ void adamw8_body(const TensorEntry* te, const QuantEntry* qe, int64_t e0,
-                                            int ngroups, const StepScalars& s, uint8_t* lds_m,
-                                            uint8_t* lds_v)
-{
-    const int tid = threadIdx.x;
-    const uint32_t ng = static_cast<uint32_t>(ngroups);
-    const __amdgpu_buffer_rsrc_t W = rsrc(te->master + e0, ng * 16u);
-    const __amdgpu_buffer_rsrc_t G = rsrc(static_cast<const char*>(te->grad) + e0 * (kBf16 ? 2 : 4),
-                                          ng * (kBf16 ? 8u : 16u));
-    const bool copy = te->param_bf16 != nullptr;
-    const __amdgpu_buffer_rsrc_t P = rsrc(copy ? te->param_bf16 + e0 : nullptr, copy ? ng * 8u : 0u);
-    const __amdgpu_buffer_rsrc_t MQ = rsrc(qe->m_codes + e0, ng * 4u);
-    const __amdgpu_buffer_rsrc_t VQ = rsrc(qe->v_codes + e0, ng * 4u);
-    const __amdgpu_buffer_rsrc_t MS = rsrc(qe->m_scales + e0 / kQuantBlock, ng / 8u);
-    const __amdgpu_buffer_rsrc_t VS = rsrc(qe->v_scales + e0 / kQuantBlock, ng / 8u);
-
-    // Two tiles are held in registers in turn, as in the fp32 kernel: the
-    // next tile's loads are in flight while this one is computed.  Groups past
-    // the end read zeros and their stores are dropped; the eight lanes of a
-    // run are either all inside or all past the end.
+struct Body8 {
     struct Tile {
         f32x4 w;
         u32x4 g;  // bf16: g[0..1] hold the four gradients; fp32: all four
         uint32_t mq, vq, ms, vs;
     };
-    auto load_tile = [&](Tile& t, int base) {
-        const uint32_t q = base + tid;
+    __amdgpu_buffer_rsrc_t W, G, P, MQ, VQ, MS, VS;
+    bool copy;
+    uint32_t ng;
+
+    template <class Entry>
+    __device__ __forceinline__ Body8(const Entry* te, const QuantEntry* qe, int64_t e0, int ngroups)
+        : W(rsrc(te->master + e0, static_cast<uint32_t>(ngroups) * 16u)),
+          G(rsrc(static_cast<const char*>(te->grad) + e0 * (kBf16 ? 2 : 4),
+                 static_cast<uint32_t>(ngroups) * (kBf16 ? 8u : 16u))),
+          P(rsrc(te->param_bf16 ? te->param_bf16 + e0 : nullptr,
+                 te->param_bf16 ? static_cast<uint32_t>(ngroups) * 8u : 0u)),
+          MQ(rsrc(qe->m_codes + e0, static_cast<uint32_t>(ngroups) * 4u)),
+          VQ(rsrc(qe->v_codes + e0, static_cast<uint32_t>(ngroups) * 4u)),
+          MS(rsrc(qe->m_scales + e0 / kQuantBlock, static_cast<uint32_t>(ngroups) / 8u)),
+          VS(rsrc(qe->v_scales + e0 / kQuantBlock, static_cast<uint32_t>(ngroups) / 8u)),
+          copy(te->param_bf16 != nullptr),
+          ng(static_cast<uint32_t>(ngroups))
+    {
+    }
+
+    __device__ __forceinline__ void load(Tile& t, int base) const
+    {
+        const uint32_t q = base + threadIdx.x;
         t.w = __builtin_bit_cast(f32x4, load_u32x4<kQ8WPolicy>(W, q * 16u));
         if (kBf16) {
             const u32x2 h = load_u32x2_policy<kQ8WPolicy>(G, q * 8u);
@@ -291,8 +304,13 @@ __device__ __forceinline__ void adamw8_body(const TensorEntry* te, const QuantEn
         t.vq = load_u32<kQ8CodePolicy>(VQ, q * 4u);
         t.ms = load_byte<kQ8ScalePolicy>(MS, q / 8u);
         t.vs = load_byte<kQ8ScalePolicy>(VS, q / 8u);
-    };
-    auto update_tile = [&](Tile& t, int base) {
+    }
+
+    // A run's quad leader leaves its two scale bytes in lds_m / lds_v.
+    __device__ __forceinline__ void update(Tile& t, int base, const StepScalars& s, uint8_t* lds_m,
+                                           uint8_t* lds_v) const
+    {
+        const int tid = threadIdx.x;
         const uint32_t q = base + tid;
         float w[4], m[4], v[4], g[4];
 #pragma unroll
@@ -326,37 +344,79 @@ __device__ __forceinline__ void adamw8_body(const TensorEntry* te, const QuantEn
             lds_m[q / 8u] = static_cast<uint8_t>(mb);
             lds_v[q / 8u] = static_cast<uint8_t>(vb);
         }
-    };
+    }
 
-    Tile a, b;
-    load_tile(a, 0);
-    for (int base = 0; base < ngroups; base += 2 * kBlock) {
-        load_tile(b, base + kBlock);
-        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
-        update_tile(a, base);
-        if (base + kBlock >= ngroups) break;  // uniform: the other tile is empty
-        load_tile(a, base + 2 * kBlock);
-        __builtin_amdgcn_sched_barrier(0);
-        update_tile(b, base + kBlock);
+    // Streams the body (`a` already holds its first tile's loads), then
+    // stores the scale bytes from lds_m / lds_v (kMaxRunsPerBody bytes
+    // each) with consecutive threads.
+    __device__ __forceinline__ void run(Tile& a, const StepScalars& s, uint8_t* lds_m,
+                                        uint8_t* lds_v) const
+    {
+        const int ngroups = static_cast<int>(ng);
+        Tile b;
+        for (int base = 0; base < ngroups; base += 2 * kBlock) {
+            load(b, base + kBlock);
+            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+            update(a, base, s, lds_m, lds_v);
+            if (base + kBlock >= ngroups) break;  // uniform: the other tile is empty
+            load(a, base + 2 * kBlock);
+            __builtin_amdgcn_sched_barrier(0);
+            update(b, base + kBlock, s, lds_m, lds_v);
+        }
+        __syncthreads();
+        for (uint32_t r = threadIdx.x; r < ng / 8u; r += kBlock) {
+            store_byte(lds_m[r], MS, r);
+            store_byte(lds_v[r], VS, r);
+        }
     }
-    __syncthreads();
-    for (uint32_t r = tid; r < ng / 8u; r += kBlock) {
-        store_byte(lds_m[r], MS, r);
-        store_byte(lds_v[r], VS, r);
+};
+
+// The element range of chunk c of a tensor and the end of its vector part:
+// the whole runs of an aligned tensor take the vector body, the tensor's
+// last partial run (and every element of an unaligned tensor) the element
+// path.
+struct Chunk8 {
+    int64_t begin, vend, end;
+};
+
+template <class Entry>
+__device__ __forceinline__ Chunk8 chunk8_span(const Entry* te, int c, int64_t chunk_elems)
+{
+    Chunk8 k;
+    k.begin = static_cast<int64_t>(c - te->first_chunk) * chunk_elems;
+    k.end = min(k.begin + chunk_elems, te->numel);
+    const int64_t whole = te->numel - te->numel % kQuantBlock;
+    k.vend = te->head < 0 ? k.begin : max(k.begin, min(k.end, whole));
+    return k;
+}
+
+// Chunk c of one tensor in full.  `parity` picks this block's pair of scale
+// buffers and flips after each body: the barrier that ends one body also
+// separates the readers of a pair from the writers of the body after next.
+template <bool kBf16, class Entry>
+__device__ __forceinline__ void adamw8_chunk(const Entry* te, const QuantEntry* qe, int c,
+                                             int64_t chunk_elems, const StepScalars& s,
+                                             int& parity)
+{
+    const Chunk8 k = chunk8_span(te, c, chunk_elems);
+    if (k.vend > k.begin) {
+        const Body8<kBf16> body(te, qe, k.begin, static_cast<int>((k.vend - k.begin) / 4));
+        typename Body8<kBf16>::Tile a;
+        body.load(a, 0);
+        body.run(a, s, scale_lds()[parity][0], scale_lds()[parity][1]);
+        parity ^= 1;
     }
+    if (k.end > k.vend) adamw8_elements<kBf16>(te, qe, k.vend, k.end, s);
 }
 
 // Chunks b, b + G, ... of this block, as in the fp32 kernel (the next
-// chunk's table entries are fetched before this chunk streams).  Within a
-// chunk the whole runs of an aligned tensor take the vector body and the
-// tensor's last partial run the element path.
+// chunk's table entries are fetched before this chunk streams).
 template <bool kBf16>
 __device__ __forceinline__ void update8_chunks(const TensorEntry* __restrict__ tensors,
                                                const QuantEntry* __restrict__ quant,
                                                const uint32_t* __restrict__ chunk_map, int n_chunks,
                                                int64_t chunk_elems, const StepScalars& s)
 {
-    __shared__ uint8_t scale_lds[2][2][kMaxRunsPerBody];
     int parity = 0;
     TensorEntry next{};
     QuantEntry next_q{};
@@ -373,20 +433,7 @@ __device__ __forceinline__ void update8_chunks(const TensorEntry* __restrict__ t
             next = tensors[k];
             next_q = quant[k];
         }
-        const int64_t begin = static_cast<int64_t>(c - te.first_chunk) * chunk_elems;
-        const int64_t end = min(begin + chunk_elems, te.numel);
-        if (te.head < 0) {
-            adamw8_elements<kBf16>(&te, &qe, begin, end, s);
-            continue;
-        }
-        const int64_t whole = te.numel - te.numel % kQuantBlock;
-        const int64_t vend = max(begin, min(end, whole));
-        if (vend > begin) {
-            adamw8_body<kBf16>(&te, &qe, begin, static_cast<int>((vend - begin) / 4), s,
-                               scale_lds[parity][0], scale_lds[parity][1]);
-            parity ^= 1;
-        }
-        if (end > vend) adamw8_elements<kBf16>(&te, &qe, vend, end, s);
+        adamw8_chunk<kBf16>(&te, &qe, c, chunk_elems, s, parity);
     }
 }
 
@@ -410,36 +457,70 @@ __global__ __launch_bounds__(kBlock) void adamw8_step_kernel(
 // kernel: every block sums the norm launch's partials in block order (the
 // same bits as the norm's own second stage), forms the coefficient, and takes
 // t from the header, where the norm launch left it; block 0 publishes S, the
-// coefficient and the new count.
+// coefficient and the new count.  A list with one tensor brings that
+// tensor's entries with the launch, and the loads of each block's first
+// tile are issued before the tag and the partials are waited for, as in the
+// fp32 kernel; nothing is stored before the tag has matched.
 template <bool kBf16>
 __global__ __launch_bounds__(kBlock) void adamw8_clipped_kernel(
-    WorkspaceHeader* header, const TensorEntry* __restrict__ tensors,
-    const QuantEntry* __restrict__ quant, const uint32_t* __restrict__ chunk_map, int n_chunks,
-    int64_t chunk_elems, uint64_t tag, const double* __restrict__ partials, int n_partials,
-    double max_norm, double grad_scale, int skip_if_nonfinite, double* d_sumsq, float* d_coef,
-    int32_t* d_step, HyperParams hp)
+    WorkspaceView ws, const QuantEntry* __restrict__ quant, int n_partials, double max_norm,
+    double grad_scale, int skip_if_nonfinite, double* d_sumsq, float* d_coef, int32_t* d_step,
+    HyperParams hp)
 {
-    const int tid = threadIdx.x;
-    const uint64_t seen = header->tag;
-    const int32_t t = header->pending_step;
-    if (seen != tag) {  // tables overwritten: touch nothing, report NaN
-        if (blockIdx.x == 0 && tid == 0) {
-            if (d_sumsq) *d_sumsq = __builtin_nan("");
-            if (d_coef) *d_coef = __builtin_nanf("");
+    // The header first: scalar loads, which the vector-memory counter does
+    // not wait for.
+    const uint64_t seen = ws.header->tag;
+    const int32_t t = ws.header->pending_step;
+    __shared__ double lds[kWavesPerBlock];
+
+    if (ws.solo_tensor >= 0) {
+        const SoloEntry& te = ws.solo;
+        const QuantEntry& qe = ws.solo_quant;
+        const int c0 = blockIdx.x;
+        const bool whole = c0 < ws.n_chunks;
+        const Chunk8 k = chunk8_span(&te, min(c0, ws.n_chunks - 1), ws.chunk_elems);
+        const bool vector = whole && k.vend > k.begin;
+        // A block without a vector body loads nothing (an empty range).
+        const Body8<kBf16> body(&te, &qe, k.begin,
+                                vector ? static_cast<int>((k.vend - k.begin) / 4) : 0);
+        // Loads in issue order: the partials, then the tile, so the sum of
+        // the partials can start while the tile is still in flight.
+        __builtin_amdgcn_sched_barrier(0);
+        const PartialSlots slots = load_partials<false>(ws.partials);
+        __builtin_amdgcn_sched_barrier(0);
+        typename Body8<kBf16>::Tile a;
+        body.load(a, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const double total = block_sum(partial_share(slots, n_partials), lds);
+        if (seen != ws.tag) {
+            report_stale_clip(d_sumsq, d_coef);
+            return;
+        }
+        const float clip = clip_from_sumsq(total, max_norm, grad_scale);
+        if (publish_clip(total, clip, t, skip_if_nonfinite, d_sumsq, d_coef, d_step)) return;
+        const StepScalars s = step_scalars(t, hp, clip);
+        int parity = 0;
+        if (vector) {
+            body.run(a, s, scale_lds()[0][0], scale_lds()[0][1]);
+            parity = 1;
+            if (k.end > k.vend) adamw8_elements<kBf16>(&te, &qe, k.vend, k.end, s);
+        } else if (whole) {
+            adamw8_chunk<kBf16>(&te, &qe, c0, ws.chunk_elems, s, parity);
+        }
+        for (int c = c0 + static_cast<int>(gridDim.x); c < ws.n_chunks; c += gridDim.x) {
+            adamw8_chunk<kBf16>(&te, &qe, c, ws.chunk_elems, s, parity);
         }
         return;
     }
-    __shared__ double lds[kWavesPerBlock];
-    const double total = sum_partials<false>(partials, n_partials, lds);
-    const float clip = clip_from_sumsq(total, max_norm, grad_scale);
-    const bool skip = skip_if_nonfinite && !__builtin_isfinite(total);
-    if (blockIdx.x == 0 && tid == 0) {
-        if (d_sumsq) *d_sumsq = total;
-        if (d_coef) *d_coef = clip;
-        if (!skip) *d_step = t;
+
+    if (seen != ws.tag) {
+        report_stale_clip(d_sumsq, d_coef);
+        return;
     }
-    if (skip) return;
-    update8_chunks<kBf16>(tensors, quant, chunk_map, n_chunks, chunk_elems,
+    const double total = sum_partials<false>(ws.partials, n_partials, lds);
+    const float clip = clip_from_sumsq(total, max_norm, grad_scale);
+    if (publish_clip(total, clip, t, skip_if_nonfinite, d_sumsq, d_coef, d_step)) return;
+    update8_chunks<kBf16>(ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems,
                           step_scalars(t, hp, clip));
 }
 
@@ -501,13 +582,11 @@ hipError_t launch_adamw8_clipped(const WorkspaceView& ws, const QuantEntry* quan
 {
     if (grad_bf16) {
         adamw8_clipped_kernel<true><<<grid, kBlock, 0, stream>>>(
-            ws.header, ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag,
-            ws.partials, n_partials, max_norm, grad_scale, skip_if_nonfinite, d_sumsq, d_coef,
+            ws, quant, n_partials, max_norm, grad_scale, skip_if_nonfinite, d_sumsq, d_coef,
             d_step, hp);
     } else {
         adamw8_clipped_kernel<false><<<grid, kBlock, 0, stream>>>(
-            ws.header, ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag,
-            ws.partials, n_partials, max_norm, grad_scale, skip_if_nonfinite, d_sumsq, d_coef,
+            ws, quant, n_partials, max_norm, grad_scale, skip_if_nonfinite, d_sumsq, d_coef,
             d_step, hp);
     }
     return hipGetLastError();

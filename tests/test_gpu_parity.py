@@ -341,20 +341,28 @@ def test_nonfinite_gradients():
     run_and_check(cols, t=1, what="inf grad")
 
 
-def test_overwritten_workspace_is_detected():
+@pytest.mark.parametrize("form", ["three calls", "clipped"])
+@pytest.mark.parametrize("sizes", [[5000], [5000, 300]], ids=["one tensor", "two tensors"])
+def test_overwritten_workspace_is_detected(form, sizes):
     """If the workspace tables are overwritten behind the library's back the
-    kernels leave every buffer alone (the norm reports NaN)."""
-    cols = make_cols([5000], False, False, seed=15)
-    before = [t.clone() for t in cols["master"]]
+    kernels leave every buffer alone (the norm reports NaN).  A one-tensor
+    list takes its tensor from the launch and checks the tag after its first
+    reads, a longer list before; both are covered in both two-launch forms."""
+    cols = make_cols(sizes, False, False, seed=15)
+    before = [t.clone() for t in cols["master"] + cols["exp_avg"] + cols["exp_avg_sq"]]
     st = Step(cols, completed_steps=0)
     st.norm().results()  # uploads the tables
     ws = st.tl._ws_storage
     off = st.tl.workspace_ptr - ws.data_ptr()
     ws[off:off + 64].zero_()
-    st.norm().clip(1.0).update(**_hp())
-    S, _, step = st.results()
-    assert np.isnan(S) and step == 0
-    assert torch.equal(cols["master"][0], before[0])
+    if form == "clipped":
+        st.clipped(1.0, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+    else:
+        st.norm().clip(1.0).update(**_hp())
+    S, c, step = st.results()
+    assert np.isnan(S) and np.isnan(c) and step == 0
+    after = cols["master"] + cols["exp_avg"] + cols["exp_avg_sq"]
+    assert all(torch.equal(a, b) for a, b in zip(after, before))
 
 
 def test_one_workspace_shared_by_two_lists():
