@@ -51,8 +51,15 @@ def parse():
                    help="workload 1..5 (default 2: Llama-3.1-8B FSDP2 shard at 128-way)")
     p.add_argument("--rotate", type=int, default=1,
                    help="cycle over this many independent buffer sets (cache-cold small shards)")
+    p.add_argument("--trials", type=int, default=5,
+                   help="time the K steps this many times (the first is the reported value; "
+                        "all give the p10 / median / p90 of ms per step)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
-                   help="host time budget of the oracle baseline (0 = skip)")
+                   help="host time budget of each oracle baseline: one thread, then all "
+                        "threads (0 = skip)")
+    p.add_argument("--cpu-threads", type=int, default=0,
+                   help="threads of the all-cores oracle baseline (default: the CPUs this "
+                        "process may use, at most 16)")
     p.add_argument("--no-kernel-events", action="store_true")
     p.add_argument("--launches", choices=("separate", "clipped", "fused"), default="clipped",
                    help="separate: grad_norm_sq with the clip output, then "
@@ -197,6 +204,38 @@ def main():
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
 
+    # The same K steps timed again, for the spread between trials.
+    trial_ms = [ms_per_step]
+    for _ in range(args.trials - 1):
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(args.steps):
+            one_step(sets[i % len(sets)][1])
+        end.record()
+        torch.cuda.synchronize()
+        trial_ms.append(start.elapsed_time(end) / args.steps)
+    trials = {"n": len(trial_ms), "ms_per_step": [round(x, 5) for x in trial_ms],
+              **{k: round(v, 5) for k, v in zip(("p10", "median", "p90"),
+                                                _quantiles(trial_ms, (10, 50, 90)))}}
+    log("trials (us/step): " + ", ".join(f"{x * 1e3:.1f}" for x in trial_ms))
+
+    # With rotating buffer sets, also the warm figure: K steps on one set.
+    warm = None
+    if len(sets) > 1:
+        for _ in range(args.warmup):
+            one_step(sets[0][1])
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            one_step(sets[0][1])
+        end.record()
+        torch.cuda.synchronize()
+        warm_ms = start.elapsed_time(end) / args.steps
+        warm = {"ms_per_step": round(warm_ms, 5),
+                "params_per_s": w.numel / (warm_ms * 1e-3),
+                "what": "the same K steps on one buffer set (its data stays in the caches)"}
+        log(f"warm, one buffer set: {warm_ms * 1e3:.1f} us/step")
+
     # Per-kernel durations: the same K steps again with events between the
     # launches, on the stream the kernels run on.
     kern_us = None
@@ -270,8 +309,9 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = (cpu_baseline8(w, sets[0][0], args.cpu_seconds) if args.state8
-               else cpu_baseline(w, sets[0][0], args.cpu_seconds))
+        threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+        cpu = (cpu_baseline8(w, sets[0][0], args.cpu_seconds, threads) if args.state8
+               else cpu_baseline(w, sets[0][0], args.cpu_seconds, threads))
 
     out = {
         "metric": "params updated/sec and achieved HBM GB/s (fraction of peak) per AdamW step",
@@ -296,6 +336,8 @@ def main():
         "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "kernel_us": kern_us,
         "step_us_spread": spread,
+        "trials": trials,
+        "warm_same_buffers": warm,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -305,11 +347,50 @@ def main():
 CPU_SAMPLE_MAX_ELEMS = 64 << 20
 
 
-def cpu_baseline(w, cols, budget_s):
-    """The oracle, untuned and single-threaded, on the host: whole steps
-    (norm, clip, update) over a bounded sample of the workload — its first
-    tensors, at most CPU_SAMPLE_MAX_ELEMS elements (the whole shard when it is
-    smaller) — repeated until the time budget is spent.  Scaled to params/s."""
+def _quantiles(xs, qs):
+    xs = sorted(xs)
+    return [xs[min(len(xs) - 1, int(q / 100 * len(xs)))] for q in qs]
+
+
+def _slices(n, parts, align=1):
+    """Bounds of `parts` contiguous slices of n elements, each starting at a
+    multiple of `align` (empty slices dropped)."""
+    cuts = [min(n, (n * k // parts) // align * align) for k in range(parts)] + [n]
+    return [(a, b) for a, b in zip(cuts, cuts[1:]) if b > a]
+
+
+def _time_steps(step, budget_s):
+    """Calls step(i) for i = 0, 1, ... until budget_s has passed."""
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        step(steps)
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            return steps, time.perf_counter() - t0
+
+
+def _threads_timing(parts, norm_part, update_part, clip, budget_s):
+    """Whole steps with the sample cut into parts, one per thread: the norm
+    of each part, the sum of the partial sums, the clip, the update of each
+    part.  The oracle's C functions run outside the interpreter lock."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    with ThreadPoolExecutor(max_workers=len(parts)) as pool:
+        def step(i):
+            S = sum(pool.map(norm_part, parts))
+            c = clip(S)
+            list(pool.map(lambda part: update_part(part, c, i), parts))
+        return _time_steps(step, budget_s)
+
+
+def cpu_baseline(w, cols, budget_s, threads):
+    """The oracle, untuned, on the host: whole steps (norm, clip, update) over
+    a bounded sample of the workload — its first tensors, at most
+    CPU_SAMPLE_MAX_ELEMS elements (the whole shard when it is smaller) —
+    repeated until the time budget is spent, on one thread; then the same
+    sample on `threads` threads, each running the same oracle functions on
+    its own slice of every tensor.  Scaled to params/s."""
     import oracle
     from mixed_precision_sharded_amd.synth import to_numpy
 
@@ -325,38 +406,57 @@ def cpu_baseline(w, cols, budget_s):
             host[k].append(None if t is None else to_numpy(t[:n]).copy())
         taken += n
     n_tensors = len(host["master"])
-    t_done = w.step
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def update(i, lo, hi, c, t):
+        p = host["param_bf16"][i]
+        o.adamw_step(host["master"][i][lo:hi], host["exp_avg"][i][lo:hi],
+                     host["exp_avg_sq"][i][lo:hi], host["grad"][i][lo:hi],
+                     None if p is None else p[lo:hi], c, t, w.lr, w.beta1, w.beta2, w.eps,
+                     w.weight_decay)
+
+    def one_thread(k):
         S = o.grad_norm_sq(host["grad"])
         c = o.clip_coef(S, w.max_norm)
         for i in range(n_tensors):
-            o.adamw_step(host["master"][i], host["exp_avg"][i], host["exp_avg_sq"][i],
-                         host["grad"][i], host["param_bf16"][i], c, t_done, w.lr, w.beta1,
-                         w.beta2, w.eps, w.weight_decay)
-        t_done += 1
-        steps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
+            update(i, 0, host["master"][i].size, c, w.step + k)
+
+    steps, dt = _time_steps(one_thread, budget_s)
+    t_next = w.step + steps
     whole = taken == w.numel
     what = (f"whole {w.name} shard" if whole else
             f"first {n_tensors} of {w.n_tensors} tensors of {w.name}")
-    log(f"cpu oracle: {steps} steps of {taken:,} params in {dt:.2f} s")
+    log(f"cpu oracle: {steps} steps of {taken:,} params in {dt:.2f} s, 1 thread")
+
+    # Thread k takes slice k of every tensor.
+    parts = [[] for _ in range(threads)]
+    for i in range(n_tensors):
+        for k, (lo, hi) in enumerate(_slices(host["master"][i].size, threads)):
+            parts[k].append((i, lo, hi))
+    parts = [p for p in parts if p]
+    steps_t, dt_t = _threads_timing(
+        parts, lambda part: o.grad_norm_sq([host["grad"][i][lo:hi] for i, lo, hi in part]),
+        lambda part, c, k: [update(i, lo, hi, c, t_next + k) for i, lo, hi in part],
+        lambda S: o.clip_coef(S, w.max_norm), budget_s)
+    log(f"cpu oracle: {steps_t} steps of {taken:,} params in {dt_t:.2f} s, {len(parts)} threads")
     return {"value": taken * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"{what} ({taken:,} params): norm + clip + update, {steps} consecutive "
                       f"steps, 1 thread, {dt:.1f} s",
+            "all_cores": {"value": taken * steps_t / dt_t, "unit": "params/s",
+                          "cores": len(parts),
+                          "sample": f"the same sample, {steps_t} consecutive steps, each "
+                                    f"tensor cut into {len(parts)} slices, one thread per "
+                                    f"slice, partial sums added, {dt_t:.1f} s"},
             "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
 
 
 CPU_SAMPLE_MAX_ELEMS_Q8 = 2 << 20
 
 
-def cpu_baseline8(w, cols, budget_s):
+def cpu_baseline8(w, cols, budget_s, threads):
     """The oracle's 8-bit-moment step, as cpu_baseline, on the first tensors
     of the workload up to CPU_SAMPLE_MAX_ELEMS_Q8 elements (its nearest-code
-    search is much slower per element than the fp32 update)."""
+    search is much slower per element than the fp32 update); the threaded
+    run cuts every tensor at multiples of the 32-element scale runs."""
     import oracle
     from mixed_precision_sharded_amd.synth import to_numpy
 
@@ -375,26 +475,44 @@ def cpu_baseline8(w, cols, budget_s):
                          vc=vc[:n].cpu().numpy().copy(), vs=vs[:nb].cpu().numpy().copy(),
                          p=None if p is None else to_numpy(p[:n]).copy()))
         taken += n
-    t_done = w.step
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def update(h, lo, hi, c, t):
+        r0, r1 = lo // 32, (hi + 31) // 32
+        o.adamw8_step(h["w"][lo:hi], h["mc"][lo:hi], h["ms"][r0:r1], h["vc"][lo:hi],
+                      h["vs"][r0:r1], h["g"][lo:hi], None if h["p"] is None else h["p"][lo:hi],
+                      c, t, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
+
+    def one_thread(k):
         S = o.grad_norm_sq([h["g"] for h in host])
         c = o.clip_coef(S, w.max_norm)
         for h in host:
-            o.adamw8_step(h["w"], h["mc"], h["ms"], h["vc"], h["vs"], h["g"], h["p"], c, t_done,
-                          w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
-        t_done += 1
-        steps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
+            update(h, 0, h["w"].size, c, w.step + k)
+
+    steps, dt = _time_steps(one_thread, budget_s)
+    t_next = w.step + steps
     what = (f"whole {w.name} shard" if taken == w.numel else
             f"first {len(host)} of {w.n_tensors} tensors of {w.name}")
-    log(f"cpu oracle (8-bit moments): {steps} steps of {taken:,} params in {dt:.2f} s")
+    log(f"cpu oracle (8-bit moments): {steps} steps of {taken:,} params in {dt:.2f} s, 1 thread")
+
+    parts = [[] for _ in range(threads)]
+    for h in host:
+        for k, (lo, hi) in enumerate(_slices(h["w"].size, threads, align=32)):
+            parts[k].append((h, lo, hi))
+    parts = [p for p in parts if p]
+    steps_t, dt_t = _threads_timing(
+        parts, lambda part: o.grad_norm_sq([h["g"][lo:hi] for h, lo, hi in part]),
+        lambda part, c, k: [update(h, lo, hi, c, t_next + k) for h, lo, hi in part],
+        lambda S: o.clip_coef(S, w.max_norm), budget_s)
+    log(f"cpu oracle (8-bit moments): {steps_t} steps of {taken:,} params in {dt_t:.2f} s, "
+        f"{len(parts)} threads")
     return {"value": taken * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"{what}, first {taken:,} params: norm + clip + 8-bit-moment update, "
                       f"{steps} consecutive steps, 1 thread, {dt:.1f} s",
+            "all_cores": {"value": taken * steps_t / dt_t, "unit": "params/s",
+                          "cores": len(parts),
+                          "sample": f"the same sample, {steps_t} consecutive steps, each "
+                                    f"tensor cut at 32-element runs into {len(parts)} slices, "
+                                    f"one thread per slice, partial sums added, {dt_t:.1f} s"},
             "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
 
 

@@ -35,3 +35,32 @@ def test_no_gpu_fails_loudly():
     assert r.returncode == 1
     assert "needs a GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_slices_cover_every_element_once_at_the_alignment():
+    sys.path.insert(0, ROOT)
+    import bench
+
+    for n in (0, 1, 5, 31, 32, 100, 1000, 4097):
+        for parts in (1, 3, 8, 16):
+            for align in (1, 32):
+                s = bench._slices(n, parts, align)
+                assert len(s) <= parts
+                assert [e for lo, hi in s for e in range(lo, hi)] == list(range(n))
+                assert all(lo % align == 0 and hi > lo for lo, hi in s)
+
+
+def test_cpu_baseline_reports_one_thread_and_all_threads():
+    """The oracle leg of the bench on host tensors: one-thread and threaded
+    timings of the same sample, each with its core count."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from mixed_precision_sharded_amd import synth
+    from mixed_precision_sharded_amd.configs import Workload
+
+    w = Workload(cfg=1, name="tiny_two_tensors", tensors=(("a", 3000), ("b", 70)),
+                 grad_bf16=True, copy_bf16=True, step=1)
+    cols = synth.workload_inputs(w, torch.device("cpu"))
+    r = bench.cpu_baseline(w, cols, 0.05, 3)
+    assert r["cores"] == 1 and r["kind"] == "oracle" and r["value"] > 0
+    assert r["all_cores"]["cores"] == 3 and r["all_cores"]["value"] > 0
