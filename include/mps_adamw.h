@@ -94,7 +94,8 @@ typedef struct mps_tensor {
 /*
  * Size in bytes of the device workspace that the fp32-state entry points need
  * for this list (a header, the per-tensor and per-chunk tables, the lines of
- * the blocks' ticket counters, and one fp64 partial per norm block).  It
+ * the blocks' ticket counters, two constants, and one fp64 partial per norm
+ * block).  It
  * grows with the number of tensors and chunks, not with the bytes of state.
  * Returns 0 and sets the last error if the list is invalid.
  *

@@ -51,6 +51,7 @@ struct Plan {
     size_t quant_off = 0;   // 8-bit lists: QuantEntry table (else == chunks_off)
     size_t chunks_off = 0;
     size_t tickets_off = 0;
+    size_t constants_off = 0;
     size_t partials_off = 0;
     size_t total_bytes = 0;
     int n_chunks = 0;
@@ -152,14 +153,18 @@ int layout_plan(std::vector<TensorEntry>& entries, const std::vector<mps::QuantE
     // that the kernels' first lookup is always in the table.
     const int64_t map_slots = n_chunks > 0 ? n_chunks : 1;
     plan.tickets_off = round_up(plan.chunks_off + sizeof(uint32_t) * map_slots, 128);
-    plan.partials_off = round_up(plan.tickets_off + sizeof(uint32_t) * mps::kTicketStride *
-                                                        (mps::kTicketGroups + 1), 256);
+    plan.constants_off = plan.tickets_off +
+                         sizeof(uint32_t) * mps::kTicketStride * (mps::kTicketGroups + 1);
+    plan.partials_off = round_up(plan.constants_off + sizeof(mps::WorkspaceConstants), 256);
     plan.total_bytes = plan.partials_off + sizeof(double) * mps::kPartials;
 
     plan.image.assign(plan.partials_off, 0);
     unsigned char* base = plan.image.data();
     std::memcpy(base + plan.tensors_off, entries.data(), sizeof(TensorEntry) * n);
     if (quant) std::memcpy(base + plan.quant_off, quant->data(), sizeof(mps::QuantEntry) * n);
+    auto* constants = reinterpret_cast<mps::WorkspaceConstants*>(base + plan.constants_off);
+    constants->zero = 0.0;
+    constants->one = 1.0f;
     uint32_t* map = reinterpret_cast<uint32_t*>(base + plan.chunks_off);
     for (int i = 0; i < n; ++i) {
         const int64_t k = (entries[i].numel + plan.chunk_elems - 1) / plan.chunk_elems;
@@ -416,6 +421,22 @@ mps::WorkspaceView view_of(void* ws, const Plan& plan)
     return v;
 }
 
+// The optional inputs of the update: the caller's pointer, or the
+// workspace constant that stands for "absent" (coefficient 1, never skip).
+const float* coef_or_one(const float* d_coef, void* ws, const Plan& plan)
+{
+    return d_coef ? d_coef
+                  : &reinterpret_cast<const mps::WorkspaceConstants*>(
+                         static_cast<unsigned char*>(ws) + plan.constants_off)->one;
+}
+
+const double* skip_or_zero(const double* d_skip, void* ws, const Plan& plan)
+{
+    return d_skip ? d_skip
+                  : &reinterpret_cast<const mps::WorkspaceConstants*>(
+                         static_cast<unsigned char*>(ws) + plan.constants_off)->zero;
+}
+
 // At most `cap` blocks, every block taking the same number of chunks (the
 // last one possibly fewer): ceil(n / ceil(n / cap)).
 int grid_for(int n_chunks, int cap)
@@ -584,8 +605,10 @@ int adamw_multi_tensor_step(const mps_tensor* tensors, int n_tensors, mps_dtype 
     }
     mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
     const int grid = grid_for(plan.n_chunks, mps::kStepMaxBlocks);
-    hipError_t e = mps::launch_adamw_step(view_of(d_workspace, plan), grad_dtype == MPS_DTYPE_BF16,
-                                          grid, d_coef, d_skip_if_nonfinite, d_step, hp, st);
+    hipError_t e = mps::launch_adamw_step(
+        view_of(d_workspace, plan), grad_dtype == MPS_DTYPE_BF16, grid,
+        coef_or_one(d_coef, d_workspace, plan),
+        skip_or_zero(d_skip_if_nonfinite, d_workspace, plan), d_step, hp, st);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "adamw_step launch: %s", hipGetErrorString(e));
     return ok();
 }
@@ -691,9 +714,10 @@ int adamw8_multi_tensor_step(const mps_tensor8* tensors, int n_tensors, mps_dtyp
     const int grid = grid_for(plan.n_chunks, mps::kQ8MaxBlocks);
     const auto* quant = reinterpret_cast<const mps::QuantEntry*>(static_cast<unsigned char*>(d_workspace) +
                                                                  plan.quant_off);
-    hipError_t e = mps::launch_adamw8_step(view_of(d_workspace, plan), quant,
-                                           grad_dtype == MPS_DTYPE_BF16, grid, d_coef,
-                                           d_skip_if_nonfinite, d_step, hp, st);
+    hipError_t e = mps::launch_adamw8_step(
+        view_of(d_workspace, plan), quant, grad_dtype == MPS_DTYPE_BF16, grid,
+        coef_or_one(d_coef, d_workspace, plan),
+        skip_or_zero(d_skip_if_nonfinite, d_workspace, plan), d_step, hp, st);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "adamw8_step launch: %s", hipGetErrorString(e));
     return ok();
 }

@@ -51,6 +51,8 @@ hipError_t launch_grad_norm_partials(const WorkspaceView& ws, bool grad_bf16, in
 hipError_t launch_clip_coef(const double* d_sumsq, double max_norm, double grad_scale,
                             float* d_coef, hipStream_t stream);
 
+// d_coef and d_skip_if_nonfinite are never NULL here: the library passes
+// the workspace's constants (1 and 0) for inputs the caller left out.
 hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, int grid,
                              const float* d_coef, const double* d_skip_if_nonfinite,
                              int32_t* d_step, const HyperParams& hp, hipStream_t stream);
@@ -73,7 +75,8 @@ hipError_t launch_fused_step(const WorkspaceView& ws, bool grad_bf16, int grid, 
                              const HyperParams& hp, hipStream_t stream);
 
 // 8-bit moment state (kernels_q8.hip).  `quant` is the QuantEntry table in
-// the same workspace.
+// the same workspace; d_coef and d_skip_if_nonfinite are never NULL (as in
+// launch_adamw_step).
 hipError_t launch_adamw8_step(const WorkspaceView& ws, const QuantEntry* quant, bool grad_bf16,
                               int grid, const float* d_coef, const double* d_skip_if_nonfinite,
                               int32_t* d_step, const HyperParams& hp, hipStream_t stream);

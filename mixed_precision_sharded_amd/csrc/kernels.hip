@@ -468,24 +468,90 @@ __device__ __forceinline__ void update_chunks(const WorkspaceView& ws, TensorEnt
     }
 }
 
+// A block's walk over a one-tensor list, whose tensor came with the launch
+// (no table is read).  The constructor does the address arithmetic of the
+// block's first chunk (chunk blockIdx.x of the strided walk); load_first()
+// issues the loads of its first tile, so that a kernel can put them in
+// flight before it waits for anything; finish() streams that chunk and the
+// block's later ones.  A block whose first chunk has no vector body loads
+// nothing there (an empty range).
+template <bool kBf16, int kUnroll>
+struct SoloWalk {
+    const SoloEntry* te;
+    int n_chunks;
+    int64_t chunk_elems;
+    ChunkSpan k;
+    bool whole, vector;
+    Body<kBf16, kUnroll> body;
+    typename Body<kBf16, kUnroll>::Tile a;
+
+    __device__ __forceinline__ explicit SoloWalk(const WorkspaceView& ws)
+        : te(&ws.solo),
+          n_chunks(ws.n_chunks),
+          chunk_elems(ws.chunk_elems),
+          k(chunk_span(&ws.solo, min(static_cast<int>(blockIdx.x), ws.n_chunks - 1),
+                       ws.chunk_elems)),
+          whole(static_cast<int>(blockIdx.x) < ws.n_chunks),
+          vector(whole && ws.solo.head >= 0),
+          body(&ws.solo, vector ? k.qbegin : k.begin, vector ? k.nquad : 0)
+    {
+    }
+
+    __device__ __forceinline__ void load_first() { body.load(a, 0); }
+
+    __device__ __forceinline__ void finish(const StepScalars& s)
+    {
+        const int tid = threadIdx.x;
+        if (vector) {
+            if (tid < k.qbegin - k.begin) adamw_scalar_at<kBf16>(te, k.begin + tid, s);
+            body.run(a, s);
+            if (tid < k.end - k.tail) adamw_scalar_at<kBf16>(te, k.tail + tid, s);
+        } else if (whole) {
+            adamw_chunk<kBf16, kUnroll>(te, static_cast<int>(blockIdx.x), chunk_elems, s);
+        }
+        for (int c = blockIdx.x + gridDim.x; c < n_chunks; c += gridDim.x) {
+            adamw_chunk<kBf16, kUnroll>(te, c, chunk_elems, s);
+        }
+    }
+};
+
 template <bool kBf16, int kUnroll>
 __global__ __launch_bounds__(kBlock) void adamw_step_kernel(
     WorkspaceView ws, const float* d_coef, const double* d_skip_if_nonfinite, int32_t* d_step,
     HyperParams hp)
 {
+    if (ws.solo_tensor >= 0) {
+        // The address arithmetic of the first tile from the kernel
+        // arguments, then the scalar loads and that tile's loads, all in
+        // flight together; the tag is compared before anything is stored.
+        SoloWalk<kBf16, kUnroll> walk(ws);
+        const uint64_t seen = ws.header->tag;
+        const int32_t count = *d_step;
+        const float coef = *d_coef;
+        const double skip_value = *d_skip_if_nonfinite;
+        walk.load_first();
+        __builtin_amdgcn_sched_barrier(0);
+        if (seen != ws.tag) return;                  // tables overwritten: touch nothing
+        if (!__builtin_isfinite(skip_value)) return;  // a skipped step writes nothing
+        const int64_t t = static_cast<int64_t>(count) + 1;
+        walk.finish(step_scalars(t, hp, coef));
+        advance_step(ws.tickets, d_step, t);
+        return;
+    }
+
     // Independent loads, in flight together (the first chunk is chunk
     // blockIdx.x of the strided walk).
     const uint64_t seen = ws.header->tag;
     const int32_t count = *d_step;
-    const float coef = d_coef ? *d_coef : 1.0f;
-    const double skip_value = d_skip_if_nonfinite ? *d_skip_if_nonfinite : 0.0;
+    const float coef = *d_coef;
+    const double skip_value = *d_skip_if_nonfinite;
+    const int64_t t = static_cast<int64_t>(count) + 1;
     const TensorEntry first = ws.tensors[prologue_tensor(ws, blockIdx.x)];
     if (seen != ws.tag) return;  // tables overwritten: touch nothing
     // A skipped step writes nothing and leaves the counter.  The value is
     // uniform, so every block makes the same choice.
     if (!__builtin_isfinite(skip_value)) return;
 
-    const int64_t t = static_cast<int64_t>(count) + 1;
     update_chunks<kBf16, kUnroll>(ws, first, step_scalars(t, hp, coef));
     advance_step(ws.tickets, d_step, t);
 }
@@ -514,7 +580,6 @@ __global__ __launch_bounds__(kBlock) void adamw_clipped_kernel(
     WorkspaceView ws, int n_partials, double max_norm, double grad_scale, int skip_if_nonfinite,
     double* d_sumsq, float* d_coef, int32_t* d_step, HyperParams hp)
 {
-    const int tid = threadIdx.x;
     // The header first: read before anything else, these are scalar loads,
     // which the vector-memory counter does not wait for.
     const uint64_t seen = ws.header->tag;
@@ -522,13 +587,7 @@ __global__ __launch_bounds__(kBlock) void adamw_clipped_kernel(
     __shared__ double lds[kWavesPerBlock];
 
     if (ws.solo_tensor >= 0) {
-        const SoloEntry& te = ws.solo;
-        const int c0 = blockIdx.x;
-        const bool whole = c0 < ws.n_chunks;
-        const bool vector = whole && te.head >= 0;
-        const ChunkSpan k = chunk_span(&te, min(c0, ws.n_chunks - 1), ws.chunk_elems);
-        // A block without a vector body loads nothing (an empty range).
-        const Body<kBf16, kUnroll> body(&te, vector ? k.qbegin : k.begin, vector ? k.nquad : 0);
+        SoloWalk<kBf16, kUnroll> walk(ws);
         // The vector-memory counter is waited for in issue order.  All the
         // address arithmetic comes first, then the loads of the partials,
         // then the tile's: the sum of the partials can start while the tile
@@ -536,8 +595,7 @@ __global__ __launch_bounds__(kBlock) void adamw_clipped_kernel(
         __builtin_amdgcn_sched_barrier(0);
         const PartialSlots slots = load_partials<false>(ws.partials);
         __builtin_amdgcn_sched_barrier(0);
-        typename Body<kBf16, kUnroll>::Tile a;
-        body.load(a, 0);
+        walk.load_first();
         __builtin_amdgcn_sched_barrier(0);
         const double total = block_sum(partial_share(slots, n_partials), lds);
         if (seen != ws.tag) {
@@ -546,17 +604,7 @@ __global__ __launch_bounds__(kBlock) void adamw_clipped_kernel(
         }
         const float clip = clip_from_sumsq(total, max_norm, grad_scale);
         if (publish_clip(total, clip, t, skip_if_nonfinite, d_sumsq, d_coef, d_step)) return;
-        const StepScalars s = step_scalars(t, hp, clip);
-        if (vector) {
-            if (tid < k.qbegin - k.begin) adamw_scalar_at<kBf16>(&te, k.begin + tid, s);
-            body.run(a, s);
-            if (tid < k.end - k.tail) adamw_scalar_at<kBf16>(&te, k.tail + tid, s);
-        } else if (whole) {
-            adamw_chunk<kBf16, kUnroll>(&te, c0, ws.chunk_elems, s);
-        }
-        for (int c = c0 + static_cast<int>(gridDim.x); c < ws.n_chunks; c += gridDim.x) {
-            adamw_chunk<kBf16, kUnroll>(&te, c, ws.chunk_elems, s);
-        }
+        walk.finish(step_scalars(t, hp, clip));
         return;
     }
 

@@ -437,20 +437,89 @@ __device__ __forceinline__ void update8_chunks(const TensorEntry* __restrict__ t
     }
 }
 
+// A block's walk over a one-tensor list whose entries came with the launch,
+// as SoloWalk in the fp32 kernels: the constructor does the address
+// arithmetic of the block's first chunk, load_first() issues the loads of
+// its first tile, finish() streams that chunk and the block's later ones.
+template <bool kBf16>
+struct Solo8Walk {
+    const SoloEntry* te;
+    const QuantEntry* qe;
+    int n_chunks;
+    int64_t chunk_elems;
+    Chunk8 k;
+    bool whole, vector;
+    Body8<kBf16> body;
+    typename Body8<kBf16>::Tile a;
+
+    __device__ __forceinline__ explicit Solo8Walk(const WorkspaceView& ws)
+        : te(&ws.solo),
+          qe(&ws.solo_quant),
+          n_chunks(ws.n_chunks),
+          chunk_elems(ws.chunk_elems),
+          k(chunk8_span(&ws.solo, min(static_cast<int>(blockIdx.x), ws.n_chunks - 1),
+                        ws.chunk_elems)),
+          whole(static_cast<int>(blockIdx.x) < ws.n_chunks),
+          vector(whole && k.vend > k.begin),
+          // A block without a vector body loads nothing (an empty range).
+          body(&ws.solo, &ws.solo_quant, k.begin,
+               vector ? static_cast<int>((k.vend - k.begin) / 4) : 0)
+    {
+    }
+
+    __device__ __forceinline__ void load_first() { body.load(a, 0); }
+
+    __device__ __forceinline__ void finish(const StepScalars& s)
+    {
+        int parity = 0;
+        if (vector) {
+            body.run(a, s, scale_lds()[0][0], scale_lds()[0][1]);
+            parity = 1;
+            if (k.end > k.vend) adamw8_elements<kBf16>(te, qe, k.vend, k.end, s);
+        } else if (whole) {
+            adamw8_chunk<kBf16>(te, qe, static_cast<int>(blockIdx.x), chunk_elems, s, parity);
+        }
+        for (int c = blockIdx.x + gridDim.x; c < n_chunks; c += gridDim.x) {
+            adamw8_chunk<kBf16>(te, qe, c, chunk_elems, s, parity);
+        }
+    }
+};
+
 template <bool kBf16>
 __global__ __launch_bounds__(kBlock) void adamw8_step_kernel(
-    WorkspaceHeader* header, const TensorEntry* __restrict__ tensors,
-    const QuantEntry* __restrict__ quant, const uint32_t* __restrict__ chunk_map, int n_chunks,
-    int64_t chunk_elems, uint64_t tag, uint32_t* tickets,
-    const float* d_coef, const double* d_skip_if_nonfinite, int32_t* d_step, HyperParams hp)
+    WorkspaceView ws, const QuantEntry* __restrict__ quant, const float* d_coef,
+    const double* d_skip_if_nonfinite, int32_t* d_step, HyperParams hp)
 {
-    if (header->tag != tag) return;  // tables overwritten: touch nothing
-    if (d_skip_if_nonfinite && !__builtin_isfinite(*d_skip_if_nonfinite)) return;
+    if (ws.solo_tensor >= 0) {
+        // As in the fp32 step kernel: the first tile's addresses from the
+        // kernel arguments, then the scalar loads and the tile's loads
+        // together; the tag is compared before anything is stored.
+        Solo8Walk<kBf16> walk(ws);
+        const uint64_t seen = ws.header->tag;
+        const int32_t count = *d_step;
+        const float coef = *d_coef;
+        const double skip_value = *d_skip_if_nonfinite;
+        walk.load_first();
+        __builtin_amdgcn_sched_barrier(0);
+        if (seen != ws.tag) return;                  // tables overwritten: touch nothing
+        if (!__builtin_isfinite(skip_value)) return;  // a skipped step writes nothing
+        const int64_t t = static_cast<int64_t>(count) + 1;
+        walk.finish(step_scalars(t, hp, coef));
+        advance_step(ws.tickets, d_step, t);
+        return;
+    }
 
-    const int64_t t = static_cast<int64_t>(*d_step) + 1;
-    const StepScalars s = step_scalars(t, hp, d_coef ? *d_coef : 1.0f);
-    update8_chunks<kBf16>(tensors, quant, chunk_map, n_chunks, chunk_elems, s);
-    advance_step(tickets, d_step, t);
+    // Independent scalar loads, in flight together.
+    const uint64_t seen = ws.header->tag;
+    const int32_t count = *d_step;
+    const float coef = *d_coef;
+    const double skip_value = *d_skip_if_nonfinite;
+    const int64_t t = static_cast<int64_t>(count) + 1;
+    if (seen != ws.tag) return;  // tables overwritten: touch nothing
+    if (!__builtin_isfinite(skip_value)) return;
+    update8_chunks<kBf16>(ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems,
+                          step_scalars(t, hp, coef));
+    advance_step(ws.tickets, d_step, t);
 }
 
 // The update with the end of the norm folded in, as the fp32 state's clipped
@@ -474,22 +543,13 @@ __global__ __launch_bounds__(kBlock) void adamw8_clipped_kernel(
     __shared__ double lds[kWavesPerBlock];
 
     if (ws.solo_tensor >= 0) {
-        const SoloEntry& te = ws.solo;
-        const QuantEntry& qe = ws.solo_quant;
-        const int c0 = blockIdx.x;
-        const bool whole = c0 < ws.n_chunks;
-        const Chunk8 k = chunk8_span(&te, min(c0, ws.n_chunks - 1), ws.chunk_elems);
-        const bool vector = whole && k.vend > k.begin;
-        // A block without a vector body loads nothing (an empty range).
-        const Body8<kBf16> body(&te, &qe, k.begin,
-                                vector ? static_cast<int>((k.vend - k.begin) / 4) : 0);
+        Solo8Walk<kBf16> walk(ws);
         // Loads in issue order: the partials, then the tile, so the sum of
         // the partials can start while the tile is still in flight.
         __builtin_amdgcn_sched_barrier(0);
         const PartialSlots slots = load_partials<false>(ws.partials);
         __builtin_amdgcn_sched_barrier(0);
-        typename Body8<kBf16>::Tile a;
-        body.load(a, 0);
+        walk.load_first();
         __builtin_amdgcn_sched_barrier(0);
         const double total = block_sum(partial_share(slots, n_partials), lds);
         if (seen != ws.tag) {
@@ -498,18 +558,7 @@ __global__ __launch_bounds__(kBlock) void adamw8_clipped_kernel(
         }
         const float clip = clip_from_sumsq(total, max_norm, grad_scale);
         if (publish_clip(total, clip, t, skip_if_nonfinite, d_sumsq, d_coef, d_step)) return;
-        const StepScalars s = step_scalars(t, hp, clip);
-        int parity = 0;
-        if (vector) {
-            body.run(a, s, scale_lds()[0][0], scale_lds()[0][1]);
-            parity = 1;
-            if (k.end > k.vend) adamw8_elements<kBf16>(&te, &qe, k.vend, k.end, s);
-        } else if (whole) {
-            adamw8_chunk<kBf16>(&te, &qe, c0, ws.chunk_elems, s, parity);
-        }
-        for (int c = c0 + static_cast<int>(gridDim.x); c < ws.n_chunks; c += gridDim.x) {
-            adamw8_chunk<kBf16>(&te, &qe, c, ws.chunk_elems, s, parity);
-        }
+        walk.finish(step_scalars(t, hp, clip));
         return;
     }
 
@@ -564,13 +613,11 @@ hipError_t launch_adamw8_step(const WorkspaceView& ws, const QuantEntry* quant, 
                               int32_t* d_step, const HyperParams& hp, hipStream_t stream)
 {
     if (grad_bf16) {
-        adamw8_step_kernel<true><<<grid, kBlock, 0, stream>>>(
-            ws.header, ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag,
-            ws.tickets, d_coef, d_skip_if_nonfinite, d_step, hp);
+        adamw8_step_kernel<true><<<grid, kBlock, 0, stream>>>(ws, quant, d_coef,
+                                                              d_skip_if_nonfinite, d_step, hp);
     } else {
-        adamw8_step_kernel<false><<<grid, kBlock, 0, stream>>>(
-            ws.header, ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems, ws.tag,
-            ws.tickets, d_coef, d_skip_if_nonfinite, d_step, hp);
+        adamw8_step_kernel<false><<<grid, kBlock, 0, stream>>>(ws, quant, d_coef,
+                                                               d_skip_if_nonfinite, d_step, hp);
     }
     return hipGetLastError();
 }

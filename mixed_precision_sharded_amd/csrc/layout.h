@@ -7,6 +7,7 @@
 //   [.., + 4*max(K, 1))          uint32 chunk -> tensor index, K chunks
 //   [.. rounded to 128, + 128*(kTicketGroups + 1))  the update's step tickets,
 //                                one uint32 per 128-byte line
+//   [.., + 16)                   WorkspaceConstants
 //   [.. rounded to 256, + 8*kPartials)  fp64 per-block partial sums of the norm
 // Everything before the partials is written by one host-to-device copy when
 // the list changes (the tickets start at zero and every complete launch
@@ -85,6 +86,16 @@ struct alignas(64) WorkspaceHeader {
                             // for its update launch
 };
 static_assert(sizeof(WorkspaceHeader) == 64, "header is one 64-byte record");
+
+// Values the update kernels read where the caller passed no pointer: the
+// skip value 0 (never skip) and the clip coefficient 1.  With a pointer
+// always present, a kernel's first loads carry no branch and go out
+// together.
+struct alignas(16) WorkspaceConstants {
+    double zero;
+    float one;
+    uint32_t unused;
+};
 
 struct alignas(64) TensorEntry {
     float* master;
