@@ -9,13 +9,15 @@ in one launch) followed by adamw_multi_tensor_step instead.  Prints ONE JSON
 line: params updated per second (value), the step's algorithmic GB/s, and for
 the dominant kernel (the update) its roofline against MI355X's 8 TB/s HBM
 peak, timed live with events on the launch stream; plus the CPU oracle timed
-on a bounded sample on the host (single thread).
+on a bounded sample on the host (one thread, then all threads).
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--rotate R] [--state8]
 
---state8 times the same workload with 8-bit moments (adamw8_grad_norm_sq,
-then adamw8_multi_tensor_step): m and v are the workload's, encoded once
-before the timed region.
+Without --warmup the warm-up lasts at least 10 steps and 0.25 s: the GPU's
+clock needs some tens of milliseconds of work to settle (an 8-bit step on
+the 8B shard starts ~10 % slower than it runs after ~150 steps).  --state8
+times the same workload with 8-bit moments: m and v are the workload's,
+encoded once before the timed region.
 """
 import argparse
 import hashlib
@@ -46,7 +48,12 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed warm-up steps (default: at least 10 and at least "
+                        "--warmup-seconds of steps)")
+    p.add_argument("--warmup-seconds", type=float, default=0.25,
+                   help="with the default --warmup, warm up for at least this long: the "
+                        "GPU's clock takes some tens of milliseconds of work to settle")
     p.add_argument("--config", type=int, default=2,
                    help="workload 1..5 (default 2: Llama-3.1-8B FSDP2 shard at 128-way)")
     p.add_argument("--rotate", type=int, default=1,
@@ -187,8 +194,20 @@ def main():
         if ev is not None:
             ev[2].record()
 
-    for i in range(args.warmup):
-        one_step(sets[i % len(sets)][1])
+    # Warm-up: exactly --warmup steps if given, else at least 10 steps and at
+    # least --warmup-seconds of them.
+    warmup = 0
+    t_warm = time.perf_counter()
+    while True:
+        if args.warmup is not None:
+            if warmup >= args.warmup:
+                break
+        elif warmup >= 10 and warmup % 10 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_warm >= args.warmup_seconds:
+                break
+        one_step(sets[warmup % len(sets)][1])
+        warmup += 1
     torch.cuda.synchronize()
 
     # Timed region: K whole steps back to back.
@@ -222,7 +241,7 @@ def main():
     # With rotating buffer sets, also the warm figure: K steps on one set.
     warm = None
     if len(sets) > 1:
-        for _ in range(args.warmup):
+        for _ in range(10):
             one_step(sets[0][1])
         torch.cuda.synchronize()
         start.record()
@@ -319,7 +338,7 @@ def main():
         "unit": "params/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
