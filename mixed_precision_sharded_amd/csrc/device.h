@@ -45,6 +45,87 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 
 
 // ------------------------------------------------------ buffer resources ---
 
+// Table entries in scalar registers.  An entry read from the workspace with
+// vector loads is the same in every lane, but the compiler cannot prove it:
+// buffer resources built from it would then run every load and store in a
+// loop over the lanes' distinct descriptors (one pass, but a branch and an
+// exec-mask change around each access, and a full wait for memory where the
+// next tile's loads should stay in flight).  readfirstlane states the fact.
+__device__ __forceinline__ uint64_t uniform64(uint64_t x)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p)
+{
+    return reinterpret_cast<T*>(uniform64(reinterpret_cast<uintptr_t>(p)));
+}
+
+// A view of workspace tables for reading them with scalar loads: the tables
+// do not change while a kernel runs, so the constant address space is
+// correct for them, and its loads are counted apart from the vector memory
+// operations (reading the next chunk's entry then does not wait for the
+// stores of the chunk before).
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* constant_view(const T* p)
+{
+    return (const __attribute__((address_space(4))) T*)p;
+}
+
+// Entry i of a table, read field by field through the constant view.
+__device__ __forceinline__ TensorEntry read_entry(const TensorEntry* table, uint32_t i)
+{
+    const __attribute__((address_space(4))) TensorEntry* e = constant_view(table) + i;
+    TensorEntry r;
+    r.master = e->master;
+    r.exp_avg = e->exp_avg;
+    r.exp_avg_sq = e->exp_avg_sq;
+    r.grad = e->grad;
+    r.param_bf16 = e->param_bf16;
+    r.numel = e->numel;
+    r.first_chunk = e->first_chunk;
+    r.head = e->head;
+    return r;
+}
+
+__device__ __forceinline__ QuantEntry read_entry(const QuantEntry* table, uint32_t i)
+{
+    const __attribute__((address_space(4))) QuantEntry* e = constant_view(table) + i;
+    QuantEntry r;
+    r.m_codes = e->m_codes;
+    r.m_scales = e->m_scales;
+    r.v_codes = e->v_codes;
+    r.v_scales = e->v_scales;
+    return r;
+}
+
+__device__ __forceinline__ TensorEntry uniform_entry(const TensorEntry& e)
+{
+    TensorEntry u;
+    u.master = uniform_ptr(e.master);
+    u.exp_avg = uniform_ptr(e.exp_avg);
+    u.exp_avg_sq = uniform_ptr(e.exp_avg_sq);
+    u.grad = uniform_ptr(e.grad);
+    u.param_bf16 = uniform_ptr(e.param_bf16);
+    u.numel = static_cast<int64_t>(uniform64(static_cast<uint64_t>(e.numel)));
+    u.first_chunk = __builtin_amdgcn_readfirstlane(e.first_chunk);
+    u.head = __builtin_amdgcn_readfirstlane(e.head);
+    return u;
+}
+
+__device__ __forceinline__ QuantEntry uniform_entry(const QuantEntry& e)
+{
+    QuantEntry u;
+    u.m_codes = uniform_ptr(e.m_codes);
+    u.m_scales = uniform_ptr(e.m_scales);
+    u.v_codes = uniform_ptr(e.v_codes);
+    u.v_scales = uniform_ptr(e.v_scales);
+    return u;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
@@ -75,6 +156,26 @@ __device__ __forceinline__ void store_f32x4(f32x4 v, __amdgpu_buffer_rsrc_t r, u
 __device__ __forceinline__ void store_u32x2(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kStorePolicy);
+}
+
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kLoadPolicy));
+}
+
+__device__ __forceinline__ uint16_t load_u16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kLoadPolicy);
+}
+
+__device__ __forceinline__ void store_f32(float v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kStorePolicy);
+}
+
+__device__ __forceinline__ void store_u16(uint16_t v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kStorePolicy);
 }
 
 // ----------------------------------------------------------------- bf16 ---

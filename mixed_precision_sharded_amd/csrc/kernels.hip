@@ -76,7 +76,8 @@ __device__ __forceinline__ ChunkRun block_run(int n_chunks)
 // needs no chunk-map read.
 __device__ __forceinline__ uint32_t tensor_of_chunk(const WorkspaceView& ws, int c)
 {
-    return ws.solo_tensor >= 0 ? static_cast<uint32_t>(ws.solo_tensor) : ws.chunk_map[c];
+    return ws.solo_tensor >= 0 ? static_cast<uint32_t>(ws.solo_tensor)
+                               : constant_view(ws.chunk_map)[c];
 }
 
 // The tensor index of chunk c for a kernel's prologue: c is clamped into the
@@ -170,7 +171,8 @@ __device__ __forceinline__ double norm_of_run(const WorkspaceView& ws, uint32_t 
     for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
 
     for (int c = run_first; c < run_stop;) {
-        const TensorEntry te = tensors[c == run_first ? first_tensor : tensor_of_chunk(ws, c)];
+        const TensorEntry te =
+            read_entry(tensors, c == run_first ? first_tensor : tensor_of_chunk(ws, c));
         const int tensor_chunks = static_cast<int>((te.numel + chunk_elems - 1) / chunk_elems);
         const int c_lo = c;  // this stretch: chunks [c_lo, c_hi) of one tensor
         const int c_hi = min(run_stop, te.first_chunk + tensor_chunks);
@@ -309,16 +311,34 @@ __global__ __launch_bounds__(kWave) void clip_coef_kernel(const double* d_sumsq,
 // ---------------------------------------------------------------- update ---
 
 
+// Elements [base, base + count) of one tensor (0 <= count <= kBlock), one
+// per lane, through buffer resources like the vector body: lanes past count
+// read zeros and their stores are dropped.  Plain pointer accesses here
+// would be flat memory operations, which the compiler cannot order against
+// the body's buffer operations; it then waited for every load in flight
+// before each tile, the next tile's loads included.
 template <bool kBf16, class Entry>
-__device__ __forceinline__ void adamw_scalar_at(const Entry* te, int64_t i, const StepScalars& s)
+__device__ __forceinline__ void adamw_elements_at(const Entry* te, int64_t base, int64_t count,
+                                                  const StepScalars& s)
 {
-    const float grad = grad_at<kBf16>(te->grad, i);
-    float w = te->master[i], m = te->exp_avg[i], v = te->exp_avg_sq[i];
-    adamw_element(w, m, v, grad, s);
-    te->master[i] = w;
-    te->exp_avg[i] = m;
-    te->exp_avg_sq[i] = v;
-    if (te->param_bf16) te->param_bf16[i] = bf16_one(w);
+    if (count <= 0) return;  // uniform
+    const uint32_t n = static_cast<uint32_t>(count);
+    const __amdgpu_buffer_rsrc_t W = rsrc(te->master + base, n * 4u);
+    const __amdgpu_buffer_rsrc_t M = rsrc(te->exp_avg + base, n * 4u);
+    const __amdgpu_buffer_rsrc_t V = rsrc(te->exp_avg_sq + base, n * 4u);
+    const __amdgpu_buffer_rsrc_t G = rsrc(static_cast<const char*>(te->grad) + base * (kBf16 ? 2 : 4),
+                                          n * (kBf16 ? 2u : 4u));
+    const __amdgpu_buffer_rsrc_t P = rsrc(te->param_bf16 ? te->param_bf16 + base : nullptr,
+                                          te->param_bf16 ? n * 2u : 0u);
+    const uint32_t o = threadIdx.x;
+    float w = load_f32(W, o * 4u), m = load_f32(M, o * 4u), v = load_f32(V, o * 4u);
+    const float g = kBf16 ? __uint_as_float(static_cast<uint32_t>(load_u16(G, o * 2u)) << 16)
+                          : load_f32(G, o * 4u);
+    adamw_element(w, m, v, g, s);
+    store_f32(w, W, o * 4u);
+    store_f32(m, M, o * 4u);
+    store_f32(v, V, o * 4u);
+    store_u16(bf16_one(w), P, o * 2u);
 }
 
 // The aligned body of one chunk: `nquad` groups of four elements starting at
@@ -329,8 +349,11 @@ __device__ __forceinline__ void adamw_scalar_at(const Entry* te, int64_t i, cons
 // zeros and their stores are dropped, so the tail needs no branches.
 template <bool kBf16, int kUnroll>
 struct Body {
+    // The gradient stays in its loaded bits until the arithmetic: converting
+    // bf16 in load() would wait for the load right after issuing it.
     struct Tile {
-        f32x4 w[kUnroll], m[kUnroll], v[kUnroll], g[kUnroll];
+        f32x4 w[kUnroll], m[kUnroll], v[kUnroll];
+        u32x4 g[kUnroll];  // fp32: four values; bf16: g[0..1] hold four
     };
     __amdgpu_buffer_rsrc_t W, M, V, G, P;
     bool copy;
@@ -360,22 +383,26 @@ struct Body {
             t.v[u] = load_f32x4(V, q * 16u);
             if (kBf16) {
                 const u32x2 h = load_u32x2(G, q * 8u);
-                t.g[u] = f32x4{bf16_lo(h[0]), bf16_hi(h[0]), bf16_lo(h[1]), bf16_hi(h[1])};
+                t.g[u] = u32x4{h[0], h[1], 0u, 0u};
             } else {
-                t.g[u] = load_f32x4(G, q * 16u);
+                t.g[u] = __builtin_bit_cast(u32x4, load_f32x4(G, q * 16u));
             }
         }
     }
 
+    template <bool kCopy>
     __device__ __forceinline__ void update(Tile& t, int base, const StepScalars& s) const
     {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint32_t q = base + u * kBlock + threadIdx.x;
+            const f32x4 g = kBf16 ? f32x4{bf16_lo(t.g[u][0]), bf16_hi(t.g[u][0]),
+                                          bf16_lo(t.g[u][1]), bf16_hi(t.g[u][1])}
+                                  : __builtin_bit_cast(f32x4, t.g[u]);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 float wk = t.w[u][k], mk = t.m[u][k], vk = t.v[u][k];
-                adamw_element(wk, mk, vk, t.g[u][k], s);
+                adamw_element(wk, mk, vk, g[k], s);
                 t.w[u][k] = wk;
                 t.m[u][k] = mk;
                 t.v[u][k] = vk;
@@ -383,7 +410,7 @@ struct Body {
             store_f32x4(t.w[u], W, q * 16u);
             store_f32x4(t.m[u], M, q * 16u);
             store_f32x4(t.v[u], V, q * 16u);
-            if (copy) {
+            if (kCopy) {
                 u32x2 packed;
                 packed[0] = bf16_pack2(t.w[u][0], t.w[u][1]);
                 packed[1] = bf16_pack2(t.w[u][2], t.w[u][3]);
@@ -393,18 +420,31 @@ struct Body {
     }
 
     // Streams the body; `a` already holds the loads of its first tile.
+    // The copy is decided once per body: a branch inside the loop would make
+    // the compiler wait for every load in flight, the next tile's included,
+    // before each tile's arithmetic.
     __device__ __forceinline__ void run(Tile& a, const StepScalars& s) const
+    {
+        if (copy) {
+            run_tiles<true>(a, s);
+        } else {
+            run_tiles<false>(a, s);
+        }
+    }
+
+    template <bool kCopy>
+    __device__ __forceinline__ void run_tiles(Tile& a, const StepScalars& s) const
     {
         constexpr int kStride = kBlock * kUnroll;
         Tile b;
         for (int base = 0; base < nquad; base += 2 * kStride) {
             load(b, base + kStride);
             __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
-            update(a, base, s);
+            update<kCopy>(a, base, s);
             if (base + kStride >= nquad) break;  // uniform: the other tile is empty
             load(a, base + 2 * kStride);
             __builtin_amdgcn_sched_barrier(0);
-            update(b, base + kStride, s);
+            update<kCopy>(b, base + kStride, s);
         }
     }
 };
@@ -434,20 +474,21 @@ template <bool kBf16, int kUnroll, class Entry>
 __device__ __forceinline__ void adamw_chunk(const Entry* te, int c, int64_t chunk_elems,
                                             const StepScalars& s)
 {
-    const int tid = threadIdx.x;
     if (te->head < 0) {  // streams share no alignment: element-wise
         const int64_t begin = static_cast<int64_t>(c - te->first_chunk) * chunk_elems;
         const int64_t end = min(begin + chunk_elems, te->numel);
-        for (int64_t i = begin + tid; i < end; i += kBlock) adamw_scalar_at<kBf16>(te, i, s);
+        for (int64_t b = begin; b < end; b += kBlock) {
+            adamw_elements_at<kBf16>(te, b, min(static_cast<int64_t>(kBlock), end - b), s);
+        }
         return;
     }
     const ChunkSpan k = chunk_span(te, c, chunk_elems);
-    if (tid < k.qbegin - k.begin) adamw_scalar_at<kBf16>(te, k.begin + tid, s);
+    adamw_elements_at<kBf16>(te, k.begin, k.qbegin - k.begin, s);
     const Body<kBf16, kUnroll> body(te, k.qbegin, k.nquad);
     typename Body<kBf16, kUnroll>::Tile a;
     body.load(a, 0);
     body.run(a, s);
-    if (tid < k.end - k.tail) adamw_scalar_at<kBf16>(te, k.tail + tid, s);
+    adamw_elements_at<kBf16>(te, k.tail, k.end - k.tail, s);
 }
 
 // Update the chunks b, b + G, b + 2G, ... of this block (G = gridDim.x): at
@@ -461,9 +502,11 @@ __device__ __forceinline__ void update_chunks(const WorkspaceView& ws, TensorEnt
 {
     const int n_chunks = ws.n_chunks;
     for (int c = blockIdx.x; c < n_chunks; c += gridDim.x) {
-        const TensorEntry entry = next;
+        const TensorEntry entry = uniform_entry(next);
         const int c_next = c + static_cast<int>(gridDim.x);
-        if (ws.solo_tensor < 0 && c_next < n_chunks) next = ws.tensors[ws.chunk_map[c_next]];
+        if (ws.solo_tensor < 0 && c_next < n_chunks) {
+            next = read_entry(ws.tensors, constant_view(ws.chunk_map)[c_next]);
+        }
         adamw_chunk<kBf16, kUnroll>(&entry, c, ws.chunk_elems, s);
     }
 }
@@ -501,11 +544,10 @@ struct SoloWalk {
 
     __device__ __forceinline__ void finish(const StepScalars& s)
     {
-        const int tid = threadIdx.x;
         if (vector) {
-            if (tid < k.qbegin - k.begin) adamw_scalar_at<kBf16>(te, k.begin + tid, s);
+            adamw_elements_at<kBf16>(te, k.begin, k.qbegin - k.begin, s);
             body.run(a, s);
-            if (tid < k.end - k.tail) adamw_scalar_at<kBf16>(te, k.tail + tid, s);
+            adamw_elements_at<kBf16>(te, k.tail, k.end - k.tail, s);
         } else if (whole) {
             adamw_chunk<kBf16, kUnroll>(te, static_cast<int>(blockIdx.x), chunk_elems, s);
         }
@@ -546,7 +588,7 @@ __global__ __launch_bounds__(kBlock) void adamw_step_kernel(
     const float coef = *d_coef;
     const double skip_value = *d_skip_if_nonfinite;
     const int64_t t = static_cast<int64_t>(count) + 1;
-    const TensorEntry first = ws.tensors[prologue_tensor(ws, blockIdx.x)];
+    const TensorEntry first = read_entry(ws.tensors, prologue_tensor(ws, blockIdx.x));
     if (seen != ws.tag) return;  // tables overwritten: touch nothing
     // A skipped step writes nothing and leaves the counter.  The value is
     // uniform, so every block makes the same choice.
@@ -608,7 +650,7 @@ __global__ __launch_bounds__(kBlock) void adamw_clipped_kernel(
         return;
     }
 
-    const TensorEntry first = ws.tensors[prologue_tensor(ws, blockIdx.x)];
+    const TensorEntry first = read_entry(ws.tensors, prologue_tensor(ws, blockIdx.x));
     if (seen != ws.tag) {
         report_stale_clip(d_sumsq, d_coef);
         return;
@@ -703,7 +745,8 @@ __global__ __launch_bounds__(kBlock) void adamw_fused_kernel(
                                            __HIP_MEMORY_SCOPE_AGENT);
     if (skip_if_nonfinite && !__builtin_isfinite(total)) return;
     const StepScalars s = step_scalars(t, hp, clip_from_sumsq(total, max_norm, grad_scale));
-    update_chunks<kBf16, kStepUnroll>(ws, ws.tensors[prologue_tensor(ws, blockIdx.x)], s);
+    update_chunks<kBf16, kStepUnroll>(
+        ws, read_entry(ws.tensors, prologue_tensor(ws, blockIdx.x)), s);
 }
 
 }  // namespace

@@ -207,34 +207,47 @@ __device__ __forceinline__ void store8_u32(uint32_t v, __amdgpu_buffer_rsrc_t r,
 // ---------------------------------------------------------------- update ---
 
 // Elements [begin, end) of one tensor, one element per lane; `begin` is a
-// multiple of 32, so each half wavefront holds one run.
+// multiple of 32, so each half wavefront holds one run.  Every access goes
+// through a buffer resource, like the vector body's (lanes past the end read
+// zeros and their stores are dropped): flat accesses here would keep the
+// compiler from counting the body's loads in issue order.
 template <bool kBf16, class Entry>
 __device__ __forceinline__ void adamw8_elements(const Entry* te, const QuantEntry* qe,
                                                 int64_t begin, int64_t end, const StepScalars& s)
 {
     for (int64_t base = begin; base < end; base += kBlock) {
-        const int64_t i = base + threadIdx.x;
-        const bool valid = i < end;
-        float w = 0.0f, m = 0.0f, v = 0.0f, g = 0.0f;
-        if (valid) {
-            const int64_t run = i / kQuantBlock;
-            w = te->master[i];
-            g = grad_at<kBf16>(te->grad, i);
-            m = decode1<true>(qe->m_codes[i], scale_value(qe->m_scales[run]));
-            v = decode1<false>(qe->v_codes[i], scale_value(qe->v_scales[run]));
-        }
+        const uint32_t n = static_cast<uint32_t>(min(static_cast<int64_t>(kBlock), end - base));
+        const int64_t r0 = base / kQuantBlock;
+        const uint32_t runs = (n + kQuantBlock - 1) / kQuantBlock;
+        const __amdgpu_buffer_rsrc_t W = rsrc(te->master + base, n * 4u);
+        const __amdgpu_buffer_rsrc_t G = rsrc(static_cast<const char*>(te->grad) + base * (kBf16 ? 2 : 4),
+                                              n * (kBf16 ? 2u : 4u));
+        const __amdgpu_buffer_rsrc_t P = rsrc(te->param_bf16 ? te->param_bf16 + base : nullptr,
+                                              te->param_bf16 ? n * 2u : 0u);
+        const __amdgpu_buffer_rsrc_t MC = rsrc(qe->m_codes + base, n);
+        const __amdgpu_buffer_rsrc_t VC = rsrc(qe->v_codes + base, n);
+        const __amdgpu_buffer_rsrc_t MS = rsrc(qe->m_scales + r0, runs);
+        const __amdgpu_buffer_rsrc_t VS = rsrc(qe->v_scales + r0, runs);
+        const uint32_t o = threadIdx.x;
+        const uint32_t run = o / kQuantBlock;
+        const bool valid = o < n;
+        float w = load_f32(W, o * 4u);
+        const float g = kBf16 ? __uint_as_float(static_cast<uint32_t>(load_u16(G, o * 2u)) << 16)
+                              : load_f32(G, o * 4u);
+        float m = decode1<true>(load_byte<kQ8CodePolicy>(MC, o),
+                                scale_value(load_byte<kQ8ScalePolicy>(MS, run)));
+        float v = decode1<false>(load_byte<kQ8CodePolicy>(VC, o),
+                                 scale_value(load_byte<kQ8ScalePolicy>(VS, run)));
         adamw_element(w, m, v, g, s);
         const uint32_t mb = scale_byte<kE4M3TopExp>(half_wave_max(valid ? abs_bits(m) : 0u));
         const uint32_t vb = scale_byte<kE5M2TopExp>(half_wave_max(valid ? abs_bits(v) : 0u));
-        if (valid) {
-            te->master[i] = w;
-            qe->m_codes[i] = static_cast<uint8_t>(encode1<true>(m, mb));
-            qe->v_codes[i] = static_cast<uint8_t>(encode1<false>(v, vb));
-            if (te->param_bf16) te->param_bf16[i] = bf16_one(w);
-            if (i % kQuantBlock == 0) {
-                qe->m_scales[i / kQuantBlock] = static_cast<uint8_t>(mb);
-                qe->v_scales[i / kQuantBlock] = static_cast<uint8_t>(vb);
-            }
+        store_f32(w, W, o * 4u);
+        store_byte(encode1<true>(m, mb), MC, o);
+        store_byte(encode1<false>(v, vb), VC, o);
+        store_u16(bf16_one(w), P, o * 2u);
+        if (o % kQuantBlock == 0) {
+            store_byte(mb, MS, run);
+            store_byte(vb, VS, run);
         }
     }
 }
@@ -307,6 +320,7 @@ struct Body8 {
     }
 
     // A run's quad leader leaves its two scale bytes in lds_m / lds_v.
+    template <bool kCopy>
     __device__ __forceinline__ void update(Tile& t, int base, const StepScalars& s, uint8_t* lds_m,
                                            uint8_t* lds_v) const
     {
@@ -339,7 +353,7 @@ struct Body8 {
                            __float_as_uint(w[3])}, W, q * 16u);
         store8_u32(encode4<true>(m, mb), MQ, q * 4u);
         store8_u32(encode4<false>(v, vb), VQ, q * 4u);
-        if (copy) store8_u32x2(u32x2{bf16_pack2(w[0], w[1]), bf16_pack2(w[2], w[3])}, P, q * 8u);
+        if (kCopy) store8_u32x2(u32x2{bf16_pack2(w[0], w[1]), bf16_pack2(w[2], w[3])}, P, q * 8u);
         if ((tid & 7) == 0 && q < ng) {
             lds_m[q / 8u] = static_cast<uint8_t>(mb);
             lds_v[q / 8u] = static_cast<uint8_t>(vb);
@@ -348,25 +362,37 @@ struct Body8 {
 
     // Streams the body (`a` already holds its first tile's loads), then
     // stores the scale bytes from lds_m / lds_v (kMaxRunsPerBody bytes
-    // each) with consecutive threads.
+    // each) with consecutive threads.  The copy is decided once per body,
+    // not per tile, for the compiler's waits (as in the fp32 body).
     __device__ __forceinline__ void run(Tile& a, const StepScalars& s, uint8_t* lds_m,
                                         uint8_t* lds_v) const
+    {
+        if (copy) {
+            run_tiles<true>(a, s, lds_m, lds_v);
+        } else {
+            run_tiles<false>(a, s, lds_m, lds_v);
+        }
+        __syncthreads();
+        for (uint32_t r = threadIdx.x; r < ng / 8u; r += kBlock) {
+            store_byte(lds_m[r], MS, r);
+            store_byte(lds_v[r], VS, r);
+        }
+    }
+
+    template <bool kCopy>
+    __device__ __forceinline__ void run_tiles(Tile& a, const StepScalars& s, uint8_t* lds_m,
+                                              uint8_t* lds_v) const
     {
         const int ngroups = static_cast<int>(ng);
         Tile b;
         for (int base = 0; base < ngroups; base += 2 * kBlock) {
             load(b, base + kBlock);
             __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
-            update(a, base, s, lds_m, lds_v);
+            update<kCopy>(a, base, s, lds_m, lds_v);
             if (base + kBlock >= ngroups) break;  // uniform: the other tile is empty
             load(a, base + 2 * kBlock);
             __builtin_amdgcn_sched_barrier(0);
-            update(b, base + kBlock, s, lds_m, lds_v);
-        }
-        __syncthreads();
-        for (uint32_t r = threadIdx.x; r < ng / 8u; r += kBlock) {
-            store_byte(lds_m[r], MS, r);
-            store_byte(lds_v[r], VS, r);
+            update<kCopy>(b, base + kBlock, s, lds_m, lds_v);
         }
     }
 };
@@ -421,17 +447,17 @@ __device__ __forceinline__ void update8_chunks(const TensorEntry* __restrict__ t
     TensorEntry next{};
     QuantEntry next_q{};
     if (static_cast<int>(blockIdx.x) < n_chunks) {
-        const uint32_t k = chunk_map[blockIdx.x];
-        next = tensors[k];
-        next_q = quant[k];
+        const uint32_t k = constant_view(chunk_map)[blockIdx.x];
+        next = read_entry(tensors, k);
+        next_q = read_entry(quant, k);
     }
     for (int c = blockIdx.x; c < n_chunks; c += gridDim.x) {
-        const TensorEntry te = next;
-        const QuantEntry qe = next_q;
+        const TensorEntry te = uniform_entry(next);
+        const QuantEntry qe = uniform_entry(next_q);
         if (c + static_cast<int>(gridDim.x) < n_chunks) {
-            const uint32_t k = chunk_map[c + gridDim.x];
-            next = tensors[k];
-            next_q = quant[k];
+            const uint32_t k = constant_view(chunk_map)[c + gridDim.x];
+            next = read_entry(tensors, k);
+            next_q = read_entry(quant, k);
         }
         adamw8_chunk<kBf16>(&te, &qe, c, chunk_elems, s, parity);
     }
