@@ -20,14 +20,15 @@ namespace mps {
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X).
 // Both kernels walk the chunks with a persistent grid (block b takes chunks
-// b, b + G, ...): few, long-lived waves streaming neighbouring addresses
-// beat one block per chunk on MI355X's HBM3E (measured: 2 update blocks and
-// 1 norm block per CU).
+// b, b + G, ...): long-lived waves streaming neighbouring addresses beat one
+// block per chunk on MI355X's HBM3E.  Measured: 1 norm block per CU; for the
+// fp32-state update up to 5 blocks per CU (with the grid a whole number of
+// blocks per CU: 2.5 per CU was 5 % slower), for the 8-bit update 3.
 #ifndef MPS_NORM_MAX_BLOCKS
 #define MPS_NORM_MAX_BLOCKS 256    // norm grid cap (= number of fp64 partials)
 #endif
 #ifndef MPS_STEP_MAX_BLOCKS
-#define MPS_STEP_MAX_BLOCKS 512    // update grid cap
+#define MPS_STEP_MAX_BLOCKS 1280   // update grid cap
 #endif
 #ifndef MPS_CHUNK_MIN
 #define MPS_CHUNK_MIN 2048
