@@ -661,12 +661,16 @@ int adamw_clipped_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_
     }
     const bool bf16 = grad_dtype == MPS_DTYPE_BF16;
     const mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
-    const int grid = grid_for(plan.n_chunks, mps::kStepMaxBlocks);
+    // Very long lists take the wide tiles (on fewer blocks).
+    const bool wide = plan.n_chunks >= mps::kStepWideMinChunks;
+    const int grid =
+        grid_for(plan.n_chunks, wide ? mps::kStepWideMaxBlocks : mps::kStepMaxBlocks);
     return run_clipped(plan, bf16, d_step, d_workspace, stream_, mid_event,
                        [&](const mps::WorkspaceView& ws, int norm_grid, hipStream_t st) {
-                           return mps::launch_clipped_step(ws, bf16, grid, norm_grid, max_norm,
-                                                           grad_scale, skip_if_nonfinite ? 1 : 0,
-                                                           d_sumsq, d_coef, d_step, hp, st);
+                           return mps::launch_clipped_step(ws, bf16, wide, grid, norm_grid,
+                                                           max_norm, grad_scale,
+                                                           skip_if_nonfinite ? 1 : 0, d_sumsq,
+                                                           d_coef, d_step, hp, st);
                        });
 }
 

@@ -59,10 +59,12 @@ hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, int grid,
 
 // The update that finishes the norm from the `n_partials` partials a
 // launch_grad_norm_partials of grid n_partials left in the workspace.
-hipError_t launch_clipped_step(const WorkspaceView& ws, bool grad_bf16, int grid, int n_partials,
-                               double max_norm, double grad_scale, int skip_if_nonfinite,
-                               double* d_sumsq, float* d_coef, int32_t* d_step,
-                               const HyperParams& hp, hipStream_t stream);
+// `wide`: tiles of MPS_STEP_WIDE_UNROLL groups of four per thread (for very
+// long lists, with a grid of at most kStepWideMaxBlocks).
+hipError_t launch_clipped_step(const WorkspaceView& ws, bool grad_bf16, bool wide, int grid,
+                               int n_partials, double max_norm, double grad_scale,
+                               int skip_if_nonfinite, double* d_sumsq, float* d_coef,
+                               int32_t* d_step, const HyperParams& hp, hipStream_t stream);
 
 // Largest grid of the single-launch step whose blocks can all be resident.
 hipError_t fused_grid_limit(bool grad_bf16, int* max_blocks);

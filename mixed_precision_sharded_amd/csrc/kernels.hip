@@ -809,17 +809,36 @@ hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, int grid,
     return hipGetLastError();
 }
 
-hipError_t launch_clipped_step(const WorkspaceView& ws, bool grad_bf16, int grid, int n_partials,
-                               double max_norm, double grad_scale, int skip_if_nonfinite,
-                               double* d_sumsq, float* d_coef, int32_t* d_step,
-                               const HyperParams& hp, hipStream_t stream)
+namespace {
+
+template <int kUnroll>
+void clipped_launch(const WorkspaceView& ws, bool grad_bf16, int grid, int n_partials,
+                    double max_norm, double grad_scale, int skip_if_nonfinite, double* d_sumsq,
+                    float* d_coef, int32_t* d_step, const HyperParams& hp, hipStream_t stream)
 {
     if (grad_bf16) {
-        adamw_clipped_kernel<true, MPS_STEP_UNROLL><<<grid, kBlock, 0, stream>>>(
+        adamw_clipped_kernel<true, kUnroll><<<grid, kBlock, 0, stream>>>(
             ws, n_partials, max_norm, grad_scale, skip_if_nonfinite, d_sumsq, d_coef, d_step, hp);
     } else {
-        adamw_clipped_kernel<false, MPS_STEP_UNROLL><<<grid, kBlock, 0, stream>>>(
+        adamw_clipped_kernel<false, kUnroll><<<grid, kBlock, 0, stream>>>(
             ws, n_partials, max_norm, grad_scale, skip_if_nonfinite, d_sumsq, d_coef, d_step, hp);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_clipped_step(const WorkspaceView& ws, bool grad_bf16, bool wide, int grid,
+                               int n_partials, double max_norm, double grad_scale,
+                               int skip_if_nonfinite, double* d_sumsq, float* d_coef,
+                               int32_t* d_step, const HyperParams& hp, hipStream_t stream)
+{
+    if (wide) {
+        clipped_launch<MPS_STEP_WIDE_UNROLL>(ws, grad_bf16, grid, n_partials, max_norm,
+                                             grad_scale, skip_if_nonfinite, d_sumsq, d_coef,
+                                             d_step, hp, stream);
+    } else {
+        clipped_launch<MPS_STEP_UNROLL>(ws, grad_bf16, grid, n_partials, max_norm, grad_scale,
+                                        skip_if_nonfinite, d_sumsq, d_coef, d_step, hp, stream);
     }
     return hipGetLastError();
 }

@@ -22,7 +22,7 @@ hipError_t launch_grad_norm_partials(const WorkspaceView&, bool, int, int, const
 hipError_t launch_clip_coef(const double*, double, double, float*, hipStream_t) { reached("clip"); }
 hipError_t launch_adamw_step(const WorkspaceView&, bool, int, const float*, const double*,
                              int32_t*, const HyperParams&, hipStream_t) { reached("adamw_step"); }
-hipError_t launch_clipped_step(const WorkspaceView&, bool, int, int, double, double, int, double*,
+hipError_t launch_clipped_step(const WorkspaceView&, bool, bool, int, int, double, double, int, double*,
                                float*, int32_t*, const HyperParams&, hipStream_t) { reached("clipped"); }
 hipError_t fused_grid_limit(bool, int*) { reached("fused_grid_limit"); }
 hipError_t launch_fused_step(const WorkspaceView&, bool, int, int, double, double, int, double*,
