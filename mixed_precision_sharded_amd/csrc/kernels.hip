@@ -24,11 +24,18 @@
 //                     optional bf16 copy.
 //   adamw_fused_kernel the whole step in one cooperative launch.
 //
-// Memory access: each chunk's aligned body is addressed through buffer
-// resources (base and size in scalar registers, 32-bit per-lane offsets).
-// Lanes past the end of the body read zeros and their stores are dropped by
-// the hardware range check, so the loops carry no per-load branches.  The
-// streams are touched once, so loads and stores use the nontemporal policy.
+// Memory access: every access of the updates to the tensors goes through a
+// buffer resource (base and size in scalar registers, 32-bit per-lane
+// offsets): the vector bodies, and the per-element heads, tails and
+// unaligned tensors, one element per lane.  Lanes past the end read zeros
+// and their stores are dropped by the hardware range check, so the loops
+// carry no per-load branches.  The workspace tables are read with scalar
+// loads (a constant-address-space view).  Both matter to the compiler's
+// waits: with only buffer operations in flight it counts them in issue
+// order and keeps the next tile's loads in flight while a tile is computed;
+// one flat access, a descriptor it cannot prove uniform or a branch inside
+// the tile loop made it wait for everything.  The streams are touched once,
+// so their loads and stores use the nontemporal policy.
 //
 // Build with -ffp-contract=off: every fp32 operation below must round once,
 // in source order; division and sqrt are the correctly rounded defaults.
