@@ -165,3 +165,47 @@ def test_clipped_is_bitwise_the_three_call_step(sizes, grad_bf16):
         for x, y in zip(a[k], b[k]):
             if x is not None:
                 assert torch.equal(x.view(torch.int16), y.view(torch.int16)), k
+
+
+def big_cols(sizes, seed):
+    """fp32 state and bf16 gradients drawn on the GPU (lists of a billion
+    elements and more; only GPU results are compared with each other)."""
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    cols = {"master": [], "exp_avg": [], "exp_avg_sq": [], "grad": [], "param_bf16": []}
+    for n in sizes:
+        cols["master"].append(torch.randn(n, device="cuda", generator=gen).mul_(0.02))
+        cols["exp_avg"].append(torch.randn(n, device="cuda", generator=gen).mul_(1e-4))
+        cols["exp_avg_sq"].append(torch.randn(n, device="cuda", generator=gen).abs_().mul_(1e-8))
+        cols["grad"].append(torch.randn(n, device="cuda", generator=gen).mul_(1e-3)
+                            .to(torch.bfloat16))
+        cols["param_bf16"].append(torch.zeros(n, dtype=torch.bfloat16, device="cuda"))
+    return cols
+
+
+def test_wide_tiles_are_bitwise_the_three_call_step():
+    """81,924 chunks of 16,384 elements (1.34e9 parameters, ragged ends):
+    the clipped step takes its wide tiles (two groups of four elements per
+    thread, fewer blocks), the three-call update its one-group tiles.  Every
+    element of the state must come out the same, on two steps in a row."""
+    sizes = [81920 * 16384 - 5000, 7, 40000]
+    free, _ = torch.cuda.mem_get_info()
+    need = 2 * sum(sizes) * 16 + (8 << 30)
+    if free < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB free, {free / 2**30:.0f} GiB available")
+    say("generating two copies of a 1.34e9-parameter list")
+    a = big_cols(sizes, seed=91)
+    b = {k: [t.clone() for t in v] for k, v in a.items()}
+    sa = Step(a, completed_steps=41)
+    sb = Step(b, completed_steps=41)
+    for i in range(2):
+        say(f"step {i + 1}")
+        sa.clipped(1.0, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+        sb.norm_clip(1.0).update(HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+        Sa, ca, ta = sa.results()
+        Sb, cb, tb = sb.results()
+        assert np.float64(Sa).tobytes() == np.float64(Sb).tobytes()
+        assert np.float32(ca).tobytes() == np.float32(cb).tobytes() and ta == tb == 42 + i
+    for k in ("master", "exp_avg", "exp_avg_sq", "param_bf16"):
+        for x, y in zip(a[k], b[k]):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16)), k
+    del sa, sb, a, b

@@ -21,8 +21,10 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 # 2048 elements per chunk for lists this size; the fp32 update's grid is at
-# most 512 blocks, the 8-bit update's 768.
-SIZES = [1, 5, 2047, 2048, 2049, 3 * 2048 + 17, 512 * 2048 - 3, 512 * 2048 + 5, 768 * 2048 + 33]
+# most 1280 blocks (one chunk each up to 1280 chunks, then two or more), the
+# 8-bit update's 768, the norm's 256.
+SIZES = [1, 5, 2047, 2048, 2049, 3 * 2048 + 17, 256 * 2048 + 1, 768 * 2048 + 33,
+         1280 * 2048 - 3, 1280 * 2048 + 5, 2560 * 2048 + 2049]
 
 
 @pytest.fixture(autouse=True)
