@@ -16,7 +16,7 @@
 #define MPS_STEP_UNROLL 1   // groups of four elements per thread per tile
 #endif
 #ifndef MPS_NORM_UNROLL
-#define MPS_NORM_UNROLL 8   // 16-byte vectors per thread per iteration
+#define MPS_NORM_UNROLL 4   // 16-byte vectors per thread per tile (two tiles in flight)
 #endif
 // Buffer cache policies (the aux operand of buffer loads and stores):
 // 0 = default, 2 = nontemporal.
