@@ -104,10 +104,11 @@ typedef struct mps_tensor {
  * the call's stream) only when the list differs from the one it last
  * uploaded into that workspace, and when a call passes the same tensor array
  * (byte for byte) as the call that last planned the workspace, it reuses
- * that plan without validating and chunking the list again.  Before freeing a workspace, or handing its
- * memory to another user, call adamw_workspace_release on it.  A workspace
- * whose tables were overwritten behind the library's back is detected by the
- * kernels, which then leave every buffer untouched (grad_norm_sq writes NaN).
+ * that plan without validating and chunking the list again.  Before freeing
+ * a workspace, or handing its memory to another user, call
+ * adamw_workspace_release on it.  A workspace whose tables were overwritten
+ * behind the library's back is detected by the kernels, which then leave
+ * every buffer untouched (grad_norm_sq writes NaN).
  */
 size_t adamw_workspace_bytes(const mps_tensor* tensors, int n_tensors);
 
