@@ -104,16 +104,22 @@ typedef struct mps_tensor {
  * the call's stream) only when the list differs from the one it last
  * uploaded into that workspace, and when a call passes the same tensor array
  * (byte for byte) as the call that last planned the workspace, it reuses
- * that plan without validating and chunking the list again.  Before freeing
- * a workspace, or handing its memory to another user, call
- * adamw_workspace_release on it.  A workspace whose tables were overwritten
- * behind the library's back is detected by the kernels, which then leave
- * every buffer untouched (grad_norm_sq writes NaN).
+ * that plan without validating and chunking the list again.  The upload
+ * goes through pinned host buffers that the library allocates (with
+ * hipHostMalloc) and keeps per workspace, each reused only once the device
+ * has finished its copy, so that a list change never waits for the device
+ * (a copy from pageable memory would).  Before freeing a workspace, or
+ * handing its memory to another user, call adamw_workspace_release on it.
+ * A workspace whose header was overwritten behind the library's back is
+ * detected by the kernels (a tag in the header), which then leave every
+ * buffer untouched (grad_norm_sq writes NaN); a tensor index read from the
+ * chunk map is always clamped into the tensor table.
  */
 size_t adamw_workspace_bytes(const mps_tensor* tensors, int n_tensors);
 
-/* Forget what the library uploaded into `d_workspace`.  Waits for the last
- * table upload into it, if any, to finish.  Always returns 0. */
+/* Forget what the library uploaded into `d_workspace` and free its pinned
+ * staging buffers.  The one call that may wait: for the table copies into
+ * the workspace that are still running.  Always returns 0. */
 int adamw_workspace_release(void* d_workspace);
 
 /*
@@ -279,6 +285,29 @@ int adamw_fused_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dt
                      double* d_sumsq, float* d_coef, int32_t* d_step, double lr,
                      double beta1, double beta2, double eps, double weight_decay,
                      void* d_workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * adamw_fused_status — the single-launch step's error flag, on the device:
+ * enqueues on `stream` a copy of the workspace's flag into *d_error (0: every
+ * barrier wait since the last call completed; 1: a wait ran out) and clears
+ * the flag.  The barrier of adamw_fused_step waits at most about a second per
+ * block (never reached when the cooperative launch made every block
+ * resident).  A block that runs out gives the launch up before the last block
+ * publishes: then no element is written, *d_step is left as it is, and
+ * *d_sumsq and *d_coef (if given) read NaN, so a failed step cannot pass for
+ * a good one; the flag says which it was.  (Should a block run out after the
+ * last block published, only that block's chunks are left unwritten; the
+ * flag is set as well.)  The environment variable MPS_FUSED_SPIN_LIMIT, if
+ * set to a positive number, replaces the wait's bound in rounds of about
+ * 0.1 us: a test hook that makes the give-up path run while every block
+ * still ends normally.
+ *
+ *   d_workspace, workspace_bytes : the workspace of the adamw_fused_step
+ *                      calls (256-byte aligned, at least 64 bytes).
+ *   d_error          : device uint32, written.
+ */
+int adamw_fused_status(void* d_workspace, size_t workspace_bytes, uint32_t* d_error,
+                       void* stream);
 
 /* ---------------------------------------------------- 8-bit moment state ---
  *

@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.adamw_clipped_step.argtypes = whole_step + [P]
         L.adamw_fused_step.restype = ctypes.c_int
         L.adamw_fused_step.argtypes = whole_step
+        L.adamw_fused_status.restype = ctypes.c_int
+        L.adamw_fused_status.argtypes = [P, ctypes.c_size_t, P, P]
         T8 = ctypes.POINTER(MpsTensor8)
         L.adamw8_workspace_bytes.restype = ctypes.c_size_t
         L.adamw8_workspace_bytes.argtypes = [T8, ctypes.c_int]
@@ -364,6 +366,18 @@ def adamw_fused_step(tl: TensorList, step: torch.Tensor, lr: float, beta1: float
     """Norm, clip and update in one launch (see adamw_fused_step in the header)."""
     _whole_step("adamw_fused_step", tl, step, lr, beta1, beta2, eps, weight_decay, max_norm,
                 grad_scale, skip_if_nonfinite, sumsq_out, coef_out, stream)
+
+
+def adamw_fused_status(tl: TensorList, out: torch.Tensor,
+                       stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """out[0] (int32 or uint32-sized tensor on the device) = the single-launch
+    step's error flag of the list's workspace (1: a barrier wait ran out since
+    the last query), which is then cleared."""
+    if out.dtype != torch.int32 or out.device != tl.device or out.numel() < 1:
+        raise ValueError("out: int32 tensor on the list's device")
+    _check(lib().adamw_fused_status(tl.workspace_ptr, tl.workspace_bytes, out.data_ptr(),
+                                    _stream_handle(stream)), "adamw_fused_status")
+    return out
 
 
 # ------------------------------------------------------ 8-bit moment state ---

@@ -43,19 +43,6 @@ def build(out: str = LIB, extra=()) -> str:
     return out
 
 
-CEILING_SRC = os.path.join(CSRC, "stream_ceiling.hip")
-CEILING_BIN = os.path.join(HERE, "stream_ceiling")
-
-
-def build_ceiling(out: str = CEILING_BIN) -> str:
-    """Compile the streaming-ceiling probe (an executable, not part of the library)."""
-    tmp = out + ".tmp%d" % os.getpid()
-    flags = [f for f in FLAGS if f not in ("-shared", "-fPIC")]
-    subprocess.run([HIPCC, *flags, "-o", tmp, CEILING_SRC], check=True)
-    os.replace(tmp, out)
-    return out
-
-
 def isa(out_dir: str) -> list:
     """Write the gfx950 assembly of kernels.hip under out_dir (for reading)."""
     os.makedirs(out_dir, exist_ok=True)
@@ -67,8 +54,7 @@ def isa(out_dir: str) -> list:
 
 
 if __name__ == "__main__":
-    if len(sys.argv) > 1 and sys.argv[1] == "--isa":
-        print(isa(sys.argv[2] if len(sys.argv) > 2 else os.path.join(HERE, "..", "_work", "isa")))
+    if len(sys.argv) > 2 and sys.argv[1] == "--isa":
+        print(isa(sys.argv[2]))
     else:
         print(build())
-        print(build_ceiling())

@@ -7,7 +7,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <deque>
 #include <mutex>
 #include <string>
 #include <unordered_map>
@@ -54,6 +56,7 @@ struct Plan {
     size_t constants_off = 0;
     size_t partials_off = 0;
     size_t total_bytes = 0;
+    int n_tensors = 0;
     int n_chunks = 0;
     int solo_tensor = -1;   // the one tensor with elements, else -1
     mps::SoloEntry solo{};  // its entry, passed with every launch
@@ -129,6 +132,7 @@ int layout_plan(std::vector<TensorEntry>& entries, const std::vector<mps::QuantE
         n_chunks += (e.numel + plan.chunk_elems - 1) / plan.chunk_elems;
         if (n_chunks > INT32_MAX) return fail(MPS_ERR_INVALID_ARGUMENT, "too many chunks");
     }
+    plan.n_tensors = n;
     plan.n_chunks = static_cast<int>(n_chunks);
     plan.solo_tensor = -1;
     for (int i = 0; i < n; ++i) {
@@ -299,10 +303,21 @@ int build_plan8(const mps_tensor8* tensors, int n, int grad_dtype, bool need_sta
 
 // -------------------------------------------------- workspace upload cache ---
 
+// A pinned host buffer that carries one table upload.  Copies from pageable
+// memory are performed synchronously by the HIP runtime (they would make a
+// list change wait for the stream); from pinned memory the copy is only
+// enqueued, and the buffer must then stay untouched until the copy is done,
+// which its event tells.
+struct Staging {
+    void* host = nullptr;
+    size_t capacity = 0;
+    hipEvent_t done = nullptr;
+};
+
 struct Uploaded {
-    uint64_t tag = 0;
-    std::vector<unsigned char> image;  // source of the last upload, kept alive
-    hipEvent_t done = nullptr;         // recorded after that upload
+    uint64_t tag = 0;             // tables the workspace holds (enqueued), 0 = none
+    std::deque<Staging> in_flight;  // uploads whose copies may still run, oldest first
+    std::vector<Staging> idle;      // buffers whose copies have finished
     // The call that last planned this workspace: list kind, gradient dtype
     // and the caller's tensor array, byte for byte; whether its state
     // pointers were checked (a norm-only call leaves them unchecked); and its
@@ -325,30 +340,90 @@ int check_workspace(void* ws, size_t bytes, const Plan& plan)
     return MPS_OK;
 }
 
+// Move the uploads whose copies have finished to the idle buffers, oldest
+// first, without waiting: the first one still running stops the scan.
+int reap_uploads(Uploaded& u)
+{
+    while (!u.in_flight.empty()) {
+        const hipError_t e = hipEventQuery(u.in_flight.front().done);
+        if (e == hipErrorNotReady) break;
+        if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "hipEventQuery: %s", hipGetErrorString(e));
+        u.idle.push_back(u.in_flight.front());
+        u.in_flight.pop_front();
+    }
+    return MPS_OK;
+}
+
+// An idle buffer of at least `bytes` (the smallest that fits), or a new one.
+int staging_buffer(Uploaded& u, size_t bytes, Staging& out)
+{
+    size_t best = u.idle.size();
+    for (size_t i = 0; i < u.idle.size(); ++i) {
+        if (u.idle[i].capacity >= bytes &&
+            (best == u.idle.size() || u.idle[i].capacity < u.idle[best].capacity)) {
+            best = i;
+        }
+    }
+    if (best < u.idle.size()) {
+        out = u.idle[best];
+        u.idle.erase(u.idle.begin() + static_cast<std::ptrdiff_t>(best));
+        return MPS_OK;
+    }
+    Staging s;
+    s.capacity = std::max<size_t>(4096, round_up(bytes, 4096));
+    hipError_t e = hipHostMalloc(&s.host, s.capacity, hipHostMallocDefault);
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "hipHostMalloc (table staging): %s", hipGetErrorString(e));
+    e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        (void)hipHostFree(s.host);
+        return fail(MPS_ERR_DEVICE, "hipEventCreate: %s", hipGetErrorString(e));
+    }
+    out = s;
+    return MPS_OK;
+}
+
 // Make the workspace hold `plan`'s tables (stream-ordered), uploading them
-// only when the workspace last received different ones.
+// only when the workspace last received different ones.  Never waits for
+// the device: the image goes through a pinned buffer, which is reused only
+// after its copy's event has completed.
 int ensure_uploaded(void* ws, Plan& plan, hipStream_t stream)
 {
     std::lock_guard<std::mutex> lock(g_cache_mutex);
     Uploaded& u = g_cache[ws];
-    if (u.tag == plan.tag && u.done) return MPS_OK;
-    if (u.done) {
-        // The previous upload may still be reading the old image.
-        hipError_t e = hipEventSynchronize(u.done);
-        if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "hipEventSynchronize: %s", hipGetErrorString(e));
-    } else {
-        hipError_t e = hipEventCreateWithFlags(&u.done, hipEventDisableTiming);
-        if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "hipEventCreate: %s", hipGetErrorString(e));
-    }
+    if (u.tag == plan.tag) return MPS_OK;
+    int rc = reap_uploads(u);
+    if (rc) return rc;
+    Staging buf;
+    if ((rc = staging_buffer(u, plan.image.size(), buf))) return rc;
     u.tag = 0;
     u.key.clear();  // until this upload is enqueued, no plan matches the workspace
-    u.image.swap(plan.image);
-    hipError_t e = hipMemcpyAsync(ws, u.image.data(), u.image.size(), hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "table upload: %s", hipGetErrorString(e));
-    e = hipEventRecord(u.done, stream);
-    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "hipEventRecord: %s", hipGetErrorString(e));
+    std::memcpy(buf.host, plan.image.data(), plan.image.size());
+    hipError_t e = hipMemcpyAsync(ws, buf.host, plan.image.size(), hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipEventRecord(buf.done, stream);
+    if (e != hipSuccess) {
+        // The copy may have been enqueued: keep the buffer until its event
+        // (recorded or not) reports completion.
+        u.in_flight.push_back(buf);
+        return fail(MPS_ERR_DEVICE, "table upload: %s", hipGetErrorString(e));
+    }
+    u.in_flight.push_back(buf);
     u.tag = plan.tag;
     return MPS_OK;
+}
+
+// Release every buffer of a workspace's uploads (waits for running copies).
+void release_uploads(Uploaded& u)
+{
+    for (Staging& s : u.in_flight) {
+        (void)hipEventSynchronize(s.done);
+        u.idle.push_back(s);
+    }
+    u.in_flight.clear();
+    for (Staging& s : u.idle) {
+        (void)hipEventDestroy(s.done);
+        (void)hipHostFree(s.host);
+    }
+    u.idle.clear();
 }
 
 int plan_list(const mps_tensor* t, int n, int grad_dtype, bool need_state, Plan& plan)
@@ -361,29 +436,46 @@ int plan_list(const mps_tensor8* t, int n, int grad_dtype, bool need_state, Plan
     return build_plan8(t, n, grad_dtype, need_state, plan);
 }
 
+// The key of a call: record size and gradient dtype, then the caller's
+// tensor array byte for byte.
+template <class Tensor>
+bool same_key(const std::vector<unsigned char>& key, const Tensor* tensors, int n, int grad_dtype)
+{
+    const size_t bytes = sizeof(Tensor) * static_cast<size_t>(n);
+    return key.size() == bytes + 2 && key[0] == static_cast<unsigned char>(sizeof(Tensor)) &&
+           key[1] == static_cast<unsigned char>(grad_dtype) &&
+           std::memcmp(key.data() + 2, tensors, bytes) == 0;
+}
+
+template <class Tensor>
+void set_key(std::vector<unsigned char>& key, const Tensor* tensors, int n, int grad_dtype)
+{
+    const auto* raw = reinterpret_cast<const unsigned char*>(tensors);
+    key.assign(2 + sizeof(Tensor) * static_cast<size_t>(n), 0);
+    key[0] = static_cast<unsigned char>(sizeof(Tensor));
+    key[1] = static_cast<unsigned char>(grad_dtype);
+    std::memcpy(key.data() + 2, raw, sizeof(Tensor) * static_cast<size_t>(n));
+}
+
 // The plan of a call, with its tables in the workspace.  When the workspace
 // was last planned for this very list (same kind, gradient dtype and tensor
 // array, byte for byte, and the state pointers checked if this call needs
 // them), that plan is reused: validating, chunking and hashing a list costs
 // the host 7 us for one tensor and 0.4 ms for 1137 (3 ms for the 8B-parameter
-// list of 291 tensors, 490K chunks), on every call.  Otherwise the list is
-// validated, planned and, if its tables differ from the workspace's,
-// uploaded.  The device still compares the table tag, so a workspace written
-// behind the library's back is never trusted.
+// list of 291 tensors, 490K chunks), on every call.  The reuse compares in
+// place and allocates nothing.  Otherwise the list is validated, planned
+// and, if its tables differ from the workspace's, uploaded.  The device
+// still compares the table tag, so a workspace written behind the library's
+// back is never trusted.
 template <class Tensor>
 int prepare(const Tensor* tensors, int n, int grad_dtype, bool need_state, void* ws,
             size_t ws_bytes, hipStream_t stream, Plan& plan)
 {
-    std::vector<unsigned char> key;
     if (tensors && n > 0) {
-        const unsigned char head[2] = {static_cast<unsigned char>(sizeof(Tensor)),
-                                       static_cast<unsigned char>(grad_dtype)};
-        key.assign(head, head + 2);
-        const auto* raw = reinterpret_cast<const unsigned char*>(tensors);
-        key.insert(key.end(), raw, raw + sizeof(Tensor) * static_cast<size_t>(n));
         std::lock_guard<std::mutex> lock(g_cache_mutex);
         auto it = g_cache.find(ws);
-        if (it != g_cache.end() && it->second.done && it->second.key == key &&
+        if (it != g_cache.end() && it->second.tag != 0 &&
+            same_key(it->second.key, tensors, n, grad_dtype) &&
             (!need_state || it->second.state_checked)) {
             plan = it->second.meta;
             return check_workspace(ws, ws_bytes, plan);
@@ -395,7 +487,7 @@ int prepare(const Tensor* tensors, int n, int grad_dtype, bool need_state, void*
     if ((rc = ensure_uploaded(ws, plan, stream))) return rc;
     std::lock_guard<std::mutex> lock(g_cache_mutex);
     Uploaded& u = g_cache[ws];
-    u.key.swap(key);
+    set_key(u.key, tensors, n, grad_dtype);
     u.state_checked = need_state;
     u.meta = plan;
     u.meta.image.clear();
@@ -412,6 +504,7 @@ mps::WorkspaceView view_of(void* ws, const Plan& plan)
     v.chunk_map = reinterpret_cast<const uint32_t*>(base + plan.chunks_off);
     v.tickets = reinterpret_cast<uint32_t*>(base + plan.tickets_off);
     v.partials = reinterpret_cast<double*>(base + plan.partials_off);
+    v.n_tensors = plan.n_tensors;
     v.n_chunks = plan.n_chunks;
     v.solo_tensor = plan.solo_tensor;
     v.solo = plan.solo;
@@ -488,6 +581,18 @@ int norm_cached_blocks(const Plan& plan, bool bf16, int grid)
     return static_cast<int>(std::min<int64_t>(grid, mps::kNormCacheBudget / run_bytes));
 }
 
+// Rounds of the single-launch step's bounded barrier wait: 0 (the kernel's
+// default, about 1 s) unless MPS_FUSED_SPIN_LIMIT holds a positive number.
+// That variable is a test hook: a tiny limit makes waiters give the launch
+// up, so the failure path runs while every block still ends normally.
+uint32_t fused_spin_limit()
+{
+    const char* v = std::getenv("MPS_FUSED_SPIN_LIMIT");
+    if (!v || !*v) return 0;
+    const unsigned long x = std::strtoul(v, nullptr, 10);
+    return x > 0 && x < 0xFFFFFFFFul ? static_cast<uint32_t>(x) : 0;
+}
+
 // Launch the norm (and optionally the clip coefficient) over a planned list.
 int run_grad_norm(const Plan& plan, bool bf16, double* d_sumsq, double max_norm,
                   double grad_scale, float* d_coef, void* d_workspace, hipStream_t st)
@@ -551,10 +656,7 @@ int adamw_workspace_release(void* d_workspace)
     std::lock_guard<std::mutex> lock(g_cache_mutex);
     auto it = g_cache.find(d_workspace);
     if (it != g_cache.end()) {
-        if (it->second.done) {
-            (void)hipEventSynchronize(it->second.done);
-            (void)hipEventDestroy(it->second.done);
-        }
+        release_uploads(it->second);
         g_cache.erase(it);
     }
     return ok();
@@ -639,8 +741,25 @@ int adamw_fused_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dt
     mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
     e = mps::launch_fused_step(view_of(d_workspace, plan), bf16, grid,
                                norm_cached_blocks(plan, bf16, grid), max_norm, grad_scale,
-                               skip_if_nonfinite ? 1 : 0, d_sumsq, d_coef, d_step, hp, st);
+                               skip_if_nonfinite ? 1 : 0, d_sumsq, d_coef, d_step, hp,
+                               fused_spin_limit(), st);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "fused step launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int adamw_fused_status(void* d_workspace, size_t workspace_bytes, uint32_t* d_error, void* stream)
+{
+    if (!d_error) return fail(MPS_ERR_INVALID_ARGUMENT, "d_error is NULL");
+    if (!d_workspace) return fail(MPS_ERR_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(d_workspace) % 256) {
+        return fail(MPS_ERR_WORKSPACE, "workspace not 256-byte aligned");
+    }
+    if (workspace_bytes < sizeof(WorkspaceHeader)) {
+        return fail(MPS_ERR_WORKSPACE, "workspace too small: %zu bytes", workspace_bytes);
+    }
+    hipError_t e = mps::launch_fused_status(static_cast<WorkspaceHeader*>(d_workspace), d_error,
+                                            static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "fused status launch: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -102,6 +102,13 @@ __device__ __forceinline__ QuantEntry read_entry(const QuantEntry* table, uint32
     return r;
 }
 
+// A tensor index read from the chunk map, clamped into a table of n >= 1
+// entries (one scalar min: a map in its uploaded state is never changed).
+__device__ __forceinline__ uint32_t table_index(uint32_t raw, int n)
+{
+    return min(raw, static_cast<uint32_t>(n - 1));
+}
+
 __device__ __forceinline__ TensorEntry uniform_entry(const TensorEntry& e)
 {
     TensorEntry u;

@@ -28,6 +28,7 @@ struct WorkspaceView {
     const uint32_t* chunk_map;
     uint32_t* tickets;  // the update's step-ticket tree (kTicketGroups + 1 lines)
     double* partials;
+    int n_tensors;    // entries in `tensors` (>= 1): a chunk-map value is clamped below it
     int n_chunks;
     int solo_tensor;  // the index every chunk maps to, or -1 (several tensors)
     int64_t chunk_elems;
@@ -70,11 +71,16 @@ hipError_t launch_clipped_step(const WorkspaceView& ws, bool grad_bf16, bool wid
 hipError_t fused_grid_limit(bool grad_bf16, int* max_blocks);
 
 // The single-launch step (cooperative launch; `grid` must not exceed
-// fused_grid_limit nor kFusedMaxBlocks).
+// fused_grid_limit nor kFusedMaxBlocks).  `spin_limit`: rounds of the
+// barrier's bounded wait (0: the default, about 1 s).
 hipError_t launch_fused_step(const WorkspaceView& ws, bool grad_bf16, int grid, int cached_blocks,
                              double max_norm, double grad_scale, int skip_if_nonfinite,
                              double* d_sumsq, float* d_coef, int32_t* d_step,
-                             const HyperParams& hp, hipStream_t stream);
+                             const HyperParams& hp, uint32_t spin_limit, hipStream_t stream);
+
+// Copies the single-launch step's error flag from the header into *d_error
+// and clears it.
+hipError_t launch_fused_status(WorkspaceHeader* header, uint32_t* d_error, hipStream_t stream);
 
 // 8-bit moment state (kernels_q8.hip).  `quant` is the QuantEntry table in
 // the same workspace; d_coef and d_skip_if_nonfinite are never NULL (as in

@@ -80,11 +80,14 @@ __device__ __forceinline__ ChunkRun block_run(int n_chunks)
 }
 
 // The tensor index of chunk c.  A list whose chunks all belong to one tensor
-// needs no chunk-map read.
+// needs no chunk-map read.  The value read from the map is clamped into the
+// tensor table, whose size comes with the launch: the prologues read the
+// entry before the header's tag has been compared, and a map overwritten
+// behind the library's back must not send that read past the table.
 __device__ __forceinline__ uint32_t tensor_of_chunk(const WorkspaceView& ws, int c)
 {
     return ws.solo_tensor >= 0 ? static_cast<uint32_t>(ws.solo_tensor)
-                               : constant_view(ws.chunk_map)[c];
+                               : table_index(constant_view(ws.chunk_map)[c], ws.n_tensors);
 }
 
 // The tensor index of chunk c for a kernel's prologue: c is clamped into the
@@ -512,7 +515,7 @@ __device__ __forceinline__ void update_chunks(const WorkspaceView& ws, TensorEnt
         const TensorEntry entry = uniform_entry(next);
         const int c_next = c + static_cast<int>(gridDim.x);
         if (ws.solo_tensor < 0 && c_next < n_chunks) {
-            next = read_entry(ws.tensors, constant_view(ws.chunk_map)[c_next]);
+            next = read_entry(ws.tensors, tensor_of_chunk(ws, c_next));
         }
         adamw_chunk<kBf16, kUnroll>(&entry, c, ws.chunk_elems, s);
     }
@@ -670,16 +673,35 @@ __global__ __launch_bounds__(kBlock) void adamw_clipped_kernel(
 
 // ------------------------------------------------------ single launch ---
 
-constexpr uint32_t kSpinLimit = 1u << 23;  // x s_sleep(2): about 1 s, never reached
+// The barrier's wait is bounded: kSpinLimit rounds of s_sleep(2), about 1 s,
+// never reached in a launch whose blocks are all resident.  The host may pass
+// a smaller limit (the library's test hook), so that the give-up path can be
+// exercised with every block still ending normally.
+constexpr uint32_t kSpinLimit = 1u << 23;
+
+// A waiter gives launch k up: it takes the launch's one decision (k -> k + 1)
+// if the last block has not taken it yet.  True if this call decided.
+__device__ __forceinline__ bool take_decision(WorkspaceHeader* header, uint32_t k)
+{
+    uint32_t expected = k;
+    return __hip_atomic_compare_exchange_strong(&header->fused_decided, &expected, k + 1u,
+                                                __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // The whole step in one launch: norm, grid barrier, clip, update.  Launched
-// cooperatively, so every block is resident and the barrier completes; the
-// bounded wait only guards against a broken launch (it then flags the error
-// and the waiting block stops without writing state).
+// cooperatively, so every block is resident and the barrier completes.  The
+// bounded wait guards against a broken launch: the first waiter to run out
+// abandons the launch (if the last block has not already published), and an
+// abandoned launch writes no element, leaves the counter, and reports NaN for
+// S and the coefficient, with the workspace's error flag set.  A waiter that
+// runs out after the last block has published keeps waiting for the release
+// (it is on its way), again bounded; running out a second time only sets the
+// flag.
 template <bool kBf16, int kNormUnroll, int kStepUnroll>
 __global__ __launch_bounds__(kBlock) void adamw_fused_kernel(
     WorkspaceView ws, int cached_blocks, double max_norm, double grad_scale, int skip_if_nonfinite,
-    double* d_sumsq, float* d_coef, int32_t* d_step, HyperParams hp)
+    double* d_sumsq, float* d_coef, int32_t* d_step, HyperParams hp, uint32_t spin_limit)
 {
     const int tid = threadIdx.x;
     const int grid = gridDim.x;
@@ -715,37 +737,61 @@ __global__ __launch_bounds__(kBlock) void adamw_fused_kernel(
         failed = false;
     }
     __syncthreads();
+    const uint32_t k = static_cast<uint32_t>(launch);
 
-    // Barrier.  The last block to arrive sums the partials in block order,
-    // publishes S and the new step count, then releases the others.
+    // Barrier.  The last block to arrive sums the partials in block order and,
+    // unless a waiter gave the launch up first, publishes S and the new step
+    // count; either way it then releases the others.
     if (last) {
         const double total = sum_partials<true>(ws.partials, grid, lds);
         if (tid == 0) {
-            const bool skip = skip_if_nonfinite && !__builtin_isfinite(total);
-            __hip_atomic_store(&header->fused_sumsq, total, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            if (d_sumsq) *d_sumsq = total;
-            if (d_coef) *d_coef = clip_from_sumsq(total, max_norm, grad_scale);
-            if (!skip) *d_step = static_cast<int32_t>(t);
-            __builtin_amdgcn_s_waitcnt(0);  // S is visible before the release
+            if (take_decision(header, k)) {
+                const bool skip = skip_if_nonfinite && !__builtin_isfinite(total);
+                __hip_atomic_store(&header->fused_sumsq, total, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                if (d_sumsq) *d_sumsq = total;
+                if (d_coef) *d_coef = clip_from_sumsq(total, max_norm, grad_scale);
+                if (!skip) *d_step = static_cast<int32_t>(t);
+            } else {
+                __hip_atomic_store(&header->fused_abandoned, k + 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                if (d_sumsq) *d_sumsq = __builtin_nan("");
+                if (d_coef) *d_coef = __builtin_nanf("");
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // all of it is visible before the release
             __hip_atomic_store(&header->fused_released, launch + 1, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     } else if (tid == 0) {
         uint32_t spins = 0;
+        bool gave_up_once = false;
         while (__hip_atomic_load(&header->fused_released, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT) < launch + 1) {
             __builtin_amdgcn_s_sleep(2);
-            if (++spins == kSpinLimit) {
-                __hip_atomic_store(&header->fused_error, 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                failed = true;
-                break;
+            if (++spins < spin_limit) continue;
+            if (!gave_up_once && !take_decision(header, k)) {
+                gave_up_once = true;  // the last block has published: wait for its release
+                spins = 0;
+                continue;
             }
+            __hip_atomic_store(&header->fused_error, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            if (!gave_up_once) {  // this block abandoned the launch
+                if (d_sumsq) *d_sumsq = __builtin_nan("");
+                if (d_coef) *d_coef = __builtin_nanf("");
+            }
+            failed = true;
+            break;
         }
     }
     __syncthreads();
     if (failed) return;
+    // An abandoned launch (the last block recorded it before the release)
+    // writes no element.
+    if (__hip_atomic_load(&header->fused_abandoned, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        k + 1u) {
+        return;
+    }
 
     // Phase 2: every block sees the same S, hence the same coefficient.
     const double total = __hip_atomic_load(&header->fused_sumsq, __ATOMIC_RELAXED,
@@ -754,6 +800,15 @@ __global__ __launch_bounds__(kBlock) void adamw_fused_kernel(
     const StepScalars s = step_scalars(t, hp, clip_from_sumsq(total, max_norm, grad_scale));
     update_chunks<kBf16, kStepUnroll>(
         ws, read_entry(ws.tensors, prologue_tensor(ws, blockIdx.x)), s);
+}
+
+// The single-launch step's error flag: copied out and cleared (one lane).
+__global__ __launch_bounds__(kWave) void fused_status_kernel(WorkspaceHeader* header,
+                                                             uint32_t* d_error)
+{
+    if (threadIdx.x != 0) return;
+    *d_error = __hip_atomic_exchange(&header->fused_error, 0u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -878,12 +933,13 @@ hipError_t fused_grid_limit(bool grad_bf16, int* max_blocks)
 hipError_t launch_fused_step(const WorkspaceView& ws, bool grad_bf16, int grid, int cached_blocks,
                              double max_norm, double grad_scale, int skip_if_nonfinite,
                              double* d_sumsq, float* d_coef, int32_t* d_step,
-                             const HyperParams& hp, hipStream_t stream)
+                             const HyperParams& hp, uint32_t spin_limit, hipStream_t stream)
 {
     WorkspaceView view = ws;
     HyperParams params = hp;
+    if (spin_limit == 0) spin_limit = kSpinLimit;
     void* args[] = {&view,    &cached_blocks, &max_norm, &grad_scale, &skip_if_nonfinite,
-                    &d_sumsq, &d_coef,        &d_step,   &params};
+                    &d_sumsq, &d_coef,        &d_step,   &params,     &spin_limit};
     const void* fn = grad_bf16 ? reinterpret_cast<const void*>(fused_kernel<true>())
                                : reinterpret_cast<const void*>(fused_kernel<false>());
     // Cooperative: the runtime refuses the launch unless every block can be
@@ -891,6 +947,12 @@ hipError_t launch_fused_step(const WorkspaceView& ws, bool grad_bf16, int grid, 
     // costs about 20 us more than a plain one, so the single-launch step is
     // slower than the two-launch step even on a 2^20-parameter shard.)
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kBlock), args, 0, stream);
+}
+
+hipError_t launch_fused_status(WorkspaceHeader* header, uint32_t* d_error, hipStream_t stream)
+{
+    fused_status_kernel<<<1, kWave, 0, stream>>>(header, d_error);
+    return hipGetLastError();
 }
 
 }  // namespace mps

@@ -443,14 +443,15 @@ __device__ __forceinline__ void adamw8_chunk(const Entry* te, const QuantEntry* 
 template <bool kBf16>
 __device__ __forceinline__ void update8_chunks(const TensorEntry* __restrict__ tensors,
                                                const QuantEntry* __restrict__ quant,
-                                               const uint32_t* __restrict__ chunk_map, int n_chunks,
-                                               int64_t chunk_elems, const StepScalars& s)
+                                               const uint32_t* __restrict__ chunk_map,
+                                               int n_tensors, int n_chunks, int64_t chunk_elems,
+                                               const StepScalars& s)
 {
     int parity = 0;
     TensorEntry next{};
     QuantEntry next_q{};
     if (static_cast<int>(blockIdx.x) < n_chunks) {
-        const uint32_t k = constant_view(chunk_map)[blockIdx.x];
+        const uint32_t k = table_index(constant_view(chunk_map)[blockIdx.x], n_tensors);
         next = read_entry(tensors, k);
         next_q = read_entry(quant, k);
     }
@@ -458,7 +459,7 @@ __device__ __forceinline__ void update8_chunks(const TensorEntry* __restrict__ t
         const TensorEntry te = uniform_entry(next);
         const QuantEntry qe = uniform_entry(next_q);
         if (c + static_cast<int>(gridDim.x) < n_chunks) {
-            const uint32_t k = constant_view(chunk_map)[c + gridDim.x];
+            const uint32_t k = table_index(constant_view(chunk_map)[c + gridDim.x], n_tensors);
             next = read_entry(tensors, k);
             next_q = read_entry(quant, k);
         }
@@ -546,7 +547,7 @@ __global__ __launch_bounds__(kBlock) void adamw8_step_kernel(
     const int64_t t = static_cast<int64_t>(count) + 1;
     if (seen != ws.tag) return;  // tables overwritten: touch nothing
     if (!__builtin_isfinite(skip_value)) return;
-    update8_chunks<kBf16>(ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems,
+    update8_chunks<kBf16>(ws.tensors, quant, ws.chunk_map, ws.n_tensors, ws.n_chunks, ws.chunk_elems,
                           step_scalars(t, hp, coef));
     advance_step(ws.tickets, d_step, t);
 }
@@ -598,7 +599,7 @@ __global__ __launch_bounds__(kBlock) void adamw8_clipped_kernel(
     const double total = sum_partials<false>(ws.partials, n_partials, lds);
     const float clip = clip_from_sumsq(total, max_norm, grad_scale);
     if (publish_clip(total, clip, t, skip_if_nonfinite, d_sumsq, d_coef, d_step)) return;
-    update8_chunks<kBf16>(ws.tensors, quant, ws.chunk_map, ws.n_chunks, ws.chunk_elems,
+    update8_chunks<kBf16>(ws.tensors, quant, ws.chunk_map, ws.n_tensors, ws.n_chunks, ws.chunk_elems,
                           step_scalars(t, hp, clip));
 }
 

@@ -89,7 +89,13 @@ constexpr int64_t kChunkTarget = MPS_CHUNK_TARGET;
 constexpr int64_t kNormCacheBudget = MPS_NORM_CACHE_BUDGET;
 
 struct alignas(64) WorkspaceHeader {
-    uint32_t reserved[2];
+    // The single-launch step's outcome, decided once per launch k (low 32
+    // bits of k) by whichever comes first: the last block to arrive at the
+    // barrier (publish) or a waiter that gave up (abandon).  `fused_decided`
+    // goes from k to k + 1 by compare-and-swap; `fused_abandoned` holds
+    // k + 1 when launch k was abandoned.
+    uint32_t fused_decided;
+    uint32_t fused_abandoned;
     uint64_t tag;           // identifies the uploaded tables
     int32_t n_tensors;
     int32_t n_chunks;
@@ -100,7 +106,8 @@ struct alignas(64) WorkspaceHeader {
     uint64_t fused_arrived;
     uint64_t fused_released;
     double fused_sumsq;     // S, published by the last block to arrive
-    uint32_t fused_error;   // set if a barrier wait ever ran out (never expected)
+    uint32_t fused_error;   // set when a barrier wait ran out (never expected); read
+                            // and cleared by adamw_fused_status
     int32_t pending_step;   // the clipped step: t, written by its norm launch
                             // for its update launch
 };

@@ -37,7 +37,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "adamw_workspace_bytes", "adamw_workspace_release", "grad_norm_sq", "clip_coef",
-        "adamw_multi_tensor_step", "adamw_clipped_step", "adamw_fused_step", "adamw_last_error",
+        "adamw_multi_tensor_step", "adamw_clipped_step", "adamw_fused_step",
+        "adamw_fused_status", "adamw_last_error",
         "adamw8_workspace_bytes", "adamw8_grad_norm_sq", "adamw8_multi_tensor_step",
         "adamw8_clipped_step",
         "adamw8_quantize", "adamw8_dequantize"])
@@ -268,3 +269,13 @@ def test_header_is_plain_c(tmp_path):
         assert r.returncode == 0, (compiler, r.stderr)
     # the ctypes mirrors have the C layout
     assert ctypes.sizeof(binding.MpsTensor) == 48 and ctypes.sizeof(binding.MpsTensor8) == 64
+
+
+def test_fused_status_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p
+    assert lib.adamw_fused_status(P(0x7f0000000000), 4096, None, None) == EINVAL
+    assert "d_error" in binding.last_error()
+    assert lib.adamw_fused_status(None, 4096, P(0x1000), None) == EWORKSPACE
+    assert lib.adamw_fused_status(P(0x7f0000000010), 4096, P(0x1000), None) == EWORKSPACE
+    assert lib.adamw_fused_status(P(0x7f0000000000), 32, P(0x1000), None) == EWORKSPACE
+    assert "too small" in binding.last_error()

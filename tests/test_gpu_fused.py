@@ -1,10 +1,16 @@
 """GPU parity of the single-launch step (adamw_fused_step) against the oracle:
 norm, clip and update from one cooperative launch, on the same cases as the
 three-call path, plus repeated launches on one workspace (the grid barrier's
-counters only grow) and the barrier's error flag."""
+counters only grow) and the barrier's error flag, read through
+adamw_fused_status.  The give-up path of the barrier is forced from the host
+with the library's spin-limit hook (every block still ends normally)."""
+import os
+
 import numpy as np
 import pytest
 import torch
+
+from mixed_precision_sharded_amd import binding
 
 import oracle
 from gpu_harness import NORM_REL_TOL, Step, compare_state, host_copy, oracle_norm, oracle_step, say
@@ -21,6 +27,13 @@ ARRIVED, RELEASED, ERROR = 4, 5, 7
 
 def error_flag(words):
     return words[ERROR] & 0xFFFFFFFF
+
+
+def fused_status(st):
+    """The workspace's barrier error flag through the C ABI (read and cleared)."""
+    out = torch.full((1,), -1, dtype=torch.int32, device=st.tl.device)
+    binding.adamw_fused_status(st.tl, out)
+    return int(out.item())
 
 
 @pytest.fixture(autouse=True)
@@ -48,6 +61,7 @@ def fused_and_check(cols, t, hp=HP, max_norm=1.0, grad_scale=1.0, what=""):
         f"non-bitwise w/m/v/p = {stats['w'][0]}/{stats['m'][0]}/{stats['v'][0]}/{stats['p'][0]}")
     words = st.header_words()
     assert error_flag(words) == 0, "barrier wait ran out"
+    assert fused_status(st) == 0
     assert words[ARRIVED] % max(1, words[RELEASED]) == 0
     return stats
 
@@ -92,6 +106,7 @@ def test_fused_consecutive_launches_match_the_oracle():
     words = st.header_words()
     assert words[RELEASED] == 5 and words[ARRIVED] == 5 * (words[ARRIVED] // 5)
     assert error_flag(words) == 0
+    assert fused_status(st) == 0
 
 
 def test_fused_skip_if_nonfinite():
@@ -108,20 +123,81 @@ def test_fused_skip_if_nonfinite():
     assert error_flag(st.header_words()) == 0
 
 
-def test_fused_and_two_launch_paths_agree_given_the_same_coefficient():
-    """Same inputs through both paths: the coefficients may differ in the last
-    bit (different summation orders of S); where they are equal the states are
-    bitwise equal."""
+def test_fused_and_two_launch_paths_each_match_the_oracle():
+    """Same inputs through both paths.  Their sums of squares come from
+    different block counts (so their coefficients may differ in the last
+    bit); each path's state must equal the oracle stepped with that path's own
+    coefficient, and where the coefficients are equal the two states are
+    bitwise equal as well."""
     a = make_cols([250000, 3], False, False, seed=64)
     b = make_cols([250000, 3], False, False, seed=64)
+    host_a, host_b = host_copy(a), host_copy(b)
     sa = Step(a, completed_steps=1).fused(1.0, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"],
                                           HP["wd"])
     sb = Step(b, completed_steps=1).norm_clip(1.0).update(HP["lr"], HP["beta1"], HP["beta2"],
                                                           HP["eps"], HP["wd"])
-    Sa, ca, _ = sa.results()
-    Sb, cb, _ = sb.results()
+    Sa, ca, ta = sa.results()
+    Sb, cb, tb = sb.results()
+    assert ta == tb == 2
     assert abs(Sa - Sb) <= 1e-12 * Sb
+    o = oracle.default()
+    assert ca == o.clip_coef(Sa, 1.0) and cb == o.clip_coef(Sb, 1.0)
+    for cols, host, c, what in ((a, host_a, ca, "fused"), (b, host_b, cb, "three calls")):
+        oracle_step(host, c, 2, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+        stats = compare_state(cols, host, what)
+        assert stats["w"][0] == stats["m"][0] == stats["v"][0] == 0, what
     if ca == cb:
         for k in ("master", "exp_avg", "exp_avg_sq"):
             for x, y in zip(a[k], b[k]):
                 assert torch.equal(x.view(torch.int32), y.view(torch.int32)), k
+    assert fused_status(sa) == 0
+
+
+def test_fused_barrier_give_up_is_reported_and_writes_nothing():
+    """The barrier's bound forced down to one round from the host: the blocks
+    that wait give the launch up.  Every block still ends normally.  The flag
+    reads 1 through adamw_fused_status; an abandoned launch leaves every
+    element and the counter as they were and reports NaN for S and the
+    coefficient.  (Should a waiter lose the race to the last block, which then
+    publishes, each element is either updated as the oracle says or left as
+    it was.)  The next launch with the normal bound is a good step."""
+    cols = make_cols([300001, 77], False, True, seed=65)
+    before = {k: [t.clone() for t in v] for k, v in cols.items()}
+    st = Step(cols, completed_steps=3)
+    os.environ["MPS_FUSED_SPIN_LIMIT"] = "1"
+    try:
+        st.fused(1.0, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["MPS_FUSED_SPIN_LIMIT"]
+    S, c, step = st.results()
+    assert fused_status(st) == 1
+    assert fused_status(st) == 0  # cleared by the read
+    if np.isnan(S):
+        say("[fused give-up] launch abandoned")
+        assert np.isnan(c) and step == 3
+        for k in ("master", "exp_avg", "exp_avg_sq", "param_bf16"):
+            for x, y in zip(cols[k], before[k]):
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16)), k
+    else:
+        say("[fused give-up] published before a waiter gave up")
+        assert step == 4
+        ref = host_copy(before)
+        oracle_step(ref, c, 4, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+        for k in ("master", "exp_avg", "exp_avg_sq"):
+            for i, got in enumerate(cols[k]):
+                g = got.cpu().numpy().view(np.int32)
+                new = ref[k][i].view(np.int32)
+                old = before[k][i].cpu().numpy().view(np.int32)
+                assert ((g == new) | (g == old)).all(), (k, i)
+        return
+    # A normal launch on the same workspace afterwards: the barrier's counters
+    # and the launch's decision word are consistent.
+    host = host_copy(cols)
+    st.fused(1.0, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+    S, c, step = st.results()
+    assert step == 4 and np.isfinite(S) and c == oracle.default().clip_coef(S, 1.0)
+    oracle_step(host, c, 4, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+    stats = compare_state(cols, host, "after an abandoned launch")
+    assert stats["w"][0] == stats["m"][0] == stats["v"][0] == 0
+    assert fused_status(st) == 0

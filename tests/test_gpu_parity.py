@@ -343,18 +343,25 @@ def test_nonfinite_gradients():
 
 @pytest.mark.parametrize("form", ["three calls", "clipped"])
 @pytest.mark.parametrize("sizes", [[5000], [5000, 300]], ids=["one tensor", "two tensors"])
-def test_overwritten_workspace_is_detected(form, sizes):
+@pytest.mark.parametrize("overwrite", ["header", "everything"])
+def test_overwritten_workspace_is_detected(form, sizes, overwrite):
     """If the workspace tables are overwritten behind the library's back the
     kernels leave every buffer alone (the norm reports NaN).  A one-tensor
     list takes its tensor from the launch and checks the tag after its first
-    reads, a longer list before; both are covered in both two-launch forms."""
+    reads, a longer list before; both are covered in both two-launch forms.
+    The header alone is zeroed, or every byte of the workspace set to 0xFF:
+    then the chunk map holds 0xFFFFFFFF, which the prologues (reading a table
+    entry before the tag has been compared) clamp into the tensor table."""
     cols = make_cols(sizes, False, False, seed=15)
     before = [t.clone() for t in cols["master"] + cols["exp_avg"] + cols["exp_avg_sq"]]
     st = Step(cols, completed_steps=0)
     st.norm().results()  # uploads the tables
     ws = st.tl._ws_storage
     off = st.tl.workspace_ptr - ws.data_ptr()
-    ws[off:off + 64].zero_()
+    if overwrite == "header":
+        ws[off:off + 64].zero_()
+    else:
+        ws[off:off + st.tl.workspace_bytes].fill_(0xFF)
     if form == "clipped":
         st.clipped(1.0, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
     else:

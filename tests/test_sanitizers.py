@@ -5,7 +5,11 @@ oracle over ragged sizes, non-finite values and both 8-bit formats with
 exactly sized buffers; the other takes the library's host side (list
 validation, chunking, workspace tables, argument checks of every entry
 point) through valid and invalid lists with stand-ins for the kernel
-launchers that abort if reached.  No GPU code is built with a sanitizer."""
+launchers that abort if reached.  A third drives the library's table
+uploads against a fake in-order device (tests/sanitize/fake_device.cpp):
+list changes must never make the host wait, copies must come from pinned
+buffers, and a staging buffer must not be reused before its copy ran.  No
+GPU code is built with a sanitizer."""
 import os
 import shutil
 import subprocess
@@ -53,3 +57,54 @@ def test_library_host_code_under_sanitizers(tmp_path):
                     os.path.join(ROOT, "mixed_precision_sharded_amd", "csrc", "api.cpp"),
                     "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"], check=True)
     assert "host driver ok" in run(exe)
+
+
+UPLOAD_SOURCES = [os.path.join(HERE, "upload_driver.cpp"), os.path.join(HERE, "fake_device.cpp")]
+
+
+def build_upload_driver(exe, api_cpp):
+    subprocess.run(["g++", *SAN, "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    "-o", exe, *UPLOAD_SOURCES, api_cpp], check=True)
+
+
+@pytest.mark.skipif(shutil.which("g++") is None or not os.path.isdir("/opt/rocm/include"),
+                    reason="no g++ or ROCm headers")
+def test_table_uploads_never_wait_for_the_device(tmp_path):
+    exe = str(tmp_path / "upload_driver")
+    build_upload_driver(exe, os.path.join(ROOT, "mixed_precision_sharded_amd", "csrc", "api.cpp"))
+    assert "upload driver ok" in run(exe)
+
+
+@pytest.mark.skipif(shutil.which("g++") is None or not os.path.isdir("/opt/rocm/include"),
+                    reason="no g++ or ROCm headers")
+@pytest.mark.parametrize("plant,symptom", [
+    # staging buffers treated as free before their copies ran
+    ("const hipError_t e = hipEventQuery(u.in_flight.front().done);",
+     "a launch found another list's tables"),
+    # an upload that waits for the previous one
+    ("int rc = reap_uploads(u);",
+     "hipEventSynchronize: a call made the host wait"),
+])
+def test_the_upload_driver_catches_planted_mistakes(tmp_path, plant, symptom):
+    src = os.path.join(ROOT, "mixed_precision_sharded_amd", "csrc", "api.cpp")
+    text = open(src).read()
+    assert plant in text
+    if "hipEventQuery" in plant:
+        bad = "const hipError_t e = hipSuccess; (void)hipEventQuery(u.in_flight.front().done);"
+    else:
+        bad = ("if (!u.in_flight.empty()) (void)hipEventSynchronize(u.in_flight.back().done); "
+               "int rc = reap_uploads(u);")
+    d = tmp_path / "csrc"
+    d.mkdir()
+    for name in os.listdir(os.path.dirname(src)):
+        if name.endswith(".h"):
+            shutil.copy(os.path.join(os.path.dirname(src), name), d / name)
+    (tmp_path / "include").mkdir()
+    shutil.copy(os.path.join(ROOT, "include", "mps_adamw.h"), tmp_path / "include" / "mps_adamw.h")
+    planted = d / "api.cpp"
+    planted.write_text(text.replace(plant, bad).replace('"../../include/mps_adamw.h"',
+                                                        '"../include/mps_adamw.h"'))
+    exe = str(tmp_path / "upload_driver_planted")
+    build_upload_driver(exe, str(planted))
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=ENV)
+    assert r.returncode != 0 and symptom in r.stderr, r.stdout + r.stderr
