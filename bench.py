@@ -11,7 +11,14 @@ the dominant kernel (the update) its roofline against MI355X's 8 TB/s HBM
 peak, timed live with events on the launch stream; plus the CPU oracle timed
 on a bounded sample on the host (one thread, then all threads).
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--rotate R] [--state8]
+    python bench.py [--steps K] [--warmup W] [--config 3] [--rotate R] [--state8]
+
+The default workload is the largest one that fits one GPU: the full
+Llama-3.1-8B as a 291-tensor list (8,030,261,248 parameters, 128.5 GB of
+state).  The line also carries, measured in the same process: a practical
+ceiling (a plain device copy of 2 GiB, read + write bytes over its time) and
+the two-launch latency floor (the same call on a list whose one tensor is
+empty: the two launches with no bytes to move).
 
 Without --warmup the warm-up lasts at least 10 steps and 0.25 s: the GPU's
 clock needs some tens of milliseconds of work to settle (an 8-bit step on
@@ -54,8 +61,11 @@ def parse():
     p.add_argument("--warmup-seconds", type=float, default=0.25,
                    help="with the default --warmup, warm up for at least this long: the "
                         "GPU's clock takes some tens of milliseconds of work to settle")
-    p.add_argument("--config", type=int, default=2,
-                   help="workload 1..5 (default 2: Llama-3.1-8B FSDP2 shard at 128-way)")
+    p.add_argument("--config", type=int, default=3,
+                   help="workload 1..5 (default 3: the full Llama-3.1-8B as a 291-tensor list, "
+                        "the largest that fits one GPU)")
+    p.add_argument("--ceiling-mib", type=int, default=2048,
+                   help="size of the same-run copy ceiling's buffers (0 = skip)")
     p.add_argument("--rotate", type=int, default=1,
                    help="cycle over this many independent buffer sets (cache-cold small shards)")
     p.add_argument("--trials", type=int, default=5,
@@ -316,6 +326,12 @@ def main():
                     "avg_launch_us": round(us, 2)}
         log(f"kernels (us): " + ", ".join(f"{k} {v:.1f}" for k, v in kern_us.items()))
 
+    floor = None if args.no_kernel_events else latency_floor(args, dev)
+    ceiling = None if args.ceiling_mib <= 0 else copy_ceiling(args.ceiling_mib, dev)
+    if roofline is not None and ceiling is not None:
+        roofline["ceiling"] = ceiling
+        roofline["frac_of_ceiling"] = round(roofline["achieved"] / ceiling["achieved"], 4)
+
     if args.copy_calibration_mib > 0:
         n_f32 = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n_f32, dtype=torch.float32, device=dev)
@@ -358,9 +374,89 @@ def main():
         "trials": trials,
         "warm_same_buffers": warm,
         "roofline": roofline,
+        "latency_floor": floor,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def copy_ceiling(mib, dev, reps=10):
+    """A plain device-to-device copy of `mib` MiB (torch's copy kernel), timed
+    with events on the current stream after two warm-ups: read + write bytes
+    over the average time.  The practical bound of a stream that reads and
+    writes the same number of bytes, measured beside the step on the same GPU
+    in the same process."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    gbps = 2 * n * 4 / (us * 1e-6) / 1e9
+    log(f"copy ceiling: {mib} MiB in {us:.1f} us, {gbps:.0f} GB/s")
+    return {"achieved": round(gbps, 1), "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "what": f"device copy of {mib} MiB (torch), read + write bytes / time, mean of {reps}"}
+
+
+def latency_floor(args, dev, steps=200):
+    """The same call as a step, on a list whose one tensor is empty: the two
+    launches (or one, or three calls) and their dependencies with no bytes to
+    move.  No step on any list can take less."""
+    import torch
+
+    from mixed_precision_sharded_amd import binding
+
+    e = torch.empty(0, dtype=torch.float32, device=dev)
+    g = torch.empty(0, dtype=torch.bfloat16, device=dev)
+    sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+    coef = torch.zeros(1, dtype=torch.float32, device=dev)
+    step = torch.zeros(1, dtype=torch.int32, device=dev)
+    if args.state8:
+        z = torch.empty(0, dtype=torch.uint8, device=dev)
+        tl = binding.TensorList8([e], [(z, z, z, z)], [g])
+    else:
+        tl = binding.TensorList([e], [e], [e], [g])
+
+    def one():
+        if args.launches == "fused" and not args.state8:
+            binding.adamw_fused_step(tl, step, 3e-4, 0.9, 0.95, 1e-8, 0.1, 1.0, sumsq_out=sumsq,
+                                     coef_out=coef)
+        elif args.launches == "clipped":
+            fn = binding.adamw8_clipped_step if args.state8 else binding.adamw_clipped_step
+            fn(tl, step, 3e-4, 0.9, 0.95, 1e-8, 0.1, 1.0, sumsq_out=sumsq, coef_out=coef)
+        elif args.state8:
+            binding.adamw8_grad_norm_sq(tl, sumsq, 1.0, coef)
+            binding.adamw8_multi_tensor_step(tl, coef, step, 3e-4, 0.9, 0.95, 1e-8, 0.1)
+        else:
+            binding.grad_norm_sq(tl, sumsq, 1.0, coef)
+            binding.adamw_multi_tensor_step(tl, coef, step, 3e-4, 0.9, 0.95, 1e-8, 0.1)
+
+    for _ in range(20):
+        one()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        one()
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / steps
+    tl.release()
+    log(f"latency floor: {us:.1f} us per step on an empty list")
+    return {"us_per_step": round(us, 2),
+            "what": f"the same call on a list of one empty tensor, {steps} steps back to back "
+                    "(launches and their dependencies, no bytes)"}
 
 
 CPU_SAMPLE_MAX_ELEMS = 64 << 20

@@ -124,6 +124,61 @@ def check_f32(got, want, what, rel=REL_TOL):
     return nbit, worst
 
 
+def check_f32_bitwise_first(got, want, what, rel=REL_TOL, piece=1 << 26):
+    """check_f32 for very long arrays: elements that are bitwise equal meet
+    every condition of check_f32 (zero error, NaN for NaN, the same infinity),
+    so only the others go through it; in pieces, to bound the temporaries."""
+    got = np.asarray(got, np.float32)
+    want = np.asarray(want, np.float32)
+    assert got.shape == want.shape, what
+    nbit, worst = 0, 0.0
+    for lo in range(0, got.size, piece):
+        g, w = got[lo:lo + piece], want[lo:lo + piece]
+        neq = g.view(np.uint32) != w.view(np.uint32)
+        if neq.any():
+            nb, wr = check_f32(g[neq], w[neq], f"{what} [{lo}:]", rel)
+            nbit += nb
+            worst = max(worst, wr)
+    return nbit, worst
+
+
+def check_bf16_bitwise_first(got, want, what, ulps=BF16_ULP_TOL, piece=1 << 26):
+    """check_bf16 for very long arrays, bitwise-equal elements skipped."""
+    got = np.asarray(got, np.uint16)
+    want = np.asarray(want, np.uint16)
+    assert got.shape == want.shape, what
+    nbit, worst = 0, 0
+    for lo in range(0, got.size, piece):
+        g, w = got[lo:lo + piece], want[lo:lo + piece]
+        neq = g != w
+        if neq.any():
+            nb, wr = check_bf16(g[neq], w[neq], f"{what} [{lo}:]", ulps)
+            nbit += nb
+            worst = max(worst, wr)
+    return nbit, worst
+
+
+def oracle_step_threads(w, m, v, g, p, c, t, lr, beta1, beta2, eps, wd, threads=16):
+    """The oracle's step on host arrays (in place), each array cut into
+    `threads` contiguous slices stepped by one thread each: the oracle's
+    arithmetic is per element, so slicing changes nothing in the results
+    (its C code runs outside the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    o = oracle.default()
+    n = w.size
+    cuts = [n * k // threads for k in range(threads)] + [n]
+
+    def one(k):
+        lo, hi = cuts[k], cuts[k + 1]
+        if hi > lo:
+            o.adamw_step(w[lo:hi], m[lo:hi], v[lo:hi], g[lo:hi], None if p is None else p[lo:hi],
+                         c, t, lr, beta1, beta2, eps, wd)
+
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        list(pool.map(one, range(threads)))
+
+
 def bf16_order(bits):
     """Map bf16 bit patterns to integers ordered like their values."""
     b = bits.astype(np.int32)

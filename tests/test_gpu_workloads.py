@@ -2,18 +2,24 @@
 configuration bench.py times (adamw_clipped_step on the same list; one case
 runs the three-call step instead).
 
-The sum of squares is checked against the oracle over every gradient; the
-update is checked element by element on sampled positions (random ones, the
-first and last elements of every tensor, and chunk edges), which the oracle
-computes one by one from the inputs gathered before the step.  Whole-tensor
-properties (finite state, step counter) are checked at every position.
+The sum of squares is checked against the oracle over every gradient.  The
+update is checked against the oracle on EVERY element of the 405B share
+(792.7M parameters, 1137 tensors) and, for the 8B-parameter list, on every
+element of whole tensors (the embedding, the first and last layers, the
+final norm, the output head: 1.5e9 elements, all taking the wide tiles that
+only lists of this length use) plus sampled positions (random ones, the
+first and last elements of every tensor, and chunk edges) of every other
+tensor.  For the whole-tensor checks each tensor's inputs are generated a
+second time from their seeds (the generator is deterministic on the device),
+copied to the host, and stepped by the oracle with the GPU's coefficient.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_harness import NORM_REL_TOL, Step, check_bf16, check_f32, sample_indices, say
+from gpu_harness import (NORM_REL_TOL, Step, check_bf16, check_bf16_bitwise_first, check_f32,
+                         check_f32_bitwise_first, oracle_step_threads, sample_indices, say)
 from mixed_precision_sharded_amd import synth
 from mixed_precision_sharded_amd.configs import WORKLOADS, Workload, warm
 from mixed_precision_sharded_amd.synth import to_numpy
@@ -32,10 +38,61 @@ def _gpu_only():
     torch.cuda.empty_cache()
 
 
-def sampled_parity(w, per_tensor, seed, extra=(), clipped=True):
+def whole_tensor_parity(w, cols, i, c):
+    """Every element of tensor i after the step against the oracle stepped
+    from the tensor's regenerated inputs with the GPU's coefficient."""
+    fresh = synth.tensor_inputs(w, i, "cuda")
+    host = {k: to_numpy(fresh[k]).copy() for k in FIELDS + ("grad",)}
+    del fresh
+    pv = np.zeros(host["master"].size, np.uint16) if w.copy_bf16 else None
+    oracle_step_threads(host["master"], host["exp_avg"], host["exp_avg_sq"], host["grad"], pv, c,
+                        w.step, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
+    nbit = 0
+    for k in FIELDS:
+        nb, _ = check_f32_bitwise_first(to_numpy(cols[k][i]), host[k], f"{w.name} tensor {i} {k}")
+        nbit += nb
+    if w.copy_bf16:
+        nb, _ = check_bf16_bitwise_first(to_numpy(cols["param_bf16"][i]), pv,
+                                         f"{w.name} tensor {i} param_bf16")
+        nbit += nb
+    return host["master"].size, nbit
+
+
+def full_parity(w, clipped=True):
+    """Every element of every tensor of workload w against the oracle."""
+    say(f"workload {w.name}: {w.numel:,} params in {w.n_tensors} tensors; generating")
+    cols = synth.workload_inputs(w, "cuda")
+    torch.cuda.synchronize()
+    o = oracle.default()
+    S_ref = o.grad_norm_sq(to_numpy(g) for g in cols["grad"])
+    say(f"GPU step ({'clipped' if clipped else 'three calls'})")
+    st = Step(cols, completed_steps=w.step - 1)
+    if clipped:
+        st.clipped(w.max_norm, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
+    else:
+        st.full(w)
+    S, c, step = st.results()
+    assert step == w.step
+    assert abs(S - S_ref) <= NORM_REL_TOL * S_ref, (S, S_ref)
+    assert c == o.clip_coef(S, w.max_norm)
+    say(f"S={S:.9e} oracle {S_ref:.9e} rel {abs(S - S_ref) / S_ref:.2e} c={c}; "
+        "every element against the oracle")
+    n_checked = nbit = 0
+    for i in range(w.n_tensors):
+        n, nb = whole_tensor_parity(w, cols, i, c)
+        n_checked += n
+        nbit += nb
+    assert n_checked == w.numel
+    say(f"{n_checked:,} elements checked (master, m, v{', copy' if w.copy_bf16 else ''}); "
+        f"{nbit} not bitwise equal")
+    del st, cols
+
+
+def sampled_parity(w, per_tensor, seed, extra=(), clipped=True, whole=()):
     """`extra`: more element indices to check in every tensor (where they
     exist).  `clipped`: one adamw_clipped_step call, else grad_norm_sq with
-    the clip output followed by adamw_multi_tensor_step."""
+    the clip output followed by adamw_multi_tensor_step.  `whole`: tensors
+    checked on every element as well."""
     say(f"workload {w.name}: {w.numel:,} params in {w.n_tensors} tensors; generating")
     cols = synth.workload_inputs(w, "cuda")
     torch.cuda.synchronize()
@@ -79,24 +136,41 @@ def sampled_parity(w, per_tensor, seed, extra=(), clipped=True):
         n_checked += wv.size
         assert bool(torch.isfinite(cols["master"][i]).all()), i
     say(f"{n_checked:,} sampled elements checked; {nbit} not bitwise equal")
+    n_whole = nbit_whole = 0
+    for i in whole:
+        n, nb = whole_tensor_parity(w, cols, i, c)
+        n_whole += n
+        nbit_whole += nb
+    if whole:
+        say(f"{len(whole)} whole tensors, {n_whole:,} elements checked; {nbit_whole} not bitwise "
+            "equal")
     del st, cols
 
 
-def test_llama405b_share_sampled():
-    sampled_parity(WORKLOADS[5], per_tensor=2000, seed=50)
+def test_llama405b_share_every_element():
+    full_parity(WORKLOADS[5])
 
 
-def test_llama405b_share_warm_moments_sampled():
-    sampled_parity(warm(WORKLOADS[5]), per_tensor=2000, seed=51, clipped=False)
+def test_llama405b_share_warm_moments_every_element():
+    full_parity(warm(WORKLOADS[5]), clipped=False)
 
 
-def test_llama8b_full_list_sampled():
-    """8,030,261,248 parameters (128.5 GB of state) on one GPU."""
+def test_llama8b_full_list_sampled_and_whole_tensors():
+    """8,030,261,248 parameters (128.5 GB of state) on one GPU: sampled
+    elements of every tensor, and every element of the embedding, the first
+    and last layers (wq, wk, wv, wo, w1, w2, w3, both norms), the final norm
+    and the output head."""
+    w = WORKLOADS[3]
     free, total = torch.cuda.mem_get_info()
-    need = WORKLOADS[3].numel * WORKLOADS[3].state_bytes_per_param() + (8 << 30)
+    need = w.numel * w.state_bytes_per_param() + (16 << 30)
     if free < need:
         pytest.skip(f"needs {need / 2**30:.0f} GiB free, {free / 2**30:.0f} GiB available")
-    sampled_parity(WORKLOADS[3], per_tensor=20000, seed=52)
+    names = [name for name, _ in w.tensors]
+    whole = ([0] + [i for i, name in enumerate(names)
+                    if name.startswith("layers.0.") or name.startswith("layers.31.")] +
+             [names.index("norm"), names.index("output")])
+    assert len(whole) == 21
+    sampled_parity(w, per_tensor=20000, seed=52, whole=whole)
 
 
 # A single tensor of more than 2^31 elements: element offsets, chunk indices
