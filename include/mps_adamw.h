@@ -251,6 +251,40 @@ int adamw_clipped_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_
                        void* mid_event);
 
 /*
+ * adamw_clipped_step_noalloc — adamw_clipped_step for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same two launches and the same
+ * results, with the library's own workspace instead of the caller's.  That
+ * workspace is a device array of MPS_NOALLOC_WORKSPACE_BYTES (4 MiB) that the
+ * library holds on every GPU it runs on until the process ends; its address
+ * is looked up once per device, on the first call there.  The call makes no
+ * allocation of any kind (no hipMalloc, hipFree or pinned host memory).
+ *
+ *   Arguments as adamw_clipped_step, without d_workspace and workspace_bytes;
+ *   the current device must be the stream's device.
+ *   Lists whose tables need more than MPS_NOALLOC_WORKSPACE_BYTES (about 950K
+ *   chunks, or 60K tensors: every list of the shapes this library was
+ *   measured on fits) are refused with MPS_ERR_WORKSPACE before anything is
+ *   enqueued.
+ *   Every call on a GPU shares that GPU's array, which keeps the last call's
+ *   tables: calls that could overlap on one GPU (unordered streams, several
+ *   host threads) race and must be ordered by the caller.  A call whose list
+ *   differs from the one the array last held copies the new tables from host
+ *   memory the library holds (not pinned, so the runtime performs that copy
+ *   synchronously); a call with the same list enqueues the two launches and
+ *   nothing else, and may be captured in a graph.  Nothing in the array needs
+ *   clearing between calls: each upload writes every table and counter, and
+ *   each step's norm launch writes the partial sums its update reads.
+ */
+#define MPS_NOALLOC_WORKSPACE_BYTES (4u << 20)
+
+int adamw_clipped_step_noalloc(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
+                               double max_norm, double grad_scale, int skip_if_nonfinite,
+                               double* d_sumsq, float* d_coef, int32_t* d_step, double lr,
+                               double beta1, double beta2, double eps, double weight_decay,
+                               void* stream, void* mid_event);
+
+/*
  * adamw_fused_step — the whole step in ONE launch: the sum of squares, the
  * clip coefficient (with grad_scale folded in, exactly as clip_coef), the
  * optional skip on non-finite gradients, and the update of every tensor,

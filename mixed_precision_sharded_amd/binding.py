@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
             ctypes.c_double, ctypes.c_double, ctypes.c_double, P, ctypes.c_size_t, P]
         L.adamw_clipped_step.restype = ctypes.c_int
         L.adamw_clipped_step.argtypes = whole_step + [P]
+        L.adamw_clipped_step_noalloc.restype = ctypes.c_int
+        L.adamw_clipped_step_noalloc.argtypes = whole_step[:-3] + [P, P]
         L.adamw_fused_step.restype = ctypes.c_int
         L.adamw_fused_step.argtypes = whole_step
         L.adamw_fused_status.restype = ctypes.c_int
@@ -143,7 +145,8 @@ class TensorList:
 
     def __init__(self, masters: Sequence[torch.Tensor], exp_avgs: Sequence[torch.Tensor],
                  exp_avg_sqs: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
-                 params_bf16: Optional[Sequence[Optional[torch.Tensor]]] = None):
+                 params_bf16: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                 workspace: bool = True):
         n = len(masters)
         if not (len(exp_avgs) == len(exp_avg_sqs) == len(grads) == n) or n == 0:
             raise ValueError("masters, exp_avgs, exp_avg_sqs and grads: same non-zero length")
@@ -169,7 +172,12 @@ class TensorList:
         self.n = n
         self._refs = (list(masters), list(exp_avgs), list(exp_avg_sqs), list(grads),
                       list(params_bf16))
-        self._allocate_workspace(lib().adamw_workspace_bytes(self.array, n), "adamw_workspace_bytes")
+        if workspace:
+            self._allocate_workspace(lib().adamw_workspace_bytes(self.array, n),
+                                     "adamw_workspace_bytes")
+        else:  # for adamw_clipped_step_noalloc, which brings its own
+            self._ws_storage = None
+            self.workspace_ptr, self.workspace_bytes = None, 0
 
     def _allocate_workspace(self, nbytes: int, where: str) -> None:
         if nbytes == 0:
@@ -348,6 +356,30 @@ def adamw_clipped_step(tl: TensorList, step: torch.Tensor, lr: float, beta1: flo
     _whole_step("adamw_clipped_step", tl, step, lr, beta1, beta2, eps, weight_decay, max_norm,
                 grad_scale, skip_if_nonfinite, sumsq_out, coef_out, stream,
                 _event_handle(mid_event))
+
+
+def adamw_clipped_step_noalloc(tl: TensorList, step: torch.Tensor, lr: float, beta1: float,
+                               beta2: float, eps: float, weight_decay: float, max_norm: float,
+                               grad_scale: float = 1.0, skip_if_nonfinite: bool = False,
+                               sumsq_out: Optional[torch.Tensor] = None,
+                               coef_out: Optional[torch.Tensor] = None,
+                               stream: Optional[torch.cuda.Stream] = None,
+                               mid_event: Optional[torch.cuda.Event] = None) -> None:
+    """adamw_clipped_step on the library's own workspace (no allocation; see
+    the header).  `tl` may be built with workspace=False."""
+    if isinstance(tl, TensorList8):
+        raise TypeError("adamw_clipped_step_noalloc takes a TensorList")
+    if step.dtype != torch.int32 or step.device != tl.device:
+        raise ValueError("step: int32 tensor on the list's device")
+    if sumsq_out is not None and (sumsq_out.dtype != torch.float64 or sumsq_out.device != tl.device):
+        raise ValueError("sumsq_out: float64 tensor on the list's device, or None")
+    if coef_out is not None and (coef_out.dtype != torch.float32 or coef_out.device != tl.device):
+        raise ValueError("coef_out: float32 tensor on the list's device, or None")
+    _check(lib().adamw_clipped_step_noalloc(
+        tl.array, tl.n, tl.grad_dtype, float(max_norm), float(grad_scale),
+        1 if skip_if_nonfinite else 0, _ptr(sumsq_out), _ptr(coef_out), step.data_ptr(),
+        float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+        _stream_handle(stream), _event_handle(mid_event)), "adamw_clipped_step_noalloc")
 
 
 def _event_handle(event: Optional[torch.cuda.Event]):

@@ -24,6 +24,9 @@ namespace {
 using mps::TensorEntry;
 using mps::WorkspaceHeader;
 
+static_assert(mps::kScratchBytes == MPS_NOALLOC_WORKSPACE_BYTES,
+              "the header states the library-held workspace's size");
+
 thread_local std::string g_last_error;
 
 int fail(int code, const char* fmt, ...)
@@ -385,12 +388,23 @@ int staging_buffer(Uploaded& u, size_t bytes, Staging& out)
 // Make the workspace hold `plan`'s tables (stream-ordered), uploading them
 // only when the workspace last received different ones.  Never waits for
 // the device: the image goes through a pinned buffer, which is reused only
-// after its copy's event has completed.
-int ensure_uploaded(void* ws, Plan& plan, hipStream_t stream)
+// after its copy's event has completed.  `allocate` false: no staging buffer
+// is allocated; the copy then comes from the plan's own (pageable) image,
+// which the runtime copies synchronously, so the image may go right after.
+int ensure_uploaded(void* ws, Plan& plan, hipStream_t stream, bool allocate)
 {
     std::lock_guard<std::mutex> lock(g_cache_mutex);
     Uploaded& u = g_cache[ws];
     if (u.tag == plan.tag) return MPS_OK;
+    if (!allocate) {
+        u.tag = 0;
+        u.key.clear();
+        const hipError_t e =
+            hipMemcpyAsync(ws, plan.image.data(), plan.image.size(), hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "table upload: %s", hipGetErrorString(e));
+        u.tag = plan.tag;
+        return MPS_OK;
+    }
     int rc = reap_uploads(u);
     if (rc) return rc;
     Staging buf;
@@ -469,7 +483,7 @@ void set_key(std::vector<unsigned char>& key, const Tensor* tensors, int n, int 
 // back is never trusted.
 template <class Tensor>
 int prepare(const Tensor* tensors, int n, int grad_dtype, bool need_state, void* ws,
-            size_t ws_bytes, hipStream_t stream, Plan& plan)
+            size_t ws_bytes, hipStream_t stream, Plan& plan, bool allocate = true)
 {
     if (tensors && n > 0) {
         std::lock_guard<std::mutex> lock(g_cache_mutex);
@@ -484,7 +498,7 @@ int prepare(const Tensor* tensors, int n, int grad_dtype, bool need_state, void*
     int rc = plan_list(tensors, n, grad_dtype, need_state, plan);
     if (rc) return rc;
     if ((rc = check_workspace(ws, ws_bytes, plan))) return rc;
-    if ((rc = ensure_uploaded(ws, plan, stream))) return rc;
+    if ((rc = ensure_uploaded(ws, plan, stream, allocate))) return rc;
     std::lock_guard<std::mutex> lock(g_cache_mutex);
     Uploaded& u = g_cache[ws];
     set_key(u.key, tensors, n, grad_dtype);
@@ -637,6 +651,27 @@ int run_clipped(const Plan& plan, bool bf16, const int32_t* d_step, void* d_work
     return ok();
 }
 
+// The clipped step on a prepared workspace (the caller's or the library's).
+int clipped_step_on(const Plan& plan, mps_dtype grad_dtype, double max_norm, double grad_scale,
+                    int skip_if_nonfinite, double* d_sumsq, float* d_coef, int32_t* d_step,
+                    double lr, double beta1, double beta2, double eps, double weight_decay,
+                    void* d_workspace, hipStream_t stream_, void* mid_event)
+{
+    const bool bf16 = grad_dtype == MPS_DTYPE_BF16;
+    const mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
+    // Very long lists take the wide tiles (on fewer blocks).
+    const bool wide = plan.n_chunks >= mps::kStepWideMinChunks;
+    const int grid =
+        grid_for(plan.n_chunks, wide ? mps::kStepWideMaxBlocks : mps::kStepMaxBlocks);
+    return run_clipped(plan, bf16, d_step, d_workspace, stream_, mid_event,
+                       [&](const mps::WorkspaceView& ws, int norm_grid, hipStream_t st) {
+                           return mps::launch_clipped_step(ws, bf16, wide, grid, norm_grid,
+                                                           max_norm, grad_scale,
+                                                           skip_if_nonfinite ? 1 : 0, d_sumsq,
+                                                           d_coef, d_step, hp, st);
+                       });
+}
+
 }  // namespace
 
 extern "C" {
@@ -778,19 +813,42 @@ int adamw_clipped_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_
                       plan))) {
         return rc;
     }
-    const bool bf16 = grad_dtype == MPS_DTYPE_BF16;
-    const mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
-    // Very long lists take the wide tiles (on fewer blocks).
-    const bool wide = plan.n_chunks >= mps::kStepWideMinChunks;
-    const int grid =
-        grid_for(plan.n_chunks, wide ? mps::kStepWideMaxBlocks : mps::kStepMaxBlocks);
-    return run_clipped(plan, bf16, d_step, d_workspace, stream_, mid_event,
-                       [&](const mps::WorkspaceView& ws, int norm_grid, hipStream_t st) {
-                           return mps::launch_clipped_step(ws, bf16, wide, grid, norm_grid,
-                                                           max_norm, grad_scale,
-                                                           skip_if_nonfinite ? 1 : 0, d_sumsq,
-                                                           d_coef, d_step, hp, st);
-                       });
+    return clipped_step_on(plan, grad_dtype, max_norm, grad_scale, skip_if_nonfinite, d_sumsq,
+                           d_coef, d_step, lr, beta1, beta2, eps, weight_decay, d_workspace,
+                           stream_, mid_event);
+}
+
+int adamw_clipped_step_noalloc(const mps_tensor* tensors, int n_tensors, mps_dtype grad_dtype,
+                               double max_norm, double grad_scale, int skip_if_nonfinite,
+                               double* d_sumsq, float* d_coef, int32_t* d_step, double lr,
+                               double beta1, double beta2, double eps, double weight_decay,
+                               void* stream, void* mid_event)
+{
+    int rc = check_clipped_arguments(d_step, max_norm, grad_scale, lr, beta1, beta2, eps,
+                                     weight_decay);
+    if (rc) return rc;
+    int device = -1;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    void* scratch = nullptr;
+    if ((e = mps::scratch_address(device, &scratch)) != hipSuccess) {
+        return fail(MPS_ERR_DEVICE, "library workspace of device %d: %s", device,
+                    hipGetErrorString(e));
+    }
+    Plan plan;
+    hipStream_t stream_ = static_cast<hipStream_t>(stream);
+    rc = prepare(tensors, n_tensors, grad_dtype, true, scratch, mps::kScratchBytes, stream_, plan,
+                 /*allocate=*/false);
+    if (rc == MPS_ERR_WORKSPACE) {
+        return fail(MPS_ERR_WORKSPACE,
+                    "the list needs %zu bytes of workspace, more than the library's %zu "
+                    "(use adamw_clipped_step with a workspace of your own)",
+                    plan.total_bytes, mps::kScratchBytes);
+    }
+    if (rc) return rc;
+    return clipped_step_on(plan, grad_dtype, max_norm, grad_scale, skip_if_nonfinite, d_sumsq,
+                           d_coef, d_step, lr, beta1, beta2, eps, weight_decay, scratch, stream_,
+                           mid_event);
 }
 
 size_t adamw8_workspace_bytes(const mps_tensor8* tensors, int n_tensors)

@@ -82,6 +82,11 @@ hipError_t launch_fused_step(const WorkspaceView& ws, bool grad_bf16, int grid, 
 // and clears it.
 hipError_t launch_fused_status(WorkspaceHeader* header, uint32_t* d_error, hipStream_t stream);
 
+// The device address of the library-held workspace (kScratchBytes) on the
+// current device, `device`: looked up once per device, with that device
+// current, and kept.
+hipError_t scratch_address(int device, void** ptr);
+
 // 8-bit moment state (kernels_q8.hip).  `quant` is the QuantEntry table in
 // the same workspace; d_coef and d_skip_if_nonfinite are never NULL (as in
 // launch_adamw_step).

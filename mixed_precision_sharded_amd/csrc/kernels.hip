@@ -41,6 +41,8 @@
 // in source order; division and sqrt are the correctly rounded defaults.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -953,6 +955,33 @@ hipError_t launch_fused_status(WorkspaceHeader* header, uint32_t* d_error, hipSt
 {
     fused_status_kernel<<<1, kWave, 0, stream>>>(header, d_error);
     return hipGetLastError();
+}
+
+// ------------------------------------------------ library-held workspace ---
+
+// The workspace of adamw_clipped_step_noalloc, for callers that cannot
+// allocate device memory: a file-scope device array, one copy on every GPU
+// the library runs on, held until the process ends.  In host code its name
+// only stands for the symbol; its device address on each GPU comes from
+// hipGetSymbolAddress, called once per device with that device current, and
+// only that address is ever passed to a kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(int device, void** ptr)
+{
+    static std::mutex mutex;
+    static void* address[kScratchMaxDevices] = {};
+    if (device < 0 || device >= kScratchMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mutex);
+    if (!address[device]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        address[device] = p;
+    }
+    *ptr = address[device];
+    return hipSuccess;
 }
 
 }  // namespace mps

@@ -88,6 +88,12 @@ constexpr int64_t kChunkMax = MPS_CHUNK_MAX;
 constexpr int64_t kChunkTarget = MPS_CHUNK_TARGET;
 constexpr int64_t kNormCacheBudget = MPS_NORM_CACHE_BUDGET;
 
+// The library-held workspace of adamw_clipped_step_noalloc: one array of
+// this many bytes per GPU (enough for about 950K chunks, or 60K tensors;
+// MPS_NOALLOC_WORKSPACE_BYTES in the C header).
+constexpr size_t kScratchBytes = size_t{4} << 20;
+constexpr int kScratchMaxDevices = 64;
+
 struct alignas(64) WorkspaceHeader {
     // The single-launch step's outcome, decided once per launch k (low 32
     // bits of k) by whichever comes first: the last block to arrive at the

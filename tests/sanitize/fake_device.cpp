@@ -157,6 +157,12 @@ hipError_t hipMemcpyAsync(void* dst, const void* src, size_t bytes, hipMemcpyKin
 
 const char* hipGetErrorString(hipError_t) { return "fake device error"; }
 
+hipError_t hipGetDevice(int* device)
+{
+    *device = 0;
+    return hipSuccess;
+}
+
 }  // extern "C"
 
 namespace mps {
@@ -197,6 +203,7 @@ hipError_t launch_fused_step(const WorkspaceView& ws, bool, int, int, double, do
     return hipSuccess;
 }
 hipError_t launch_fused_status(WorkspaceHeader*, uint32_t*, hipStream_t) { return hipSuccess; }
+hipError_t scratch_address(int, void**) { return hipErrorInvalidDevice; }
 hipError_t launch_adamw8_step(const WorkspaceView& ws, const QuantEntry*, bool, int, const float*,
                               const double*, int32_t*, const HyperParams&, hipStream_t)
 {

@@ -28,6 +28,7 @@ hipError_t fused_grid_limit(bool, int*) { reached("fused_grid_limit"); }
 hipError_t launch_fused_step(const WorkspaceView&, bool, int, int, double, double, int, double*,
                              float*, int32_t*, const HyperParams&, uint32_t, hipStream_t) { reached("fused"); }
 hipError_t launch_fused_status(WorkspaceHeader*, uint32_t*, hipStream_t) { reached("fused_status"); }
+hipError_t scratch_address(int, void**) { reached("scratch_address"); }
 hipError_t launch_adamw8_step(const WorkspaceView&, const QuantEntry*, bool, int, const float*,
                               const double*, int32_t*, const HyperParams&, hipStream_t) { reached("adamw8"); }
 hipError_t launch_adamw8_clipped(const WorkspaceView&, const QuantEntry*, bool, int, int, double,

@@ -37,8 +37,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "adamw_workspace_bytes", "adamw_workspace_release", "grad_norm_sq", "clip_coef",
-        "adamw_multi_tensor_step", "adamw_clipped_step", "adamw_fused_step",
-        "adamw_fused_status", "adamw_last_error",
+        "adamw_multi_tensor_step", "adamw_clipped_step", "adamw_clipped_step_noalloc",
+        "adamw_fused_step", "adamw_fused_status", "adamw_last_error",
         "adamw8_workspace_bytes", "adamw8_grad_norm_sq", "adamw8_multi_tensor_step",
         "adamw8_clipped_step",
         "adamw8_quantize", "adamw8_dequantize"])
@@ -279,3 +279,14 @@ def test_fused_status_rejects_bad_arguments(lib):
     assert lib.adamw_fused_status(P(0x7f0000000010), 4096, P(0x1000), None) == EWORKSPACE
     assert lib.adamw_fused_status(P(0x7f0000000000), 32, P(0x1000), None) == EWORKSPACE
     assert "too small" in binding.last_error()
+
+
+def test_noalloc_step_checks_arguments_before_the_device(lib):
+    arr = fake_list(2, 1000)
+    args = [arr, 2, binding.MPS_DTYPE_F32, 1.0, 1.0, 0, None, None]
+    hp = [3e-4, 0.9, 0.95, 1e-8, 0.1, None, None]
+    assert lib.adamw_clipped_step_noalloc(*args, None, *hp) == EINVAL  # no step counter
+    assert "d_step" in binding.last_error()
+    bad_hp = [3e-4, 1.5, 0.95, 1e-8, 0.1, None, None]
+    assert lib.adamw_clipped_step_noalloc(*args, ctypes.c_void_p(0x1000), *bad_hp) == EINVAL
+    assert "beta1" in binding.last_error()

@@ -1,0 +1,97 @@
+"""GPU: adamw_clipped_step_noalloc (the clipped step on the library-held
+workspace, for callers that cannot allocate) against adamw_clipped_step on
+a workspace of the caller's, through the C ABI, on identical inputs: two
+calls in a row on different lists, the second smaller, then the second list
+again (its tables are still in the array).  S, the coefficient, the counter
+and every element of master, m, v and the bf16 copy must be bitwise equal
+(the same kernels, grids and summation order), and the no-alloc results are
+also checked against the oracle (relative error <= 2e-6, bf16 copy <= 1 ulp).
+A list whose tables exceed the array is refused before anything runs."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_harness import NORM_REL_TOL, Step, compare_state, host_copy, oracle_norm, oracle_step, say
+from mixed_precision_sharded_amd import binding
+from test_gpu_parity import HP, make_cols
+
+pytestmark = pytest.mark.gpu
+
+FIELDS = ("master", "exp_avg", "exp_avg_sq", "grad", "param_bf16")
+
+
+@pytest.fixture(autouse=True)
+def _gpu_only():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def clone(cols):
+    return {k: [None if t is None else t.clone() for t in v] for k, v in cols.items()}
+
+
+def noalloc_against_workspace_step(cols, t, what):
+    twin = clone(cols)
+    host = host_copy(cols)
+    hp = (HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+
+    ref = Step(cols, completed_steps=t - 1)
+    ref.clipped(1.0, *hp)
+    S_ref, c_ref, t_ref = ref.results()
+
+    dev = twin["master"][0].device
+    tl = binding.TensorList(*(twin[k] for k in FIELDS), workspace=False)
+    sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+    coef = torch.zeros(1, dtype=torch.float32, device=dev)
+    step = torch.tensor([t - 1], dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    allocated = torch.cuda.memory_allocated()
+    binding.adamw_clipped_step_noalloc(tl, step, *hp, 1.0, sumsq_out=sumsq, coef_out=coef)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == allocated, "the call allocated through torch"
+    S, c, t_got = float(sumsq.item()), np.float32(coef.item()), int(step.item())
+
+    say(f"[no-alloc {what}] S={S:.9e} (workspace step {S_ref:.9e}) c={c} t={t_got}")
+    assert np.float64(S).view(np.int64) == np.float64(S_ref).view(np.int64), (S, S_ref)
+    assert c.view(np.int32) == c_ref.view(np.int32) and t_got == t_ref == t
+    for k in ("master", "exp_avg", "exp_avg_sq", "param_bf16"):
+        for i, (x, y) in enumerate(zip(twin[k], cols[k])):
+            if x is None:
+                continue
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (what, k, i)
+
+    # The bar against the oracle as well (its own norm and, given the GPU's
+    # coefficient, its update).
+    S_o = oracle_norm(host["grad"])
+    assert abs(S - S_o) <= NORM_REL_TOL * S_o
+    oracle_step(host, c, t, *hp)
+    stats = compare_state(twin, host, f"no-alloc {what}")
+    assert stats["w"][0] == stats["m"][0] == stats["v"][0] == 0
+    return twin
+
+
+def test_noalloc_equals_the_workspace_step_on_consecutive_lists():
+    big = make_cols([300001, 5, 77, 0, 4096, 1 << 20], True, True, seed=70)
+    noalloc_against_workspace_step(big, t=3, what="first list, 1.35M params, bf16 + copy")
+    small = make_cols([70001, 3], False, False, seed=71)
+    after = noalloc_against_workspace_step(small, t=1, what="second list, smaller, fp32")
+    # The same (smaller) list once more: its tables are already in the array.
+    noalloc_against_workspace_step(after, t=2, what="second list again")
+
+
+def test_noalloc_refuses_a_list_beyond_its_workspace():
+    n = 70000  # 64 bytes of table per tensor: 4.5 MB > 4 MiB
+    dev = torch.device("cuda")
+    flat = torch.zeros(n, device=dev)
+    grads = torch.zeros(n, dtype=torch.bfloat16, device=dev)
+    views = [flat[i:i + 1] for i in range(n)]
+    tl = binding.TensorList(views, views, views, [grads[i:i + 1] for i in range(n)],
+                            workspace=False)
+    step = torch.zeros(1, dtype=torch.int32, device=dev)
+    with pytest.raises(binding.MpsError) as err:
+        binding.adamw_clipped_step_noalloc(tl, step, *(3e-4, 0.9, 0.95, 1e-8, 0.1), 1.0)
+    assert err.value.code == -28 and "more than the library's" in str(err.value)
+    torch.cuda.synchronize()
+    assert int(step.item()) == 0
