@@ -262,10 +262,11 @@ int adamw_clipped_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_
  *
  *   Arguments as adamw_clipped_step, without d_workspace and workspace_bytes;
  *   the current device must be the stream's device.
- *   Lists whose tables need more than MPS_NOALLOC_WORKSPACE_BYTES (about 950K
- *   chunks, or 60K tensors: every list of the shapes this library was
- *   measured on fits) are refused with MPS_ERR_WORKSPACE before anything is
- *   enqueued.
+ *   Lists whose tables need more than MPS_NOALLOC_WORKSPACE_BYTES (about 1M
+ *   chunks — a shard of up to 2^30 parameters has at most 262K, a whole
+ *   model of 17e9 parameters 1M — or 60K tensors: every list of the shapes
+ *   this library was measured on fits, the 8.03e9-parameter one included)
+ *   are refused with MPS_ERR_WORKSPACE before anything is enqueued.
  *   Every call on a GPU shares that GPU's array, which keeps the last call's
  *   tables: calls that could overlap on one GPU (unordered streams, several
  *   host threads) race and must be ordered by the caller.  A call whose list

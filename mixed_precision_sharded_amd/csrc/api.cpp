@@ -65,15 +65,16 @@ struct Plan {
     mps::SoloEntry solo{};  // its entry, passed with every launch
     mps::QuantEntry solo_quant{};  // an 8-bit list: its 8-bit state
     int64_t chunk_elems = 0;
+    bool large = false;     // an fp32-state list of at least kLargeListElems elements
     uint64_t tag = 0;
 };
 
-int64_t pick_chunk_elems(int64_t total)
+int64_t pick_chunk_elems(int64_t total, int64_t max_elems)
 {
     int64_t c = total / mps::kChunkTarget;
     c = (c / mps::kChunkQuantum) * mps::kChunkQuantum;
     if (c < mps::kChunkMin) c = mps::kChunkMin;
-    if (c > mps::kChunkMax) c = mps::kChunkMax;
+    if (c > max_elems) c = max_elems;
     return c;
 }
 
@@ -128,7 +129,9 @@ int layout_plan(std::vector<TensorEntry>& entries, const std::vector<mps::QuantE
                 int64_t total, Plan& plan)
 {
     const int n = static_cast<int>(entries.size());
-    plan.chunk_elems = pick_chunk_elems(total);
+    plan.large = !quant && total >= mps::kLargeListElems;
+    plan.chunk_elems = pick_chunk_elems(
+        total, quant ? mps::kQ8ChunkMax : (plan.large ? mps::kLargeChunkMax : mps::kChunkMax));
     int64_t n_chunks = 0;
     for (TensorEntry& e : entries) {
         e.first_chunk = static_cast<int32_t>(n_chunks);
@@ -553,6 +556,19 @@ int grid_for(int n_chunks, int cap)
     return (n_chunks + per_block - 1) / per_block;
 }
 
+// The fp32-state update's grid: for a whole-model list at most
+// kLargeMaxBlocks; for a shard one block per chunk up to kStepSpreadChunks
+// chunks (its step is bound by latency: the fewer chunks one block walks in
+// turn, the shorter), else at most one block per CU.  Every block walks the
+// same number of chunks but the last.
+int step_grid(const Plan& plan)
+{
+    const int n_chunks = plan.n_chunks;
+    if (plan.large) return grid_for(n_chunks, mps::kLargeMaxBlocks);
+    return n_chunks <= mps::kStepSpreadChunks ? std::max(n_chunks, 1)
+                                              : grid_for(n_chunks, mps::kStepMaxBlocks);
+}
+
 bool finite_in(double x, double lo, double hi_exclusive)
 {
     return std::isfinite(x) && x >= lo && x < hi_exclusive;
@@ -659,13 +675,10 @@ int clipped_step_on(const Plan& plan, mps_dtype grad_dtype, double max_norm, dou
 {
     const bool bf16 = grad_dtype == MPS_DTYPE_BF16;
     const mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
-    // Very long lists take the wide tiles (on fewer blocks).
-    const bool wide = plan.n_chunks >= mps::kStepWideMinChunks;
-    const int grid =
-        grid_for(plan.n_chunks, wide ? mps::kStepWideMaxBlocks : mps::kStepMaxBlocks);
+    const int grid = step_grid(plan);
     return run_clipped(plan, bf16, d_step, d_workspace, stream_, mid_event,
                        [&](const mps::WorkspaceView& ws, int norm_grid, hipStream_t st) {
-                           return mps::launch_clipped_step(ws, bf16, wide, grid, norm_grid,
+                           return mps::launch_clipped_step(ws, bf16, plan.large, grid, norm_grid,
                                                            max_norm, grad_scale,
                                                            skip_if_nonfinite ? 1 : 0, d_sumsq,
                                                            d_coef, d_step, hp, st);
@@ -741,9 +754,9 @@ int adamw_multi_tensor_step(const mps_tensor* tensors, int n_tensors, mps_dtype 
         return rc;
     }
     mps::HyperParams hp{lr, beta1, beta2, eps, weight_decay};
-    const int grid = grid_for(plan.n_chunks, mps::kStepMaxBlocks);
+    const int grid = step_grid(plan);
     hipError_t e = mps::launch_adamw_step(
-        view_of(d_workspace, plan), grad_dtype == MPS_DTYPE_BF16, grid,
+        view_of(d_workspace, plan), grad_dtype == MPS_DTYPE_BF16, plan.large, grid,
         coef_or_one(d_coef, d_workspace, plan),
         skip_or_zero(d_skip_if_nonfinite, d_workspace, plan), d_step, hp, st);
     if (e != hipSuccess) return fail(MPS_ERR_DEVICE, "adamw_step launch: %s", hipGetErrorString(e));

@@ -12,8 +12,8 @@
 
 #include "layout.h"
 
-#ifndef MPS_STEP_UNROLL
-#define MPS_STEP_UNROLL 1   // groups of four elements per thread per tile
+#ifndef MPS_FUSED_STEP_UNROLL
+#define MPS_FUSED_STEP_UNROLL 1   // the single-launch step: groups of four per thread per tile
 #endif
 #ifndef MPS_NORM_UNROLL
 #define MPS_NORM_UNROLL 4   // 16-byte vectors per thread per tile (two tiles in flight)

@@ -54,15 +54,15 @@ hipError_t launch_clip_coef(const double* d_sumsq, double max_norm, double grad_
 
 // d_coef and d_skip_if_nonfinite are never NULL here: the library passes
 // the workspace's constants (1 and 0) for inputs the caller left out.
-hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, int grid,
+// `large`: a whole-model list (MPS_LARGE_LIST_ELEMS elements or more), whose
+// update takes MPS_LARGE_UNROLL groups of four per thread per tile.
+hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, bool large, int grid,
                              const float* d_coef, const double* d_skip_if_nonfinite,
                              int32_t* d_step, const HyperParams& hp, hipStream_t stream);
 
 // The update that finishes the norm from the `n_partials` partials a
 // launch_grad_norm_partials of grid n_partials left in the workspace.
-// `wide`: tiles of MPS_STEP_WIDE_UNROLL groups of four per thread (for very
-// long lists, with a grid of at most kStepWideMaxBlocks).
-hipError_t launch_clipped_step(const WorkspaceView& ws, bool grad_bf16, bool wide, int grid,
+hipError_t launch_clipped_step(const WorkspaceView& ws, bool grad_bf16, bool large, int grid,
                                int n_partials, double max_norm, double grad_scale,
                                int skip_if_nonfinite, double* d_sumsq, float* d_coef,
                                int32_t* d_step, const HyperParams& hp, hipStream_t stream);

@@ -859,50 +859,63 @@ hipError_t launch_clip_coef(const double* d_sumsq, double max_norm, double grad_
     return hipGetLastError();
 }
 
-hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, int grid,
-                             const float* d_coef, const double* d_skip_if_nonfinite,
-                             int32_t* d_step, const HyperParams& hp, hipStream_t stream)
-{
-    if (grad_bf16) {
-        adamw_step_kernel<true, MPS_STEP_UNROLL><<<grid, kBlock, 0, stream>>>(
-            ws, d_coef, d_skip_if_nonfinite, d_step, hp);
-    } else {
-        adamw_step_kernel<false, MPS_STEP_UNROLL><<<grid, kBlock, 0, stream>>>(
-            ws, d_coef, d_skip_if_nonfinite, d_step, hp);
-    }
-    return hipGetLastError();
-}
-
 namespace {
 
-template <int kUnroll>
-void clipped_launch(const WorkspaceView& ws, bool grad_bf16, int grid, int n_partials,
-                    double max_norm, double grad_scale, int skip_if_nonfinite, double* d_sumsq,
-                    float* d_coef, int32_t* d_step, const HyperParams& hp, hipStream_t stream)
+// The update kernels' tile depth (groups of four per thread): a whole-model
+// list's, or a shard's by gradient type.
+template <bool kBf16, bool kLarge>
+constexpr int step_unroll()
 {
-    if (grad_bf16) {
-        adamw_clipped_kernel<true, kUnroll><<<grid, kBlock, 0, stream>>>(
-            ws, n_partials, max_norm, grad_scale, skip_if_nonfinite, d_sumsq, d_coef, d_step, hp);
-    } else {
-        adamw_clipped_kernel<false, kUnroll><<<grid, kBlock, 0, stream>>>(
-            ws, n_partials, max_norm, grad_scale, skip_if_nonfinite, d_sumsq, d_coef, d_step, hp);
-    }
+    return kLarge ? MPS_LARGE_UNROLL : (kBf16 ? MPS_STEP_UNROLL_BF16 : MPS_STEP_UNROLL_F32);
+}
+
+template <bool kBf16, bool kLarge>
+void step_launch(const WorkspaceView& ws, int grid, const float* d_coef,
+                 const double* d_skip_if_nonfinite, int32_t* d_step, const HyperParams& hp,
+                 hipStream_t stream)
+{
+    adamw_step_kernel<kBf16, step_unroll<kBf16, kLarge>()><<<grid, kBlock, 0, stream>>>(
+        ws, d_coef, d_skip_if_nonfinite, d_step, hp);
+}
+
+template <bool kBf16, bool kLarge>
+void clipped_launch(const WorkspaceView& ws, int grid, int n_partials, double max_norm,
+                    double grad_scale, int skip_if_nonfinite, double* d_sumsq, float* d_coef,
+                    int32_t* d_step, const HyperParams& hp, hipStream_t stream)
+{
+    adamw_clipped_kernel<kBf16, step_unroll<kBf16, kLarge>()><<<grid, kBlock, 0, stream>>>(
+        ws, n_partials, max_norm, grad_scale, skip_if_nonfinite, d_sumsq, d_coef, d_step, hp);
 }
 
 }  // namespace
 
-hipError_t launch_clipped_step(const WorkspaceView& ws, bool grad_bf16, bool wide, int grid,
+hipError_t launch_adamw_step(const WorkspaceView& ws, bool grad_bf16, bool large, int grid,
+                             const float* d_coef, const double* d_skip_if_nonfinite,
+                             int32_t* d_step, const HyperParams& hp, hipStream_t stream)
+{
+    if (grad_bf16) {
+        (large ? step_launch<true, true> : step_launch<true, false>)(
+            ws, grid, d_coef, d_skip_if_nonfinite, d_step, hp, stream);
+    } else {
+        (large ? step_launch<false, true> : step_launch<false, false>)(
+            ws, grid, d_coef, d_skip_if_nonfinite, d_step, hp, stream);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_clipped_step(const WorkspaceView& ws, bool grad_bf16, bool large, int grid,
                                int n_partials, double max_norm, double grad_scale,
                                int skip_if_nonfinite, double* d_sumsq, float* d_coef,
                                int32_t* d_step, const HyperParams& hp, hipStream_t stream)
 {
-    if (wide) {
-        clipped_launch<MPS_STEP_WIDE_UNROLL>(ws, grad_bf16, grid, n_partials, max_norm,
-                                             grad_scale, skip_if_nonfinite, d_sumsq, d_coef,
-                                             d_step, hp, stream);
+    if (grad_bf16) {
+        (large ? clipped_launch<true, true> : clipped_launch<true, false>)(
+            ws, grid, n_partials, max_norm, grad_scale, skip_if_nonfinite, d_sumsq, d_coef,
+            d_step, hp, stream);
     } else {
-        clipped_launch<MPS_STEP_UNROLL>(ws, grad_bf16, grid, n_partials, max_norm, grad_scale,
-                                        skip_if_nonfinite, d_sumsq, d_coef, d_step, hp, stream);
+        (large ? clipped_launch<false, true> : clipped_launch<false, false>)(
+            ws, grid, n_partials, max_norm, grad_scale, skip_if_nonfinite, d_sumsq, d_coef,
+            d_step, hp, stream);
     }
     return hipGetLastError();
 }
@@ -912,7 +925,7 @@ namespace {
 template <bool kBf16>
 auto fused_kernel()
 {
-    return adamw_fused_kernel<kBf16, MPS_NORM_UNROLL, MPS_STEP_UNROLL>;
+    return adamw_fused_kernel<kBf16, MPS_NORM_UNROLL, MPS_FUSED_STEP_UNROLL>;
 }
 
 }  // namespace

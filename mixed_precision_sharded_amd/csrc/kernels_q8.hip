@@ -260,8 +260,10 @@ __device__ __forceinline__ void adamw8_elements(const Entry* te, const QuantEntr
 // each wavefront writes 64 contiguous bytes per moment instead of 16-byte
 // pieces.  Two buffers alternate between consecutive bodies of a block: the
 // barrier that ends one body also separates the readers of a buffer from the
-// writers of the body after next.
-constexpr int kMaxRunsPerBody = MPS_CHUNK_MAX / kQuantBlock;
+// writers of the body after next.  A body is at most one chunk of an 8-bit
+// list, whose chunks are at most kQ8ChunkMax elements (the host's plan).
+constexpr int kMaxRunsPerBody = static_cast<int>(kQ8ChunkMax / kQuantBlock);
+static_assert(kQ8ChunkMax % kQuantBlock == 0, "a chunk of an 8-bit list holds whole runs");
 
 // The two pairs of scale-byte buffers (m, v) that consecutive bodies of a
 // block alternate between, one LDS allocation however often this is inlined.

@@ -21,36 +21,67 @@ namespace mps {
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X).
 // Both kernels walk the chunks with a persistent grid (block b takes chunks
 // b, b + G, ...): long-lived waves streaming neighbouring addresses beat one
-// block per chunk on MI355X's HBM3E.  Measured: 1 norm block per CU; for the
-// fp32-state update up to 5 blocks per CU (with the grid a whole number of
-// blocks per CU: 2.5 per CU was 5 % slower), for the 8-bit update 3.
+// block per chunk on MI355X's HBM3E.  The update's grid, chunk size and tile
+// depth were measured with library builds side by side in one process, on
+// the workloads' own inputs (random values, one allocation per tensor), in
+// three fresh processes each (the placement of the allocations moves every
+// figure by up to 5 %, and the ranking of close variants with it):
+//   - one GPU's shard (the 8B shard, the 70B and 405B shares): one block per
+//     CU (256) with 4096-element chunks streamed 5.8-6.3 % faster than the
+//     earlier 1280 blocks with 16384; 512, 768 and 1280 blocks and
+//     8192-element chunks were slower on most shards;
+//   - a whole model (the 8B-parameter list, 291 tensors): the wide walk wins
+//     instead, 1280 blocks with 16384-element chunks, 1.0-2.0 % faster than
+//     768 blocks and 3-5 % faster than 256 (on buffers carved from one
+//     allocation the order was reversed, so the choice follows the
+//     workloads' own layout);
+//   - a small list, whose step is latency-bound, is spread one chunk per
+//     block.
 #ifndef MPS_NORM_MAX_BLOCKS
 #define MPS_NORM_MAX_BLOCKS 256    // norm grid cap (= number of fp64 partials)
 #endif
 #ifndef MPS_STEP_MAX_BLOCKS
-#define MPS_STEP_MAX_BLOCKS 1280   // update grid cap
+#define MPS_STEP_MAX_BLOCKS 256    // update grid cap for a shard: one block per CU
 #endif
-// Lists of at least MPS_STEP_WIDE_MIN_CHUNKS chunks (about 64 per block at
-// the cap above) take the clipped update with tiles of
-// MPS_STEP_WIDE_UNROLL groups of four per thread, on at most
-// MPS_STEP_WIDE_MAX_BLOCKS blocks (their registers allow 3 blocks per CU).
-// Measured on the 8B-parameter list (490K chunks): 43.2 -> 40.8 ms per step;
-// the same tiles slowed the 62.7M-parameter shard and the 70B and 405B
-// shares (3.8K-48K chunks) by 0.6-1 %.
-#ifndef MPS_STEP_WIDE_MIN_CHUNKS
-#define MPS_STEP_WIDE_MIN_CHUNKS 81920
+#ifndef MPS_STEP_SPREAD_CHUNKS
+#define MPS_STEP_SPREAD_CHUNKS 1280  // lists of at most this many chunks: one block per chunk
 #endif
-#ifndef MPS_STEP_WIDE_UNROLL
-#define MPS_STEP_WIDE_UNROLL 2
+// Lists of at least MPS_LARGE_LIST_ELEMS elements (a whole model rather
+// than one GPU's shard of it) walk wider: at most MPS_LARGE_MAX_BLOCKS
+// blocks, chunks of at most MPS_LARGE_CHUNK_MAX elements, tiles of
+// MPS_LARGE_UNROLL groups of four per thread.
+#ifndef MPS_LARGE_LIST_ELEMS
+#define MPS_LARGE_LIST_ELEMS (1ll << 30)
 #endif
-#ifndef MPS_STEP_WIDE_MAX_BLOCKS
-#define MPS_STEP_WIDE_MAX_BLOCKS 768
+#ifndef MPS_LARGE_MAX_BLOCKS
+#define MPS_LARGE_MAX_BLOCKS 1280
+#endif
+#ifndef MPS_LARGE_CHUNK_MAX
+#define MPS_LARGE_CHUNK_MAX 16384
+#endif
+#ifndef MPS_LARGE_UNROLL
+#define MPS_LARGE_UNROLL 1
+#endif
+// Groups of four elements per thread per tile of a shard's update, by
+// gradient type (two tiles are in flight): two for bf16 gradients (the 405B
+// share 3.3 % faster than with one), one for fp32.
+#ifndef MPS_STEP_UNROLL_BF16
+#define MPS_STEP_UNROLL_BF16 2
+#endif
+#ifndef MPS_STEP_UNROLL_F32
+#define MPS_STEP_UNROLL_F32 1
 #endif
 #ifndef MPS_CHUNK_MIN
 #define MPS_CHUNK_MIN 2048
 #endif
+// Chunk sizes of a shard's fp32-state list (above) and of an 8-bit-moment
+// list: those keep 16384, their update (768 blocks, three per CU) measured up
+// to 3.4 % slower with 4096.
 #ifndef MPS_CHUNK_MAX
-#define MPS_CHUNK_MAX 16384
+#define MPS_CHUNK_MAX 4096
+#endif
+#ifndef MPS_Q8_CHUNK_MAX
+#define MPS_Q8_CHUNK_MAX 16384
 #endif
 #ifndef MPS_CHUNK_TARGET
 #define MPS_CHUNK_TARGET 3072       // aim for about this many chunks
@@ -75,8 +106,10 @@ namespace mps {
 constexpr int kBlock = 256;                        // threads per block, all kernels
 constexpr int kNormMaxBlocks = MPS_NORM_MAX_BLOCKS;
 constexpr int kStepMaxBlocks = MPS_STEP_MAX_BLOCKS;
-constexpr int kStepWideMinChunks = MPS_STEP_WIDE_MIN_CHUNKS;
-constexpr int kStepWideMaxBlocks = MPS_STEP_WIDE_MAX_BLOCKS;
+constexpr int kStepSpreadChunks = MPS_STEP_SPREAD_CHUNKS;
+constexpr int64_t kLargeListElems = MPS_LARGE_LIST_ELEMS;
+constexpr int kLargeMaxBlocks = MPS_LARGE_MAX_BLOCKS;
+constexpr int64_t kLargeChunkMax = MPS_LARGE_CHUNK_MAX;
 constexpr int kFusedMaxBlocks = MPS_FUSED_MAX_BLOCKS;
 constexpr int kQ8MaxBlocks = MPS_Q8_MAX_BLOCKS;
 constexpr int kPartials = kNormMaxBlocks > kFusedMaxBlocks ? kNormMaxBlocks : kFusedMaxBlocks;
@@ -85,12 +118,14 @@ constexpr int kTicketStride = 32;                  // uint32s between tickets (1
 constexpr int64_t kChunkQuantum = 2048;            // chunk sizes are multiples of this
 constexpr int64_t kChunkMin = MPS_CHUNK_MIN;
 constexpr int64_t kChunkMax = MPS_CHUNK_MAX;
+constexpr int64_t kQ8ChunkMax = MPS_Q8_CHUNK_MAX;
 constexpr int64_t kChunkTarget = MPS_CHUNK_TARGET;
 constexpr int64_t kNormCacheBudget = MPS_NORM_CACHE_BUDGET;
 
 // The library-held workspace of adamw_clipped_step_noalloc: one array of
-// this many bytes per GPU (enough for about 950K chunks, or 60K tensors;
-// MPS_NOALLOC_WORKSPACE_BYTES in the C header).
+// this many bytes per GPU (enough for about 1M chunks — a shard of up to
+// 2^30 parameters has at most 262K, a whole model of 17e9 parameters 1M —
+// or 60K tensors; MPS_NOALLOC_WORKSPACE_BYTES in the C header).
 constexpr size_t kScratchBytes = size_t{4} << 20;
 constexpr int kScratchMaxDevices = 64;
 

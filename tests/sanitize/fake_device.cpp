@@ -179,7 +179,7 @@ hipError_t launch_grad_norm_partials(const WorkspaceView& ws, bool, int, int, co
     return hipSuccess;
 }
 hipError_t launch_clip_coef(const double*, double, double, float*, hipStream_t) { return hipSuccess; }
-hipError_t launch_adamw_step(const WorkspaceView& ws, bool, int, const float*, const double*,
+hipError_t launch_adamw_step(const WorkspaceView& ws, bool, bool, int, const float*, const double*,
                              int32_t*, const HyperParams&, hipStream_t)
 {
     enqueue_launch(ws);

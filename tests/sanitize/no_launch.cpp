@@ -20,7 +20,7 @@ hipError_t launch_grad_norm(const WorkspaceView&, bool, int, int, double*, doubl
 hipError_t launch_grad_norm_partials(const WorkspaceView&, bool, int, int, const int32_t*,
                                      hipStream_t) { reached("grad_norm_partials"); }
 hipError_t launch_clip_coef(const double*, double, double, float*, hipStream_t) { reached("clip"); }
-hipError_t launch_adamw_step(const WorkspaceView&, bool, int, const float*, const double*,
+hipError_t launch_adamw_step(const WorkspaceView&, bool, bool, int, const float*, const double*,
                              int32_t*, const HyperParams&, hipStream_t) { reached("adamw_step"); }
 hipError_t launch_clipped_step(const WorkspaceView&, bool, bool, int, int, double, double, int, double*,
                                float*, int32_t*, const HyperParams&, hipStream_t) { reached("clipped"); }

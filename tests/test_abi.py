@@ -69,7 +69,7 @@ def test_workspace_bytes(lib):
     # chunk tables grow with the parameter count, the fixed part does not
     big = lib.adamw_workspace_bytes(fake_list(3, 50_000_000), 3)
     assert big > size
-    assert big < 50_000_000 * 3 // 1000  # far below one byte per parameter
+    assert big < 50_000_000 * 3 // 900  # a 4-byte map slot per chunk of 4096: ~1 B per 1000
 
 
 def test_workspace_bytes_rejects_bad_lists(lib):

@@ -20,11 +20,12 @@ from test_gpu_q8 import oracle_step as oracle_step8
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
-# 2048 elements per chunk for lists this size; the fp32 update's grid is at
-# most 1280 blocks (one chunk each up to 1280 chunks, then two or more), the
-# 8-bit update's 768, the norm's 256.
+# 2048 elements per chunk for lists below 12,582,912 elements, 4096 from
+# there; the fp32 update's grid is one block per chunk up to 1280 chunks,
+# then at most 256 blocks (one per CU) walking several chunks each; the
+# 8-bit update's grid is at most 768 blocks, the norm's 256.
 SIZES = [1, 5, 2047, 2048, 2049, 3 * 2048 + 17, 256 * 2048 + 1, 768 * 2048 + 33,
-         1280 * 2048 - 3, 1280 * 2048 + 5, 2560 * 2048 + 2049]
+         1280 * 2048 - 3, 1280 * 2048 + 5, 2560 * 2048 + 2049, 12582912 + 4097]
 
 
 @pytest.fixture(autouse=True)

@@ -6,8 +6,7 @@ The sum of squares is checked against the oracle over every gradient.  The
 update is checked against the oracle on EVERY element of the 405B share
 (792.7M parameters, 1137 tensors) and, for the 8B-parameter list, on every
 element of whole tensors (the embedding, the first and last layers, the
-final norm, the output head: 1.5e9 elements, all taking the wide tiles that
-only lists of this length use) plus sampled positions (random ones, the
+final norm, the output head: 1.5e9 elements) plus sampled positions (random ones, the
 first and last elements of every tensor, and chunk edges) of every other
 tensor.  For the whole-tensor checks each tensor's inputs are generated a
 second time from their seeds (the generator is deterministic on the device),

@@ -7,6 +7,8 @@ and every element of master, m, v and the bf16 copy must be bitwise equal
 (the same kernels, grids and summation order), and the no-alloc results are
 also checked against the oracle (relative error <= 2e-6, bf16 copy <= 1 ulp).
 A list whose tables exceed the array is refused before anything runs."""
+from types import SimpleNamespace
+
 import numpy as np
 import pytest
 import torch
@@ -82,13 +84,20 @@ def test_noalloc_equals_the_workspace_step_on_consecutive_lists():
 
 
 def test_noalloc_refuses_a_list_beyond_its_workspace():
-    n = 70000  # 64 bytes of table per tensor: 4.5 MB > 4 MiB
+    """270,000 one-element tensors need 64 bytes of table each: 17.3 MB, more
+    than the 4 MiB array.  The records point into one real buffer (nothing
+    would be touched anyway: the call is refused before anything is
+    enqueued)."""
+    n = 270000
     dev = torch.device("cuda")
-    flat = torch.zeros(n, device=dev)
+    buf = torch.zeros(4 * n, device=dev)
     grads = torch.zeros(n, dtype=torch.bfloat16, device=dev)
-    views = [flat[i:i + 1] for i in range(n)]
-    tl = binding.TensorList(views, views, views, [grads[i:i + 1] for i in range(n)],
-                            workspace=False)
+    arr = (binding.MpsTensor * n)()
+    w0, g0 = buf.data_ptr(), grads.data_ptr()
+    for i in range(n):
+        arr[i] = binding.MpsTensor(w0 + 4 * i, w0 + 4 * (n + i), w0 + 4 * (2 * n + i),
+                                   g0 + 2 * i, None, 1)
+    tl = SimpleNamespace(array=arr, n=n, grad_dtype=binding.MPS_DTYPE_BF16, device=buf.device)
     step = torch.zeros(1, dtype=torch.int32, device=dev)
     with pytest.raises(binding.MpsError) as err:
         binding.adamw_clipped_step_noalloc(tl, step, *(3e-4, 0.9, 0.95, 1e-8, 0.1), 1.0)
