@@ -16,7 +16,8 @@ on a bounded sample on the host (one thread, then all threads).
 The default workload is the largest one that fits one GPU: the full
 Llama-3.1-8B as a 291-tensor list (8,030,261,248 parameters, 128.5 GB of
 state).  The line also carries, measured in the same process: a practical
-ceiling (a plain device copy of 2 GiB, read + write bytes over its time) and
+ceiling for the update (a plain kernel with the update's exact streams and
+trivial arithmetic, bench_ceiling.hip; a 2 GiB device copy beside it) and
 the two-launch latency floor (the same call on a list whose one tensor is
 empty: the two launches with no bytes to move).
 
@@ -65,7 +66,8 @@ def parse():
                    help="workload 1..5 (default 3: the full Llama-3.1-8B as a 291-tensor list, "
                         "the largest that fits one GPU)")
     p.add_argument("--ceiling-mib", type=int, default=2048,
-                   help="size of the same-run copy ceiling's buffers (0 = skip)")
+                   help="size of the same-run copy's buffers, reported beside the same-stream "
+                        "ceiling (0 = skip both ceilings)")
     p.add_argument("--rotate", type=int, default=1,
                    help="cycle over this many independent buffer sets (cache-cold small shards)")
     p.add_argument("--trials", type=int, default=5,
@@ -86,6 +88,10 @@ def parse():
     p.add_argument("--fused", action="store_true", help="same as --launches fused")
     p.add_argument("--state8", action="store_true",
                    help="8-bit moment state (m: E4M3, v: E5M2, a scale byte per 32 elements)")
+    p.add_argument("--no-placement-warmup", dest="placement_warmup", action="store_false",
+                   help="time the inputs' first allocation only (by default it is timed, "
+                        "released, the allocator cycled through 1.1 times the footprint, and "
+                        "the inputs allocated again for the reported run)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="after the measurement, run 5 plain device copies of this many MiB "
                         "(known bytes, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -145,25 +151,30 @@ def main():
         f"{'bf16' if w.grad_bf16 else 'fp32'} grads, copy={w.copy_bf16}, rotate={args.rotate}, "
         f"moments={'8-bit' if args.state8 else 'fp32'}")
 
-    sets = []
-    for r in range(args.rotate):
-        cols = synth.workload_inputs(w, dev, cfg_key=w.cfg * 1000 + r if r else None)
-        if args.state8:
-            states = []
-            for m, v in zip(cols["exp_avg"], cols["exp_avg_sq"]):
-                st = binding.zeros_q8_state(m.numel(), dev)
-                if m.numel():
-                    binding.adamw8_quantize(m, binding.MPS_Q8_E4M3, st[0], st[1])
-                    binding.adamw8_quantize(v, binding.MPS_Q8_E5M2, st[2], st[3])
-                states.append(st)
-            torch.cuda.synchronize()
-            cols["exp_avg"] = cols["exp_avg_sq"] = None  # only the 8-bit state stays resident
-            cols["q8_state"] = states
-            tl = binding.TensorList8(cols["master"], states, cols["grad"], cols["param_bf16"])
-        else:
-            tl = binding.TensorList(cols["master"], cols["exp_avg"], cols["exp_avg_sq"],
-                                    cols["grad"], cols["param_bf16"])
-        sets.append((cols, tl))
+    def make_sets():
+        sets = []
+        for r in range(args.rotate):
+            cols = synth.workload_inputs(w, dev, cfg_key=w.cfg * 1000 + r if r else None)
+            if args.state8:
+                states = []
+                for m, v in zip(cols["exp_avg"], cols["exp_avg_sq"]):
+                    st = binding.zeros_q8_state(m.numel(), dev)
+                    if m.numel():
+                        binding.adamw8_quantize(m, binding.MPS_Q8_E4M3, st[0], st[1])
+                        binding.adamw8_quantize(v, binding.MPS_Q8_E5M2, st[2], st[3])
+                    states.append(st)
+                torch.cuda.synchronize()
+                cols["exp_avg"] = cols["exp_avg_sq"] = None  # only the 8-bit state stays resident
+                cols["q8_state"] = states
+                tl = binding.TensorList8(cols["master"], states, cols["grad"], cols["param_bf16"])
+            else:
+                tl = binding.TensorList(cols["master"], cols["exp_avg"], cols["exp_avg_sq"],
+                                        cols["grad"], cols["param_bf16"])
+            sets.append((cols, tl))
+        torch.cuda.synchronize()
+        return sets
+
+    sets = make_sets()
     sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
     coef = torch.zeros(1, dtype=torch.float32, device=dev)
     step = torch.tensor([w.step - 1], dtype=torch.int32, device=dev)
@@ -203,6 +214,31 @@ def main():
                                         w.weight_decay)
         if ev is not None:
             ev[2].record()
+
+    # The workload's first allocation in this process, timed, then released:
+    # on a freshly started GPU the first allocation of a large footprint
+    # streams several per cent slower than any later one (measured on the
+    # 8B-parameter list: 5.49 TB/s for the update, steady for a minute, against
+    # 5.94-6.04 TB/s once the allocator has been cycled), so the run below
+    # first cycles the allocator through 1.1 times the footprint and then
+    # allocates the inputs again.
+    first_allocation = None
+    if args.placement_warmup:
+        first_allocation = time_first_allocation(args, w, sets, one_step, step, dev)
+        footprint = torch.cuda.memory_allocated()
+        for cols, tl in sets:
+            tl.release()
+        del sets, cols, tl
+        torch.cuda.empty_cache()
+        cycle = torch.empty(int(1.1 * footprint), dtype=torch.uint8, device=dev)
+        cycle.fill_(1)
+        torch.cuda.synchronize()
+        del cycle
+        torch.cuda.empty_cache()
+        sets = make_sets()
+        step.fill_(w.step - 1)
+        torch.cuda.synchronize()
+        log(f"allocator cycled through {1.1 * footprint / 2**30:.1f} GiB; inputs allocated again")
 
     # Warm-up: exactly --warmup steps if given, else at least 10 steps and at
     # least --warmup-seconds of them.
@@ -327,8 +363,9 @@ def main():
         log(f"kernels (us): " + ", ".join(f"{k} {v:.1f}" for k, v in kern_us.items()))
 
     floor = None if args.no_kernel_events else latency_floor(args, dev)
-    ceiling = None if args.ceiling_mib <= 0 else copy_ceiling(args.ceiling_mib, dev)
-    if roofline is not None and ceiling is not None:
+    if roofline is not None and args.ceiling_mib > 0 and not args.state8:
+        ceiling = same_stream_ceiling(w, dev)
+        ceiling["copy"] = copy_ceiling(args.ceiling_mib, dev)
         roofline["ceiling"] = ceiling
         roofline["frac_of_ceiling"] = round(roofline["achieved"] / ceiling["achieved"], 4)
 
@@ -375,9 +412,82 @@ def main():
         "warm_same_buffers": warm,
         "roofline": roofline,
         "latency_floor": floor,
+        "first_allocation": first_allocation,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+CEILING_LIB = os.path.join(ROOT, "bench_ceiling.so")
+CEILING_ELEMS = 1 << 28
+
+
+def time_first_allocation(args, w, sets, one_step, step, dev):
+    """The workload's K steps on the inputs' first allocation in this process
+    (after its own warm-up of W steps), with the update's event time."""
+    import torch
+
+    for i in range(args.warmup if args.warmup is not None else 10):
+        one_step(sets[i % len(sets)][1])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        e[1].record()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        one_step(sets[i % len(sets)][1], evs[i])
+    torch.cuda.synchronize()
+    ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
+    upd_us = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e3
+    log(f"first allocation: {ms * 1e3:.1f} us/step, update {upd_us:.1f} us")
+    return {"ms_per_step": round(ms, 5), "params_per_s": w.numel / (ms * 1e-3),
+            "update_us": round(upd_us, 2),
+            "what": "the same K steps on the inputs' first allocation in this process, before "
+                    "the allocator was cycled (a fresh GPU's first large allocation streams "
+                    "slower); value is the run after it"}
+
+
+def same_stream_ceiling(w, dev, n=CEILING_ELEMS):
+    """The update's streams without its arithmetic (bench_ceiling.hip): a
+    plain grid-stride kernel reading and writing fp32 master, m and v,
+    reading the workload's gradient type and writing the bf16 copy where the
+    workload has one, over fresh buffers of n elements (2^28: 4 to 4.3 GB,
+    far beyond the caches), timed on the same GPU in the same process.  The
+    best of four launch shapes; the GB/s count the same bytes per element as
+    the update's roofline."""
+    import ctypes
+
+    import torch
+
+    if not os.path.exists(CEILING_LIB):
+        raise RuntimeError(f"{CEILING_LIB} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(CEILING_LIB)
+    fn = lib.stream_ceiling_us
+    fn.restype = ctypes.c_double
+    P = ctypes.c_void_p
+    fn.argtypes = [ctypes.c_int, P, P, P, P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_int, P]
+    bufs = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(3)]
+    g = torch.zeros(n, dtype=torch.bfloat16 if w.grad_bf16 else torch.float32, device=dev)
+    p = torch.zeros(n, dtype=torch.bfloat16, device=dev) if w.copy_bf16 else None
+    stream = torch.cuda.current_stream().cuda_stream
+    bytes_per_elem = w.update_bytes_per_param()
+    shapes = {}
+    for grid, unroll in ((256, 1), (256, 2), (1280, 1), (1024, 2)):
+        us = fn(1 if w.grad_bf16 else 0, *(b.data_ptr() for b in bufs), g.data_ptr(),
+                None if p is None else p.data_ptr(), n, grid, unroll, 10, stream)
+        if us <= 0:
+            raise RuntimeError(f"stream_ceiling_us failed ({us})")
+        shapes[f"{grid} blocks x {unroll} group(s) of 4"] = round(bytes_per_elem * n / us / 1e3, 1)
+    del bufs, g, p
+    torch.cuda.empty_cache()
+    best = max(shapes, key=shapes.get)
+    log(f"same-stream ceiling: {shapes[best]:.0f} GB/s ({best}); all: {shapes}")
+    return {"achieved": shapes[best], "unit": "GB/s", "frac": round(shapes[best] / HBM_PEAK_GBPS, 4),
+            "what": f"plain kernel with the update's streams ({bytes_per_elem} B per element, "
+                    f"{'bf16' if w.grad_bf16 else 'fp32'} gradient{', bf16 copy' if w.copy_bf16 else ''}), "
+                    f"trivial arithmetic, {n:,} elements, best launch shape of 4, same process",
+            "shapes": shapes}
 
 
 def copy_ceiling(mib, dev, reps=10):

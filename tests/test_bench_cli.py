@@ -64,3 +64,23 @@ def test_cpu_baseline_reports_one_thread_and_all_threads():
     r = bench.cpu_baseline(w, cols, 0.05, 3)
     assert r["cores"] == 1 and r["kind"] == "oracle" and r["value"] > 0
     assert r["all_cores"]["cores"] == 3 and r["all_cores"]["value"] > 0
+
+
+def test_same_stream_ceiling_library_rejects_bad_arguments():
+    """bench_ceiling.so (the benchmark's same-stream ceiling kernel) exports
+    its one function and refuses bad sizes before any HIP call."""
+    import ctypes
+    path = os.path.join(ROOT, "bench_ceiling.so")
+    if not os.path.exists(path):
+        import __graft_entry__
+        __graft_entry__.build_bench_ceiling()
+    fn = ctypes.CDLL(path).stream_ceiling_us
+    fn.restype = ctypes.c_double
+    P = ctypes.c_void_p
+    fn.argtypes = [ctypes.c_int, P, P, P, P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_int, P]
+    fake = 0x7f0000000000
+    assert fn(1, fake, fake, fake, fake, None, 0, 256, 1, 10, None) < 0       # no elements
+    assert fn(1, fake, fake, fake, fake, None, 6, 256, 1, 10, None) < 0       # not a multiple of 4
+    assert fn(1, fake, fake, fake, fake, None, 1024, 256, 3, 10, None) < 0    # unroll 3
+    assert fn(1, None, fake, fake, fake, None, 1024, 256, 1, 10, None) < 0    # NULL buffer
