@@ -230,15 +230,19 @@ def main():
             tl.release()
         del sets, cols, tl
         torch.cuda.empty_cache()
-        cycle = torch.empty(int(1.1 * footprint), dtype=torch.uint8, device=dev)
-        cycle.fill_(1)
-        torch.cuda.synchronize()
-        del cycle
+        try:
+            cycle = torch.empty(int(1.1 * footprint), dtype=torch.uint8, device=dev)
+            cycle.fill_(1)
+            torch.cuda.synchronize()
+            del cycle
+            log(f"allocator cycled through {1.1 * footprint / 2**30:.1f} GiB")
+        except torch.cuda.OutOfMemoryError:
+            log("no room to cycle the allocator through 1.1 times the footprint; skipped")
         torch.cuda.empty_cache()
         sets = make_sets()
         step.fill_(w.step - 1)
         torch.cuda.synchronize()
-        log(f"allocator cycled through {1.1 * footprint / 2**30:.1f} GiB; inputs allocated again")
+        log("inputs allocated again")
 
     # Warm-up: exactly --warmup steps if given, else at least 10 steps and at
     # least --warmup-seconds of them.
