@@ -75,8 +75,8 @@ namespace mps {
 #define MPS_CHUNK_MIN 2048
 #endif
 // Chunk sizes of a shard's fp32-state list (above) and of an 8-bit-moment
-// list: those keep 16384, their update (768 blocks, three per CU) measured up
-// to 3.4 % slower with 4096.
+// list: those keep 16384 (4096 measured up to 3.4 % slower, 8192 and 32768
+// mixed across the workloads).
 #ifndef MPS_CHUNK_MAX
 #define MPS_CHUNK_MAX 4096
 #endif
@@ -95,8 +95,12 @@ namespace mps {
 #define MPS_NORM_CACHE_BUDGET (384ll << 20)
 #endif
 
+// 8-bit-moment update grid cap.  Measured side by side on the workloads' own
+// inputs in three fresh processes: 1280 blocks streamed 0.1-2.3 % faster
+// than 768 on every workload; 512 and 1024 lost up to 11 % on the 8B shard,
+// 256 (one per CU) 25-35 % on all of them.
 #ifndef MPS_Q8_MAX_BLOCKS
-#define MPS_Q8_MAX_BLOCKS 768      // 8-bit-moment update grid cap
+#define MPS_Q8_MAX_BLOCKS 1280
 #endif
 
 #ifndef MPS_FUSED_MAX_BLOCKS

@@ -23,7 +23,7 @@ DEV = "cuda"
 # 2048 elements per chunk for lists below 12,582,912 elements, 4096 from
 # there; the fp32 update's grid is one block per chunk up to 1280 chunks,
 # then at most 256 blocks (one per CU) walking several chunks each; the
-# 8-bit update's grid is at most 768 blocks, the norm's 256.
+# 8-bit update's grid is at most 1280 blocks, the norm's 256.
 SIZES = [1, 5, 2047, 2048, 2049, 3 * 2048 + 17, 256 * 2048 + 1, 768 * 2048 + 33,
          1280 * 2048 - 3, 1280 * 2048 + 5, 2560 * 2048 + 2049, 12582912 + 4097]
 
@@ -138,7 +138,7 @@ def q8_case(host, clipped, offset=0, what=""):
 @pytest.mark.parametrize("clipped", [False, True], ids=["three calls", "clipped"])
 @pytest.mark.parametrize("bf16", [False, True])
 def test_q8_one_tensor_sizes(clipped, bf16):
-    for n in (1, 31, 33, 2048, 2049, 3 * 2048 + 17, 768 * 2048 + 33):
+    for n in (1, 31, 33, 2048, 2049, 3 * 2048 + 17, 768 * 2048 + 33, 1280 * 2048 + 33):
         what = f"q8 clipped={clipped} n={n} bf16={bf16}"
         say(what)
         q8_case(make_host([n], seed=n % 991, bf16=bf16), clipped, what=what)
