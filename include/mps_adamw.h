@@ -257,8 +257,10 @@ int adamw_clipped_step(const mps_tensor* tensors, int n_tensors, mps_dtype grad_
  * results, with the library's own workspace instead of the caller's.  That
  * workspace is a device array of MPS_NOALLOC_WORKSPACE_BYTES (4 MiB) that the
  * library holds on every GPU it runs on until the process ends; its address
- * is looked up once per device, on the first call there.  The call makes no
- * allocation of any kind (no hipMalloc, hipFree or pinned host memory).
+ * is looked up once per device, on the first call there.  The call allocates
+ * no device or pinned host memory (it never calls hipMalloc, hipFree,
+ * hipHostMalloc or an allocator above them); planning a new list uses the
+ * ordinary host heap, as every entry point does.
  *
  *   Arguments as adamw_clipped_step, without d_workspace and workspace_bytes;
  *   the current device must be the stream's device.
