@@ -651,9 +651,7 @@ def cpu_baseline(w, cols, budget_s, threads):
 
     steps, dt = _time_steps(one_thread, budget_s)
     t_next = w.step + steps
-    whole = taken == w.numel
-    what = (f"whole {w.name} shard" if whole else
-            f"first {n_tensors} of {w.n_tensors} tensors of {w.name}")
+    what = _sample_name(w, n_tensors, taken)
     log(f"cpu oracle: {steps} steps of {taken:,} params in {dt:.2f} s, 1 thread")
 
     # Thread k takes slice k of every tensor.
@@ -668,7 +666,7 @@ def cpu_baseline(w, cols, budget_s, threads):
         lambda S: o.clip_coef(S, w.max_norm), budget_s)
     log(f"cpu oracle: {steps_t} steps of {taken:,} params in {dt_t:.2f} s, {len(parts)} threads")
     return {"value": taken * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"{what} ({taken:,} params): norm + clip + update, {steps} consecutive "
+            "sample": f"{what}: norm + clip + update, {steps} consecutive "
                       f"steps, 1 thread, {dt:.1f} s",
             "all_cores": {"value": taken * steps_t / dt_t, "unit": "params/s",
                           "cores": len(parts),
@@ -719,8 +717,7 @@ def cpu_baseline8(w, cols, budget_s, threads):
 
     steps, dt = _time_steps(one_thread, budget_s)
     t_next = w.step + steps
-    what = (f"whole {w.name} shard" if taken == w.numel else
-            f"first {len(host)} of {w.n_tensors} tensors of {w.name}")
+    what = _sample_name(w, len(host), taken)
     log(f"cpu oracle (8-bit moments): {steps} steps of {taken:,} params in {dt:.2f} s, 1 thread")
 
     parts = [[] for _ in range(threads)]
@@ -735,7 +732,7 @@ def cpu_baseline8(w, cols, budget_s, threads):
     log(f"cpu oracle (8-bit moments): {steps_t} steps of {taken:,} params in {dt_t:.2f} s, "
         f"{len(parts)} threads")
     return {"value": taken * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"{what}, first {taken:,} params: norm + clip + 8-bit-moment update, "
+            "sample": f"{what}: norm + clip + 8-bit-moment update, "
                       f"{steps} consecutive steps, 1 thread, {dt:.1f} s",
             "all_cores": {"value": taken * steps_t / dt_t, "unit": "params/s",
                           "cores": len(parts),
@@ -743,6 +740,19 @@ def cpu_baseline8(w, cols, budget_s, threads):
                                     f"tensor cut at 32-element runs into {len(parts)} slices, "
                                     f"one thread per slice, partial sums added, {dt_t:.1f} s"},
             "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
+
+
+def _sample_name(w, n_tensors, taken):
+    """What a CPU sample of `taken` leading parameters (over `n_tensors`
+    tensors in list order) covers."""
+    if taken == w.numel:
+        return f"the whole {w.name} shard ({taken:,} params)"
+    cut = sum(n for _, n in w.tensors[:n_tensors]) > taken
+    last = (f"; tensor {n_tensors - 1} ({w.tensors[n_tensors - 1][0]}) cut after "
+            f"{taken - sum(n for _, n in w.tensors[:n_tensors - 1]):,} of its "
+            f"{w.tensors[n_tensors - 1][1]:,}") if cut else ""
+    return (f"the first {taken:,} of {w.numel:,} params of {w.name} in list order "
+            f"({n_tensors} tensor{'s' if n_tensors > 1 else ''}{last})")
 
 
 def _cpu_model():
