@@ -7,6 +7,8 @@ bitwise), the codes and scale bytes are integers decided in fp32 on both
 sides and must match exactly.  The oracle's update is fed the device's clip
 coefficient; the sum of squares is checked on its own (relative 1e-5).
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -444,6 +446,91 @@ def test_q8_full_size_sampled(cfg, clipped):
     if free < need:
         pytest.skip(f"needs {need / 2**30:.0f} GiB free, {free / 2**30:.0f} GiB available")
     q8_sampled_parity(w, seed=200 + cfg, clipped=clipped)
+
+
+@pytest.mark.parametrize("cfg", [2, 4, 5])
+def test_q8_full_size_every_element(cfg):
+    """The bench's workload and launch with 8-bit moments, every element of
+    every tensor against the oracle stepped with the GPU's coefficient:
+    master (bitwise first, else the tolerance), both code arrays and both
+    scale arrays exactly.  The 8-bit oracle's nearest-code search takes 15M
+    elements/s on 16 threads, so the 8B full list (8.03e9 elements, about
+    nine minutes) is left to the sampled test above."""
+    from concurrent.futures import ThreadPoolExecutor
+    from mixed_precision_sharded_amd import synth
+    from mixed_precision_sharded_amd.configs import WORKLOADS
+    from mixed_precision_sharded_amd.synth import to_numpy
+
+    w = WORKLOADS[cfg]
+    free, _ = torch.cuda.mem_get_info()
+    need = w.numel * (w.state8_bytes_per_param() + 4) + (8 << 30)
+    if free < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB free, {free / 2**30:.0f} GiB available")
+    warm = w.m_std is not None
+    say(f"q8 every element: {w.name}, {w.numel:,} params in {w.n_tensors} tensors, warm={warm}")
+    cols = synth.workload_inputs(w, "cuda")
+    del cols["exp_avg"], cols["exp_avg_sq"]
+    rng = np.random.default_rng(300 + cfg)
+    host = [random_q8_state(n, rng, warm) for _, n in w.tensors]
+    states = [tuple(torch.from_numpy(a).cuda() for a in st) for st in host]
+    before_w = [to_numpy(t).copy() for t in cols["master"]]
+    grads = [to_numpy(t).copy() for t in cols["grad"]]
+    o = oracle.default()
+    S_ref = o.grad_norm_sq(grads)
+
+    say("GPU step (8-bit moments, clipped)")
+    tl = binding.TensorList8(cols["master"], states, cols["grad"], cols["param_bf16"])
+    sumsq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    coef = torch.zeros(1, dtype=torch.float32, device="cuda")
+    step = torch.tensor([w.step - 1], dtype=torch.int32, device="cuda")
+    binding.adamw8_clipped_step(tl, step, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay,
+                                w.max_norm, sumsq_out=sumsq, coef_out=coef)
+    torch.cuda.synchronize()
+    S, c, t = float(sumsq.item()), np.float32(coef.item()), int(step.item())
+    assert t == w.step
+    assert abs(S - S_ref) <= NORM_REL_TOL * S_ref, (S, S_ref)
+    assert c == o.clip_coef(S, w.max_norm)
+    say(f"S={S:.9e} oracle {S_ref:.9e} c={float(c)}; the oracle over every element")
+
+    # The oracle on the pre-step host state, in slices cut at multiples of
+    # the 32-element runs (one scale byte each), 16 threads.
+    copies = [np.zeros(n, np.uint16) if w.copy_bf16 else None for _, n in w.tensors]
+    piece = 1 << 20
+    items = [(i, lo, min(lo + piece, n)) for i, (_, n) in enumerate(w.tensors)
+             for lo in range(0, n, piece)]
+
+    def one(item):
+        i, lo, hi = item
+        mc, ms, vc, vs = host[i]
+        r0, r1 = lo // 32, (hi + 31) // 32
+        o.adamw8_step(before_w[i][lo:hi], mc[lo:hi], ms[r0:r1], vc[lo:hi], vs[r0:r1],
+                      grads[i][lo:hi], None if copies[i] is None else copies[i][lo:hi], c, w.step,
+                      w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
+
+    t0 = time.time()
+    with ThreadPoolExecutor(max_workers=16) as pool:
+        list(pool.map(one, items))
+    say(f"oracle done in {time.time() - t0:.0f} s; comparing")
+
+    nbit = 0
+    for i, (_, n) in enumerate(w.tensors):
+        got_w = to_numpy(cols["master"][i])
+        if not np.array_equal(got_w.view(np.uint32), before_w[i].view(np.uint32)):
+            nb, _ = check_f32(got_w, before_w[i], f"{w.name} tensor {i} master")
+            nbit += nb
+        for k, name in enumerate(("m codes", "m scales", "v codes", "v scales")):
+            got = states[i][k].cpu().numpy()
+            if not np.array_equal(got, host[i][k]):
+                bad = np.flatnonzero(got != host[i][k])
+                raise AssertionError(f"{w.name} tensor {i} {name}: {bad.size} differ, first at "
+                                     f"{bad[0]}: {got[bad[0]]} against {host[i][k][bad[0]]}")
+        if w.copy_bf16:
+            check_bf16(to_numpy(cols["param_bf16"][i]), copies[i], f"{w.name} tensor {i} copy")
+    say(f"{w.numel:,} elements checked (master, codes, scales{', copy' if w.copy_bf16 else ''}); "
+        f"{nbit} master elements not bitwise equal")
+    tl.release()
+    del tl, cols, states
+    torch.cuda.empty_cache()
 
 
 def test_q8_single_tensor_over_2g_elements_sampled():
