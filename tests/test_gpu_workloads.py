@@ -11,7 +11,9 @@ the device), copied to the host, and stepped by the oracle with the GPU's
 coefficient, one tensor at a time; so is the single tensor of 2^31 + 1003
 elements (offsets past 32 bits), whose three-call step is also checked on
 sampled positions (random ones, its first and last elements, chunk edges
-and the elements around 2^31 and 2^30).
+and the elements around 2^31 and 2^30), and so are two lists just past the
+whole-model threshold (2^30 elements) built from ragged, element-misaligned
+views, one with fp32 and one with bf16 gradients.
 """
 import time
 
@@ -68,10 +70,12 @@ def whole_tensor_parity(w, cols, i, c):
     return host["master"].size, nbit
 
 
-def full_parity(w, clipped=True):
-    """Every element of every tensor of workload w against the oracle."""
+def full_parity(w, clipped=True, cols=None):
+    """Every element of every tensor of workload w against the oracle
+    (`cols`: the workload's inputs already placed, else generated here)."""
     say(f"workload {w.name}: {w.numel:,} params in {w.n_tensors} tensors; generating")
-    cols = synth.workload_inputs(w, "cuda")
+    if cols is None:
+        cols = synth.workload_inputs(w, "cuda")
     torch.cuda.synchronize()
     o = oracle.default()
     S_ref = o.grad_norm_sq(to_numpy(g) for g in cols["grad"])
@@ -170,6 +174,49 @@ def test_llama8b_full_list_every_element():
     if free < need:
         pytest.skip(f"needs {need / 2**30:.0f} GiB free, {free / 2**30:.0f} GiB available")
     full_parity(w)
+
+
+# A list just past the whole-model threshold of 2^30 elements, with ragged
+# sizes and element-misaligned views: the whole-model walk (1280 blocks,
+# 16384-element chunks) through heads, tails, tiny tensors and the
+# element-wise path, with fp32 and with bf16 gradients.
+RAGGED_BIG = (((1 << 29) + 13, 1), (1, 0), (3, 3), (65, 2), (4097, 1), ((1 << 28) + 4001, 0),
+              (2049, 3), ((1 << 28) + 1023, 2),
+              (100003, {"master": 1, "exp_avg": 2, "exp_avg_sq": 0, "grad": 3, "param_bf16": 1}))
+
+
+def placed_inputs(w, offsets):
+    """The workload's seeded inputs, each stream of tensor i a view starting
+    offsets[i] elements into a buffer of its own (one offset for every
+    stream, or one per stream)."""
+    cols = {k: [] for k in FIELDS + ("grad", "param_bf16")}
+    for i, (_, n) in enumerate(w.tensors):
+        fresh = synth.tensor_inputs(w, i, "cuda")
+        for k in cols:
+            src = fresh.get(k)
+            if src is None:
+                cols[k].append(None)
+                continue
+            off = offsets[i] if isinstance(offsets[i], int) else offsets[i][k]
+            view = torch.empty(n + off, dtype=src.dtype, device="cuda")[off:off + n]
+            view.copy_(src)
+            cols[k].append(view)
+        del fresh
+    torch.cuda.synchronize()
+    return cols
+
+
+@pytest.mark.parametrize("grad_bf16", [False, True])
+def test_whole_model_walk_ragged_misaligned_every_element(grad_bf16):
+    w = Workload(cfg=92 + int(grad_bf16), name=f"ragged_past_2p30_{'bf16' if grad_bf16 else 'f32'}",
+                 tensors=tuple((f"t{i}", n) for i, (n, _) in enumerate(RAGGED_BIG)),
+                 grad_bf16=grad_bf16, copy_bf16=grad_bf16, step=7, m_std=1e-4, v_std=1e-8)
+    assert w.numel >= 1 << 30
+    free, _ = torch.cuda.mem_get_info()
+    need = w.numel * (w.state_bytes_per_param() + 4) + (8 << 30)
+    if free < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB free, {free / 2**30:.0f} GiB available")
+    full_parity(w, cols=placed_inputs(w, [off for _, off in RAGGED_BIG]))
 
 
 # A single tensor of more than 2^31 elements: element offsets, chunk indices
