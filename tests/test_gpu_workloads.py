@@ -13,7 +13,8 @@ elements (offsets past 32 bits), whose three-call step is also checked on
 sampled positions (random ones, its first and last elements, chunk edges
 and the elements around 2^31 and 2^30), and so are two lists just past the
 whole-model threshold (2^30 elements) built from ragged, element-misaligned
-views, one with fp32 and one with bf16 gradients.
+views, one with fp32 and one with bf16 gradients (the fp32 one also
+through the three-call step).
 """
 import time
 
@@ -206,8 +207,8 @@ def placed_inputs(w, offsets):
     return cols
 
 
-@pytest.mark.parametrize("grad_bf16", [False, True])
-def test_whole_model_walk_ragged_misaligned_every_element(grad_bf16):
+@pytest.mark.parametrize("grad_bf16,clipped", [(False, True), (True, True), (False, False)])
+def test_whole_model_walk_ragged_misaligned_every_element(grad_bf16, clipped):
     w = Workload(cfg=92 + int(grad_bf16), name=f"ragged_past_2p30_{'bf16' if grad_bf16 else 'f32'}",
                  tensors=tuple((f"t{i}", n) for i, (n, _) in enumerate(RAGGED_BIG)),
                  grad_bf16=grad_bf16, copy_bf16=grad_bf16, step=7, m_std=1e-4, v_std=1e-8)
@@ -216,7 +217,7 @@ def test_whole_model_walk_ragged_misaligned_every_element(grad_bf16):
     need = w.numel * (w.state_bytes_per_param() + 4) + (8 << 30)
     if free < need:
         pytest.skip(f"needs {need / 2**30:.0f} GiB free, {free / 2**30:.0f} GiB available")
-    full_parity(w, cols=placed_inputs(w, [off for _, off in RAGGED_BIG]))
+    full_parity(w, clipped=clipped, cols=placed_inputs(w, [off for _, off in RAGGED_BIG]))
 
 
 # A single tensor of more than 2^31 elements: element offsets, chunk indices
