@@ -271,6 +271,19 @@ def test_header_is_plain_c(tmp_path):
     assert ctypes.sizeof(binding.MpsTensor) == 48 and ctypes.sizeof(binding.MpsTensor8) == 64
 
 
+def test_c_program_builds_against_the_header(lib, oracle_lib, tmp_path):
+    """The C test program (tests/c_abi/step_from_c.c) compiles as C99 with
+    every warning an error and links against the built library."""
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location(
+        "c_abi_build", os.path.join(os.path.dirname(__file__), "c_abi", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    out = mod.build(str(tmp_path / "step_from_c"))
+    assert os.path.getsize(out) > 0
+
+
 def test_fused_status_rejects_bad_arguments(lib):
     P = ctypes.c_void_p
     assert lib.adamw_fused_status(P(0x7f0000000000), 4096, None, None) == EINVAL
