@@ -11,6 +11,7 @@ struct Counters {
     uint64_t queries = 0;           // event queries
     uint64_t launches = 0;          // kernel launches enqueued
     uint64_t launches_checked = 0;  // launches run that found their own tables
+    uint64_t tables_checked = 0;    // launches whose tables passed check_tables
 };
 void run(size_t n);        // run the next n queued operations, in order
 void run_all();

@@ -8,8 +8,12 @@ point) through valid and invalid lists with stand-ins for the kernel
 launchers that abort if reached.  A third drives the library's table
 uploads against a fake in-order device (tests/sanitize/fake_device.cpp):
 list changes must never make the host wait, copies must come from pinned
-buffers, and a staging buffer must not be reused before its copy ran.  No
-GPU code is built with a sanitizer."""
+buffers, and a staging buffer must not be reused before its copy ran.  A
+fourth takes 400 seeded random lists through every entry point against the
+same fake device, which checks the tables each launch finds (chunk map,
+alignment heads, the one-tensor entry, the whole-model flag, grid bounds);
+planted planning mistakes must make it fail.  No GPU code is built with a
+sanitizer."""
 import os
 import shutil
 import subprocess
@@ -106,5 +110,59 @@ def test_the_upload_driver_catches_planted_mistakes(tmp_path, plant, symptom):
                                                         '"../include/mps_adamw.h"'))
     exe = str(tmp_path / "upload_driver_planted")
     build_upload_driver(exe, str(planted))
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=ENV)
+    assert r.returncode != 0 and symptom in r.stderr, r.stdout + r.stderr
+
+
+PLAN_SOURCES = [os.path.join(HERE, "plan_driver.cpp"), os.path.join(HERE, "fake_device.cpp")]
+
+
+def planted_api(tmp_path, plant, bad):
+    """A copy of api.cpp with `plant` replaced by `bad`, beside copies of the
+    headers it includes."""
+    src = os.path.join(ROOT, "mixed_precision_sharded_amd", "csrc", "api.cpp")
+    text = open(src).read()
+    assert plant in text
+    d = tmp_path / "csrc"
+    d.mkdir()
+    for name in os.listdir(os.path.dirname(src)):
+        if name.endswith(".h"):
+            shutil.copy(os.path.join(os.path.dirname(src), name), d / name)
+    (tmp_path / "include").mkdir()
+    shutil.copy(os.path.join(ROOT, "include", "mps_adamw.h"), tmp_path / "include" / "mps_adamw.h")
+    planted = d / "api.cpp"
+    planted.write_text(text.replace(plant, bad).replace('"../../include/mps_adamw.h"',
+                                                        '"../include/mps_adamw.h"'))
+    return str(planted)
+
+
+def build_plan_driver(exe, api_cpp):
+    subprocess.run(["g++", *SAN, "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    "-o", exe, *PLAN_SOURCES, api_cpp], check=True)
+
+
+@pytest.mark.skipif(shutil.which("g++") is None or not os.path.isdir("/opt/rocm/include"),
+                    reason="no g++ or ROCm headers")
+def test_planning_on_random_lists(tmp_path):
+    exe = str(tmp_path / "plan_driver")
+    build_plan_driver(exe, os.path.join(ROOT, "mixed_precision_sharded_amd", "csrc", "api.cpp"))
+    assert "plan driver ok" in run(exe)
+
+
+@pytest.mark.skipif(shutil.which("g++") is None or not os.path.isdir("/opt/rocm/include"),
+                    reason="no g++ or ROCm headers")
+@pytest.mark.parametrize("plant,bad,symptom", [
+    # the bf16 gradient's alignment taken with fp32 elements
+    ("e.head = common_head(e, bf16);", "e.head = common_head(e, false);",
+     "table check: head of a tensor"),
+    # a tensor's last partial chunk dropped from the count
+    ("n_chunks += (e.numel + plan.chunk_elems - 1) / plan.chunk_elems;",
+     "n_chunks += e.numel / plan.chunk_elems;", "table check: chunk map"),
+    # a list whose elements sit in one tensor not recognised as such
+    ("plan.solo_tensor = i;", "plan.solo_tensor = -1;", "table check: the one-tensor index"),
+])
+def test_the_plan_checks_catch_planted_mistakes(tmp_path, plant, bad, symptom):
+    exe = str(tmp_path / "plan_driver_planted")
+    build_plan_driver(exe, planted_api(tmp_path, plant, bad))
     r = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=ENV)
     assert r.returncode != 0 and symptom in r.stderr, r.stdout + r.stderr
