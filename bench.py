@@ -367,8 +367,8 @@ def main():
         log(f"kernels (us): " + ", ".join(f"{k} {v:.1f}" for k, v in kern_us.items()))
 
     floor = None if args.no_kernel_events else latency_floor(args, dev)
-    if roofline is not None and args.ceiling_mib > 0 and not args.state8:
-        ceiling = same_stream_ceiling(w, dev)
+    if roofline is not None and args.ceiling_mib > 0:
+        ceiling = same_stream_ceiling8(w, dev) if args.state8 else same_stream_ceiling(w, dev)
         ceiling["copy"] = copy_ceiling(args.ceiling_mib, dev)
         roofline["ceiling"] = ceiling
         roofline["frac_of_ceiling"] = round(roofline["achieved"] / ceiling["achieved"], 4)
@@ -491,6 +491,51 @@ def same_stream_ceiling(w, dev, n=CEILING_ELEMS):
             "what": f"plain kernel with the update's streams ({bytes_per_elem} B per element, "
                     f"{'bf16' if w.grad_bf16 else 'fp32'} gradient{', bf16 copy' if w.copy_bf16 else ''}), "
                     f"trivial arithmetic, {n:,} elements, best launch shape of 4, same process",
+            "shapes": shapes}
+
+
+def same_stream_ceiling8(w, dev, n=CEILING_ELEMS):
+    """The 8-bit-moment update's streams without its arithmetic
+    (bench_ceiling.hip's stream_ceiling8_us): fp32 master, m and v codes
+    read and written, one scale byte per 32 elements read (cached) and
+    written per chunk, the workload's gradient read and its bf16 copy
+    written, over fresh buffers of n elements; the best of four grids, GB/s
+    by the update's own bytes per element."""
+    import ctypes
+
+    import torch
+
+    if not os.path.exists(CEILING_LIB):
+        raise RuntimeError(f"{CEILING_LIB} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(CEILING_LIB)
+    fn = lib.stream_ceiling8_us
+    fn.restype = ctypes.c_double
+    P = ctypes.c_void_p
+    fn.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, P]
+    master = torch.zeros(n, dtype=torch.float32, device=dev)
+    g = torch.zeros(n, dtype=torch.bfloat16 if w.grad_bf16 else torch.float32, device=dev)
+    p = torch.zeros(n, dtype=torch.bfloat16, device=dev) if w.copy_bf16 else None
+    codes = [torch.zeros(n, dtype=torch.uint8, device=dev) for _ in range(2)]
+    scales = [torch.zeros(n // 32, dtype=torch.uint8, device=dev) for _ in range(2)]
+    stream = torch.cuda.current_stream().cuda_stream
+    bytes_per_elem = w.update8_bytes_per_param()
+    shapes = {}
+    for grid in (256, 768, 1280, 2048):
+        us = fn(1 if w.grad_bf16 else 0, master.data_ptr(), g.data_ptr(),
+                None if p is None else p.data_ptr(), codes[0].data_ptr(), scales[0].data_ptr(),
+                codes[1].data_ptr(), scales[1].data_ptr(), n, grid, 10, stream)
+        if us <= 0:
+            raise RuntimeError(f"stream_ceiling8_us failed ({us})")
+        shapes[f"{grid} blocks"] = round(bytes_per_elem * n / us / 1e3, 1)
+    del master, g, p, codes, scales
+    torch.cuda.empty_cache()
+    best = max(shapes, key=shapes.get)
+    log(f"same-stream ceiling (8-bit moments): {shapes[best]:.0f} GB/s ({best}); all: {shapes}")
+    return {"achieved": shapes[best], "unit": "GB/s", "frac": round(shapes[best] / HBM_PEAK_GBPS, 4),
+            "what": f"plain kernel with the 8-bit update's streams ({bytes_per_elem} B per element, "
+                    f"{'bf16' if w.grad_bf16 else 'fp32'} gradient{', bf16 copy' if w.copy_bf16 else ''}, "
+                    f"m and v codes and scale bytes), trivial arithmetic, {n:,} elements, best grid of "
+                    f"4, same process",
             "shapes": shapes}
 
 

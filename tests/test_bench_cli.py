@@ -67,8 +67,8 @@ def test_cpu_baseline_reports_one_thread_and_all_threads():
 
 
 def test_same_stream_ceiling_library_rejects_bad_arguments():
-    """bench_ceiling.so (the benchmark's same-stream ceiling kernel) exports
-    its one function and refuses bad sizes before any HIP call."""
+    """bench_ceiling.so (the benchmark's same-stream ceiling kernels) exports
+    its two functions, and both refuse bad sizes before any HIP call."""
     import ctypes
     path = os.path.join(ROOT, "bench_ceiling.so")
     if not os.path.exists(path):
@@ -84,3 +84,17 @@ def test_same_stream_ceiling_library_rejects_bad_arguments():
     assert fn(1, fake, fake, fake, fake, None, 6, 256, 1, 10, None) < 0       # not a multiple of 4
     assert fn(1, fake, fake, fake, fake, None, 1024, 256, 3, 10, None) < 0    # unroll 3
     assert fn(1, None, fake, fake, fake, None, 1024, 256, 1, 10, None) < 0    # NULL buffer
+    fn8 = ctypes.CDLL(path).stream_ceiling8_us
+    fn8.restype = ctypes.c_double
+    fn8.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, P]
+    assert fn8(1, fake, fake, None, fake, fake, fake, fake, 0, 256, 10, None) < 0        # no elements
+    assert fn8(1, fake, fake, None, fake, fake, fake, fake, 16384 + 32, 256, 10, None) < 0  # not whole chunks
+    assert fn8(1, fake, fake, None, None, fake, fake, fake, 16384, 256, 10, None) < 0    # NULL codes
+    assert fn8(1, fake, fake, None, fake, fake, fake, fake, 16384, 0, 10, None) < 0      # no blocks
+    # Without a GPU, valid arguments pass the checks and fail at the first HIP
+    # call (-2 or -3, not the -1 of a refused argument).  Never run with a GPU:
+    # the pointers here are not device memory.
+    import torch
+    if not torch.cuda.is_available():
+        assert fn(1, fake, fake, fake, fake, None, 1 << 20, 256, 1, 10, None) <= -2
+        assert fn8(0, fake, fake, None, fake, fake, fake, fake, 1 << 20, 256, 10, None) <= -2
