@@ -3,7 +3,7 @@ HIP runtime for device memory and the stream, no Python and no torch in
 that process (tests/c_abi/step_from_c.c, built by __graft_entry__.build()).
 The program runs the clipped step, the no-alloc clipped step and the
 three-call step on ragged lists and checks every element against the
-oracle it links; this test runs it and reads its verdict."""
+oracle it links; this test runs it and reads its result."""
 import os
 import subprocess
 
