@@ -2,11 +2,12 @@
 workspace, for callers that cannot allocate) against adamw_clipped_step on
 a workspace of the caller's, through the C ABI, on identical inputs: two
 calls in a row on different lists, the second smaller, then the second list
-again (its tables are still in the array).  S, the coefficient, the counter
-and every element of master, m, v and the bf16 copy must be bitwise equal
-(the same kernels, grids and summation order), and the no-alloc results are
-also checked against the oracle (relative error <= 2e-6, bf16 copy <= 1 ulp).
-A list whose tables exceed the array is refused before anything runs."""
+again (its tables are still in the array), and the call recorded in a HIP
+graph and replayed.  S, the coefficient, the counter and every element of
+master, m, v and the bf16 copy must be bitwise equal (the same kernels,
+grids and summation order), and the no-alloc results are also checked
+against the oracle (relative error <= 2e-6, bf16 copy <= 1 ulp).  A list
+whose tables exceed the array is refused before anything runs."""
 from types import SimpleNamespace
 
 import numpy as np
@@ -81,6 +82,55 @@ def test_noalloc_equals_the_workspace_step_on_consecutive_lists():
     after = noalloc_against_workspace_step(small, t=1, what="second list, smaller, fp32")
     # The same (smaller) list once more: its tables are already in the array.
     noalloc_against_workspace_step(after, t=2, what="second list again")
+
+
+def test_noalloc_step_replays_from_a_graph():
+    """The use the entry point is for: after one eager call on a list (which
+    puts its tables in the library's array), the call recorded in a HIP graph
+    and replayed three times, with unrelated eager work and synchronizations
+    between the replays; after every replay S, the coefficient, the counter
+    and every element equal the same step run eagerly on a workspace of the
+    caller's, bitwise."""
+    cols = make_cols([100003, 4097, 5], True, True, seed=72)
+    twin = clone(cols)
+    hp = (HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"])
+    dev = cols["master"][0].device
+    ref_tl = binding.TensorList(*(cols[k] for k in FIELDS))
+    tl = binding.TensorList(*(twin[k] for k in FIELDS), workspace=False)
+    scalars = [(torch.zeros(1, dtype=torch.float64, device=dev),
+                torch.zeros(1, dtype=torch.float32, device=dev),
+                torch.zeros(1, dtype=torch.int32, device=dev)) for _ in range(2)]
+    (rs, rc, rt), (s, c, t) = scalars
+
+    def reference_step():
+        binding.adamw_clipped_step(ref_tl, rt, *hp, 1.0, sumsq_out=rs, coef_out=rc)
+
+    def noalloc_step():
+        binding.adamw_clipped_step_noalloc(tl, t, *hp, 1.0, sumsq_out=s, coef_out=c)
+
+    def check(what):
+        torch.cuda.synchronize()
+        for x, y in ((s, rs), (c, rc), (t, rt)):
+            assert torch.equal(x, y), (what, x.item(), y.item())
+        for k in ("master", "exp_avg", "exp_avg_sq", "param_bf16"):
+            for i, (x, y) in enumerate(zip(twin[k], cols[k])):
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (what, k, i)
+
+    reference_step()
+    noalloc_step()  # uploads the list's tables into the library's array
+    check("eager call")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        noalloc_step()
+    scratch = torch.randn(1 << 20, device=dev)
+    for k in range(3):
+        reference_step()
+        g.replay()
+        scratch.mul_(1.0001).add_(1.0)  # unrelated eager work between replays
+        check(f"replay {k}")
+    say(f"[no-alloc graph] four steps, S={s.item():.9e} c={c.item()} t={t.item()}, bitwise")
+    assert int(t.item()) == 4
+    ref_tl.release()
 
 
 def test_noalloc_refuses_a_list_beyond_its_workspace():
