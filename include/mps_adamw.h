@@ -33,13 +33,16 @@
  *
  * Conventions shared by every entry point:
  *   - Every buffer pointer is a DEVICE pointer owned by the caller.  The
- *     library never allocates device memory; its only device scratch is the
- *     caller's workspace.  `tensors` (a HOST array) is read during the call
- *     only.
+ *     library never allocates device memory; its device scratch is the
+ *     caller's workspace (adamw_clipped_step_noalloc: a fixed array of the
+ *     library's own instead).  `tensors` (a HOST array) is read during the
+ *     call only.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream of
  *     the current device); the current device must be the stream's device.
- *     Work is enqueued on it; no call synchronizes with the host.  The caller
- *     keeps every buffer alive until the stream has passed the work.
+ *     Work is enqueued on it; no call synchronizes with the host, except
+ *     adamw_workspace_release and the no-alloc step's table copy when its
+ *     list changes (both described below).  The caller keeps every buffer
+ *     alive until the stream has passed the work.
  *   - Return value: 0 on success, a negative MPS_ERR_* code otherwise.  On
  *     an argument error nothing is enqueued.  adamw_last_error() gives the
  *     calling thread's last message.  Faults inside kernels surface at the
